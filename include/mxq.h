@@ -1,0 +1,153 @@
+/*
+ * mxq.h — C ABI of the MI355X (gfx950) FP8 / MXFP8 training-numerics library (libmxq.so).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise. The caller allocates and owns every buffer; the
+ *     library never allocates or frees device memory, never synchronizes, and keeps no mutable global state.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call returns immediately.
+ *   - Errors found on the host (NULL pointers, shapes, alignment, workspace size) return a status at once and
+ *     enqueue nothing. A failed launch returns MXQ_ERR_HIP. Device-side faults surface at the caller's next
+ *     synchronization, as with any HIP kernel.
+ *   - bf16 and fp16 tensors are passed as their 16-bit patterns (uint16_t); FP8 tensors as bytes.
+ *   - Matrices are row-major and contiguous unless a leading dimension is given. Every pointer must be
+ *     16-byte aligned and every row of a bf16 input must start on a 16-byte boundary (cols % 8 == 0).
+ *   - Buffers must not overlap, except where an argument is documented as updated in place.
+ *   - A call whose sizes make it empty (no output elements) returns MXQ_OK at once and enqueues nothing; its
+ *     data pointers may then be NULL.
+ *
+ * Formats: E4M3 is OCP E4M3FN (max 448, no infinities), E5M2 is OCP E5M2 (max 57344). Conversions round to
+ * nearest even and saturate at the largest finite value; a NaN input gives a NaN code. E8M0 scale bytes hold
+ * 2^(byte-127); byte 0xFF (NaN) marks a 32-value block holding a NaN.
+ *
+ * Sources (page titles and sections):
+ *   [OLMO11] "OLMo-core MoE, Section 11: MXFP8 Training" — Eq. 57, Eq. 58, Figures 47/49/50, Eq. 60,
+ *            Section 11.3.5 / Table 24.
+ *   [LLMSB]  "3.8 Mixed Precision, bf16 & FP8 Training" — per-tensor scaling, delayed scaling, Exercise 6.
+ *   [FP8-LM] "FP8-LM: Training FP8 Large Language Models" — tensor scaling, AdamW update, Eq. 7-8.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MXQ_OK = 0,
+    MXQ_ERR_NULL = 1,         /* a required pointer is NULL */
+    MXQ_ERR_SHAPE = 2,        /* a size is negative, or not divisible as the operation requires */
+    MXQ_ERR_ALIGN = 3,        /* a pointer is not 16-byte aligned */
+    MXQ_ERR_UNSUPPORTED = 4,  /* an enum value or combination the library does not implement */
+    MXQ_ERR_WORKSPACE = 5,    /* workspace missing or smaller than mxq_workspace_bytes() */
+    MXQ_ERR_HIP = 6           /* a HIP launch or query failed */
+} mxq_status;
+
+typedef enum { MXQ_E4M3 = 0, MXQ_E5M2 = 1 } mxq_fp8;
+typedef enum { MXQ_SCALE_RCEIL = 0, MXQ_SCALE_FLOOR = 1 } mxq_scale_rule;
+typedef enum { MXQ_PER_TENSOR = 0, MXQ_MX_BLOCK32 = 1 } mxq_scaling;
+
+/* Static, never-NULL description of a status code. */
+const char* mxq_status_string(mxq_status s);
+/* Version of this ABI; bumped on any incompatible change. */
+int mxq_abi_version(void);
+
+/*
+ * MXFP8 quantization of a bf16 matrix x[rows][cols] ([OLMO11] Section 11.2.1, Eq. 58; orientations from
+ * Section 11.3.2, Eq. 60; scale rules from Section 11.3.5, Table 24).
+ *   For each block of 32 values: amax = max |x_i|;
+ *     RCEIL: s = the smallest power of two with amax <= 448 * s;  FLOOR: s = 2^(floor(log2 amax) - 8);
+ *     the exponent is clamped to [-127, 127] (an all-zero block gets 2^-127);
+ *   q_i = E4M3(x_i / s) (exact division by a power of two, then RNE with saturation), scale byte = log2(s) + 127.
+ * Row orientation (blocks along a row):      q_row[rows][cols],  s_row[rows][cols/32]; needs cols % 32 == 0.
+ * Column orientation (blocks down a column), stored transposed so the block runs contiguously:
+ *                                            q_col[cols][rows],  s_col[cols][rows/32]; needs rows % 32 == 0.
+ * Pass NULL for both pointers of an orientation to skip it (at least one orientation is required). One pass
+ * over x emits both orientations. Storage per orientation is 33/32 bytes per value (Eq. 57).
+ */
+mxq_status mxq_quantize(const uint16_t* x_bf16, int64_t rows, int64_t cols,
+                        uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                        mxq_scale_rule rule, hipStream_t stream);
+
+/*
+ * Per-tensor current scaling ([FP8-LM] tensor scaling FP8(x) = cast(s x), x ~ FP8(x) / s; [LLMSB] per-tensor
+ * scaling and Exercise 6's to_fp8_e4m3):
+ *   amax_out[0] = max |x|   (fp32, device);
+ *   scale_out[0] = (FMAX / max(amax, 1e-12)) * margin   (fp32 IEEE division and product; FMAX = 448 for E4M3,
+ *                  57344 for E5M2), or *scale_in when scale_in != NULL (delayed scaling: amax_out is still written);
+ *   q[rows][cols] = FP8(fp32(x * s)) and q_t[cols][rows] = its transpose; either may be NULL.
+ * The scale never leaves the device. workspace: device scratch of at least mxq_workspace_bytes("pertensor", rows*cols)
+ * bytes, clobbered by the call (its contents need no initialization). amax_out and scale_out are required.
+ */
+mxq_status fp8_quantize_pertensor(const uint16_t* x_bf16, int64_t rows, int64_t cols, mxq_fp8 fmt, float margin,
+                                  const float* scale_in, float* amax_out, float* scale_out,
+                                  uint8_t* q, uint8_t* q_t, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
+ * Scaled FP8 GEMM with fp32 accumulation and a bf16 epilogue ([OLMO11] Figure 47 and Section 11.2.3:
+ * block scales applied inside the matrix operation, BF16 output; [LLMSB] Exercise 6: de-scale by 1/(s_a s_b)):
+ *   C[M][N] (row-major, leading dimension ldc >= N, in elements) = bf16_rne( A[M][K] * B[N][K]^T ).
+ *   Both operands are K-contiguous (the "TN" layout): A row i is a_q[i*K .. i*K+K), B row j is b_q[j*K ..).
+ *   PER_TENSOR: a_scale, b_scale each point to one fp32 scale s on the device (q = x*s);
+ *               C = (sum_k val(a_q) val(b_q)) / (s_a s_b). a_fmt / b_fmt may each be E4M3 or E5M2.
+ *   MX_BLOCK32: a_scale = E8M0 bytes [M][K/32], b_scale = [N][K/32]; a_fmt = b_fmt = E4M3;
+ *               C = sum_k (val(a_q) 2^(sa-127)) (val(b_q) 2^(sb-127)).
+ * Requires K % 32 == 0 and K > 0; M, N >= 1 are arbitrary; c_bf16 needs only 2-byte alignment.
+ * Accuracy: every output is within 2^-7 |y| + 2^-20 sum_k |a_k b_k| of the exact product y of the dequantized
+ * operands on the workloads measured. gfx950's FP8 matrix instructions sum the products of each 32-value block in
+ * a narrow window (small products lose low bits), so for K < 12288 the library dequantizes the operands exactly to
+ * bf16 and uses the bf16 matrix instruction (fp32-quality accumulation, half the FP8 rate); from K >= 12288 it uses
+ * the block-scaled FP8 instruction, whose error relative to the bound shrinks with K.
+ */
+mxq_status scaled_gemm(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fmt,
+                       const uint8_t* b_q, const void* b_scale, mxq_fp8 b_fmt,
+                       int64_t M, int64_t N, int64_t K, mxq_scaling scaling,
+                       uint16_t* c_bf16, int64_t ldc, hipStream_t stream);
+
+/*
+ * Grouped MX GEMM over ragged expert groups ([OLMO11] Section 11.4.1, routed experts: the up/gate and down
+ * grouped GEMMs over dispatched MXFP8 rows; Section 11.3.1 on small, uneven expert GEMMs).
+ *   group_offsets: device int64[G+1], offsets[0] = 0, non-decreasing, each a multiple of 32, offsets[G] = total_rows.
+ *   For each group g, rows [offsets[g], offsets[g+1]) of C = those rows of A times B[g]^T (MX_BLOCK32 semantics).
+ *   a_q[total_rows][K], a_s[total_rows][K/32]; b_q[G][N][K], b_s[G][N][K/32]; c_bf16[total_rows][N].
+ * Requires K % 32 == 0, N >= 1, 1 <= G <= 4096. The offsets are read on the device only (no host round trip); the
+ * host cannot check them, so offsets that break the rules above give unspecified output rows (never stray writes:
+ * rows are clamped to [0, total_rows)).
+ */
+mxq_status grouped_scaled_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* group_offsets, int64_t G,
+                               int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s,
+                               int64_t N, int64_t K, uint16_t* c_bf16, hipStream_t stream);
+
+/* Adam hyper-parameters, passed by HOST pointer. step is the 1-based step count t. */
+typedef struct {
+    float lr, beta1, beta2, eps, weight_decay;
+    int64_t step;
+} mxq_adam_hparams;
+
+/*
+ * One precision-decoupled FP8 AdamW step over n parameters held as one tensor ([FP8-LM] AdamW update rule,
+ * Eq. 7-8: first moment in FP8 with a per-tensor scale, second moment in FP16, high-precision master weight):
+ *   master (fp32, in/out), m_q (E4M3, in/out, m ~ val(m_q) / m_scale), m_scale (fp32[1], in/out), v_fp16 (in/out),
+ *   grad_bf16 (in), w_bf16 (out, bf16 copy of the updated weight; may be NULL).
+ *   m_t = b1 m + (1-b1) g;  v_t = b2 v + (1-b2) g^2;  c1 = 1/(1-b1^t), c2 = 1/(1-b2^t);
+ *   theta -= lr ((m_t c1) / (sqrt(v_t c2) + eps) + wd theta);
+ *   the new first-moment scale is 448 / max(amax(m_t), 1e-12) (current scaling), and m_q = E4M3(m_t * scale).
+ * Every fp32 operation is rounded separately (no fused multiply-add); sqrt and division are correctly rounded; the
+ * bias-correction scalars are computed on the host in double and rounded once to float.
+ * workspace: device scratch of at least mxq_workspace_bytes("adam", n) bytes, clobbered.
+ */
+mxq_status fp8_adam_step(float* master, const uint16_t* grad_bf16, uint8_t* m_q, float* m_scale,
+                         uint16_t* v_fp16, uint16_t* w_bf16, int64_t n, const mxq_adam_hparams* hp,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by op ("pertensor" or "adam") for n elements; 0 for an unknown op. op is a host string. */
+size_t mxq_workspace_bytes(const char* op, int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXQ_H */

@@ -1,0 +1,143 @@
+"""FP8 / MXFP8 training numerics on MI355X (gfx950).
+
+The functions below take torch tensors (PyTorch supplies device memory and the current HIP stream), allocate the
+outputs, and call the C ABI of libmxq.so with raw pointers. All arithmetic happens in the library's gfx950 kernels.
+
+  mx_quantize            MXFP8 row/column quantization (E4M3 payload, E8M0 scale per 32 values)
+  pertensor_quantize     per-tensor current/delayed scaling to E4M3 or E5M2 (+ transposed copy)
+  scaled_gemm            C = A B^T with FP8 operands (per-tensor or MX block scales), fp32 accumulate, bf16 out
+  grouped_scaled_gemm    the MX GEMM over ragged expert row groups
+  fp8_adam_step          precision-decoupled FP8 AdamW step (fp32 master, E4M3 m + scale, fp16 v, bf16 copy)
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _lib
+from ._lib import E4M3, E5M2, FLOOR, MX_BLOCK32, PER_TENSOR, RCEIL, AdamHParams, MXQError  # noqa: F401
+
+__all__ = ["mx_quantize", "pertensor_quantize", "scaled_gemm", "grouped_scaled_gemm", "fp8_adam_step",
+           "workspace_bytes", "MXTensor", "AdamHParams", "MXQError", "E4M3", "E5M2", "RCEIL", "FLOOR",
+           "PER_TENSOR", "MX_BLOCK32"]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> C.c_void_p:
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class MXTensor(NamedTuple):
+    """One MXFP8 tensor in both orientations: qdata and E8M0 scales travel together (either pair may be None)."""
+    q_row: Optional[torch.Tensor]   # [rows][cols] uint8, blocks of 32 along each row
+    s_row: Optional[torch.Tensor]   # [rows][cols/32] uint8
+    q_col: Optional[torch.Tensor]   # [cols][rows] uint8, blocks of 32 down each column, stored transposed
+    s_col: Optional[torch.Tensor]   # [cols][rows/32] uint8
+
+
+def workspace_bytes(op: str, n: int) -> int:
+    return int(_lib.load().mxq_workspace_bytes(op.encode(), int(n)))
+
+
+def mx_quantize(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, rule: int = RCEIL,
+                out: Optional[MXTensor] = None) -> MXTensor:
+    _dev(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    if out is None:
+        dev = x.device
+        e = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+        out = MXTensor(e(rows, cols) if rowwise else None, e(rows, cols // 32) if rowwise else None,
+                       e(cols, rows) if colwise else None, e(cols, rows // 32) if colwise else None)
+    st = _lib.load().mxq_quantize(_ptr(x), rows, cols, _ptr(out.q_row), _ptr(out.s_row), _ptr(out.q_col),
+                                  _ptr(out.s_col), rule, _stream(x.device))
+    _lib.check("mxq_quantize", st)
+    return out
+
+
+class PerTensorFP8(NamedTuple):
+    q: Optional[torch.Tensor]       # [rows][cols] uint8
+    q_t: Optional[torch.Tensor]     # [cols][rows] uint8
+    amax: torch.Tensor              # float32[1] on the device
+    scale: torch.Tensor             # float32[1] on the device (q ~ x * scale)
+
+
+def pertensor_quantize(x: torch.Tensor, fmt: int = E4M3, margin: float = 1.0, scale_in: Optional[torch.Tensor] = None,
+                       want_q: bool = True, want_qt: bool = True, workspace: Optional[torch.Tensor] = None) -> PerTensorFP8:
+    _dev(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    dev = x.device
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev) if want_q else None
+    qt = torch.empty((cols, rows), dtype=torch.uint8, device=dev) if want_qt else None
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    nbytes = workspace_bytes("pertensor", rows * cols)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if scale_in is not None:
+        _dev(scale_in, torch.float32, "scale_in")
+    st = _lib.load().fp8_quantize_pertensor(_ptr(x), rows, cols, fmt, C.c_float(margin), _ptr(scale_in), _ptr(amax),
+                                            _ptr(scale), _ptr(q), _ptr(qt), _ptr(workspace), workspace.numel(),
+                                            _stream(dev))
+    _lib.check("fp8_quantize_pertensor", st)
+    return PerTensorFP8(q, qt, amax, scale)
+
+
+def scaled_gemm(a_q: torch.Tensor, a_scale: torch.Tensor, b_q: torch.Tensor, b_scale: torch.Tensor,
+                scaling: int = MX_BLOCK32, a_fmt: int = E4M3, b_fmt: int = E4M3,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C[M][N] = A[M][K] B[N][K]^T in bf16. MX: scales are E8M0 grids [M][K/32], [N][K/32]; per-tensor: float32[1]."""
+    _dev(a_q, torch.uint8, "a_q"); _dev(b_q, torch.uint8, "b_q")
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    if b_q.shape[1] != K:
+        raise ValueError("a_q and b_q must share K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+    ldc = out.stride(0)
+    st = _lib.load().scaled_gemm(_ptr(a_q), _ptr(a_scale), a_fmt, _ptr(b_q), _ptr(b_scale), b_fmt, M, N, K, scaling,
+                                 _ptr(out), ldc, _stream(a_q.device))
+    _lib.check("scaled_gemm", st)
+    return out
+
+
+def grouped_scaled_gemm(a_q: torch.Tensor, a_s: torch.Tensor, offsets: torch.Tensor, b_q: torch.Tensor,
+                        b_s: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _dev(a_q, torch.uint8, "a_q"); _dev(b_q, torch.uint8, "b_q"); _dev(offsets, torch.int64, "offsets")
+    total, K = a_q.shape
+    G, N, Kb = b_q.shape
+    if Kb != K or offsets.numel() != G + 1:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((total, N), dtype=torch.bfloat16, device=a_q.device)
+    st = _lib.load().grouped_scaled_gemm(_ptr(a_q), _ptr(a_s), _ptr(offsets), G, total, _ptr(b_q), _ptr(b_s), N, K,
+                                         _ptr(out), _stream(a_q.device))
+    _lib.check("grouped_scaled_gemm", st)
+    return out
+
+
+def fp8_adam_step(master: torch.Tensor, grad: torch.Tensor, m_q: torch.Tensor, m_scale: torch.Tensor,
+                  v: torch.Tensor, w: Optional[torch.Tensor], hp: AdamHParams,
+                  workspace: Optional[torch.Tensor] = None) -> None:
+    """In place on master, m_q, m_scale, v; writes w (bf16 copy) when given."""
+    _dev(master, torch.float32, "master"); _dev(grad, torch.bfloat16, "grad"); _dev(m_q, torch.uint8, "m_q")
+    _dev(m_scale, torch.float32, "m_scale"); _dev(v, torch.float16, "v")
+    n = master.numel()
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes("adam", n), dtype=torch.uint8, device=master.device)
+    st = _lib.load().fp8_adam_step(_ptr(master), _ptr(grad), _ptr(m_q), _ptr(m_scale), _ptr(v), _ptr(w), n,
+                                   C.byref(hp), _ptr(workspace), workspace.numel(), _stream(master.device))
+    _lib.check("fp8_adam_step", st)

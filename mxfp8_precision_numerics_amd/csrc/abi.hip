@@ -1,0 +1,144 @@
+// C ABI of libmxq (declared in include/mxq.h): argument validation on the host, then kernel launches.
+// Validation happens before any HIP call, so every error path returns without touching the device.
+#include <stdint.h>
+#include <string.h>
+
+#include "launch.h"
+#include "mxq.h"
+
+namespace {
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+mxq_status hip_status(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_HIP; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t pertensor_ws(int64_t n) { return round_up((size_t)mxq::pertensor_amax_parts(n) * 4u, 256); }
+size_t adam_ws(int64_t n) { return round_up((size_t)mxq::adam_parts(n) * 4u, 256) + 256; }
+
+constexpr int64_t kMaxGridY = 65535;
+
+}  // namespace
+
+extern "C" {
+
+const char* mxq_status_string(mxq_status s) {
+    switch (s) {
+        case MXQ_OK: return "ok";
+        case MXQ_ERR_NULL: return "a required pointer is NULL";
+        case MXQ_ERR_SHAPE: return "a size is negative or not divisible as the operation requires";
+        case MXQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case MXQ_ERR_UNSUPPORTED: return "unsupported format, rule or scaling mode";
+        case MXQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case MXQ_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int mxq_abi_version(void) { return 1; }
+
+size_t mxq_workspace_bytes(const char* op, int64_t n) {
+    if (!op || n < 0) return 0;
+    if (strcmp(op, "pertensor") == 0) return pertensor_ws(n);
+    if (strcmp(op, "adam") == 0) return adam_ws(n);
+    return 0;
+}
+
+mxq_status mxq_quantize(const uint16_t* x_bf16, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
+                        uint8_t* q_col, uint8_t* s_col, mxq_scale_rule rule, hipStream_t stream) {
+    if ((q_row == nullptr) != (s_row == nullptr) || (q_col == nullptr) != (s_col == nullptr)) return MXQ_ERR_NULL;
+    const bool row = q_row != nullptr, col = q_col != nullptr;
+    if (!row && !col) return MXQ_ERR_NULL;
+    if (rule != MXQ_SCALE_RCEIL && rule != MXQ_SCALE_FLOOR) return MXQ_ERR_UNSUPPORTED;
+    if (rows < 0 || cols < 0 || cols % 8 != 0) return MXQ_ERR_SHAPE;
+    if ((row && cols % 32 != 0) || (col && rows % 32 != 0)) return MXQ_ERR_SHAPE;
+    if ((rows + 127) / 128 > kMaxGridY) return MXQ_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;                 // empty: nothing to read or write
+    if (!x_bf16) return MXQ_ERR_NULL;
+    if (!al16(x_bf16) || (row && !al16(q_row)) || (col && !al16(q_col))) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_mx_quantize(x_bf16, rows, cols, q_row, s_row, q_col, s_col, (int)rule, stream));
+}
+
+mxq_status fp8_quantize_pertensor(const uint16_t* x_bf16, int64_t rows, int64_t cols, mxq_fp8 fmt, float margin,
+                                  const float* scale_in, float* amax_out, float* scale_out, uint8_t* q, uint8_t* q_t,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!amax_out || !scale_out) return MXQ_ERR_NULL;
+    if (fmt != MXQ_E4M3 && fmt != MXQ_E5M2) return MXQ_ERR_UNSUPPORTED;
+    if (rows < 0 || cols < 0 || cols % 8 != 0) return MXQ_ERR_SHAPE;
+    if (q_t && rows % 32 != 0) return MXQ_ERR_SHAPE;
+    if ((rows + 127) / 128 > kMaxGridY) return MXQ_ERR_SHAPE;
+    if (rows * cols > 0 && !x_bf16) return MXQ_ERR_NULL;       // an empty x still yields amax 0 and its scale
+    if (!al16(x_bf16) || (q && !al16(q)) || (q_t && !al16(q_t))) return MXQ_ERR_ALIGN;
+    if (!al4(amax_out) || !al4(scale_out) || (scale_in && !al4(scale_in))) return MXQ_ERR_ALIGN;
+    const int64_t n = rows * cols;
+    if (!workspace || workspace_bytes < pertensor_ws(n)) return MXQ_ERR_WORKSPACE;
+    if (!al16(workspace)) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_pertensor_quantize(x_bf16, rows, cols, (int)fmt, margin, scale_in, amax_out,
+                                                     scale_out, q, q_t, static_cast<uint32_t*>(workspace), stream));
+}
+
+mxq_status scaled_gemm(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fmt, const uint8_t* b_q,
+                       const void* b_scale, mxq_fp8 b_fmt, int64_t M, int64_t N, int64_t K, mxq_scaling scaling,
+                       uint16_t* c_bf16, int64_t ldc, hipStream_t stream) {
+    if (scaling != MXQ_PER_TENSOR && scaling != MXQ_MX_BLOCK32) return MXQ_ERR_UNSUPPORTED;
+    if ((a_fmt != MXQ_E4M3 && a_fmt != MXQ_E5M2) || (b_fmt != MXQ_E4M3 && b_fmt != MXQ_E5M2)) return MXQ_ERR_UNSUPPORTED;
+    if (scaling == MXQ_MX_BLOCK32 && (a_fmt != MXQ_E4M3 || b_fmt != MXQ_E4M3)) return MXQ_ERR_UNSUPPORTED;
+    if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || ldc < N) return MXQ_ERR_SHAPE;
+    if (M == 0 || N == 0) return MXQ_OK;                       // empty output: nothing enqueued
+    if (!a_q || !b_q || !a_scale || !b_scale || !c_bf16) return MXQ_ERR_NULL;
+    if (!al16(a_q) || !al16(b_q) || (reinterpret_cast<uintptr_t>(c_bf16) & 1u)) return MXQ_ERR_ALIGN;
+    if (scaling == MXQ_MX_BLOCK32 ? (!al16(a_scale) || !al16(b_scale)) : (!al4(a_scale) || !al4(b_scale)))
+        return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_scaled_gemm(a_q, a_scale, (int)a_fmt, b_q, b_scale, (int)b_fmt, M, N, K,
+                                              scaling == MXQ_MX_BLOCK32 ? 1 : 0, c_bf16, ldc, stream));
+}
+
+mxq_status grouped_scaled_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* group_offsets, int64_t G,
+                               int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s, int64_t N, int64_t K,
+                               uint16_t* c_bf16, hipStream_t stream) {
+    if (G < 1 || G > 4096 || total_rows < 0 || N < 1 || K <= 0 || K % 32 != 0) return MXQ_ERR_SHAPE;
+    if (!group_offsets || !b_q || !b_s) return MXQ_ERR_NULL;
+    if (total_rows == 0) return MXQ_OK;
+    if (!a_q || !a_s || !c_bf16) return MXQ_ERR_NULL;
+    if (!al16(a_q) || !al16(a_s) || !al16(b_q) || !al16(b_s) || (reinterpret_cast<uintptr_t>(c_bf16) & 1u) ||
+        (reinterpret_cast<uintptr_t>(group_offsets) & 7u))
+        return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_grouped_gemm(a_q, a_s, group_offsets, G, total_rows, b_q, b_s, N, K, c_bf16, stream));
+}
+
+mxq_status fp8_adam_step(float* master, const uint16_t* grad_bf16, uint8_t* m_q, float* m_scale, uint16_t* v_fp16,
+                         uint16_t* w_bf16, int64_t n, const mxq_adam_hparams* hp, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    if (!hp) return MXQ_ERR_NULL;
+    if (n < 0 || hp->step < 1) return MXQ_ERR_SHAPE;
+    if (n == 0) return MXQ_OK;                                 // empty: no element and no scale changes
+    if (!master || !grad_bf16 || !m_q || !m_scale || !v_fp16) return MXQ_ERR_NULL;
+    if (!al16(master) || !al16(grad_bf16) || !al16(m_q) || !al16(v_fp16) || (w_bf16 && !al16(w_bf16)) || !al4(m_scale))
+        return MXQ_ERR_ALIGN;
+    if (!workspace || workspace_bytes < adam_ws(n)) return MXQ_ERR_WORKSPACE;
+    if (!al16(workspace)) return MXQ_ERR_ALIGN;
+    // Host scalars in double, each rounded once to float. beta^t is the product of t factors (it reaches 0 long
+    // before t is large, after which further factors change nothing).
+    double p1 = 1.0, p2 = 1.0;
+    for (int64_t t = 0; t < hp->step && (p1 != 0.0 || p2 != 0.0); ++t) {
+        p1 *= (double)hp->beta1;
+        p2 *= (double)hp->beta2;
+    }
+    mxq::AdamConsts k;
+    k.b1 = hp->beta1;
+    k.ob1 = (float)(1.0 - (double)hp->beta1);
+    k.b2 = hp->beta2;
+    k.ob2 = (float)(1.0 - (double)hp->beta2);
+    k.c1 = (float)(1.0 / (1.0 - p1));
+    k.c2 = (float)(1.0 / (1.0 - p2));
+    k.lr = hp->lr;
+    k.eps = hp->eps;
+    k.wd = hp->weight_decay;
+    const size_t part_bytes = round_up((size_t)mxq::adam_parts(n) * 4u, 256);
+    uint32_t* partial = static_cast<uint32_t*>(workspace);
+    float* consts = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + part_bytes);
+    return hip_status(mxq::launch_adam(master, grad_bf16, m_q, m_scale, v_fp16, w_bf16, n, k, partial, consts, stream));
+}
+
+}  // extern "C"

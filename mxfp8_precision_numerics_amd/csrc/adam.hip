@@ -1,0 +1,197 @@
+// Precision-decoupled FP8 AdamW step for gfx950 ("FP8-LM: Training FP8 Large Language Models", AdamW update rule
+// and Eq. 7-8: first moment in FP8 with a per-tensor scale, second moment in FP16, high-precision master weight).
+//
+// Pass 1 forms m_t = b1 m_{t-1} + (1-b1) g for every element and reduces max |m_t| (per-workgroup partials).
+// A one-workgroup finalize turns it into the new first-moment scale 448 / max(amax, 1e-12) (current scaling).
+// Pass 2 recomputes m_t and v_t, applies the bias-corrected update to the fp32 master weight and stores
+// theta (fp32), m (E4M3 at the new scale), v (fp16) and the bf16 weight copy. Both passes are HBM-bound streams;
+// each thread moves 8 elements per iteration with 16-byte accesses.
+//
+// Every fp32 operation is rounded on its own: contraction into fused multiply-adds is disabled for this file,
+// and sqrt and division are the correctly rounded library forms.
+#pragma clang fp contract(off)
+#include "mxq_device.h"
+#include "launch.h"
+
+namespace mxq {
+
+constexpr int ATHREADS = 256;
+
+// Exact E4M3 (OCP E4M3FN) decode from the bit fields.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    const uint32_t s = (c & 0x80u) << 24, e = (c >> 3) & 15u, m = c & 7u;
+    if (e == 15u && m == 7u) return __uint_as_float(s | 0x7FC00000u);
+    if (e == 0u) return __uint_as_float(s | __float_as_uint((float)m * 0.001953125f));   // m * 2^-9, exact
+    return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ void adam_moments(const AdamConsts& k, float inv_s, uint32_t g16, uint32_t mq, uint32_t v16,
+                                             float& m, float& v) {
+    const float g = __uint_as_float(g16 << 16);
+    const float m_old = e4m3_to_f32(mq) * inv_s;
+    const float v_old = f16_to_f32(v16);
+    const float t1 = k.b1 * m_old;
+    const float t2 = k.ob1 * g;
+    m = t1 + t2;
+    const float gg = g * g;
+    const float t3 = k.b2 * v_old;
+    const float t4 = k.ob2 * gg;
+    v = t3 + t4;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
+    __shared__ uint32_t sh[ATHREADS / 64];
+    v = wave_max_u32(v);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        for (int i = 1; i < ATHREADS / 64; ++i) v = max(v, sh[i]);
+    return v;
+}
+
+// |m_t| as an fp32 bit pattern; unsigned comparison of magnitudes orders them, with NaN above infinity.
+__global__ __launch_bounds__(ATHREADS) void adam_amax_kernel(const uint16_t* __restrict__ g, const uint8_t* __restrict__ mq,
+                                                            const float* __restrict__ m_scale, int64_t n, AdamConsts k,
+                                                            uint32_t* __restrict__ partial) {
+    const float inv_s = 1.0f / m_scale[0];
+    uint32_t mx = 0;
+    const int64_t chunks = n / 8;
+    const int64_t stride = (int64_t)gridDim.x * ATHREADS;
+    for (int64_t i = (int64_t)blockIdx.x * ATHREADS + threadIdx.x; i < chunks; i += stride) {
+        const uint4 gv = ldnt16(g + 8 * i);
+        const uint2 mv = ldnt8(mq + 8 * i);
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t g16 = (gw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const uint32_t m8 = ((e < 4 ? mv.x : mv.y) >> (8 * (e & 3))) & 0xFFu;
+            float m, v;
+            adam_moments(k, inv_s, g16, m8, 0u, m, v);
+            mx = max(mx, __float_as_uint(m) & 0x7FFFFFFFu);
+        }
+    }
+    if (blockIdx.x == 0)
+        for (int64_t i = chunks * 8 + threadIdx.x; i < n; i += ATHREADS) {
+            float m, v;
+            adam_moments(k, inv_s, g[i], mq[i], 0u, m, v);
+            mx = max(mx, __float_as_uint(m) & 0x7FFFFFFFu);
+        }
+    mx = block_max_u32(mx);
+    if (threadIdx.x == 0) partial[blockIdx.x] = mx;
+}
+
+// consts[0] = 1 / s_old, consts[1] = s_new; m_scale[0] <- s_new.
+__global__ __launch_bounds__(ATHREADS) void adam_finalize_kernel(const uint32_t* __restrict__ partial, int nparts,
+                                                                float* __restrict__ m_scale, float* __restrict__ consts) {
+    uint32_t mx = 0;
+    for (int i = threadIdx.x; i < nparts; i += ATHREADS) mx = max(mx, partial[i]);
+    mx = block_max_u32(mx);
+    if (threadIdx.x == 0) {
+        const float amax = __uint_as_float(mx);
+        const float a = amax < 1e-12f ? 1e-12f : amax;
+        const float s_new = 448.0f / a;
+        consts[0] = 1.0f / m_scale[0];
+        consts[1] = s_new;
+        consts[2] = amax;
+        m_scale[0] = s_new;
+    }
+}
+
+__device__ __forceinline__ void adam_one(const AdamConsts& k, float inv_s, float s_new, float theta, uint32_t g16,
+                                         uint32_t mq, uint32_t v16, float& theta_out, uint32_t& m_code, uint32_t& v_out,
+                                         uint32_t& w_out) {
+    float m, v;
+    adam_moments(k, inv_s, g16, mq, v16, m, v);
+    const float mh = m * k.c1;
+    const float vh = v * k.c2;
+    const float den = __builtin_sqrtf(vh) + k.eps;
+    float u = mh / den;
+    if (k.wd != 0.0f) {
+        const float dec = k.wd * theta;
+        u = u + dec;
+    }
+    const float step = k.lr * u;
+    theta_out = theta - step;
+    const float ms = clamp_keep_nan(m * s_new, 448.0f);
+    m_code = cvt_f32_pair<FMT_E4M3, false>(0u, ms, 0.0f) & 0xFFu;
+    v_out = __builtin_bit_cast(uint16_t, (_Float16)v);
+    w_out = __builtin_bit_cast(uint16_t, (__bf16)theta_out);
+}
+
+__global__ __launch_bounds__(ATHREADS) void adam_update_kernel(float* __restrict__ master, const uint16_t* __restrict__ g,
+                                                              uint8_t* __restrict__ mq, uint16_t* __restrict__ v16,
+                                                              uint16_t* __restrict__ w, int64_t n, AdamConsts k,
+                                                              const float* __restrict__ consts) {
+    const float inv_s = consts[0], s_new = consts[1];
+    const int64_t chunks = n / 8;
+    const int64_t stride = (int64_t)gridDim.x * ATHREADS;
+    for (int64_t i = (int64_t)blockIdx.x * ATHREADS + threadIdx.x; i < chunks; i += stride) {
+        const uint4 t0 = ldnt16(master + 8 * i);
+        const uint4 t1 = ldnt16(master + 8 * i + 4);
+        const uint4 gv = ldnt16(g + 8 * i);
+        const uint2 mv = ldnt8(mq + 8 * i);
+        const uint4 vv = ldnt16(v16 + 8 * i);
+        const uint32_t th[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+        const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+        uint32_t th_o[8], vo[4] = {0, 0, 0, 0}, wo[4] = {0, 0, 0, 0}, mo[2] = {0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t g16 = (gw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const uint32_t v_16 = (vw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const uint32_t m8 = ((e < 4 ? mv.x : mv.y) >> (8 * (e & 3))) & 0xFFu;
+            float t_out;
+            uint32_t mc, vout, wout;
+            adam_one(k, inv_s, s_new, __uint_as_float(th[e]), g16, m8, v_16, t_out, mc, vout, wout);
+            th_o[e] = __float_as_uint(t_out);
+            mo[e >> 2] |= mc << (8 * (e & 3));
+            vo[e >> 1] |= vout << (16 * (e & 1));
+            wo[e >> 1] |= wout << (16 * (e & 1));
+        }
+        stnt16(master + 8 * i, make_uint4(th_o[0], th_o[1], th_o[2], th_o[3]));
+        stnt16(master + 8 * i + 4, make_uint4(th_o[4], th_o[5], th_o[6], th_o[7]));
+        stnt8(mq + 8 * i, make_uint2(mo[0], mo[1]));
+        stnt16(v16 + 8 * i, make_uint4(vo[0], vo[1], vo[2], vo[3]));
+        if (w) stnt16(w + 8 * i, make_uint4(wo[0], wo[1], wo[2], wo[3]));
+    }
+    if (blockIdx.x == 0)
+        for (int64_t i = chunks * 8 + threadIdx.x; i < n; i += ATHREADS) {
+            float t_out;
+            uint32_t mc, vout, wout;
+            adam_one(k, inv_s, s_new, master[i], g[i], mq[i], v16[i], t_out, mc, vout, wout);
+            master[i] = t_out;
+            mq[i] = (uint8_t)mc;
+            v16[i] = (uint16_t)vout;
+            if (w) w[i] = (uint16_t)wout;
+        }
+}
+
+int adam_parts(int64_t n) {
+    int64_t chunks = (n + 7) / 8;
+    int64_t parts = (chunks + ATHREADS * 4 - 1) / (ATHREADS * 4);
+    if (parts < 1) parts = 1;
+    if (parts > 4096) parts = 4096;
+    return (int)parts;
+}
+
+hipError_t launch_adam(float* master, const uint16_t* grad, uint8_t* m_q, float* m_scale, uint16_t* v16, uint16_t* w,
+                       int64_t n, const AdamConsts& k, uint32_t* partial, float* consts, hipStream_t stream) {
+    const int parts = adam_parts(n);
+    hipLaunchKernelGGL(adam_amax_kernel, dim3(parts), dim3(ATHREADS), 0, stream, grad, m_q, m_scale, n, k, partial);
+    hipLaunchKernelGGL(adam_finalize_kernel, dim3(1), dim3(ATHREADS), 0, stream, partial, parts, m_scale, consts);
+    hipLaunchKernelGGL(adam_update_kernel, dim3(parts), dim3(ATHREADS), 0, stream, master, grad, m_q, v16, w, n, k,
+                       (const float*)consts);
+    return hipGetLastError();
+}
+
+}  // namespace mxq

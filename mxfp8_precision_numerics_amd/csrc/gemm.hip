@@ -1,0 +1,379 @@
+// Scaled FP8 GEMM for gfx950: C[M][N] (bf16) = A[M][K] * B[N][K]^T with fp32 accumulation.
+//
+// MX_BLOCK32 applies one E8M0 scale per 32 values along K inside the matrix instruction ("OLMo-core MoE,
+// Section 11: MXFP8 Training", Figure 47 and Section 11.2.3: native block-scaled GEMM, BF16 operator output).
+// PER_TENSOR multiplies the fp32 accumulator by 1 / (s_a s_b) ("3.8 Mixed Precision, bf16 & FP8 Training",
+// Exercise 6: de-scale by 1/(s_x s_w)). The grouped variant runs the same tiles over ragged expert row groups
+// (Section 11.4.1, routed experts).
+//
+// Matrix instruction: v_mfma_scale_f32_32x32x64_f8f6f4. Operand layout (per lane l, g = l / 32): row l % 32;
+// bytes 0-15 hold k = 16g .. 16g+15 and bytes 16-31 hold k = 32+16g .. 32+16g+15 of the 64-wide K window. The
+// E8M0 scale for (row r, 32-block b of the window) comes from lane r + 32b, byte chosen by op_sel. Output: lane l,
+// register j -> row 8(j/4) + 4g + j%4, column l % 32. The kernel feeds B as the instruction's first operand and A
+// as its second, so a lane's four consecutive accumulator registers are four consecutive n of one output row m
+// (8-byte bf16 stores).
+//
+// Tiling: 256 threads (4 waves, 2 x 2), a 128 x 128 output tile, waves own 64 x 64 (2 x 2 instructions).
+// K advances 128 bytes per stage; stages are double-buffered in LDS. LDS rows are 128 bytes with the 16-byte chunk
+// index XOR-swizzled by (row & 7), so the 16-byte fragment reads of 8 consecutive rows hit distinct banks.
+#include "mxq_device.h"
+#include "launch.h"
+
+namespace mxq {
+
+constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int GTHREADS = 256;
+constexpr int GROUP_M = 8;
+
+struct GemmArgs {
+    const uint8_t* a;
+    const uint8_t* b;
+    const uint8_t* sa;   // MX: [rows][K/32]
+    const uint8_t* sb;   // MX: [N][K/32] (per group when grouped)
+    const float* pa;     // per-tensor scales
+    const float* pb;
+    uint16_t* c;
+    int64_t M, N, K, ldc;
+    const int64_t* offsets;   // grouped only: [G+1]
+    int64_t G;
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+
+// 8 FP8 codes (E4M3 when FMT == 0, E5M2 when 1) -> 8 bf16 equal to code * 2^E, where E is the exponent field of
+// `scale` (exact whenever the product is representable in bf16).
+template <int FMT>
+__device__ __forceinline__ v8bf dequant8_bf16(uint2 x, float scale) {
+    v2bf_t p0, p1, p2, p3;
+    if constexpr (FMT == 0) {
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x.x, scale, false);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x.x, scale, true);
+        p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x.y, scale, false);
+        p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x.y, scale, true);
+    } else {
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)x.x, scale, false);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)x.x, scale, true);
+        p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)x.y, scale, false);
+        p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)x.y, scale, true);
+    }
+    return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+template <bool MX, int FA, int FB, bool GROUPED, int MF>
+__global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * BK];
+    __shared__ uint32_t sSA[2][BM];
+    __shared__ uint32_t sSB[2][BN];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int64_t K = g.K;
+    const int64_t kblocks = K / 32;
+    const int tiles_n = (int)((g.N + BN - 1) / BN);
+
+    // ------------------------------------------------------------------ tile -> (rows, n0)
+    int64_t m0, m_end, n0;
+    const uint8_t* Bq = g.b;
+    const uint8_t* Bs = g.sb;
+    if constexpr (GROUPED) {
+        const int64_t bid = blockIdx.x;
+        const int64_t t = bid / tiles_n;
+        n0 = (bid % tiles_n) * BN;
+        int64_t acc = 0, grp = -1, lo = 0, hi = 0;
+        for (int64_t q = 0; q < g.G; ++q) {
+            int64_t a0 = g.offsets[q], a1 = g.offsets[q + 1];
+            a0 = a0 < 0 ? 0 : (a0 > g.M ? g.M : a0);
+            a1 = a1 < a0 ? a0 : (a1 > g.M ? g.M : a1);
+            int64_t nt = (a1 - a0 + BM - 1) / BM;
+            if (t < acc + nt) { grp = q; lo = a0 + (t - acc) * BM; hi = a1; break; }
+            acc += nt;
+        }
+        if (grp < 0) return;                          // more workgroups than tiles: nothing to do
+        m0 = lo;
+        m_end = (lo + BM < hi) ? lo + BM : hi;
+        Bq = g.b + grp * g.N * K;
+        Bs = MX ? g.sb + grp * g.N * kblocks : nullptr;
+    } else {
+        const int tiles_m = (int)((g.M + BM - 1) / BM);
+        const int bid = blockIdx.x;
+        const int per_group = GROUP_M * tiles_n;
+        const int first_m = (bid / per_group) * GROUP_M;
+        const int gm = min(GROUP_M, tiles_m - first_m);
+        const int r = bid % per_group;
+        m0 = (int64_t)(first_m + r % gm) * BM;
+        n0 = (int64_t)(r / gm) * BN;
+        m_end = (m0 + BM < g.M) ? m0 + BM : g.M;
+    }
+    const int64_t n_end = (n0 + BN < g.N) ? n0 + BN : g.N;
+
+    // ------------------------------------------------------------------ global -> registers (one stage)
+    uint4 ra[4], rb[4];
+    uint32_t rs = 0x7F7F7F7Fu;
+    const bool scale_dword = (kblocks & 3) == 0;
+
+    auto load_stage = [&](int64_t k0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = (tid >> 3) + 32 * j, ch = tid & 7;
+            const int64_t kk = k0 + ch * 16;
+            const int64_t ar = m0 + row, br = n0 + row;
+            ra[j] = (ar < m_end && kk < K) ? *reinterpret_cast<const uint4*>(g.a + ar * K + kk) : make_uint4(0, 0, 0, 0);
+            rb[j] = (br < n_end && kk < K) ? *reinterpret_cast<const uint4*>(Bq + br * K + kk) : make_uint4(0, 0, 0, 0);
+        }
+        if constexpr (MX) {
+            const int row = tid & 127;
+            const bool isA = tid < 128;
+            const int64_t rr = isA ? m0 + row : n0 + row;
+            const bool ok = isA ? rr < m_end : rr < n_end;
+            const uint8_t* sp = isA ? g.sa : Bs;
+            const int64_t kb = k0 / 32;
+            if (ok && scale_dword && kb + 4 <= kblocks) {
+                rs = *reinterpret_cast<const uint32_t*>(sp + rr * kblocks + kb);
+            } else {
+                uint32_t v = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t byte = (ok && kb + i < kblocks) ? sp[rr * kblocks + kb + i] : 127u;
+                    v |= byte << (8 * i);
+                }
+                rs = v;
+            }
+        }
+    };
+    auto store_stage = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = (tid >> 3) + 32 * j, ch = tid & 7;
+            *reinterpret_cast<uint4*>(&sA[buf][swz(row, ch)]) = ra[j];
+            *reinterpret_cast<uint4*>(&sB[buf][swz(row, ch)]) = rb[j];
+        }
+        if constexpr (MX) {
+            if (tid < 128) sSA[buf][tid] = rs; else sSB[buf][tid - 128] = rs;
+        }
+    };
+
+    // accumulators: MF 0 -> 2 x 2 tiles of 32x32 (16 regs); MF 1 -> 4 x 4 tiles of 16x16 (4 regs)
+    v16f acc[2][2];
+    v4f acc4[4][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc4[i][j] = v4f{};
+
+    const int nk = (int)((K + BK - 1) / BK);
+    const int fr = lane & 31, fg = lane >> 5;
+
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) load_stage((int64_t)(kt + 1) * BK);
+
+        if constexpr (MF == 0) {
+            uint32_t sa_reg[2], sb_reg[2];
+            if constexpr (MX) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) sa_reg[j] = sSA[buf][wm * 64 + j * 32 + fr] >> (8 * fg);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) sb_reg[i] = sSB[buf][wn * 64 + i * 32 + fr] >> (8 * fg);
+            } else {
+                sa_reg[0] = sa_reg[1] = sb_reg[0] = sb_reg[1] = 0x7F7F7F7Fu;
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                v8i fa[2], fb[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int row = wm * 64 + j * 32 + fr;
+                    uint4 x0 = *reinterpret_cast<const uint4*>(&sA[buf][swz(row, 4 * h + fg)]);
+                    uint4 x1 = *reinterpret_cast<const uint4*>(&sA[buf][swz(row, 4 * h + 2 + fg)]);
+                    fa[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int row = wn * 64 + i * 32 + fr;
+                    uint4 x0 = *reinterpret_cast<const uint4*>(&sB[buf][swz(row, 4 * h + fg)]);
+                    uint4 x1 = *reinterpret_cast<const uint4*>(&sB[buf][swz(row, 4 * h + 2 + fg)]);
+                    fb[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        if (h == 0)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 0,
+                                                                                       (int)sb_reg[i], 0, (int)sa_reg[j]);
+                        else
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 2,
+                                                                                       (int)sb_reg[i], 2, (int)sa_reg[j]);
+                    }
+            }
+        } else if constexpr (MF == 2) {
+            // Exact-accumulation variant: dequantize the FP8 codes (times their E8M0 block scale) to bf16 in
+            // registers and use v_mfma_f32_32x32x16_bf16 (lane l: row l % 32, k = 8(l/32) .. +7 of a 16-wide window).
+            // Window t of the 128-byte stage is LDS chunk t; lane half g reads its bytes 8g .. 8g+7.
+            uint32_t sa_w[2], sb_w[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) sa_w[j] = MX ? sSA[buf][wm * 64 + j * 32 + fr] : 0x7F7F7F7Fu;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) sb_w[i] = MX ? sSB[buf][wn * 64 + i * 32 + fr] : 0x7F7F7F7Fu;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                v8bf fa[2], fb[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int row = wm * 64 + j * 32 + fr;
+                    const uint2 x = *reinterpret_cast<const uint2*>(&sA[buf][swz(row, t) + 8 * fg]);
+                    fa[j] = dequant8_bf16<FA>(x, scale_operand((sa_w[j] >> (8 * (t >> 1))) & 0xFFu));
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int row = wn * 64 + i * 32 + fr;
+                    const uint2 x = *reinterpret_cast<const uint2*>(&sB[buf][swz(row, t) + 8 * fg]);
+                    fb[i] = dequant8_bf16<FB>(x, scale_operand((sb_w[i] >> (8 * (t >> 1))) & 0xFFu));
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[j], acc[i][j], 0, 0, 0);
+            }
+        } else {
+            // 16x16x128: lane l holds row l % 16; bytes 0-15 = k 16q..16q+15, bytes 16-31 = k 64+16q.. (q = l / 16);
+            // its scale byte is block q of that row.
+            const int r16 = lane & 15, q16 = lane >> 4;
+            uint32_t sa_reg[4], sb_reg[4];
+            v8i fa[4], fb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = wm * 64 + j * 16 + r16;
+                sa_reg[j] = MX ? (sSA[buf][row] >> (8 * q16)) : 0x7F7F7F7Fu;
+                uint4 x0 = *reinterpret_cast<const uint4*>(&sA[buf][swz(row, q16)]);
+                uint4 x1 = *reinterpret_cast<const uint4*>(&sA[buf][swz(row, 4 + q16)]);
+                fa[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = wn * 64 + i * 16 + r16;
+                sb_reg[i] = MX ? (sSB[buf][row] >> (8 * q16)) : 0x7F7F7F7Fu;
+                uint4 x0 = *reinterpret_cast<const uint4*>(&sB[buf][swz(row, q16)]);
+                uint4 x1 = *reinterpret_cast<const uint4*>(&sB[buf][swz(row, 4 + q16)]);
+                fb[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc4[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[i], fa[j], acc4[i][j], FB, FA, 0,
+                                                                                 (int)sb_reg[i], 0, (int)sa_reg[j]);
+        }
+
+        if (kt + 1 < nk) store_stage(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ------------------------------------------------------------------ epilogue: fp32 -> bf16, store
+    float post = 1.0f;
+    if constexpr (!MX) post = 1.0f / (g.pa[0] * g.pb[0]);
+    const bool vec_ok = (g.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 7) == 0;
+    auto store4 = [&](int64_t m, int64_t n, float v0, float v1, float v2, float v3) {
+        if (m >= m_end) return;
+        float v[4] = {v0, v1, v2, v3};
+        uint16_t h4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float x = v[e];
+            if constexpr (!MX) x = x * post;
+            h4[e] = __builtin_bit_cast(uint16_t, (__bf16)x);
+        }
+        uint16_t* dst = g.c + m * g.ldc + n;
+        if (vec_ok && n + 4 <= n_end) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)h4[0] | ((uint32_t)h4[1] << 16),
+                                                        (uint32_t)h4[2] | ((uint32_t)h4[3] << 16));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n + e < n_end) dst[e] = h4[e];
+        }
+    };
+    if constexpr (MF == 0 || MF == 2) {
+        // 32x32 output: lane -> m = l % 32; register 4q+e -> n = 8q + 4(l/32) + e
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    store4(m0 + wm * 64 + j * 32 + fr, n0 + wn * 64 + i * 32 + 8 * q + 4 * fg, acc[i][j][4 * q],
+                           acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    } else {
+        // 16x16 output: lane -> m = l % 16; register e -> n = 4(l/16) + e
+        const int r16 = lane & 15, q16 = lane >> 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                store4(m0 + wm * 64 + j * 16 + r16, n0 + wn * 64 + i * 16 + 4 * q16, acc4[i][j][0], acc4[i][j][1],
+                       acc4[i][j][2], acc4[i][j][3]);
+    }
+}
+
+// Path selection. The FP8 matrix instructions (v_mfma_*_f8f6f4 and the older *_fp8_fp8 forms) sum the products of
+// one 32-value block with a narrow internal window: products far below the block's largest lose low-order bits,
+// an error of up to ~2^-12 of sum |a b| per instruction on wide-range data, while block sums and the fp32
+// accumulator input are combined exactly. The bf16 instruction accumulates at fp32 quality. Measured on MX-quantized
+// N(0,1) operands against the bound |err| <= 2^-7 |y| + 2^-20 sum|a b|, the FP8 path's worst ratio is 2.2 at K = 1024,
+// 0.98 at 4096, 0.89 at 8192, 0.70 at 12288 and 0.49 at 36864 (0.5 is bf16 output rounding alone). The FP8 path is
+// therefore used from K >= kFp8MinK (worst ratio <= 0.75); below it the operands are dequantized to bf16 (exact) for the bf16 instruction.
+constexpr int64_t kFp8MinK = 12288;
+
+template <bool MX, int FA, int FB, bool GROUPED>
+static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks, hipStream_t stream) {
+    if (a.K >= kFp8MinK)
+        hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GROUPED, 1>), dim3(blocks), dim3(GTHREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GROUPED, 2>), dim3(blocks), dim3(GTHREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt, const uint8_t* b_q,
+                              const void* b_scale, int b_fmt, int64_t M, int64_t N, int64_t K, int mx,
+                              uint16_t* c, int64_t ldc, hipStream_t stream) {
+    GemmArgs a{};
+    a.a = a_q; a.b = b_q; a.c = c; a.M = M; a.N = N; a.K = K; a.ldc = ldc;
+    if (mx) { a.sa = (const uint8_t*)a_scale; a.sb = (const uint8_t*)b_scale; }
+    else { a.pa = (const float*)a_scale; a.pb = (const float*)b_scale; }
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const unsigned blocks = (unsigned)tiles;
+    if (mx) return launch_gemm_t<true, 0, 0, false>(a, blocks, stream);
+    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 0, 0, false>(a, blocks, stream);
+    if (a_fmt == FMT_E5M2 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 1, 0, false>(a, blocks, stream);
+    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E5M2) return launch_gemm_t<false, 0, 1, false>(a, blocks, stream);
+    return launch_gemm_t<false, 1, 1, false>(a, blocks, stream);
+}
+
+hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* offsets, int64_t G,
+                               int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s, int64_t N, int64_t K,
+                               uint16_t* c, hipStream_t stream) {
+    GemmArgs a{};
+    a.a = a_q; a.sa = a_s; a.b = b_q; a.sb = b_s; a.c = c;
+    a.M = total_rows; a.N = N; a.K = K; a.ldc = N; a.offsets = offsets; a.G = G;
+    const int64_t row_tiles = (total_rows + BM - 1) / BM + G;   // each group adds at most one partial tile
+    const int64_t blocks = row_tiles * ((N + BN - 1) / BN);
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    return launch_gemm_t<true, 0, 0, true>(a, (unsigned)blocks, stream);
+}
+
+}  // namespace mxq

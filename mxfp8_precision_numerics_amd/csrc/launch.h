@@ -1,0 +1,33 @@
+// Host-side launchers of the gfx950 kernels (internal to libmxq; the public C ABI is include/mxq.h).
+// Each launcher enqueues on `stream` and returns the launch status; arguments are validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+struct AdamConsts {
+    float b1, ob1, b2, ob2, c1, c2, lr, eps, wd;
+};
+
+hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
+                              uint8_t* q_col, uint8_t* s_col, int rule, hipStream_t stream);
+
+int pertensor_amax_parts(int64_t n);
+hipError_t launch_pertensor_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, float margin,
+                                     const float* scale_in, float* amax_out, float* scale_out, uint8_t* q,
+                                     uint8_t* q_t, uint32_t* partial, hipStream_t stream);
+
+hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt, const uint8_t* b_q,
+                              const void* b_scale, int b_fmt, int64_t M, int64_t N, int64_t K, int mx,
+                              uint16_t* c, int64_t ldc, hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* offsets, int64_t G,
+                               int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s, int64_t N, int64_t K,
+                               uint16_t* c, hipStream_t stream);
+
+int adam_parts(int64_t n);
+hipError_t launch_adam(float* master, const uint16_t* grad, uint8_t* m_q, float* m_scale, uint16_t* v16, uint16_t* w,
+                       int64_t n, const AdamConsts& k, uint32_t* partial, float* consts, hipStream_t stream);
+
+}  // namespace mxq

@@ -1,0 +1,264 @@
+// Operand quantization kernels for gfx950: MXFP8 (32-value blocks, E8M0 scales, row and column orientation)
+// and per-tensor scaled E4M3/E5M2 (current or delayed scaling).
+//
+// MXFP8 follows "OLMo-core MoE, Section 11: MXFP8 Training": Eq. 58 (q = E4M3(x/s), power-of-two s per block of
+// 32 along the reduction dimension), Section 11.3.5 / Table 24 (rceil and floor scale rules) and Eq. 60 (forward,
+// dgrad and wgrad need both orientations). Per-tensor scaling follows "3.8 Mixed Precision, bf16 & FP8 Training"
+// (per-tensor scale from amax, Exercise 6) and the tensor-scaling formula of the FP8-LM summary page.
+//
+// Design (HBM-bound): one workgroup owns a 128 x 128 bf16 tile. 16-byte coalesced loads land in registers; the
+// row orientation is encoded straight from registers (a 32-value block spans 4 lanes; its amax is a DPP quad max)
+// while the tile is also written to LDS, from which each thread re-reads a column pair of 32 rows for the column
+// orientation, stored transposed so each block's 32 codes are contiguous. One pass over x emits both.
+#include "mxq_device.h"
+#include "launch.h"
+
+namespace mxq {
+
+constexpr int QT = 128;            // tile rows and columns
+constexpr int QTHREADS = 256;
+
+enum : int { QM_MX_RCEIL = 0, QM_MX_FLOOR = 1, QM_PT_E4M3 = 2, QM_PT_E5M2 = 3 };
+
+struct QuantArgs {
+    const uint16_t* x;
+    int64_t rows, cols;
+    uint8_t* q_row;     // MX: q_row ; per-tensor: q
+    uint8_t* s_row;     // MX only
+    uint8_t* q_col;     // MX: q_col ; per-tensor: q_t
+    uint8_t* s_col;     // MX only
+    const float* scale; // per-tensor only
+};
+
+template <int MODE>
+__device__ __forceinline__ uint32_t pt_cvt_quad(float s, uint32_t p0, uint32_t p1) {
+    constexpr int FMT = MODE == QM_PT_E4M3 ? FMT_E4M3 : FMT_E5M2;
+    constexpr float FMAX = MODE == QM_PT_E4M3 ? 448.0f : 57344.0f;
+    float a = clamp_keep_nan(bf16_lo(p0) * s, FMAX), b = clamp_keep_nan(bf16_hi(p0) * s, FMAX);
+    float c = clamp_keep_nan(bf16_lo(p1) * s, FMAX), d = clamp_keep_nan(bf16_hi(p1) * s, FMAX);
+    return cvt_f32_pair<FMT, true>(cvt_f32_pair<FMT, false>(0u, a, b), c, d);
+}
+
+template <int MODE, bool ROW, bool COL>
+__global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
+    constexpr bool MX = MODE == QM_MX_RCEIL || MODE == QM_MX_FLOOR;
+    constexpr int RULE = MODE == QM_MX_FLOOR ? RULE_FLOOR : RULE_RCEIL;
+    __shared__ uint32_t lds[COL ? QT * QT / 2 : 1];
+
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.y * QT, c0 = (int64_t)blockIdx.x * QT;
+    const int ch = tid & 15;                     // 16-byte chunk within a tile row (8 bf16)
+    const int64_t gc = c0 + ch * 8;
+    const bool col_ok = gc < a.cols;             // cols % 8 == 0, so a chunk is all in or all out
+    float pt_scale = 0.0f;
+    if constexpr (!MX) pt_scale = *a.scale;
+
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int row = (tid >> 4) + 16 * j;
+        const int64_t gr = r0 + row;
+        if (col_ok && gr < a.rows)
+            v[j] = ldnt16(a.x + gr * a.cols + gc);
+        else
+            v[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    if constexpr (COL) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = (tid >> 4) + 16 * j;
+            *reinterpret_cast<uint4*>(&lds[row * (QT / 2) + ch * 4]) = v[j];
+        }
+    }
+
+    if constexpr (ROW) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t gr = r0 + (tid >> 4) + 16 * j;
+            uint32_t lo, hi;
+            if constexpr (MX) {
+                uint32_t m = quad_max(amax_bits8(v[j]));
+                uint32_t byte = mx_scale_byte(m, RULE);
+                float s = scale_operand(byte);
+                lo = cvt_mx_quad(v[j].x, v[j].y, s);
+                hi = cvt_mx_quad(v[j].z, v[j].w, s);
+                if (RULE == RULE_FLOOR || m >= 0x7F80u) {
+                    uint32_t thr = mx_sat_threshold(byte);
+                    lo = mx_patch4(lo, v[j].x, v[j].y, thr);
+                    hi = mx_patch4(hi, v[j].z, v[j].w, thr);
+                }
+                if (col_ok && gr < a.rows) {
+                    *reinterpret_cast<uint2*>(a.q_row + gr * a.cols + gc) = make_uint2(lo, hi);
+                    if ((tid & 3) == 0) a.s_row[gr * (a.cols / 32) + gc / 32] = (uint8_t)byte;
+                }
+            } else {
+                lo = pt_cvt_quad<MODE>(pt_scale, v[j].x, v[j].y);
+                hi = pt_cvt_quad<MODE>(pt_scale, v[j].z, v[j].w);
+                if (col_ok && gr < a.rows) *reinterpret_cast<uint2*>(a.q_row + gr * a.cols + gc) = make_uint2(lo, hi);
+            }
+        }
+    }
+
+    if constexpr (COL) {
+        __syncthreads();
+        const int p = tid & 63;                  // column pair within the tile
+        const int b = tid >> 6;                  // 32-row block within the tile
+        uint32_t d[32];
+#pragma unroll
+        for (int r = 0; r < 32; ++r) d[r] = lds[(32 * b + r) * (QT / 2) + p];
+        const int64_t gcol = c0 + 2 * p;
+        const int64_t grow = r0 + 32 * b;
+        const bool ok0 = gcol < a.cols && grow + 32 <= a.rows;
+        const bool ok1 = gcol + 1 < a.cols && grow + 32 <= a.rows;
+        uint32_t out0[8], out1[8];
+        if constexpr (MX) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) m = max_u16x2(m, d[r] & 0x7FFF7FFFu);
+            const uint32_t m0 = m & 0xFFFFu, m1 = m >> 16;
+            const uint32_t b0 = mx_scale_byte(m0, RULE), b1 = mx_scale_byte(m1, RULE);
+            const float s0 = scale_operand(b0), s1 = scale_operand(b1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                // pairs down the column: lo halves -> column 2p, hi halves -> column 2p+1
+                uint32_t a0 = __builtin_amdgcn_perm(d[4 * i + 1], d[4 * i + 0], 0x05040100u);
+                uint32_t a1 = __builtin_amdgcn_perm(d[4 * i + 3], d[4 * i + 2], 0x05040100u);
+                uint32_t h0 = __builtin_amdgcn_perm(d[4 * i + 1], d[4 * i + 0], 0x07060302u);
+                uint32_t h1 = __builtin_amdgcn_perm(d[4 * i + 3], d[4 * i + 2], 0x07060302u);
+                out0[i] = cvt_mx_quad(a0, a1, s0);
+                out1[i] = cvt_mx_quad(h0, h1, s1);
+                if (RULE == RULE_FLOOR || m0 >= 0x7F80u) out0[i] = mx_patch4(out0[i], a0, a1, mx_sat_threshold(b0));
+                if (RULE == RULE_FLOOR || m1 >= 0x7F80u) out1[i] = mx_patch4(out1[i], h0, h1, mx_sat_threshold(b1));
+            }
+            if (ok0) a.s_col[gcol * (a.rows / 32) + grow / 32] = (uint8_t)b0;
+            if (ok1) a.s_col[(gcol + 1) * (a.rows / 32) + grow / 32] = (uint8_t)b1;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t a0 = __builtin_amdgcn_perm(d[4 * i + 1], d[4 * i + 0], 0x05040100u);
+                uint32_t a1 = __builtin_amdgcn_perm(d[4 * i + 3], d[4 * i + 2], 0x05040100u);
+                uint32_t h0 = __builtin_amdgcn_perm(d[4 * i + 1], d[4 * i + 0], 0x07060302u);
+                uint32_t h1 = __builtin_amdgcn_perm(d[4 * i + 3], d[4 * i + 2], 0x07060302u);
+                out0[i] = pt_cvt_quad<MODE>(pt_scale, a0, a1);
+                out1[i] = pt_cvt_quad<MODE>(pt_scale, h0, h1);
+            }
+        }
+        if (ok0) {
+            uint4* dst = reinterpret_cast<uint4*>(a.q_col + gcol * a.rows + grow);
+            dst[0] = make_uint4(out0[0], out0[1], out0[2], out0[3]);
+            dst[1] = make_uint4(out0[4], out0[5], out0[6], out0[7]);
+        }
+        if (ok1) {
+            uint4* dst = reinterpret_cast<uint4*>(a.q_col + (gcol + 1) * a.rows + grow);
+            dst[0] = make_uint4(out1[0], out1[1], out1[2], out1[3]);
+            dst[1] = make_uint4(out1[4], out1[5], out1[6], out1[7]);
+        }
+    }
+}
+
+template <int MODE>
+static hipError_t launch_quant_mode(const QuantArgs& a, bool row, bool col, hipStream_t stream) {
+    dim3 grid((unsigned)((a.cols + QT - 1) / QT), (unsigned)((a.rows + QT - 1) / QT));
+    if (row && col) hipLaunchKernelGGL((quant_tile_kernel<MODE, true, true>), grid, dim3(QTHREADS), 0, stream, a);
+    else if (row) hipLaunchKernelGGL((quant_tile_kernel<MODE, true, false>), grid, dim3(QTHREADS), 0, stream, a);
+    else hipLaunchKernelGGL((quant_tile_kernel<MODE, false, true>), grid, dim3(QTHREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
+                              uint8_t* q_col, uint8_t* s_col, int rule, hipStream_t stream) {
+    QuantArgs a{x, rows, cols, q_row, s_row, q_col, s_col, nullptr};
+    bool row = q_row != nullptr, col = q_col != nullptr;
+    return rule == RULE_FLOOR ? launch_quant_mode<QM_MX_FLOOR>(a, row, col, stream)
+                              : launch_quant_mode<QM_MX_RCEIL>(a, row, col, stream);
+}
+
+// ---------------------------------------------------------------------------------------- per-tensor amax
+constexpr int AMAX_THREADS = 256;
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* sh) {
+    v = wave_max(v);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) sh[w] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int i = 1; i < (int)(blockDim.x >> 6); ++i) v = max(v, sh[i]);
+    }
+    return v;
+}
+
+// Partial max of |x| (bf16 magnitude bit patterns; NaN patterns sort above infinity) per workgroup.
+__global__ __launch_bounds__(AMAX_THREADS) void pt_amax_partial_kernel(const uint4* __restrict__ x, int64_t nchunks,
+                                                                      uint32_t* __restrict__ partial) {
+    __shared__ uint32_t sh[AMAX_THREADS / 64];
+    uint32_t m = 0;
+    const int64_t stride = (int64_t)gridDim.x * AMAX_THREADS;
+    int64_t i = (int64_t)blockIdx.x * AMAX_THREADS + threadIdx.x;
+    for (; i + 3 * stride < nchunks; i += 4 * stride) {
+        uint4 a0 = ldnt16(x + i), a1 = ldnt16(x + i + stride);
+        uint4 a2 = ldnt16(x + i + 2 * stride), a3 = ldnt16(x + i + 3 * stride);
+        m = max(m, max(max(amax_bits8(a0), amax_bits8(a1)), max(amax_bits8(a2), amax_bits8(a3))));
+    }
+    for (; i < nchunks; i += stride) m = max(m, amax_bits8(ldnt16(x + i)));
+    m = block_max(m, sh);
+    if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+// amax_out = max|x| (fp32), scale_out = (FMAX / max(amax, 1e-12)) * margin, or *scale_in in delayed mode.
+__global__ __launch_bounds__(AMAX_THREADS) void pt_finalize_kernel(const uint32_t* __restrict__ partial, int nparts,
+                                                                  float fmax, float margin,
+                                                                  const float* __restrict__ scale_in,
+                                                                  float* __restrict__ amax_out,
+                                                                  float* __restrict__ scale_out) {
+    __shared__ uint32_t sh[AMAX_THREADS / 64];
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nparts; i += AMAX_THREADS) m = max(m, partial[i]);
+    m = block_max(m, sh);
+    if (threadIdx.x == 0) {
+        float amax = __uint_as_float(m << 16);
+        float s;
+        if (scale_in) {
+            s = *scale_in;
+        } else {
+            float a = amax < 1e-12f ? 1e-12f : amax;
+            s = fmax / a;
+            s = s * margin;
+        }
+        *amax_out = amax;
+        *scale_out = s;
+    }
+}
+
+int pertensor_amax_parts(int64_t n) {
+    int64_t chunks = n / 8;
+    int64_t parts = (chunks + AMAX_THREADS * 8 - 1) / (AMAX_THREADS * 8);
+    if (parts < 1) parts = 1;
+    if (parts > 2048) parts = 2048;
+    return (int)parts;
+}
+
+hipError_t launch_pertensor_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, float margin,
+                                     const float* scale_in, float* amax_out, float* scale_out, uint8_t* q,
+                                     uint8_t* q_t, uint32_t* partial, hipStream_t stream) {
+    const int64_t n = rows * cols;
+    const int parts = pertensor_amax_parts(n);
+    hipLaunchKernelGGL(pt_amax_partial_kernel, dim3(parts), dim3(AMAX_THREADS), 0, stream,
+                       reinterpret_cast<const uint4*>(x), n / 8, partial);
+    hipLaunchKernelGGL(pt_finalize_kernel, dim3(1), dim3(AMAX_THREADS), 0, stream, partial, parts,
+                       fmt == FMT_E4M3 ? 448.0f : 57344.0f, margin, scale_in, amax_out, scale_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (!q && !q_t) return hipSuccess;
+    QuantArgs a{x, rows, cols, q, nullptr, q_t, nullptr, scale_out};
+    return fmt == FMT_E4M3 ? launch_quant_mode<QM_PT_E4M3>(a, q != nullptr, q_t != nullptr, stream)
+                           : launch_quant_mode<QM_PT_E5M2>(a, q != nullptr, q_t != nullptr, stream);
+}
+
+}  // namespace mxq

@@ -55,7 +55,7 @@ def lib():
         L.orc_f16_from_f32_array.argtypes = [P, I64, P]
         L.orc_mx_scale_exp_array.argtypes = [P, I64, I, P]
         L.orc_mx_quantize.argtypes = [P, I64, I64, I, P, P, P, P, I]
-        L.orc_pertensor_quantize.argtypes = [P, I64, I64, I, F, P, P, P, P, P]
+        L.orc_pertensor_quantize.argtypes = [P, I64, I64, I, F, P, P, P, P, P, I]
         L.orc_gemm_ref.argtypes = [P, P, I, P, P, I, I64, I64, I64, I, P, I64, P, I64, P, P, I]
         L.orc_grouped_gemm_ref.argtypes = [P, P, P, I64, P, P, I64, I64, P, I64, P, I64, P, P, I]
         L.orc_adam_step.restype = F
@@ -76,7 +76,11 @@ def _c(a, dtype):
 
 
 def default_threads() -> int:
-    return max(1, min(64, len(os.sched_getaffinity(0))))
+    """Threads for the oracle's independent outputs: MXQ_ORACLE_THREADS if set, else the CPUs available (max 16)."""
+    env = os.environ.get("MXQ_ORACLE_THREADS")
+    if env:
+        return max(1, int(env))
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 # ---------------------------------------------------------------- codecs
@@ -139,7 +143,7 @@ def mx_quantize(x_bf16, rule: int = RCEIL, rowwise: bool = True, colwise: bool =
 
 
 def pertensor_quantize(x_bf16, fmt: int = E4M3, margin: float = 1.0, scale_in: float | None = None,
-                       want_q: bool = True, want_qt: bool = True):
+                       want_q: bool = True, want_qt: bool = True, nthreads: int | None = None):
     """Returns (amax, scale, q, q_t)."""
     x = _c(x_bf16, np.uint16)
     R, Ccols = x.shape
@@ -148,7 +152,8 @@ def pertensor_quantize(x_bf16, fmt: int = E4M3, margin: float = 1.0, scale_in: f
     sin = None if scale_in is None else np.array([scale_in], np.float32)
     q = np.empty((R, Ccols), np.uint8) if want_q else None
     qt = np.empty((Ccols, R), np.uint8) if want_qt else None
-    lib().orc_pertensor_quantize(_p(x), R, Ccols, fmt, C.c_float(margin), _p(sin), _p(amax), _p(scale), _p(q), _p(qt))
+    lib().orc_pertensor_quantize(_p(x), R, Ccols, fmt, C.c_float(margin), _p(sin), _p(amax), _p(scale), _p(q), _p(qt),
+                                 nthreads or default_threads())
     return float(amax[0]), np.float32(scale[0]), q, qt
 
 

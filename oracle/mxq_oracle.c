@@ -251,14 +251,51 @@ void orc_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int rule, ui
  *   amax = max |x|;  s = (FMAX / max(amax, 1e-12)) * margin  (fp32);  q = FP8(fp32(x * s));  x ~ q / s.
  * With scale_in given (delayed scaling) s = *scale_in and amax is still reported.
  * ------------------------------------------------------------------------------------------------------ */
+typedef struct {
+    const uint16_t* x; int64_t rows, cols; int fmt; float s;
+    uint8_t *q, *q_t; float amax; int pass; int nthreads, tid;
+} pt_job;
+
+static void* pt_worker(void* p)
+{
+    pt_job* j = (pt_job*)p;
+    int64_t lo = j->rows * j->tid / j->nthreads, hi = j->rows * (j->tid + 1) / j->nthreads;
+    if (j->pass == 1) {
+        float amax = 0.0f;
+        for (int64_t i = lo * j->cols; i < hi * j->cols; ++i) {
+            float a = fabsf(orc_bf16_to_f32(j->x[i]));
+            if (isnan(a) || isnan(amax)) amax = NAN;
+            else if (a > amax) amax = a;
+        }
+        j->amax = amax;
+        return NULL;
+    }
+    for (int64_t r = lo; r < hi; ++r)
+        for (int64_t c = 0; c < j->cols; ++c) {
+            float p = orc_bf16_to_f32(j->x[r * j->cols + c]) * j->s;     /* one fp32 rounding */
+            uint8_t code = orc_fp8_encode((double)p, j->fmt);
+            if (j->q) j->q[r * j->cols + c] = code;
+            if (j->q_t) j->q_t[c * j->rows + r] = code;
+        }
+    return NULL;
+}
+
 void orc_pertensor_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, float margin,
-                            const float* scale_in, float* amax_out, float* scale_out, uint8_t* q, uint8_t* q_t)
+                            const float* scale_in, float* amax_out, float* scale_out, uint8_t* q, uint8_t* q_t,
+                            int nthreads)
 {
     tables();
-    int64_t n = rows * cols;
+    nthreads = clamp_threads(nthreads);
+    pthread_t th[256];
+    pt_job jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (pt_job){x, rows, cols, fmt, 0.0f, q, q_t, 0.0f, 1, nthreads, t};
+        pthread_create(&th[t], NULL, pt_worker, &jobs[t]);
+    }
     float amax = 0.0f;
-    for (int64_t i = 0; i < n; ++i) {
-        float a = fabsf(orc_bf16_to_f32(x[i]));
+    for (int t = 0; t < nthreads; ++t) {
+        pthread_join(th[t], NULL);
+        float a = jobs[t].amax;
         if (isnan(a) || isnan(amax)) amax = NAN;
         else if (a > amax) amax = a;
     }
@@ -273,13 +310,12 @@ void orc_pertensor_quantize(const uint16_t* x, int64_t rows, int64_t cols, int f
     }
     if (amax_out) *amax_out = amax;
     if (scale_out) *scale_out = s;
-    for (int64_t r = 0; r < rows; ++r)
-        for (int64_t c = 0; c < cols; ++c) {
-            float p = orc_bf16_to_f32(x[r * cols + c]) * s;     /* one fp32 rounding */
-            uint8_t code = orc_fp8_encode((double)p, fmt);
-            if (q) q[r * cols + c] = code;
-            if (q_t) q_t[c * rows + r] = code;
-        }
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t].pass = 2;
+        jobs[t].s = s;
+        pthread_create(&th[t], NULL, pt_worker, &jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
 }
 
 /* ------------------------------------------------------------------------------------------------------

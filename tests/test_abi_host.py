@@ -1,0 +1,102 @@
+"""Host-side checks of the C ABI (no GPU needed): libmxq.so loads, exports every function include/mxq.h declares,
+and argument validation returns the documented status codes before anything is enqueued. Only inputs that fail
+validation are passed here (fake, aligned pointer values are never dereferenced)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from mxfp8_precision_numerics_amd import _lib
+
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+P = 0x10000          # a fake 16-byte-aligned address: validation rejects before any use
+MIS = 0x10001        # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)) - {"defined"})
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    assert lib.mxq_abi_version() == 1
+    for s in range(7):
+        assert lib.mxq_status_string(s)
+    assert lib.mxq_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes():
+    lib = _lib.load()
+    assert lib.mxq_workspace_bytes(b"pertensor", 16384 * 8192) >= 4
+    assert lib.mxq_workspace_bytes(b"adam", 1_300_000_000) >= 4 * 16
+    assert lib.mxq_workspace_bytes(b"nope", 10) == 0
+    assert lib.mxq_workspace_bytes(b"adam", -1) == 0
+
+
+def test_mx_quantize_validation():
+    f = _lib.load().mxq_quantize
+    ok = 0
+    assert f(None, 64, 64, P, P, P, P, 0, None) == 1                  # NULL x
+    assert f(P, 64, 64, None, None, None, None, 0, None) == 1         # no orientation requested
+    assert f(P, 64, 64, P, None, None, None, 0, None) == 1            # q_row without s_row
+    assert f(P, 64, 48, P, P, None, None, 0, None) == 2               # row orientation needs cols % 32
+    assert f(P, 48, 64, None, None, P, P, 0, None) == 2               # col orientation needs rows % 32
+    assert f(P, 64, 36, None, None, P, P, 0, None) == 2               # cols % 8
+    assert f(P, -32, 64, P, P, None, None, 0, None) == 2
+    assert f(P, 64, 64, P, P, None, None, 7, None) == 4               # unknown rule
+    assert f(MIS, 64, 64, P, P, None, None, 0, None) == 3
+    assert f(P, 64, 64, MIS, P, None, None, 0, None) == 3
+    assert f(P, 0, 64, P, P, P, P, 0, None) == ok                      # empty: nothing enqueued
+
+
+def test_pertensor_validation():
+    f = _lib.load().fp8_quantize_pertensor
+    ws = _lib.load().mxq_workspace_bytes(b"pertensor", 64 * 64)
+    assert f(P, 64, 64, 0, C.c_float(1.0), None, None, P, P, P, P, ws, None) == 1
+    assert f(P, 64, 64, 2, C.c_float(1.0), None, P, P, P, P, P, ws, None) == 4
+    assert f(P, 48, 64, 0, C.c_float(1.0), None, P, P, P, P, P, ws, None) == 2    # q_t needs rows % 32
+    assert f(P, 64, 64, 0, C.c_float(1.0), None, P, P, P, P, None, ws, None) == 5
+    assert f(P, 64, 64, 0, C.c_float(1.0), None, P, P, P, P, P, ws - 1, None) == 5
+    assert f(MIS, 64, 64, 0, C.c_float(1.0), None, P, P, P, P, P, ws, None) == 3
+
+
+def test_gemm_validation():
+    f = _lib.load().scaled_gemm
+    assert f(None, P, 0, P, P, 0, 64, 64, 64, 1, P, 64, None) == 1
+    assert f(P, P, 0, P, P, 0, 64, 64, 48, 1, P, 64, None) == 2        # K % 32
+    assert f(P, P, 0, P, P, 0, 64, 64, 0, 1, P, 64, None) == 2         # K > 0
+    assert f(P, P, 0, P, P, 0, 64, 64, 64, 1, P, 32, None) == 2        # ldc < N
+    assert f(P, P, 0, P, P, 0, 64, 64, 64, 1, P + 1, 64, None) == 3    # C must be 2-byte aligned
+    assert f(P, P, 1, P, P, 0, 64, 64, 64, 1, P, 64, None) == 4        # MX needs E4M3
+    assert f(P, P, 0, P, P, 0, 64, 64, 64, 5, P, 64, None) == 4
+    assert f(P, P, 0, MIS, P, 0, 64, 64, 64, 1, P, 64, None) == 3
+    assert f(P, P, 0, P, P, 0, 0, 64, 64, 1, P, 64, None) == 0         # empty
+
+
+def test_grouped_and_adam_validation():
+    lib = _lib.load()
+    g = lib.grouped_scaled_gemm
+    assert g(P, P, None, 4, 128, P, P, 64, 64, P, None) == 1
+    assert g(P, P, P, 0, 128, P, P, 64, 64, P, None) == 2
+    assert g(P, P, P, 4, 128, P, P, 64, 40, P, None) == 2
+    assert g(P, P, P + 4, 4, 128, P, P, 64, 64, P, None) == 3
+    hp = _lib.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.0, 0)
+    ws = lib.mxq_workspace_bytes(b"adam", 1024)
+    a = lib.fp8_adam_step
+    assert a(P, P, P, P, P, None, 1024, C.byref(hp), P, ws, None) == 2          # step must be >= 1
+    hp.step = 1
+    assert a(P, P, P, P, P, None, 1024, None, P, ws, None) == 1
+    assert a(P, P, P, P, P, None, 1024, C.byref(hp), P, ws - 1, None) == 5
+    assert a(P, MIS, P, P, P, None, 1024, C.byref(hp), P, ws, None) == 3

@@ -1,0 +1,97 @@
+"""GPU parity of fp8_adam_step against the oracle: master weight, E4M3 first moment, its scale, the fp16 second
+moment and the bf16 weight copy must match bit for bit, over several consecutive steps."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_precision_numerics_amd as mxq
+import oracle
+from gpu_util import DEV, need_gpu, say, u16, u8
+from mxfp8_precision_numerics_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _hp(t, wd):
+    return mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, wd, t), oracle.AdamHP(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8,
+                                                                       weight_decay=wd, step=t)
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 1000, 1_000_003])
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_adam_steps_bit_exact(n, wd):
+    need_gpu()
+    say("adam", n, wd)
+    theta = workloads.workload5_params(n, DEV)
+    m_q = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    m_scale = torch.ones(1, dtype=torch.float32, device=DEV)
+    v = torch.zeros(n, dtype=torch.float16, device=DEV)
+    w = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    o_theta = theta.cpu().numpy().copy()
+    o_mq = np.zeros(n, np.uint8); o_ms = np.ones(1, np.float32); o_v = np.zeros(n, np.uint16)
+    for t in (1, 2, 3, 4):
+        g = workloads.workload5_grad(n, t, DEV)
+        hp, ohp = _hp(t, wd)
+        mxq.fp8_adam_step(theta, g, m_q, m_scale, v, w, hp)
+        torch.cuda.synchronize()
+        _, o_w = oracle.adam_step(o_theta, u16(g), o_mq, o_ms, o_v, ohp)
+        assert np.array_equal(theta.cpu().numpy().view(np.uint32), o_theta.view(np.uint32)), f"theta t={t}"
+        assert np.array_equal(u8(m_q), o_mq), f"m_q t={t}"
+        assert np.float32(m_scale.item()) == o_ms[0], f"m_scale t={t}"
+        assert np.array_equal(u16(v), o_v), f"v t={t}"
+        assert np.array_equal(u16(w), o_w), f"w t={t}"
+
+
+def test_adam_without_weight_copy_and_zero_length():
+    need_gpu()
+    n = 4099
+    theta = workloads.workload5_params(n, DEV)
+    t2 = theta.clone()
+    m_q = torch.zeros(n, dtype=torch.uint8, device=DEV); m2 = m_q.clone()
+    ms = torch.ones(1, device=DEV); ms2 = ms.clone()
+    v = torch.zeros(n, dtype=torch.float16, device=DEV); v2 = v.clone()
+    g = workloads.workload5_grad(n, 1, DEV)
+    hp, _ = _hp(1, 0.0)
+    mxq.fp8_adam_step(theta, g, m_q, ms, v, None, hp)
+    mxq.fp8_adam_step(t2, g, m2, ms2, v2, torch.empty(n, dtype=torch.bfloat16, device=DEV), hp)
+    torch.cuda.synchronize()
+    assert torch.equal(theta, t2) and torch.equal(m_q, m2) and torch.equal(ms, ms2) and torch.equal(v, v2)
+    e = torch.empty(0, device=DEV)
+    mxq.fp8_adam_step(e, torch.empty(0, dtype=torch.bfloat16, device=DEV), torch.empty(0, dtype=torch.uint8, device=DEV),
+                      torch.ones(1, device=DEV), torch.empty(0, dtype=torch.float16, device=DEV), None, hp)
+    torch.cuda.synchronize()
+
+
+def test_adam_workload5_full_size_sampled():
+    """1.3e9 parameters as one tensor, steps 1 and 2: the m scale must match the oracle's amax over every element,
+    and one million sampled elements must match bit for bit (the oracle sees the full pre-step state)."""
+    need_gpu()
+    n = 1_300_000_000
+    say("adam full size", n)
+    theta = workloads.workload5_params(n, DEV)
+    m_q = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    m_scale = torch.ones(1, dtype=torch.float32, device=DEV)
+    v = torch.zeros(n, dtype=torch.float16, device=DEV)
+    w = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    rng = np.random.default_rng(6)
+    for t in (1, 2):
+        g = workloads.workload5_grad(n, t, DEV)
+        hp, ohp = _hp(t, 0.0)
+        idx = np.unique(np.concatenate([rng.choice(n, 1_000_000, replace=False), [0, n - 1]])).astype(np.int64)
+        gh = u16(g); mh = u8(m_q); vh = u16(v); s_old = np.float32(m_scale.item())
+        idx_t = torch.from_numpy(idx).to(DEV)
+        th_s = theta[idx_t].cpu().numpy()
+        amax = oracle.adam_amax(gh, mh, vh, s_old, ohp)
+        s_new = np.float32(448.0) / np.float32(max(amax, 1e-12))
+        # the oracle's element pass needs full arrays only at the sampled indices
+        full_th = np.zeros(n, np.float32); full_th[idx] = th_s
+        om, oq, ov, ow = oracle.adam_elements(full_th, gh, mh, vh, s_old, s_new, idx, ohp)
+        del gh, mh, vh, full_th
+        mxq.fp8_adam_step(theta, g, m_q, m_scale, v, w, hp)
+        torch.cuda.synchronize()
+        assert np.float32(m_scale.item()) == s_new
+        assert np.array_equal(theta[idx_t].cpu().numpy().view(np.uint32), om.view(np.uint32))
+        assert np.array_equal(m_q[idx_t].cpu().numpy(), oq)
+        assert np.array_equal(v[idx_t].cpu().numpy().view(np.uint16), ov)
+        assert np.array_equal(w[idx_t].view(torch.int16).cpu().numpy().view(np.uint16), ow)
+        del g

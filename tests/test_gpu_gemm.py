@@ -1,0 +1,219 @@
+"""GPU parity of scaled_gemm and grouped_scaled_gemm against the oracle's fp64 GEMM of the dequantized operands.
+
+Acceptance per checked element: |C_gpu - y_ref| <= 2^-7 |y_ref| + 2^-20 S, with S = sum_k |a_hat b_hat|.
+Small shapes are checked on every element (several tiles plus ragged tails in M, N and K); the full-size shapes
+on sampled full rows and full columns. Exact special cases (identity, all ones) must match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_precision_numerics_amd as mxq
+import oracle
+from gpu_util import DEV, need_gpu, say, u16, u8
+from mxfp8_precision_numerics_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+REL, ABS_S = 2.0 ** -7, 2.0 ** -20
+
+
+def _bound_check(c_gpu, y, S, what):
+    got = c_gpu.astype(np.float64)
+    err = np.abs(got - y)
+    lim = REL * np.abs(y) + ABS_S * S
+    bad = err > lim
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements outside the bound; first at {tuple(i)}: "
+                             f"gpu={got[tuple(i)]!r} ref={y[tuple(i)]!r} S={S[tuple(i)]!r} err/S={err[tuple(i)] / S[tuple(i)]:.3e}")
+    return float(np.max(err / np.maximum(S, 1e-300)))
+
+
+def _mx_operands(A_bf16, B_bf16_nk):
+    qa = mxq.mx_quantize(A_bf16, rowwise=True, colwise=False)
+    qb = mxq.mx_quantize(B_bf16_nk, rowwise=True, colwise=False)
+    return qa.q_row, qa.s_row, qb.q_row, qb.s_row
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (200, 136, 96), (130, 260, 160), (1, 1, 32), (64, 512, 2048),
+                                   (384, 128, 1024), (33, 47, 224)])
+def test_mx_gemm_all_elements(M, N, K):
+    need_gpu()
+    say("mx gemm", M, N, K)
+    A = workloads.normal_bf16((M, K), 1.0, 21, M, DEV)
+    B = workloads.normal_bf16((N, K), 1.0, 21, 1000 + N, DEV)
+    qa, sa, qb, sb = _mx_operands(A, B)
+    C = mxq.scaled_gemm(qa, sa, qb, sb, mxq.MX_BLOCK32)
+    torch.cuda.synchronize()
+    y, S = oracle.gemm_ref(u8(qa), u8(sa), oracle.E4M3, u8(qb), u8(sb), oracle.E4M3, oracle.MX_BLOCK32)
+    worst = _bound_check(C.float().cpu().numpy(), y, S, f"mx {M}x{N}x{K}")
+    say("  worst |err|/S", worst)
+
+
+def test_mx_gemm_workload1():
+    """256 x 256 x 256: A row-quantized, B (K x N) column-quantized into the [N][K] operand."""
+    need_gpu()
+    A, B = workloads.workload1(DEV)
+    qa = mxq.mx_quantize(A, rowwise=True, colwise=False)
+    qb = mxq.mx_quantize(B, rowwise=False, colwise=True)
+    C = mxq.scaled_gemm(qa.q_row, qa.s_row, qb.q_col, qb.s_col, mxq.MX_BLOCK32)
+    torch.cuda.synchronize()
+    y, S = oracle.gemm_ref(u8(qa.q_row), u8(qa.s_row), oracle.E4M3, u8(qb.q_col), u8(qb.s_col), oracle.E4M3,
+                           oracle.MX_BLOCK32)
+    _bound_check(C.float().cpu().numpy(), y, S, "workload1")
+    # and close to the bf16 product itself (quantization error of two E4M3 operands)
+    exact = A.double() @ B.double()
+    rel = (C.double() - exact).norm() / exact.norm()
+    assert rel.item() < 0.06
+
+
+def test_gemm_exact_special_cases():
+    need_gpu()
+    K = 256
+    A = workloads.normal_bf16((160, K), 1.0, 22, 0, DEV)
+    I = torch.eye(K, dtype=torch.bfloat16, device=DEV)
+    qa, sa, qi, si = _mx_operands(A, I)
+    C = mxq.scaled_gemm(qa, sa, qi, si, mxq.MX_BLOCK32)
+    ah = oracle.fp8_value(u8(qa), oracle.E4M3) * np.ldexp(1.0, np.repeat(u8(sa).astype(np.int64) - 127, 32, axis=1))
+    want = oracle.bf16_from_f32(ah.astype(np.float32))
+    assert np.array_equal(u16(C), want)                          # C = bf16(A_hat) exactly
+    ones = torch.ones((96, 512), dtype=torch.bfloat16, device=DEV)
+    q1, s1, q2, s2 = _mx_operands(ones, ones)
+    C = mxq.scaled_gemm(q1, s1, q2, s2, mxq.MX_BLOCK32)
+    assert torch.all(C.float() == 512.0)
+
+
+@pytest.mark.parametrize("fa,fb", [(mxq.E4M3, mxq.E4M3), (mxq.E5M2, mxq.E4M3), (mxq.E4M3, mxq.E5M2), (mxq.E5M2, mxq.E5M2)])
+@pytest.mark.parametrize("M,N,K", [(256, 384, 512), (77, 129, 96)])
+def test_pertensor_gemm_all_elements(fa, fb, M, N, K):
+    need_gpu()
+    say("per-tensor gemm", fa, fb, M, N, K)
+    A = workloads.normal_bf16((M, K), 1e-3 if fa == mxq.E5M2 else 1.0, 23, M + fa, DEV)
+    B = workloads.normal_bf16((N, K), 0.02, 23, 500 + N + fb, DEV)
+    pa = mxq.pertensor_quantize(A, fa, want_qt=False)
+    pb = mxq.pertensor_quantize(B, fb, want_qt=False)
+    C = mxq.scaled_gemm(pa.q, pa.scale, pb.q, pb.scale, mxq.PER_TENSOR, fa, fb)
+    torch.cuda.synchronize()
+    of = {mxq.E4M3: oracle.E4M3, mxq.E5M2: oracle.E5M2}
+    y, S = oracle.gemm_ref(u8(pa.q), np.float32(pa.scale.item()), of[fa], u8(pb.q), np.float32(pb.scale.item()), of[fb],
+                           oracle.PER_TENSOR)
+    _bound_check(C.float().cpu().numpy(), y, S, f"per-tensor {fa}{fb} {M}x{N}x{K}")
+
+
+def test_gemm_leading_dimension():
+    need_gpu()
+    A = workloads.normal_bf16((64, 128), 1.0, 24, 0, DEV)
+    B = workloads.normal_bf16((40, 128), 1.0, 24, 1, DEV)
+    qa, sa, qb, sb = _mx_operands(A, B)
+    big = torch.full((64, 50), 7.0, dtype=torch.bfloat16, device=DEV)
+    view = big[:, 4:44]
+    C = mxq.scaled_gemm(qa, sa, qb, sb, mxq.MX_BLOCK32, out=view)
+    ref = mxq.scaled_gemm(qa, sa, qb, sb, mxq.MX_BLOCK32)
+    torch.cuda.synchronize()
+    assert torch.equal(C, ref)
+    assert torch.all(big[:, :4] == 7.0) and torch.all(big[:, 44:] == 7.0)
+
+
+def _sampled(C, y_rows, S_rows, y_cols, S_cols, rows, cols, what):
+    Ch = C.float().cpu().numpy() if not isinstance(C, np.ndarray) else C
+    w1 = _bound_check(Ch[rows, :], y_rows, S_rows, what + " rows")
+    w2 = _bound_check(Ch[:, cols].T, y_cols.T, S_cols.T, what + " cols")
+    return max(w1, w2)
+
+
+def test_workload2_linear_fwd_dgrad_wgrad_full_size_sampled():
+    """GPT-175B QKV shape, per-tensor current scaling: Y = X W^T (E4M3 x E4M3), dX = dY W (E5M2 x E4M3, B = W^T),
+    dW = dY^T X (E5M2 x E4M3, A = dY^T, B = X^T). 8 full rows and 8 full columns of each output are checked."""
+    need_gpu()
+    X, W, dY = workloads.workload2(DEV)
+    px = mxq.pertensor_quantize(X, mxq.E4M3)
+    pw = mxq.pertensor_quantize(W, mxq.E4M3)
+    pd = mxq.pertensor_quantize(dY, mxq.E5M2)
+    sx, sw, sd = (np.float32(p.scale.item()) for p in (px, pw, pd))
+    rng = np.random.default_rng(2)
+    E4, E5 = oracle.E4M3, oracle.E5M2
+    cases = [("fwd", px.q, sx, E4, mxq.E4M3, pw.q, sw, E4, mxq.E4M3),
+             ("dgrad", pd.q, sd, E5, mxq.E5M2, pw.q_t, sw, E4, mxq.E4M3),
+             ("wgrad", pd.q_t, sd, E5, mxq.E5M2, px.q_t, sx, E4, mxq.E4M3)]
+    for name, aq, sa, oa, fa, bq, sb, ob, fb in cases:
+        M, N = aq.shape[0], bq.shape[0]
+        say("workload2", name, M, N, aq.shape[1])
+        C = mxq.scaled_gemm(aq, torch.tensor([sa], device=DEV), bq, torch.tensor([sb], device=DEV),
+                            mxq.PER_TENSOR, fa, fb)
+        torch.cuda.synchronize()
+        rows = np.sort(rng.choice(M, 8, replace=False)); cols = np.sort(rng.choice(N, 8, replace=False))
+        aqh, bqh = u8(aq), u8(bq)
+        yr, Sr = oracle.gemm_ref(aqh, sa, oa, bqh, sb, ob, oracle.PER_TENSOR, rows=rows)
+        yc, Sc = oracle.gemm_ref(aqh, sa, oa, bqh, sb, ob, oracle.PER_TENSOR, cols=cols)
+        worst = _sampled(C, yr, Sr, yc, Sc, rows, cols, name)
+        say("  worst |err|/S", worst)
+        del C
+
+
+def test_mx_gemm_workload2_fwd_shape_sampled():
+    """The dense MX GEMM at the GPT-175B QKV forward shape (4096 x 36864 x 12288)."""
+    need_gpu()
+    X, W, _ = workloads.workload2(DEV)
+    qx = mxq.mx_quantize(X, colwise=False)
+    qw = mxq.mx_quantize(W, colwise=False)
+    C = mxq.scaled_gemm(qx.q_row, qx.s_row, qw.q_row, qw.s_row, mxq.MX_BLOCK32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = np.sort(rng.choice(4096, 8, replace=False)); cols = np.sort(rng.choice(36864, 8, replace=False))
+    a, s_a, b, s_b = u8(qx.q_row), u8(qx.s_row), u8(qw.q_row), u8(qw.s_row)
+    yr, Sr = oracle.gemm_ref(a, s_a, oracle.E4M3, b, s_b, oracle.E4M3, oracle.MX_BLOCK32, rows=rows)
+    yc, Sc = oracle.gemm_ref(a, s_a, oracle.E4M3, b, s_b, oracle.E4M3, oracle.MX_BLOCK32, cols=cols)
+    say("  worst |err|/S", _sampled(C, yr, Sr, yc, Sc, rows, cols, "mx fwd"))
+
+
+# ----------------------------------------------------------------------------------------------- grouped
+def _quantize_experts(w):
+    G, N, K = w.shape
+    q = mxq.mx_quantize(w.reshape(G * N, K), colwise=False)
+    return q.q_row.reshape(G, N, K), q.s_row.reshape(G, N, K // 32)
+
+
+def test_grouped_gemm_small_all_elements():
+    need_gpu()
+    counts, padded, offsets = workloads.zipf_routing(tokens=512, experts=8, topk=2, seed=9)
+    counts[3] = 0; padded[3] = 0                                   # an empty expert
+    offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
+    total = int(offsets[-1]); K, N = 256, 192
+    say("grouped small", total, N, K)
+    A = workloads.zero_padding_rows(workloads.normal_bf16((total, K), 1.0, 25, 0, DEV), counts, padded, offsets)
+    W = workloads.normal_bf16((8, N, K), 1.0, 25, 1, DEV)
+    qa = mxq.mx_quantize(A, colwise=False)
+    qw, sw = _quantize_experts(W)
+    off_t = torch.from_numpy(offsets).to(DEV)
+    C = mxq.grouped_scaled_gemm(qa.q_row, qa.s_row, off_t, qw, sw)
+    torch.cuda.synchronize()
+    y, S = oracle.grouped_gemm_ref(u8(qa.q_row), u8(qa.s_row), offsets, u8(qw), u8(sw))
+    Ch = C.float().cpu().numpy()
+    _bound_check(Ch, y, S, "grouped small")
+    for g in range(8):
+        assert np.all(Ch[offsets[g] + counts[g]:offsets[g + 1]] == 0)      # padding rows give exactly 0
+
+
+def test_grouped_gemm_workload4_up_and_down_sampled():
+    need_gpu()
+    wl = workloads.workload4(DEV)
+    offsets, counts = wl["offsets"], wl["counts"]
+    off_t = torch.from_numpy(offsets).to(DEV)
+    rng = np.random.default_rng(4)
+    big, small = int(np.argmax(counts)), int(np.argmin(counts))
+    for name, A, W in (("up", wl["a_up"], wl["w_up"]), ("down", wl["a_down"], wl["w_down"])):
+        say("workload4", name, tuple(A.shape), tuple(W.shape))
+        qa = mxq.mx_quantize(A, colwise=False)
+        qw, sw = _quantize_experts(W)
+        C = mxq.grouped_scaled_gemm(qa.q_row, qa.s_row, off_t, qw, sw)
+        torch.cuda.synchronize()
+        rows = np.concatenate([rng.choice(np.arange(offsets[big], offsets[big + 1]), 6, replace=False),
+                               rng.choice(np.arange(offsets[small], offsets[small + 1]), 6, replace=False),
+                               rng.choice(A.shape[0], 20, replace=False)])
+        y, S = oracle.grouped_gemm_ref(u8(qa.q_row), u8(qa.s_row), offsets, u8(qw), u8(sw), rows=rows)
+        Ch = C.float().cpu().numpy()[rows]
+        pad = np.zeros(rows.size, bool)
+        for g in range(len(counts)):
+            pad |= (rows >= offsets[g] + counts[g]) & (rows < offsets[g + 1])
+        _bound_check(Ch, y, S, "workload4 " + name)
+        assert np.all(Ch[pad] == 0)
