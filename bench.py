@@ -1,0 +1,242 @@
+"""Benchmark of the FP8 / MXFP8 hot path on one MI355X.
+
+One step is one pass over every row of the hot path, on seeded synthetic inputs already resident in HBM:
+  mx_linear     GPT-175B QKV linear (X 4096x12288, W 36864x12288, dY 4096x36864) in MXFP8: quantize X, W and dY in
+                both orientations, then Y = X W^T, dX = dY W, dW = dY^T X (block-scaled GEMMs, bf16 out)
+  pt_linear     the same layer with per-tensor current scaling (E4M3 X and W, E5M2 dY; q and q^T) and three GEMMs
+  mx_quant      MX quantize of a 16384x8192 activation with 0.1% x100 outliers, row and column orientation
+  grouped       64-expert grouped MX GEMM (Zipf(1.1) top-8 routing of 16384 tokens, up 2048->1024 and down
+                1024->2048), including the row quantize of both activations (expert weights quantized once)
+  adam          precision-decoupled FP8 Adam step over 1.3e9 parameters (2 passes)
+  small         MX quantize + 256^3 block-scaled GEMM
+The headline value is the MXFP8 linear layer's GEMM FLOPs (11.13 TFLOP) divided by the device time of its quantize
+and GEMM launches ("MXFP8 GEMM TFLOP/s incl. quantize"). Device times come from events on the stream the kernels
+run on; the JSON line also carries every part's rate, the MX GEMM's roofline and the CPU oracle baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP8 GEMM TFLOP/s incl. quantize (% FP8 MFMA peak); quantize GB/s (% HBM)"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 (no sparsity)
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (multi-GPU sharding is a design "
+                                   "note, not implemented)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mxfp8_precision_numerics_amd as mxq
+    from mxfp8_precision_numerics_amd import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ------------------------------------------------------------------ inputs (resident before timing)
+    log("generating inputs")
+    X, W, dY = workloads.workload2(dev)
+    M, N, K = X.shape[0], W.shape[0], X.shape[1]
+    act3 = workloads.workload3(dev)
+    wl4 = workloads.workload4(dev)
+    off4 = torch.from_numpy(wl4["offsets"]).to(dev)
+    n_adam = 1_300_000_000
+    theta = workloads.workload5_params(n_adam, dev)
+    grad = workloads.workload5_grad(n_adam, 2, dev)
+    m_q = torch.zeros(n_adam, dtype=torch.uint8, device=dev)
+    m_scale = torch.ones(1, dtype=torch.float32, device=dev)
+    v16 = torch.zeros(n_adam, dtype=torch.float16, device=dev)
+    w16 = torch.empty(n_adam, dtype=torch.bfloat16, device=dev)
+    adam_ws = torch.empty(mxq.workspace_bytes("adam", n_adam), dtype=torch.uint8, device=dev)
+    A1, B1 = workloads.workload1(dev)
+
+    # preallocated outputs (the library never allocates)
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+    mxX = mxq.MXTensor(u8(M, K), u8(M, K // 32), u8(K, M), u8(K, M // 32))
+    mxW = mxq.MXTensor(u8(N, K), u8(N, K // 32), u8(K, N), u8(K, N // 32))
+    mxD = mxq.MXTensor(u8(M, N), u8(M, N // 32), u8(N, M), u8(N, M // 32))
+    mx3 = mxq.MXTensor(u8(*act3.shape), u8(act3.shape[0], act3.shape[1] // 32), u8(act3.shape[1], act3.shape[0]),
+                       u8(act3.shape[1], act3.shape[0] // 32))
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    ws_pt = torch.empty(mxq.workspace_bytes("pertensor", N * K), dtype=torch.uint8, device=dev)
+    # grouped: weights quantized once (cache), activations each step
+    G, d_ff, d_model = wl4["w_up"].shape
+    qwu = mxq.mx_quantize(wl4["w_up"].reshape(G * d_ff, d_model), colwise=False)
+    qwd = mxq.mx_quantize(wl4["w_down"].reshape(G * d_model, d_ff), colwise=False)
+    rows4 = wl4["a_up"].shape[0]
+    mx_up = mxq.MXTensor(u8(rows4, d_model), u8(rows4, d_model // 32), None, None)
+    mx_dn = mxq.MXTensor(u8(rows4, d_ff), u8(rows4, d_ff // 32), None, None)
+    C_up = torch.empty((rows4, d_ff), dtype=torch.bfloat16, device=dev)
+    C_dn = torch.empty((rows4, d_model), dtype=torch.bfloat16, device=dev)
+    hp = mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.0, 2)
+    torch.cuda.synchronize()
+
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    parts = ["mx_quant_XWdY", "mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "pt_quant", "pt_gemms", "mx_quant_act",
+             "grouped", "adam", "small"]
+
+    def step(ev):
+        ev[0].record(stream)
+        mxq.mx_quantize(X, out=mxX)
+        mxq.mx_quantize(W, out=mxW)
+        mxq.mx_quantize(dY, out=mxD)
+        ev[1].record(stream)
+        mxq.scaled_gemm(mxX.q_row, mxX.s_row, mxW.q_row, mxW.s_row, mxq.MX_BLOCK32, out=Y)            # Y = X W^T
+        ev[2].record(stream)
+        mxq.scaled_gemm(mxD.q_row, mxD.s_row, mxW.q_col, mxW.s_col, mxq.MX_BLOCK32, out=dX)          # dX = dY W
+        ev[3].record(stream)
+        mxq.scaled_gemm(mxD.q_col, mxD.s_col, mxX.q_col, mxX.s_col, mxq.MX_BLOCK32, out=dW)          # dW = dY^T X
+        ev[4].record(stream)
+        px = mxq.pertensor_quantize(X, mxq.E4M3, workspace=ws_pt)
+        pw = mxq.pertensor_quantize(W, mxq.E4M3, workspace=ws_pt)
+        pd = mxq.pertensor_quantize(dY, mxq.E5M2, workspace=ws_pt)
+        ev[5].record(stream)
+        mxq.scaled_gemm(px.q, px.scale, pw.q, pw.scale, mxq.PER_TENSOR, mxq.E4M3, mxq.E4M3, out=Y)
+        mxq.scaled_gemm(pd.q, pd.scale, pw.q_t, pw.scale, mxq.PER_TENSOR, mxq.E5M2, mxq.E4M3, out=dX)
+        mxq.scaled_gemm(pd.q_t, pd.scale, px.q_t, px.scale, mxq.PER_TENSOR, mxq.E5M2, mxq.E4M3, out=dW)
+        ev[6].record(stream)
+        mxq.mx_quantize(act3, out=mx3)
+        ev[7].record(stream)
+        mxq.mx_quantize(wl4["a_up"], colwise=False, out=mx_up)
+        mxq.grouped_scaled_gemm(mx_up.q_row, mx_up.s_row, off4, qwu.q_row.view(G, d_ff, d_model),
+                                qwu.s_row.view(G, d_ff, d_model // 32), out=C_up)
+        mxq.mx_quantize(wl4["a_down"], colwise=False, out=mx_dn)
+        mxq.grouped_scaled_gemm(mx_dn.q_row, mx_dn.s_row, off4, qwd.q_row.view(G, d_model, d_ff),
+                                qwd.s_row.view(G, d_model, d_ff // 32), out=C_dn)
+        ev[8].record(stream)
+        mxq.fp8_adam_step(theta, grad, m_q, m_scale, v16, w16, hp, workspace=adam_ws)
+        ev[9].record(stream)
+        qa = mxq.mx_quantize(A1, colwise=False)
+        qb = mxq.mx_quantize(B1, rowwise=False)
+        mxq.scaled_gemm(qa.q_row, qa.s_row, qb.q_col, qb.s_col, mxq.MX_BLOCK32)
+        ev[10].record(stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step([Ev() for _ in range(11)])
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    evs = [[Ev() for _ in range(11)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {p: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+          for i, p in enumerate(parts)}
+    step_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][10]) for s in range(args.steps)]))
+    log("per-part ms:", json.dumps({k: round(v, 4) for k, v in ms.items()}))
+
+    # ------------------------------------------------------------------ rates
+    flop_gemm = 2.0 * M * N * K                              # each of fwd, dgrad, wgrad
+    mx_linear_ms = ms["mx_quant_XWdY"] + ms["mx_gemm_fwd"] + ms["mx_gemm_dgrad"] + ms["mx_gemm_wgrad"]
+    value = 3 * flop_gemm / (mx_linear_ms * 1e-3) / 1e12
+    q_bytes = lambda r, c: 2 * r * c + 2 * (r * c + r * c // 32)   # read bf16, write both orientations  # noqa: E731
+    mxq_XWdY_bytes = q_bytes(M, K) + q_bytes(N, K) + q_bytes(M, N)
+    act_bytes = q_bytes(*act3.shape)
+    pt_bytes = sum(6 * r * c for r, c in ((M, K), (N, K), (M, N)))
+    rows_valid = int(wl4["counts"].sum())
+    grouped_flop = 2.0 * rows_valid * d_ff * d_model * 2
+    adam_bytes = 21 * n_adam
+    rate = {
+        "mx_linear_tflops_incl_quant": value,
+        "mx_linear_tflops_cached_weight": 3 * flop_gemm / ((mx_linear_ms - ms["mx_quant_XWdY"]
+                                                            + (q_bytes(M, K) + q_bytes(M, N)) / mxq_XWdY_bytes
+                                                            * ms["mx_quant_XWdY"]) * 1e-3) / 1e12,
+        "mx_gemm_fwd_tflops": flop_gemm / (ms["mx_gemm_fwd"] * 1e-3) / 1e12,
+        "mx_gemm_dgrad_tflops": flop_gemm / (ms["mx_gemm_dgrad"] * 1e-3) / 1e12,
+        "mx_gemm_wgrad_tflops": flop_gemm / (ms["mx_gemm_wgrad"] * 1e-3) / 1e12,
+        "mx_quant_XWdY_gbs": mxq_XWdY_bytes / (ms["mx_quant_XWdY"] * 1e-3) / 1e9,
+        "pt_linear_tflops_incl_quant": 3 * flop_gemm / ((ms["pt_quant"] + ms["pt_gemms"]) * 1e-3) / 1e12,
+        "pt_gemms_tflops": 3 * flop_gemm / (ms["pt_gemms"] * 1e-3) / 1e12,
+        "pt_quant_gbs": pt_bytes / (ms["pt_quant"] * 1e-3) / 1e9,
+        "mx_quant_act_gbs": act_bytes / (ms["mx_quant_act"] * 1e-3) / 1e9,
+        "grouped_tflops_incl_act_quant": grouped_flop / (ms["grouped"] * 1e-3) / 1e12,
+        "adam_gbs": adam_bytes / (ms["adam"] * 1e-3) / 1e9,
+        "small_us": ms["small"] * 1e3,
+    }
+    for k, v in rate.items():
+        rate[k] = round(v, 3)
+    log("rates:", json.dumps(rate))
+
+    fwd_tflops = rate["mx_gemm_fwd_tflops"]
+    roofline = {"kernel": "scaled_gemm MX_BLOCK32 fwd 4096x36864x12288 (v_mfma_scale_f32_16x16x128_f8f6f4)",
+                "bound": "mfma", "achieved": fwd_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(fwd_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(X, W, args.cpu_sample_rows)
+
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": "GPT-175B QKV linear fwd+dgrad+wgrad in MXFP8 (X 4096x12288, W 36864x12288, "
+                               "dY 4096x36864), quantize of X, W, dY included; plus per-tensor layer, MX quantize "
+                               "16384x8192, grouped 64-expert GEMM and FP8 Adam over 1.3e9 params in the same step",
+                   "gemm_flop_per_step": 3 * flop_gemm},
+        "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
+        "device_ms_per_step": round(step_ms, 3),
+        "parts_ms": {k: round(v, 4) for k, v in ms.items()},
+        "rates": rate,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(X, W, rows):
+    """The oracle (unchanged) on the host cores: MX quantize of `rows` rows of X and all of W, then the fp64 GEMM
+    of those rows against W (the forward GEMM of the MX linear layer), as TFLOP/s of the sample."""
+    import numpy as np
+
+    import oracle
+    from mxfp8_precision_numerics_amd import workloads
+
+    threads = oracle.default_threads()
+    xs = workloads.as_u16(X[:rows])
+    wh = workloads.as_u16(W)
+    t0 = time.perf_counter()
+    qx, sx, _, _ = oracle.mx_quantize(xs, oracle.RCEIL, colwise=False, nthreads=threads)
+    qw, sw, _, _ = oracle.mx_quantize(wh, oracle.RCEIL, colwise=False, nthreads=threads)
+    t1 = time.perf_counter()
+    oracle.gemm_ref(qx, sx, oracle.E4M3, qw, sw, oracle.E4M3, oracle.MX_BLOCK32, nthreads=threads)
+    t2 = time.perf_counter()
+    flop = 2.0 * rows * W.shape[0] * W.shape[1]
+    log(f"cpu oracle: quantize {t1 - t0:.2f}s, gemm {t2 - t1:.2f}s on {threads} threads")
+    return {"value": round(flop / (t2 - t0) / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"forward GEMM of the MX linear layer for {rows} of 4096 rows of X (2*{rows}*36864*12288 FLOP) "
+                      f"in fp64, including MX quantize of those rows and of all of W ({t2 - t0:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -329,6 +329,231 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
     }
 }
 
+
+// ---------------------------------------------------------------------------------------------------------------
+// Large-tile kernel (K % 128 == 0): 256 x 256 output tile per workgroup, one workgroup per CU (4 waves, 2 x 2,
+// each 128 x 128), two 64 KiB LDS stages filled straight from global memory by global_load_lds_dwordx4 (no staging
+// registers). A wave's DMA instruction writes 64 consecutive 16-byte LDS slots (8 rows of 128 bytes); lane l fetches
+// global chunk (l & 7) ^ (row & 7) of its row, which leaves each row's chunks XOR-swizzled exactly as swz() reads
+// them. Rows past the end of the operand are clamped to its last row (their outputs are never stored), so every
+// address stays inside the caller's buffers. Workgroups are ordered so that each XCD (which receives every eighth
+// workgroup) walks a contiguous run of a grouped-M tile order: its resident workgroups share A and B tiles in its L2.
+constexpr int TB = 256;
+constexpr int KS = 128;
+constexpr int GROUP_M2 = 4;
+
+template <bool MX, int FA, int FB, bool GROUPED, int MF>
+__global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) uint8_t sA[2][TB * KS];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][TB * KS];
+    __shared__ __attribute__((aligned(16))) uint32_t sSA[2][TB];
+    __shared__ __attribute__((aligned(16))) uint32_t sSB[2][TB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int64_t K = g.K;
+    const int64_t kblocks = K / 32;
+    const int tiles_n = (int)((g.N + TB - 1) / TB);
+
+    int64_t m0, m_end, n0;
+    const uint8_t* Bq = g.b;
+    const uint8_t* Bs = g.sb;
+    if constexpr (GROUPED) {
+        const int64_t bid = blockIdx.x;
+        const int64_t t = bid / tiles_n;
+        n0 = (bid % tiles_n) * TB;
+        int64_t acc_t = 0, grp = -1, lo = 0, hi = 0;
+        for (int64_t q = 0; q < g.G; ++q) {
+            int64_t a0 = g.offsets[q], a1 = g.offsets[q + 1];
+            a0 = a0 < 0 ? 0 : (a0 > g.M ? g.M : a0);
+            a1 = a1 < a0 ? a0 : (a1 > g.M ? g.M : a1);
+            const int64_t nt = (a1 - a0 + TB - 1) / TB;
+            if (t < acc_t + nt) { grp = q; lo = a0 + (t - acc_t) * TB; hi = a1; break; }
+            acc_t += nt;
+        }
+        if (grp < 0) return;
+        m0 = lo;
+        m_end = (lo + TB < hi) ? lo + TB : hi;
+        Bq = g.b + grp * g.N * K;
+        Bs = MX ? g.sb + grp * g.N * kblocks : nullptr;
+    } else {
+        const int tiles_m = (int)((g.M + TB - 1) / TB);
+        const int T = tiles_m * tiles_n;
+        const int bid = blockIdx.x;
+        const int T8 = T & ~7;
+        const int v = bid < T8 ? (bid & 7) * (T8 >> 3) + (bid >> 3) : bid;
+        const int per_group = GROUP_M2 * tiles_n;
+        const int first_m = (v / per_group) * GROUP_M2;
+        const int gm = min(GROUP_M2, tiles_m - first_m);
+        const int r = v % per_group;
+        m0 = (int64_t)(first_m + r % gm) * TB;
+        n0 = (int64_t)(r / gm) * TB;
+        m_end = (m0 + TB < g.M) ? m0 + TB : g.M;
+    }
+    const int64_t n_end = (n0 + TB < g.N) ? n0 + TB : g.N;
+
+    // ------------------------------------------------------------------ direct global -> LDS stage loads
+    const int lr = lane >> 3;                 // row within the wave's 8-row slab
+    const int lc = (lane & 7) ^ lr;           // chunk fetched by this lane (row & 7 == lr)
+    const uint8_t* a_src[8];
+    const uint8_t* b_src[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 32 * i + 8 * wave + lr;
+        const int64_t ar = (m0 + row < m_end) ? m0 + row : m_end - 1;
+        const int64_t br = (n0 + row < n_end) ? n0 + row : n_end - 1;
+        a_src[i] = g.a + ar * K + 16 * lc;
+        b_src[i] = Bq + br * K + 16 * lc;
+    }
+    const uint8_t* sa_src = nullptr;
+    const uint8_t* sb_src = nullptr;
+    if constexpr (MX) {
+        const int row = 64 * wave + lane;
+        const int64_t ar = (m0 + row < m_end) ? m0 + row : m_end - 1;
+        const int64_t br = (n0 + row < n_end) ? n0 + row : n_end - 1;
+        sa_src = g.sa + ar * kblocks;
+        sb_src = Bs + br * kblocks;
+    }
+    typedef __attribute__((address_space(3))) void* lds_ptr_t;
+    auto load_stage = [&](int stage, int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + k0), (lds_ptr_t)(&sA[stage][4096 * i + 1024 * wave]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + k0), (lds_ptr_t)(&sB[stage][4096 * i + 1024 * wave]), 16, 0, 0);
+        }
+        if constexpr (MX) {
+            __builtin_amdgcn_global_load_lds((const void*)(sa_src + k0 / 32), (lds_ptr_t)(&sSA[stage][64 * wave]), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(sb_src + k0 / 32), (lds_ptr_t)(&sSB[stage][64 * wave]), 4, 0, 0);
+        }
+    };
+
+    v4f acc4[8][8];
+    v16f acc16[4][4];
+    if constexpr (MF == 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc4[i][j] = v4f{};
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc16[i][j] = v16f{};
+    }
+
+    const int nk = (int)(K / KS);
+    load_stage(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) load_stage(buf ^ 1, (int64_t)(kt + 1) * KS);
+
+        if constexpr (MF == 1) {
+            const int r16 = lane & 15, q16 = lane >> 4;
+            v8i fa[8];
+            uint32_t sa_reg[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int row = wm * 128 + j * 16 + r16;
+                sa_reg[j] = MX ? (sSA[buf][row] >> (8 * q16)) : 0x7F7F7F7Fu;
+                const uint4 x0 = *reinterpret_cast<const uint4*>(&sA[buf][swz(row, q16)]);
+                const uint4 x1 = *reinterpret_cast<const uint4*>(&sA[buf][swz(row, 4 + q16)]);
+                fa[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = wn * 128 + i * 16 + r16;
+                const uint32_t sb_reg = MX ? (sSB[buf][row] >> (8 * q16)) : 0x7F7F7F7Fu;
+                const uint4 x0 = *reinterpret_cast<const uint4*>(&sB[buf][swz(row, q16)]);
+                const uint4 x1 = *reinterpret_cast<const uint4*>(&sB[buf][swz(row, 4 + q16)]);
+                const v8i fb = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc4[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[j], acc4[i][j], FB, FA, 0,
+                                                                                 (int)sb_reg, 0, (int)sa_reg[j]);
+            }
+        } else {
+            const int fr = lane & 31, fg = lane >> 5;
+            uint32_t sa_w[4], sb_w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sa_w[j] = MX ? sSA[buf][wm * 128 + j * 32 + fr] : 0x7F7F7F7Fu;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sb_w[i] = MX ? sSB[buf][wn * 128 + i * 32 + fr] : 0x7F7F7F7Fu;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                v8bf fa[4], fb[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = wm * 128 + j * 32 + fr;
+                    const uint2 x = *reinterpret_cast<const uint2*>(&sA[buf][swz(row, t) + 8 * fg]);
+                    fa[j] = dequant8_bf16<FA>(x, scale_operand((sa_w[j] >> (8 * (t >> 1))) & 0xFFu));
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = wn * 128 + i * 32 + fr;
+                    const uint2 x = *reinterpret_cast<const uint2*>(&sB[buf][swz(row, t) + 8 * fg]);
+                    fb[i] = dequant8_bf16<FB>(x, scale_operand((sb_w[i] >> (8 * (t >> 1))) & 0xFFu));
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc16[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[j], acc16[i][j], 0, 0, 0);
+            }
+        }
+
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // ------------------------------------------------------------------ epilogue
+    float post = 1.0f;
+    if constexpr (!MX) post = 1.0f / (g.pa[0] * g.pb[0]);
+    const bool vec_ok = (g.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 7) == 0;
+    auto store4 = [&](int64_t m, int64_t n, float v0, float v1, float v2, float v3) {
+        if (m >= m_end) return;
+        float v[4] = {v0, v1, v2, v3};
+        uint16_t h4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float x = v[e];
+            if constexpr (!MX) x = x * post;
+            h4[e] = __builtin_bit_cast(uint16_t, (__bf16)x);
+        }
+        uint16_t* dst = g.c + m * g.ldc + n;
+        if (vec_ok && n + 4 <= n_end) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)h4[0] | ((uint32_t)h4[1] << 16),
+                                                        (uint32_t)h4[2] | ((uint32_t)h4[3] << 16));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n + e < n_end) dst[e] = h4[e];
+        }
+    };
+    if constexpr (MF == 1) {
+        const int r16 = lane & 15, q16 = lane >> 4;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                store4(m0 + wm * 128 + j * 16 + r16, n0 + wn * 128 + i * 16 + 4 * q16, acc4[i][j][0], acc4[i][j][1],
+                       acc4[i][j][2], acc4[i][j][3]);
+    } else {
+        const int fr = lane & 31, fg = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    store4(m0 + wm * 128 + j * 32 + fr, n0 + wn * 128 + i * 32 + 8 * q + 4 * fg, acc16[i][j][4 * q],
+                           acc16[i][j][4 * q + 1], acc16[i][j][4 * q + 2], acc16[i][j][4 * q + 3]);
+    }
+}
+
 // Path selection. The FP8 matrix instructions (v_mfma_*_f8f6f4 and the older *_fp8_fp8 forms) sum the products of
 // one 32-value block with a narrow internal window: products far below the block's largest lose low-order bits,
 // an error of up to ~2^-12 of sum |a b| per instruction on wide-range data, while block sums and the fp32
@@ -338,12 +563,19 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
 // therefore used from K >= kFp8MinK (worst ratio <= 0.75); below it the operands are dequantized to bf16 (exact) for the bf16 instruction.
 constexpr int64_t kFp8MinK = 12288;
 
+// Large tiles when K is a whole number of 128-byte stages and the output spans at least a few tiles.
+static bool use_big(const GemmArgs& a) { return a.K % KS == 0 && a.M >= 512 && a.N >= 512; }
+
 template <bool MX, int FA, int FB, bool GROUPED>
-static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks, hipStream_t stream) {
-    if (a.K >= kFp8MinK)
-        hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GROUPED, 1>), dim3(blocks), dim3(GTHREADS), 0, stream, a);
-    else
-        hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GROUPED, 2>), dim3(blocks), dim3(GTHREADS), 0, stream, a);
+static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks_small, unsigned blocks_big, hipStream_t stream) {
+    const bool fp8 = a.K >= kFp8MinK;
+    if (use_big(a)) {
+        if (fp8) hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GROUPED, 1>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
+        else hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GROUPED, 2>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
+    } else {
+        if (fp8) hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GROUPED, 1>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
+        else hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GROUPED, 2>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
@@ -354,14 +586,15 @@ hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt
     a.a = a_q; a.b = b_q; a.c = c; a.M = M; a.N = N; a.K = K; a.ldc = ldc;
     if (mx) { a.sa = (const uint8_t*)a_scale; a.sb = (const uint8_t*)b_scale; }
     else { a.pa = (const float*)a_scale; a.pb = (const float*)b_scale; }
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const unsigned blocks = (unsigned)tiles;
-    if (mx) return launch_gemm_t<true, 0, 0, false>(a, blocks, stream);
-    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 0, 0, false>(a, blocks, stream);
-    if (a_fmt == FMT_E5M2 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 1, 0, false>(a, blocks, stream);
-    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E5M2) return launch_gemm_t<false, 0, 1, false>(a, blocks, stream);
-    return launch_gemm_t<false, 1, 1, false>(a, blocks, stream);
+    const int64_t small = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t big = ((M + TB - 1) / TB) * ((N + TB - 1) / TB);
+    if (small > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const unsigned bs = (unsigned)small, bb = (unsigned)big;
+    if (mx) return launch_gemm_t<true, 0, 0, false>(a, bs, bb, stream);
+    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 0, 0, false>(a, bs, bb, stream);
+    if (a_fmt == FMT_E5M2 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 1, 0, false>(a, bs, bb, stream);
+    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E5M2) return launch_gemm_t<false, 0, 1, false>(a, bs, bb, stream);
+    return launch_gemm_t<false, 1, 1, false>(a, bs, bb, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* offsets, int64_t G,
@@ -370,10 +603,11 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int
     GemmArgs a{};
     a.a = a_q; a.sa = a_s; a.b = b_q; a.sb = b_s; a.c = c;
     a.M = total_rows; a.N = N; a.K = K; a.ldc = N; a.offsets = offsets; a.G = G;
-    const int64_t row_tiles = (total_rows + BM - 1) / BM + G;   // each group adds at most one partial tile
-    const int64_t blocks = row_tiles * ((N + BN - 1) / BN);
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    return launch_gemm_t<true, 0, 0, true>(a, (unsigned)blocks, stream);
+    // each group adds at most one partial row tile
+    const int64_t small = ((total_rows + BM - 1) / BM + G) * ((N + BN - 1) / BN);
+    const int64_t big = ((total_rows + TB - 1) / TB + G) * ((N + TB - 1) / TB);
+    if (small > 0x7FFFFFFF) return hipErrorInvalidValue;
+    return launch_gemm_t<true, 0, 0, true>(a, (unsigned)small, (unsigned)big, stream);
 }
 
 }  // namespace mxq
