@@ -42,6 +42,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chu
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 // 8 FP8 codes (E4M3 when FMT == 0, E5M2 when 1) -> 8 bf16 equal to code * 2^E, where E is the exponent field of
 // `scale` (exact whenever the product is representable in bf16).
@@ -332,15 +333,45 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
 
 // ---------------------------------------------------------------------------------------------------------------
 // Large-tile kernel (K % 128 == 0): 256 x 256 output tile per workgroup, one workgroup per CU (4 waves, 2 x 2,
-// each 128 x 128), two 64 KiB LDS stages filled straight from global memory by global_load_lds_dwordx4 (no staging
-// registers). A wave's DMA instruction writes 64 consecutive 16-byte LDS slots (8 rows of 128 bytes); lane l fetches
-// global chunk (l & 7) ^ (row & 7) of its row, which leaves each row's chunks XOR-swizzled exactly as swz() reads
-// them. Rows past the end of the operand are clamped to its last row (their outputs are never stored), so every
+// each 128 x 128), two 64 KiB LDS stages filled straight from global memory by buffer_load_dwordx4 ... lds (no
+// staging registers). A wave's DMA instruction writes 64 consecutive 16-byte LDS slots (8 rows of 128 bytes); lane l
+// fetches global chunk (l & 7) ^ (row & 7) of its row, which leaves each row's chunks XOR-swizzled exactly as swz()
+// reads them. Rows past the end of the operand are clamped to its last row (their outputs are never stored), so every
 // address stays inside the caller's buffers. Workgroups are ordered so that each XCD (which receives every eighth
 // workgroup) walks a contiguous run of a grouped-M tile order: its resident workgroups share A and B tiles in its L2.
 constexpr int TB = 256;
 constexpr int KS = 128;
 constexpr int GROUP_M2 = 4;
+
+// Raw buffer resource (base, stride 0, 2^31 - 1 bytes, raw untyped access) for a workgroup-uniform address. The
+// address is moved to scalar registers explicitly: values derived from the tile index are computed with vector
+// instructions, and the descriptor must live in scalar registers.
+__device__ __forceinline__ v4i buffer_rsrc(const void* p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return v4i{(int)lo, (int)(hi & 0xFFFFu), 0x7FFFFFFF, 0x00020000};
+}
+
+// LDS offset (the low 32 bits of a shared-aperture address) of an LDS location, made wave-uniform.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
+}
+
+// Asynchronous copy global -> LDS: each lane reads BYTES (16 or 4) at base + voff + soff and the wave's results land
+// in consecutive slots starting at LDS offset `lds` (M0). Written as inline assembly on purpose: the compiler does
+// not then treat the copy as an LDS write, so it does not make later LDS reads of the *other* stage wait for it.
+// The caller orders it explicitly: every copy is complete (s_waitcnt vmcnt(0)) and published (s_barrier) before any
+// lane reads its destination, and a destination is only written after every wave has finished reading it.
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds(v4i rsrc, uint32_t lds, int voff, int soff) {
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
 
 template <bool MX, int FA, int FB, bool GROUPED, int MF>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
@@ -350,7 +381,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint32_t sSB[2][TB];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS copy bases go to M0
     const int wm = wave & 1, wn = wave >> 1;
     const int64_t K = g.K;
     const int64_t kblocks = K / 32;
@@ -394,37 +426,44 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     const int64_t n_end = (n0 + TB < g.N) ? n0 + TB : g.N;
 
     // ------------------------------------------------------------------ direct global -> LDS stage loads
+    // One resource per operand based at the tile's first row; a 32-bit per-lane row offset (row * K + chunk, below
+    // 2^31 because the host requires 256 K < 2^31) and the stage's k offset in a scalar register.
     const int lr = lane >> 3;                 // row within the wave's 8-row slab
     const int lc = (lane & 7) ^ lr;           // chunk fetched by this lane (row & 7 == lr)
-    const uint8_t* a_src[8];
-    const uint8_t* b_src[8];
+    const v4i rA = buffer_rsrc(g.a + m0 * K);
+    const v4i rB = buffer_rsrc(Bq + n0 * K);
+    int a_off[8], b_off[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int row = 32 * i + 8 * wave + lr;
-        const int64_t ar = (m0 + row < m_end) ? m0 + row : m_end - 1;
-        const int64_t br = (n0 + row < n_end) ? n0 + row : n_end - 1;
-        a_src[i] = g.a + ar * K + 16 * lc;
-        b_src[i] = Bq + br * K + 16 * lc;
+        const int ar = (m0 + row < m_end) ? row : (int)(m_end - 1 - m0);
+        const int br = (n0 + row < n_end) ? row : (int)(n_end - 1 - n0);
+        a_off[i] = ar * (int)K + 16 * lc;
+        b_off[i] = br * (int)K + 16 * lc;
     }
-    const uint8_t* sa_src = nullptr;
-    const uint8_t* sb_src = nullptr;
+    v4i rSA = rA, rSB = rB;
+    int sa_off = 0, sb_off = 0;
     if constexpr (MX) {
         const int row = 64 * wave + lane;
-        const int64_t ar = (m0 + row < m_end) ? m0 + row : m_end - 1;
-        const int64_t br = (n0 + row < n_end) ? n0 + row : n_end - 1;
-        sa_src = g.sa + ar * kblocks;
-        sb_src = Bs + br * kblocks;
+        const int ar = (m0 + row < m_end) ? row : (int)(m_end - 1 - m0);
+        const int br = (n0 + row < n_end) ? row : (int)(n_end - 1 - n0);
+        rSA = buffer_rsrc(g.sa + m0 * kblocks);
+        rSB = buffer_rsrc(Bs + n0 * kblocks);
+        sa_off = ar * (int)kblocks;
+        sb_off = br * (int)kblocks;
     }
-    typedef __attribute__((address_space(3))) void* lds_ptr_t;
-    auto load_stage = [&](int stage, int64_t k0) {
+    // One stage: 8 slabs of 8 rows per wave and operand, plus (MX) 64 rows of 4 scale bytes per wave.
+    auto load_stage = [&](int st, int k0) {
+        const uint32_t la = lds_offset(&sA[st][1024 * wave]);
+        const uint32_t lb = lds_offset(&sB[st][1024 * wave]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + k0), (lds_ptr_t)(&sA[stage][4096 * i + 1024 * wave]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + k0), (lds_ptr_t)(&sB[stage][4096 * i + 1024 * wave]), 16, 0, 0);
+            dma_to_lds<16>(rA, la + 4096 * i, a_off[i], k0);
+            dma_to_lds<16>(rB, lb + 4096 * i, b_off[i], k0);
         }
         if constexpr (MX) {
-            __builtin_amdgcn_global_load_lds((const void*)(sa_src + k0 / 32), (lds_ptr_t)(&sSA[stage][64 * wave]), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(sb_src + k0 / 32), (lds_ptr_t)(&sSB[stage][64 * wave]), 4, 0, 0);
+            dma_to_lds<4>(rSA, lds_offset(&sSA[st][64 * wave]), sa_off, k0 / 32);
+            dma_to_lds<4>(rSB, lds_offset(&sSB[st][64 * wave]), sb_off, k0 / 32);
         }
     };
 
@@ -447,64 +486,91 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+    // Per stage: the A fragments (and the first B fragment) are read from LDS, the next stage's copy is started into
+    // the other buffer, then each group of matrix instructions runs while the next group's B fragment is read. The
+    // barrier at the end publishes the next stage and keeps this buffer from being overwritten while a wave reads it.
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) load_stage(buf ^ 1, (int64_t)(kt + 1) * KS);
-
+        const uint8_t* cA = sA[buf];
+        const uint8_t* cB = sB[buf];
+        const uint32_t* cSA = sSA[buf];
+        const uint32_t* cSB = sSB[buf];
+        const bool more = kt + 1 < nk;
+        const int knext = (kt + 1) * KS;
         if constexpr (MF == 1) {
             const int r16 = lane & 15, q16 = lane >> 4;
+            auto frag = [&](const uint8_t* base, int row) {
+                const uint4 x0 = *reinterpret_cast<const uint4*>(base + swz(row, q16));
+                const uint4 x1 = *reinterpret_cast<const uint4*>(base + swz(row, 4 + q16));
+                return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+            };
             v8i fa[8];
             uint32_t sa_reg[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int row = wm * 128 + j * 16 + r16;
-                sa_reg[j] = MX ? (sSA[buf][row] >> (8 * q16)) : 0x7F7F7F7Fu;
-                const uint4 x0 = *reinterpret_cast<const uint4*>(&sA[buf][swz(row, q16)]);
-                const uint4 x1 = *reinterpret_cast<const uint4*>(&sA[buf][swz(row, 4 + q16)]);
-                fa[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                sa_reg[j] = MX ? (cSA[row] >> (8 * q16)) : 0x7F7F7F7Fu;
+                fa[j] = frag(cA, row);
             }
+            v8i fb = frag(cB, wn * 128 + r16);
+            uint32_t sb_reg = MX ? (cSB[wn * 128 + r16] >> (8 * q16)) : 0x7F7F7F7Fu;
+            if (more) load_stage(buf ^ 1, knext);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int row = wn * 128 + i * 16 + r16;
-                const uint32_t sb_reg = MX ? (sSB[buf][row] >> (8 * q16)) : 0x7F7F7F7Fu;
-                const uint4 x0 = *reinterpret_cast<const uint4*>(&sB[buf][swz(row, q16)]);
-                const uint4 x1 = *reinterpret_cast<const uint4*>(&sB[buf][swz(row, 4 + q16)]);
-                const v8i fb = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                v8i fb_next = fb;
+                uint32_t sb_next = sb_reg;
+                if (i < 7) {
+                    const int row = wn * 128 + (i + 1) * 16 + r16;
+                    fb_next = frag(cB, row);
+                    sb_next = MX ? (cSB[row] >> (8 * q16)) : 0x7F7F7F7Fu;
+                }
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     acc4[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[j], acc4[i][j], FB, FA, 0,
                                                                                  (int)sb_reg, 0, (int)sa_reg[j]);
+                fb = fb_next;
+                sb_reg = sb_next;
             }
         } else {
             const int fr = lane & 31, fg = lane >> 5;
             uint32_t sa_w[4], sb_w[4];
+            uint2 ra[4], rb[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sa_w[j] = MX ? sSA[buf][wm * 128 + j * 32 + fr] : 0x7F7F7F7Fu;
+            for (int j = 0; j < 4; ++j) sa_w[j] = MX ? cSA[wm * 128 + j * 32 + fr] : 0x7F7F7F7Fu;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sb_w[i] = MX ? sSB[buf][wn * 128 + i * 32 + fr] : 0x7F7F7F7Fu;
+            for (int i = 0; i < 4; ++i) sb_w[i] = MX ? cSB[wn * 128 + i * 32 + fr] : 0x7F7F7F7Fu;
+            auto read_t = [&](int t, uint2* xa, uint2* xb) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xa[j] = *reinterpret_cast<const uint2*>(cA + swz(wm * 128 + j * 32 + fr, t) + 8 * fg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xb[i] = *reinterpret_cast<const uint2*>(cB + swz(wn * 128 + i * 32 + fr, t) + 8 * fg);
+            };
+            read_t(0, ra, rb);
+            if (more) load_stage(buf ^ 1, knext);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
+                uint2 na[4], nb[4];
+                if (t < 7) read_t(t + 1, na, nb);
                 v8bf fa[4], fb[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int row = wm * 128 + j * 32 + fr;
-                    const uint2 x = *reinterpret_cast<const uint2*>(&sA[buf][swz(row, t) + 8 * fg]);
-                    fa[j] = dequant8_bf16<FA>(x, scale_operand((sa_w[j] >> (8 * (t >> 1))) & 0xFFu));
-                }
+                for (int j = 0; j < 4; ++j)
+                    fa[j] = dequant8_bf16<FA>(ra[j], scale_operand((sa_w[j] >> (8 * (t >> 1))) & 0xFFu));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = wn * 128 + i * 32 + fr;
-                    const uint2 x = *reinterpret_cast<const uint2*>(&sB[buf][swz(row, t) + 8 * fg]);
-                    fb[i] = dequant8_bf16<FB>(x, scale_operand((sb_w[i] >> (8 * (t >> 1))) & 0xFFu));
-                }
+                for (int i = 0; i < 4; ++i)
+                    fb[i] = dequant8_bf16<FB>(rb[i], scale_operand((sb_w[i] >> (8 * (t >> 1))) & 0xFFu));
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         acc16[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[j], acc16[i][j], 0, 0, 0);
+                if (t < 7) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) { ra[j] = na[j]; rb[j] = nb[j]; }
+                }
             }
         }
-
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
