@@ -341,6 +341,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
 // workgroup) walks a contiguous run of a grouped-M tile order: its resident workgroups share A and B tiles in its L2.
 constexpr int TB = 256;
 constexpr int KS = 128;
+constexpr int SG = 4;          // stages per MX scale group: one 16-byte scale load per row every SG stages
 constexpr int GROUP_M2 = 4;
 
 // Raw buffer resource (base, stride 0, 2^31 - 1 bytes, raw untyped access) for a workgroup-uniform address. The
@@ -377,8 +378,9 @@ template <bool MX, int FA, int FB, bool GROUPED, int MF>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][TB * KS];
     __shared__ __attribute__((aligned(16))) uint8_t sB[2][TB * KS];
-    __shared__ __attribute__((aligned(16))) uint32_t sSA[2][TB];
-    __shared__ __attribute__((aligned(16))) uint32_t sSB[2][TB];
+    // MX scales in groups of SG stages: [row][stage of the group] words, double-buffered by group.
+    __shared__ __attribute__((aligned(16))) uint32_t sSA[2][MX ? TB * SG : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t sSB[2][MX ? TB * SG : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -452,8 +454,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         sa_off = ar * (int)kblocks;
         sb_off = br * (int)kblocks;
     }
-    // One stage: 8 slabs of 8 rows per wave and operand, plus (MX) 64 rows of 4 scale bytes per wave.
-    auto load_stage = [&](int st, int k0) {
+    // One stage: 8 slabs of 8 rows per wave and operand. With the first stage of each scale group (MX) also the
+    // group's scales: 64 rows per wave of SG * 4 bytes (one 16-byte lane per row).
+    auto load_stage = [&](int st, int kt_load) {
+        const int k0 = kt_load * KS;
         const uint32_t la = lds_offset(&sA[st][1024 * wave]);
         const uint32_t lb = lds_offset(&sB[st][1024 * wave]);
 #pragma unroll
@@ -462,8 +466,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
             dma_to_lds<16>(rB, lb + 4096 * i, b_off[i], k0);
         }
         if constexpr (MX) {
-            dma_to_lds<4>(rSA, lds_offset(&sSA[st][64 * wave]), sa_off, k0 / 32);
-            dma_to_lds<4>(rSB, lds_offset(&sSB[st][64 * wave]), sb_off, k0 / 32);
+            if (kt_load % SG == 0) {
+                const int gb = (kt_load / SG) & 1;
+                dma_to_lds<16>(rSA, lds_offset(&sSA[gb][64 * SG * wave]), sa_off, k0 / 32);
+                dma_to_lds<16>(rSB, lds_offset(&sSB[gb][64 * SG * wave]), sb_off, k0 / 32);
+            }
         }
     };
 
@@ -493,10 +500,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         const int buf = kt & 1;
         const uint8_t* cA = sA[buf];
         const uint8_t* cB = sB[buf];
-        const uint32_t* cSA = sSA[buf];
-        const uint32_t* cSB = sSB[buf];
+        const int sg = kt % SG;                                   // this stage's word within its scale group
+        const uint32_t* cSA = sSA[(kt / SG) & 1];
+        const uint32_t* cSB = sSB[(kt / SG) & 1];
         const bool more = kt + 1 < nk;
-        const int knext = (kt + 1) * KS;
         if constexpr (MF == 1) {
             const int r16 = lane & 15, q16 = lane >> 4;
             auto frag = [&](const uint8_t* base, int row) {
@@ -509,12 +516,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int row = wm * 128 + j * 16 + r16;
-                sa_reg[j] = MX ? (cSA[row] >> (8 * q16)) : 0x7F7F7F7Fu;
+                sa_reg[j] = MX ? (cSA[row * SG + sg] >> (8 * q16)) : 0x7F7F7F7Fu;
                 fa[j] = frag(cA, row);
             }
             v8i fb = frag(cB, wn * 128 + r16);
-            uint32_t sb_reg = MX ? (cSB[wn * 128 + r16] >> (8 * q16)) : 0x7F7F7F7Fu;
-            if (more) load_stage(buf ^ 1, knext);
+            uint32_t sb_reg = MX ? (cSB[(wn * 128 + r16) * SG + sg] >> (8 * q16)) : 0x7F7F7F7Fu;
+            if (more) load_stage(buf ^ 1, kt + 1);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 v8i fb_next = fb;
@@ -522,7 +529,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
                 if (i < 7) {
                     const int row = wn * 128 + (i + 1) * 16 + r16;
                     fb_next = frag(cB, row);
-                    sb_next = MX ? (cSB[row] >> (8 * q16)) : 0x7F7F7F7Fu;
+                    sb_next = MX ? (cSB[row * SG + sg] >> (8 * q16)) : 0x7F7F7F7Fu;
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
@@ -536,9 +543,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
             uint32_t sa_w[4], sb_w[4];
             uint2 ra[4], rb[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sa_w[j] = MX ? cSA[wm * 128 + j * 32 + fr] : 0x7F7F7F7Fu;
+            for (int j = 0; j < 4; ++j) sa_w[j] = MX ? cSA[(wm * 128 + j * 32 + fr) * SG + sg] : 0x7F7F7F7Fu;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sb_w[i] = MX ? cSB[wn * 128 + i * 32 + fr] : 0x7F7F7F7Fu;
+            for (int i = 0; i < 4; ++i) sb_w[i] = MX ? cSB[(wn * 128 + i * 32 + fr) * SG + sg] : 0x7F7F7F7Fu;
             auto read_t = [&](int t, uint2* xa, uint2* xb) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -548,7 +555,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
                     xb[i] = *reinterpret_cast<const uint2*>(cB + swz(wn * 128 + i * 32 + fr, t) + 8 * fg);
             };
             read_t(0, ra, rb);
-            if (more) load_stage(buf ^ 1, knext);
+            if (more) load_stage(buf ^ 1, kt + 1);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 uint2 na[4], nb[4];
@@ -629,13 +636,17 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
 // therefore used from K >= kFp8MinK (worst ratio <= 0.75); below it the operands are dequantized to bf16 (exact) for the bf16 instruction.
 constexpr int64_t kFp8MinK = 12288;
 
-// Large tiles when K is a whole number of 128-byte stages and the output spans at least a few tiles.
-static bool use_big(const GemmArgs& a) { return a.K % KS == 0 && a.M >= 512 && a.N >= 512; }
+// Large tiles when K is a whole number of 128-byte stages, the output spans at least a few tiles, and a tile's
+// 256 rows of K bytes stay below 2^31 (the kernel's 32-bit buffer offsets).
+// MX operands also need K to be a whole number of scale groups (SG stages: 16-byte aligned scale rows).
+static bool use_big(const GemmArgs& a, bool mx) {
+    return a.K % (mx ? KS * SG : KS) == 0 && a.M >= 512 && a.N >= 512 && a.K <= (int64_t(1) << 22);
+}
 
 template <bool MX, int FA, int FB, bool GROUPED>
 static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks_small, unsigned blocks_big, hipStream_t stream) {
     const bool fp8 = a.K >= kFp8MinK;
-    if (use_big(a)) {
+    if (use_big(a, MX)) {
         if (fp8) hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GROUPED, 1>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
         else hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GROUPED, 2>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
     } else {
