@@ -40,7 +40,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=16)
+    ap.add_argument("--cpu-sample-rows", type=int, default=512)
+    ap.add_argument("--profile-kernel", choices=["mx_gemm_fwd", "copy"], default=None,
+                    help="run only this kernel (10 launches) for hardware-counter passes, print its timing, exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (multi-GPU sharding is a design "
@@ -56,6 +58,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.profile_kernel:
+        profile_kernel(args.profile_kernel, dev)
+        return
 
     # ------------------------------------------------------------------ inputs (resident before timing)
     log("generating inputs")
@@ -188,9 +193,10 @@ def main():
     log("rates:", json.dumps(rate))
 
     fwd_tflops = rate["mx_gemm_fwd_tflops"]
-    roofline = {"kernel": "scaled_gemm MX_BLOCK32 fwd 4096x36864x12288 (v_mfma_scale_f32_16x16x128_f8f6f4)",
+    roofline = {"kernel": "scaled_gemm MX_BLOCK32 fwd 4096x36864x12288 (gemm_big_kernel, block-scaled FP8 MFMA)",
                 "bound": "mfma", "achieved": fwd_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(fwd_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None}
+                "frac": round(fwd_tflops / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic(),
+                "algorithmic_flop_per_launch": flop_gemm, "avg_launch_ms": round(ms["mx_gemm_fwd"], 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -212,6 +218,61 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+GEMM_PMC_SUMMARY = os.path.join(ROOT, "profiles", "mx_gemm_fwd_4096x36864x12288_pmc.md")
+GEMM_SOURCE = os.path.join(ROOT, "mxfp8_precision_numerics_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the forward MX GEMM from the committed hardware-counter summary: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each divided by what the same counter read per byte of a plain copy of known
+    size. None when no summary exists or when the GEMM source has changed since the counters were taken."""
+    import hashlib
+    import re
+
+    try:
+        text = open(GEMM_PMC_SUMMARY).read()
+    except OSError:
+        return None
+    m = re.search(r"bench-traffic: fetch_kib=([\d.e+]+) write_kib=([\d.e+]+) copy_fetch_per_byte=([\d.e+-]+) "
+                  r"copy_write_per_byte=([\d.e+-]+) gemm_hip_sha256=([0-9a-f]{64})", text)
+    if not m:
+        return None
+    if hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest() != m.group(5):
+        return None
+    fetch = float(m.group(1)) * 1024 / float(m.group(3))
+    write = float(m.group(2)) * 1024 / float(m.group(4))
+    return round(fetch + write)
+
+
+def profile_kernel(name, dev):
+    """Ten launches of one kernel on seeded inputs, for rocprofv3 counter passes (one pass per counter set)."""
+    import torch
+
+    import mxfp8_precision_numerics_amd as mxq
+    from mxfp8_precision_numerics_amd import workloads
+
+    if name == "copy":
+        n = 1 << 30                                            # 1 GiB read + 1 GiB written per launch
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        run = lambda: dst.copy_(src)  # noqa: E731
+    else:
+        X, W, _ = workloads.workload2(dev)
+        qx = mxq.mx_quantize(X, colwise=False)
+        qw = mxq.mx_quantize(W, colwise=False)
+        Y = torch.empty((X.shape[0], W.shape[0]), dtype=torch.bfloat16, device=dev)
+        run = lambda: mxq.scaled_gemm(qx.q_row, qx.s_row, qw.q_row, qw.s_row, mxq.MX_BLOCK32, out=Y)  # noqa: E731
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_kernel": name, "avg_ms": round(e0.elapsed_time(e1) / 10, 4)}), flush=True)
 
 
 def cpu_baseline(X, W, rows):
