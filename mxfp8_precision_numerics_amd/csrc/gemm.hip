@@ -332,17 +332,25 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
 
 
 // ---------------------------------------------------------------------------------------------------------------
-// Large-tile kernel (K % 128 == 0): 256 x 256 output tile per workgroup, one workgroup per CU (4 waves, 2 x 2,
-// each 128 x 128), two 64 KiB LDS stages filled straight from global memory by buffer_load_dwordx4 ... lds (no
-// staging registers). A wave's DMA instruction writes 64 consecutive 16-byte LDS slots (8 rows of 128 bytes); lane l
-// fetches global chunk (l & 7) ^ (row & 7) of its row, which leaves each row's chunks XOR-swizzled exactly as swz()
-// reads them. Rows past the end of the operand are clamped to its last row (their outputs are never stored), so every
-// address stays inside the caller's buffers. Workgroups are ordered so that each XCD (which receives every eighth
-// workgroup) walks a contiguous run of a grouped-M tile order: its resident workgroups share A and B tiles in its L2.
+// Large-tile kernel: a 256 x 256 output tile per workgroup, one workgroup per CU (4 waves, 2 x 2, each 128 x 128 as
+// 4 x 4 tiles of 32 x 32 matrix instructions). K advances 64 bytes per stage. A ring of NST = 4 LDS stage buffers
+// (16 KiB per operand each) is filled straight from global memory by buffer_load_dwordx4 ... lds, three stages ahead
+// of the stage being multiplied, and the next stage's fragments are read into registers while the current stage's
+// matrix instructions run, so neither the copy latency nor the LDS latency sits between two stages.
+// One copy instruction of one wave fills a 16-row slab (1 KiB): lane l writes 16-byte slot l (row l / 4, position
+// l % 4) and fetches global chunk (l % 4) ^ swz4(row), so position p of a row holds chunk p ^ swz4(row); the fragment
+// reads of 16 consecutive rows (one chunk each) then land on distinct banks. Rows past the end of an operand are
+// clamped to its last row (their outputs are never stored), so every access stays inside the caller's buffers.
+// MX scales: one 16-byte lane per row covers SG = 8 stages (16 blocks); the groups are double-buffered.
+// Tile order: each XCD (which receives every eighth workgroup) walks a contiguous run of a grouped-M order, so its
+// resident workgroups share A and B tiles in its L2.
 constexpr int TB = 256;
-constexpr int KS = 128;
-constexpr int SG = 4;          // stages per MX scale group: one 16-byte scale load per row every SG stages
+constexpr int KS = 64;
+constexpr int NST = 4;
+constexpr int SG = 8;
 constexpr int GROUP_M2 = 4;
+
+__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
 // Raw buffer resource (base, stride 0, 2^31 - 1 bytes, raw untyped access) for a workgroup-uniform address. The
 // address is moved to scalar registers explicitly: values derived from the tile index are computed with vector
@@ -361,9 +369,9 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 
 // Asynchronous copy global -> LDS: each lane reads BYTES (16 or 4) at base + voff + soff and the wave's results land
 // in consecutive slots starting at LDS offset `lds` (M0). Written as inline assembly on purpose: the compiler does
-// not then treat the copy as an LDS write, so it does not make later LDS reads of the *other* stage wait for it.
-// The caller orders it explicitly: every copy is complete (s_waitcnt vmcnt(0)) and published (s_barrier) before any
-// lane reads its destination, and a destination is only written after every wave has finished reading it.
+// not then treat the copy as an LDS write, so LDS reads of other stages are not made to wait for it. The kernel
+// orders copies itself (wait_copies_barrier): a stage is read only after its copies have completed on every wave,
+// and a buffer is refilled only after every wave has finished reading it.
 template <int BYTES>
 __device__ __forceinline__ void dma_to_lds(v4i rsrc, uint32_t lds, int voff, int soff) {
     if constexpr (BYTES == 16)
@@ -374,13 +382,21 @@ __device__ __forceinline__ void dma_to_lds(v4i rsrc, uint32_t lds, int voff, int
                      :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 
+// Wait until at most N of this wave's copies are still outstanding (vector-memory counter, which retires in issue
+// order) and all its LDS reads have returned, then join the workgroup barrier. One asm statement with a memory
+// clobber, so the compiler keeps LDS accesses on their side of it.
+template <int N>
+__device__ __forceinline__ void wait_copies_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
 template <bool MX, int FA, int FB, bool GROUPED, int MF>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][TB * KS];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2][TB * KS];
-    // MX scales in groups of SG stages: [row][stage of the group] words, double-buffered by group.
-    __shared__ __attribute__((aligned(16))) uint32_t sSA[2][MX ? TB * SG : 1];
-    __shared__ __attribute__((aligned(16))) uint32_t sSB[2][MX ? TB * SG : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t sA[NST][TB * KS];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[NST][TB * KS];
+    // MX scales: [row][4 words] = 16 blocks = SG stages per row, double-buffered by group.
+    __shared__ __attribute__((aligned(16))) uint32_t sSA[2][MX ? TB * 4 : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t sSB[2][MX ? TB * 4 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -427,17 +443,19 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     }
     const int64_t n_end = (n0 + TB < g.N) ? n0 + TB : g.N;
 
-    // ------------------------------------------------------------------ direct global -> LDS stage loads
-    // One resource per operand based at the tile's first row; a 32-bit per-lane row offset (row * K + chunk, below
-    // 2^31 because the host requires 256 K < 2^31) and the stage's k offset in a scalar register.
-    const int lr = lane >> 3;                 // row within the wave's 8-row slab
-    const int lc = (lane & 7) ^ lr;           // chunk fetched by this lane (row & 7 == lr)
+    // ------------------------------------------------------------------ copies global -> LDS
+    // One resource per operand based at the tile's first row; 32-bit per-lane row offsets (row * K + chunk, below
+    // 2^31 because the host requires 256 K < 2^31); the stage's k offset goes in the scalar offset.
+    const int lq = lane >> 2;                  // row within the wave's 16-row slab
+    // Global chunk this lane fetches. swz4 reads row bits 1..4; the slabs of a wave are 16 * (4 i + wave), so bit 4
+    // of the row is wave & 1 for every slab of the wave.
+    const int lc = (lane & 3) ^ swz4(16 * wave + lq);
     const v4i rA = buffer_rsrc(g.a + m0 * K);
     const v4i rB = buffer_rsrc(Bq + n0 * K);
-    int a_off[8], b_off[8];
+    int a_off[4], b_off[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = 32 * i + 8 * wave + lr;
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * (4 * i + wave) + lq;
         const int ar = (m0 + row < m_end) ? row : (int)(m_end - 1 - m0);
         const int br = (n0 + row < n_end) ? row : (int)(n_end - 1 - n0);
         a_off[i] = ar * (int)K + 16 * lc;
@@ -454,132 +472,170 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         sa_off = ar * (int)kblocks;
         sb_off = br * (int)kblocks;
     }
-    // One stage: 8 slabs of 8 rows per wave and operand. With the first stage of each scale group (MX) also the
-    // group's scales: 64 rows per wave of SG * 4 bytes (one 16-byte lane per row).
-    auto load_stage = [&](int st, int kt_load) {
-        const int k0 = kt_load * KS;
-        const uint32_t la = lds_offset(&sA[st][1024 * wave]);
-        const uint32_t lb = lds_offset(&sB[st][1024 * wave]);
+    // Copies of one stage: on the first stage of a scale group (MX) the group's scales (64 rows per wave of 16
+    // bytes), then 4 slabs per operand per wave. The scales are issued first so that, copies retiring in issue order,
+    // "at most 8 copies outstanding" always means: everything but the newest stage's slabs has landed.
+    auto load_stage = [&](int st) {
+        const int k0 = st * KS;
+        if constexpr (MX) {
+            if (st % SG == 0) {
+                const int gb = (st / SG) & 1;
+                dma_to_lds<16>(rSA, lds_offset(&sSA[gb][256 * wave]), sa_off, k0 / 32);
+                dma_to_lds<16>(rSB, lds_offset(&sSB[gb][256 * wave]), sb_off, k0 / 32);
+            }
+        }
+        const uint32_t la = lds_offset(&sA[st % NST][1024 * wave]);
+        const uint32_t lb = lds_offset(&sB[st % NST][1024 * wave]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             dma_to_lds<16>(rA, la + 4096 * i, a_off[i], k0);
             dma_to_lds<16>(rB, lb + 4096 * i, b_off[i], k0);
         }
+    };
+
+    // ------------------------------------------------------------------ fragments
+    // 32 x 32 x 64 operand of lane l: row l % 32, global chunks g and 2 + g of the 64-byte stage row (g = l / 32),
+    // i.e. k = 16g .. 16g+15 and 32+16g .. 32+16g+15. Its scale operand is the scale of (row, block g), stage word
+    // (st % SG) / 2, byte 2 (st % 2) + g.
+    const int fr = lane & 31, fg = lane >> 5;
+    const int fsw = swz4(fr);                  // rows wm*128 + 32j + fr share bits 1..3 with fr
+    auto frag = [&](const uint8_t* base, int row) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(base + row * KS + 16 * (fg ^ fsw));
+        const uint4 x1 = *reinterpret_cast<const uint4*>(base + row * KS + 16 * ((2 + fg) ^ fsw));
+        return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    };
+    auto read_stage = [&](int st, v8i* fa, v8i* fb, uint32_t* sa, uint32_t* sb) {
+        const uint8_t* cA = sA[st % NST];
+        const uint8_t* cB = sB[st % NST];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fa[j] = frag(cA, wm * 128 + 32 * j + fr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fb[i] = frag(cB, wn * 128 + 32 * i + fr);
         if constexpr (MX) {
-            if (kt_load % SG == 0) {
-                const int gb = (kt_load / SG) & 1;
-                dma_to_lds<16>(rSA, lds_offset(&sSA[gb][64 * SG * wave]), sa_off, k0 / 32);
-                dma_to_lds<16>(rSB, lds_offset(&sSB[gb][64 * SG * wave]), sb_off, k0 / 32);
-            }
+            const uint32_t* cSA = sSA[(st / SG) & 1];
+            const uint32_t* cSB = sSB[(st / SG) & 1];
+            const int w = (st % SG) >> 1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sa[j] = cSA[(wm * 128 + 32 * j + fr) * 4 + w];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sb[i] = cSB[(wn * 128 + 32 * i + fr) * 4 + w];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { sa[j] = 0x7F7F7F7Fu; sb[j] = 0x7F7F7F7Fu; }
         }
     };
 
-    v4f acc4[8][8];
     v16f acc16[4][4];
-    if constexpr (MF == 1) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc4[i][j] = v4f{};
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc16[i][j] = v16f{};
-    }
+        for (int j = 0; j < 4; ++j) acc16[i][j] = v16f{};
 
-    const int nk = (int)(K / KS);
-    load_stage(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    // Per stage: the A fragments (and the first B fragment) are read from LDS, the next stage's copy is started into
-    // the other buffer, then each group of matrix instructions runs while the next group's B fragment is read. The
-    // barrier at the end publishes the next stage and keeps this buffer from being overwritten while a wave reads it.
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        const uint8_t* cA = sA[buf];
-        const uint8_t* cB = sB[buf];
-        const int sg = kt % SG;                                   // this stage's word within its scale group
-        const uint32_t* cSA = sSA[(kt / SG) & 1];
-        const uint32_t* cSB = sSB[(kt / SG) & 1];
-        const bool more = kt + 1 < nk;
+    // The matrix instructions of one stage, from fragments in registers.
+    auto mma_stage = [&](int kt, const v8i* fa, const v8i* fb, const uint32_t* sa, const uint32_t* sb) {
         if constexpr (MF == 1) {
-            const int r16 = lane & 15, q16 = lane >> 4;
-            auto frag = [&](const uint8_t* base, int row) {
-                const uint4 x0 = *reinterpret_cast<const uint4*>(base + swz(row, q16));
-                const uint4 x1 = *reinterpret_cast<const uint4*>(base + swz(row, 4 + q16));
-                return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-            };
-            v8i fa[8];
-            uint32_t sa_reg[8];
+            const int sh = 8 * (2 * (kt & 1) + fg);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int row = wm * 128 + j * 16 + r16;
-                sa_reg[j] = MX ? (cSA[row * SG + sg] >> (8 * q16)) : 0x7F7F7F7Fu;
-                fa[j] = frag(cA, row);
-            }
-            v8i fb = frag(cB, wn * 128 + r16);
-            uint32_t sb_reg = MX ? (cSB[(wn * 128 + r16) * SG + sg] >> (8 * q16)) : 0x7F7F7F7Fu;
-            if (more) load_stage(buf ^ 1, kt + 1);
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                v8i fb_next = fb;
-                uint32_t sb_next = sb_reg;
-                if (i < 7) {
-                    const int row = wn * 128 + (i + 1) * 16 + r16;
-                    fb_next = frag(cB, row);
-                    sb_next = MX ? (cSB[row * SG + sg] >> (8 * q16)) : 0x7F7F7F7Fu;
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc4[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[j], acc4[i][j], FB, FA, 0,
-                                                                                 (int)sb_reg, 0, (int)sa_reg[j]);
-                fb = fb_next;
-                sb_reg = sb_next;
-            }
+                for (int j = 0; j < 4; ++j)
+                    acc16[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fb[i], fa[j], acc16[i][j], FB, FA, 0, (int)(sb[i] >> sh), 0, (int)(sa[j] >> sh));
         } else {
-            const int fr = lane & 31, fg = lane >> 5;
-            uint32_t sa_w[4], sb_w[4];
-            uint2 ra[4], rb[4];
+            // Exact path: dequantize to bf16 and use the bf16 instruction. k-step s takes bytes 8s .. 8s+7 of each
+            // lane's 32 (A and B lanes hold the same k values, so the product sums every k of the stage once);
+            // steps 0, 1 lie in the stage's first 32-block, steps 2, 3 in its second.
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sa_w[j] = MX ? cSA[(wm * 128 + j * 32 + fr) * SG + sg] : 0x7F7F7F7Fu;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sb_w[i] = MX ? cSB[(wn * 128 + i * 32 + fr) * SG + sg] : 0x7F7F7F7Fu;
-            auto read_t = [&](int t, uint2* xa, uint2* xb) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    xa[j] = *reinterpret_cast<const uint2*>(cA + swz(wm * 128 + j * 32 + fr, t) + 8 * fg);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    xb[i] = *reinterpret_cast<const uint2*>(cB + swz(wn * 128 + i * 32 + fr, t) + 8 * fg);
-            };
-            read_t(0, ra, rb);
-            if (more) load_stage(buf ^ 1, kt + 1);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                uint2 na[4], nb[4];
-                if (t < 7) read_t(t + 1, na, nb);
-                v8bf fa[4], fb[4];
+            for (int s = 0; s < 4; ++s) {
+                const int sh = 8 * (2 * (kt & 1) + (s >> 1));
+                v8bf da[4], db[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    fa[j] = dequant8_bf16<FA>(ra[j], scale_operand((sa_w[j] >> (8 * (t >> 1))) & 0xFFu));
+                    da[j] = dequant8_bf16<FA>(make_uint2((uint32_t)fa[j][2 * s], (uint32_t)fa[j][2 * s + 1]),
+                                              scale_operand((sa[j] >> sh) & 0xFFu));
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    fb[i] = dequant8_bf16<FB>(rb[i], scale_operand((sb_w[i] >> (8 * (t >> 1))) & 0xFFu));
+                    db[i] = dequant8_bf16<FB>(make_uint2((uint32_t)fb[i][2 * s], (uint32_t)fb[i][2 * s + 1]),
+                                              scale_operand((sb[i] >> sh) & 0xFFu));
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        acc16[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[j], acc16[i][j], 0, 0, 0);
-                if (t < 7) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) { ra[j] = na[j]; rb[j] = nb[j]; }
-                }
+                        acc16[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(db[i], da[j], acc16[i][j], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+    };
+
+    // The matrix instructions are pure, so the optimizer may otherwise sink them past the (asm) waits and barriers.
+    // This empty statement reads every accumulator, so all of a stage's instructions are issued before the wait
+    // that follows it.
+    auto pin_accumulators = [&]() {
+        asm volatile("" :: "a"(acc16[0][0]), "a"(acc16[0][1]), "a"(acc16[0][2]), "a"(acc16[0][3]),
+                           "a"(acc16[1][0]), "a"(acc16[1][1]), "a"(acc16[1][2]), "a"(acc16[1][3]),
+                           "a"(acc16[2][0]), "a"(acc16[2][1]), "a"(acc16[2][2]), "a"(acc16[2][3]),
+                           "a"(acc16[3][0]), "a"(acc16[3][1]), "a"(acc16[3][2]), "a"(acc16[3][3]));
+    };
+
+    // Scheduling pattern for a stage: one matrix instruction, then the next LDS read (MX: two), so the next
+    // stage's fragment reads trickle out between the matrix instructions instead of queueing ahead of them.
+    auto interleave_reads = [&]() {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, MF == 1 ? 1 : 4, 0);   // matrix instructions
+            __builtin_amdgcn_sched_group_barrier(0x100, MX ? 2 : 1, 0);        // LDS reads
+        }
+    };
+
+    const int nk = (int)(K / KS);
+    const int pre = nk < 3 ? nk : 3;
+    for (int st = 0; st < pre; ++st) load_stage(st);
+    if (nk > 2) wait_copies_barrier<8>();                       // stages 0 and 1 have landed
+    else wait_copies_barrier<0>();
+    v8i fa[4], fb[4];
+    uint32_t sa[4], sb[4];
+    read_stage(0, fa, fb, sa, sb);
+    // The asm waits are invisible to the compiler; this visible lgkmcnt(0) (vmcnt 63 and expcnt 7: no wait) tells it
+    // that the fragment reads so far have returned, so it does not hold matrix instructions for them later.
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+
+    // Steady state: copy stage kt + 3 into the buffer stage kt - 1 used, read stage kt + 1's fragments (landed at the
+    // end of kt - 1), multiply stage kt, then wait until stage kt + 2 has landed (only kt + 3's 8 slabs may remain).
+    // Two stages per trip, ping-ponging between two fragment register sets (no copies between iterations).
+    v8i fa2[4], fb2[4];
+    uint32_t sa2[4], sb2[4];
+    auto steady = [&](int kt, v8i* ca, v8i* cb, uint32_t* csa, uint32_t* csb, v8i* na, v8i* nb, uint32_t* nsa,
+                      uint32_t* nsb) {
+        load_stage(kt + 3);
+        read_stage(kt + 1, na, nb, nsa, nsb);
+        mma_stage(kt, ca, cb, csa, csb);
+        interleave_reads();
+        pin_accumulators();
+        wait_copies_barrier<8>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+    };
+    int kt = 0;
+    for (; kt + 4 < nk; kt += 2) {
+        steady(kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
+        steady(kt + 1, fa2, fb2, sa2, sb2, fa, fb, sa, sb);
+    }
+    if (kt + 3 < nk) {
+        steady(kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
+        ++kt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { fa[j] = fa2[j]; fb[j] = fb2[j]; sa[j] = sa2[j]; sb[j] = sb2[j]; }
+    }
+    // Last (at most three) stages: everything has been issued; wait for all of it.
+    for (; kt < nk; ++kt) {
+        v8i na[4], nb[4];
+        uint32_t nsa[4], nsb[4];
+        if (kt + 1 < nk) read_stage(kt + 1, na, nb, nsa, nsb);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_stage(kt, fa, fb, sa, sb);
+        pin_accumulators();
+        wait_copies_barrier<0>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { fa[j] = na[j]; fb[j] = nb[j]; sa[j] = nsa[j]; sb[j] = nsb[j]; }
     }
 
     // ------------------------------------------------------------------ epilogue
@@ -606,25 +662,14 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
                 if (n + e < n_end) dst[e] = h4[e];
         }
     };
-    if constexpr (MF == 1) {
-        const int r16 = lane & 15, q16 = lane >> 4;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                store4(m0 + wm * 128 + j * 16 + r16, n0 + wn * 128 + i * 16 + 4 * q16, acc4[i][j][0], acc4[i][j][1],
-                       acc4[i][j][2], acc4[i][j][3]);
-    } else {
-        const int fr = lane & 31, fg = lane >> 5;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    store4(m0 + wm * 128 + j * 32 + fr, n0 + wn * 128 + i * 32 + 8 * q + 4 * fg, acc16[i][j][4 * q],
-                           acc16[i][j][4 * q + 1], acc16[i][j][4 * q + 2], acc16[i][j][4 * q + 3]);
-    }
+            for (int q = 0; q < 4; ++q)
+                store4(m0 + wm * 128 + j * 32 + fr, n0 + wn * 128 + i * 32 + 8 * q + 4 * fg, acc16[i][j][4 * q],
+                       acc16[i][j][4 * q + 1], acc16[i][j][4 * q + 2], acc16[i][j][4 * q + 3]);
 }
 
 // Path selection. The FP8 matrix instructions (v_mfma_*_f8f6f4 and the older *_fp8_fp8 forms) sum the products of
@@ -636,9 +681,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
 // therefore used from K >= kFp8MinK (worst ratio <= 0.75); below it the operands are dequantized to bf16 (exact) for the bf16 instruction.
 constexpr int64_t kFp8MinK = 12288;
 
-// Large tiles when K is a whole number of 128-byte stages, the output spans at least a few tiles, and a tile's
-// 256 rows of K bytes stay below 2^31 (the kernel's 32-bit buffer offsets).
-// MX operands also need K to be a whole number of scale groups (SG stages: 16-byte aligned scale rows).
+// Large tiles when K is a whole number of 64-byte stages, the output spans at least a few tiles, and a tile's
+// 256 rows of K bytes stay below 2^31 (the kernel's 32-bit buffer offsets). MX operands also need K to be a whole
+// number of scale groups (SG stages, 16 scale bytes per row).
 static bool use_big(const GemmArgs& a, bool mx) {
     return a.K % (mx ? KS * SG : KS) == 0 && a.M >= 512 && a.N >= 512 && a.K <= (int64_t(1) << 22);
 }
