@@ -16,6 +16,8 @@
 // Tiling: 256 threads (4 waves, 2 x 2), a 128 x 128 output tile, waves own 64 x 64 (2 x 2 instructions).
 // K advances 128 bytes per stage; stages are double-buffered in LDS. LDS rows are 128 bytes with the 16-byte chunk
 // index XOR-swizzled by (row & 7), so the 16-byte fragment reads of 8 consecutive rows hit distinct banks.
+#include <type_traits>
+
 #include "mxq_device.h"
 #include "launch.h"
 
@@ -504,9 +506,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         const uint4 x1 = *reinterpret_cast<const uint4*>(base + row * KS + 16 * ((2 + fg) ^ fsw));
         return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     };
-    auto read_stage = [&](int st, v8i* fa, v8i* fb, uint32_t* sa, uint32_t* sb) {
-        const uint8_t* cA = sA[st % NST];
-        const uint8_t* cB = sB[st % NST];
+    // BUF_C: std::integral_constant with the stage's ring buffer when it is known at compile time (then every LDS
+    // offset is an immediate), or -1.
+    auto read_stage = [&](auto buf_c, int st, v8i* fa, v8i* fb, uint32_t* sa, uint32_t* sb) {
+        constexpr int BUF = decltype(buf_c)::value;
+        const uint8_t* cA = sA[BUF < 0 ? st % NST : BUF];
+        const uint8_t* cB = sB[BUF < 0 ? st % NST : BUF];
 #pragma unroll
         for (int j = 0; j < 4; ++j) fa[j] = frag(cA, wm * 128 + 32 * j + fr);
 #pragma unroll
@@ -532,9 +537,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         for (int j = 0; j < 4; ++j) acc16[i][j] = v16f{};
 
     // The matrix instructions of one stage, from fragments in registers.
-    auto mma_stage = [&](int kt, const v8i* fa, const v8i* fb, const uint32_t* sa, const uint32_t* sb) {
+    auto mma_stage = [&](auto par_c, int kt, const v8i* fa, const v8i* fb, const uint32_t* sa, const uint32_t* sb) {
+        constexpr int PAR = decltype(par_c)::value;                // kt & 1 when known at compile time, else -1
+        const int odd = PAR < 0 ? (kt & 1) : PAR;
         if constexpr (MF == 1) {
-            const int sh = 8 * (2 * (kt & 1) + fg);
+            const int sh = 8 * (2 * odd + fg);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -547,7 +554,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
             // steps 0, 1 lie in the stage's first 32-block, steps 2, 3 in its second.
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const int sh = 8 * (2 * (kt & 1) + (s >> 1));
+                const int sh = 8 * (2 * odd + (s >> 1));
                 v8bf da[4], db[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -593,7 +600,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     else wait_copies_barrier<0>();
     v8i fa[4], fb[4];
     uint32_t sa[4], sb[4];
-    read_stage(0, fa, fb, sa, sb);
+    read_stage(std::integral_constant<int, 0>{}, 0, fa, fb, sa, sb);
     // The asm waits are invisible to the compiler; this visible lgkmcnt(0) (vmcnt 63 and expcnt 7: no wait) tells it
     // that the fragment reads so far have returned, so it does not hold matrix instructions for them later.
     __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -603,23 +610,32 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     // Two stages per trip, ping-ponging between two fragment register sets (no copies between iterations).
     v8i fa2[4], fb2[4];
     uint32_t sa2[4], sb2[4];
-    auto steady = [&](int kt, v8i* ca, v8i* cb, uint32_t* csa, uint32_t* csb, v8i* na, v8i* nb, uint32_t* nsa,
-                      uint32_t* nsb) {
+    // PH_C: kt % 4 as a std::integral_constant when known, else -1.
+    auto steady = [&](auto ph_c, int kt, v8i* ca, v8i* cb, uint32_t* csa, uint32_t* csb, v8i* na, v8i* nb,
+                      uint32_t* nsa, uint32_t* nsb) {
+        constexpr int PH = decltype(ph_c)::value;
         load_stage(kt + 3);
-        read_stage(kt + 1, na, nb, nsa, nsb);
-        mma_stage(kt, ca, cb, csa, csb);
+        read_stage(std::integral_constant<int, PH < 0 ? -1 : (PH + 1) % NST>{}, kt + 1, na, nb, nsa, nsb);
+        mma_stage(std::integral_constant<int, PH < 0 ? -1 : PH % 2>{}, kt, ca, cb, csa, csb);
         interleave_reads();
         pin_accumulators();
         wait_copies_barrier<8>();
         __builtin_amdgcn_s_waitcnt(0xC07F);
     };
+    using dyn = std::integral_constant<int, -1>;
     int kt = 0;
+    for (; kt + 6 < nk; kt += 4) {                               // kt % 4 == 0 on entry
+        steady(std::integral_constant<int, 0>{}, kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
+        steady(std::integral_constant<int, 1>{}, kt + 1, fa2, fb2, sa2, sb2, fa, fb, sa, sb);
+        steady(std::integral_constant<int, 2>{}, kt + 2, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
+        steady(std::integral_constant<int, 3>{}, kt + 3, fa2, fb2, sa2, sb2, fa, fb, sa, sb);
+    }
     for (; kt + 4 < nk; kt += 2) {
-        steady(kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
-        steady(kt + 1, fa2, fb2, sa2, sb2, fa, fb, sa, sb);
+        steady(dyn{}, kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
+        steady(dyn{}, kt + 1, fa2, fb2, sa2, sb2, fa, fb, sa, sb);
     }
     if (kt + 3 < nk) {
-        steady(kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
+        steady(dyn{}, kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
         ++kt;
 #pragma unroll
         for (int j = 0; j < 4; ++j) { fa[j] = fa2[j]; fb[j] = fb2[j]; sa[j] = sa2[j]; sb[j] = sb2[j]; }
@@ -628,9 +644,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     for (; kt < nk; ++kt) {
         v8i na[4], nb[4];
         uint32_t nsa[4], nsb[4];
-        if (kt + 1 < nk) read_stage(kt + 1, na, nb, nsa, nsb);
+        if (kt + 1 < nk) read_stage(std::integral_constant<int, -1>{}, kt + 1, na, nb, nsa, nsb);
         __builtin_amdgcn_sched_barrier(0);
-        mma_stage(kt, fa, fb, sa, sb);
+        mma_stage(std::integral_constant<int, -1>{}, kt, fa, fb, sa, sb);
         pin_accumulators();
         wait_copies_barrier<0>();
         __builtin_amdgcn_s_waitcnt(0xC07F);
