@@ -28,6 +28,8 @@ struct QuantArgs {
     uint8_t* q_col;     // MX: q_col ; per-tensor: q_t
     uint8_t* s_col;     // MX only
     const float* scale; // per-tensor only
+    int srow_words;     // s_row rows hold whole 4-byte words per 128-column tile (cols % 128 == 0, 4-aligned)
+    int scol_words;     // s_col likewise (rows % 128 == 0, 4-aligned)
 };
 
 template <int MODE>
@@ -88,9 +90,19 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
                     lo = mx_patch4(lo, v[j].x, v[j].y, thr);
                     hi = mx_patch4(hi, v[j].z, v[j].w, thr);
                 }
+                // The 16 lanes of a tile row hold its 4 block bytes at chunks 0, 4, 8, 12; chunk 0 gathers them.
+                const uint32_t b4 = (uint32_t)__shfl_down((int)byte, 4, 16);
+                const uint32_t b8 = (uint32_t)__shfl_down((int)byte, 8, 16);
+                const uint32_t b12 = (uint32_t)__shfl_down((int)byte, 12, 16);
                 if (col_ok && gr < a.rows) {
                     *reinterpret_cast<uint2*>(a.q_row + gr * a.cols + gc) = make_uint2(lo, hi);
-                    if ((tid & 3) == 0) a.s_row[gr * (a.cols / 32) + gc / 32] = (uint8_t)byte;
+                    if (a.srow_words) {
+                        if (ch == 0)
+                            *reinterpret_cast<uint32_t*>(a.s_row + gr * (a.cols / 32) + c0 / 32) =
+                                byte | (b4 << 8) | (b8 << 16) | (b12 << 24);
+                    } else if ((tid & 3) == 0) {
+                        a.s_row[gr * (a.cols / 32) + gc / 32] = (uint8_t)byte;
+                    }
                 }
             } else {
                 lo = pt_cvt_quad<MODE>(pt_scale, v[j].x, v[j].y);
@@ -107,18 +119,16 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
         uint32_t d[32];
 #pragma unroll
         for (int r = 0; r < 32; ++r) d[r] = lds[(32 * b + r) * (QT / 2) + p];
-        const int64_t gcol = c0 + 2 * p;
-        const int64_t grow = r0 + 32 * b;
-        const bool ok0 = gcol < a.cols && grow + 32 <= a.rows;
-        const bool ok1 = gcol + 1 < a.cols && grow + 32 <= a.rows;
         uint32_t out0[8], out1[8];
+        uint32_t sb0 = 0, sb1 = 0;
         if constexpr (MX) {
             uint32_t m = 0;
 #pragma unroll
             for (int r = 0; r < 32; ++r) m = max_u16x2(m, d[r] & 0x7FFF7FFFu);
             const uint32_t m0 = m & 0xFFFFu, m1 = m >> 16;
-            const uint32_t b0 = mx_scale_byte(m0, RULE), b1 = mx_scale_byte(m1, RULE);
-            const float s0 = scale_operand(b0), s1 = scale_operand(b1);
+            sb0 = mx_scale_byte(m0, RULE);
+            sb1 = mx_scale_byte(m1, RULE);
+            const float s0 = scale_operand(sb0), s1 = scale_operand(sb1);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 // pairs down the column: lo halves -> column 2p, hi halves -> column 2p+1
@@ -128,11 +138,9 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
                 uint32_t h1 = __builtin_amdgcn_perm(d[4 * i + 3], d[4 * i + 2], 0x07060302u);
                 out0[i] = cvt_mx_quad(a0, a1, s0);
                 out1[i] = cvt_mx_quad(h0, h1, s1);
-                if (RULE == RULE_FLOOR || m0 >= 0x7F80u) out0[i] = mx_patch4(out0[i], a0, a1, mx_sat_threshold(b0));
-                if (RULE == RULE_FLOOR || m1 >= 0x7F80u) out1[i] = mx_patch4(out1[i], h0, h1, mx_sat_threshold(b1));
+                if (RULE == RULE_FLOOR || m0 >= 0x7F80u) out0[i] = mx_patch4(out0[i], a0, a1, mx_sat_threshold(sb0));
+                if (RULE == RULE_FLOOR || m1 >= 0x7F80u) out1[i] = mx_patch4(out1[i], h0, h1, mx_sat_threshold(sb1));
             }
-            if (ok0) a.s_col[gcol * (a.rows / 32) + grow / 32] = (uint8_t)b0;
-            if (ok1) a.s_col[(gcol + 1) * (a.rows / 32) + grow / 32] = (uint8_t)b1;
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -144,15 +152,49 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
                 out1[i] = pt_cvt_quad<MODE>(pt_scale, h0, h1);
             }
         }
-        if (ok0) {
-            uint4* dst = reinterpret_cast<uint4*>(a.q_col + gcol * a.rows + grow);
-            dst[0] = make_uint4(out0[0], out0[1], out0[2], out0[3]);
-            dst[1] = make_uint4(out0[4], out0[5], out0[6], out0[7]);
+        // Transpose the codes once more through LDS so that the global stores write whole 128-byte lines: output
+        // row c (column c of x) is 128 bytes; its 16-byte chunk k sits at chunk k ^ ((c >> 1) & 7) to spread the
+        // writes of neighbouring columns over the banks.
+        __syncthreads();                                           // every thread has read its input column pair
+        uint8_t* obuf = reinterpret_cast<uint8_t*>(lds);           // 128 x 128 codes, then 128 x 4 scale bytes
+        {
+            const int c_even = 2 * p, c_odd = 2 * p + 1;
+            const int k0 = 2 * b, k1 = 2 * b + 1;                  // the two 16-byte chunks of rows 32b .. 32b+31
+            uint4* e = reinterpret_cast<uint4*>(obuf + c_even * QT);
+            uint4* o = reinterpret_cast<uint4*>(obuf + c_odd * QT);
+            e[k0 ^ ((c_even >> 1) & 7)] = make_uint4(out0[0], out0[1], out0[2], out0[3]);
+            e[k1 ^ ((c_even >> 1) & 7)] = make_uint4(out0[4], out0[5], out0[6], out0[7]);
+            o[k0 ^ ((c_odd >> 1) & 7)] = make_uint4(out1[0], out1[1], out1[2], out1[3]);
+            o[k1 ^ ((c_odd >> 1) & 7)] = make_uint4(out1[4], out1[5], out1[6], out1[7]);
+            if constexpr (MX) {
+                obuf[QT * QT + c_even * 4 + b] = (uint8_t)sb0;
+                obuf[QT * QT + c_odd * 4 + b] = (uint8_t)sb1;
+            }
         }
-        if (ok1) {
-            uint4* dst = reinterpret_cast<uint4*>(a.q_col + (gcol + 1) * a.rows + grow);
-            dst[0] = make_uint4(out1[0], out1[1], out1[2], out1[3]);
-            dst[1] = make_uint4(out1[4], out1[5], out1[6], out1[7]);
+        __syncthreads();
+#pragma unroll
+        for (int pass = 0; pass < QT / 32; ++pass) {               // 32 output rows (x columns) per pass
+            const int c = 32 * pass + (tid >> 3), k = tid & 7;
+            const int64_t gc2 = c0 + c, gr2 = r0 + 16 * k;
+            if (gc2 < a.cols && gr2 < a.rows) {                    // rows % 32 == 0: a 16-row chunk is whole
+                const uint4 val = *reinterpret_cast<const uint4*>(obuf + c * QT + 16 * (k ^ ((c >> 1) & 7)));
+                *reinterpret_cast<uint4*>(a.q_col + gc2 * a.rows + gr2) = val;
+            }
+        }
+        if constexpr (MX) {
+            if (tid < QT) {
+                const int c = tid;
+                const int64_t gc2 = c0 + c;
+                if (gc2 < a.cols) {
+                    const uint32_t w = *reinterpret_cast<const uint32_t*>(obuf + QT * QT + 4 * c);
+                    uint8_t* dst = a.s_col + gc2 * (a.rows / 32) + r0 / 32;
+                    if (a.scol_words) {
+                        *reinterpret_cast<uint32_t*>(dst) = w;
+                    } else {
+                        for (int bb = 0; bb < 4 && r0 + 32 * bb < a.rows; ++bb) dst[bb] = (uint8_t)(w >> (8 * bb));
+                    }
+                }
+            }
         }
     }
 }
@@ -168,7 +210,9 @@ static hipError_t launch_quant_mode(const QuantArgs& a, bool row, bool col, hipS
 
 hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
                               uint8_t* q_col, uint8_t* s_col, int rule, hipStream_t stream) {
-    QuantArgs a{x, rows, cols, q_row, s_row, q_col, s_col, nullptr};
+    QuantArgs a{x, rows, cols, q_row, s_row, q_col, s_col, nullptr, 0, 0};
+    a.srow_words = cols % QT == 0 && (reinterpret_cast<uintptr_t>(s_row) & 3) == 0;
+    a.scol_words = rows % QT == 0 && (reinterpret_cast<uintptr_t>(s_col) & 3) == 0;
     bool row = q_row != nullptr, col = q_col != nullptr;
     return rule == RULE_FLOOR ? launch_quant_mode<QM_MX_FLOOR>(a, row, col, stream)
                               : launch_quant_mode<QM_MX_RCEIL>(a, row, col, stream);
@@ -256,7 +300,7 @@ hipError_t launch_pertensor_quantize(const uint16_t* x, int64_t rows, int64_t co
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (!q && !q_t) return hipSuccess;
-    QuantArgs a{x, rows, cols, q, nullptr, q_t, nullptr, scale_out};
+    QuantArgs a{x, rows, cols, q, nullptr, q_t, nullptr, scale_out, 0, 0};
     return fmt == FMT_E4M3 ? launch_quant_mode<QM_PT_E4M3>(a, q != nullptr, q_t != nullptr, stream)
                            : launch_quant_mode<QM_PT_E5M2>(a, q != nullptr, q_t != nullptr, stream);
 }
