@@ -67,9 +67,7 @@ __global__ __launch_bounds__(ATHREADS) void adam_amax_kernel(const uint16_t* __r
     uint32_t mx = 0;
     const int64_t chunks = n / 8;
     const int64_t stride = (int64_t)gridDim.x * ATHREADS;
-    for (int64_t i = (int64_t)blockIdx.x * ATHREADS + threadIdx.x; i < chunks; i += stride) {
-        const uint4 gv = ldnt16(g + 8 * i);
-        const uint2 mv = ldnt8(mq + 8 * i);
+    auto reduce = [&](const uint4& gv, const uint2& mv) {
         const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -79,7 +77,18 @@ __global__ __launch_bounds__(ATHREADS) void adam_amax_kernel(const uint16_t* __r
             adam_moments(k, inv_s, g16, m8, 0u, m, v);
             mx = max(mx, __float_as_uint(m) & 0x7FFFFFFFu);
         }
+    };
+    int64_t i = (int64_t)blockIdx.x * ATHREADS + threadIdx.x;
+    for (; i + stride < chunks; i += 2 * stride) {              // two chunks per trip, loads first
+        const int64_t j = i + stride;
+        const uint4 ag = ldnt16(g + 8 * i);
+        const uint2 am = ldnt8(mq + 8 * i);
+        const uint4 bg = ldnt16(g + 8 * j);
+        const uint2 bm = ldnt8(mq + 8 * j);
+        reduce(ag, am);
+        reduce(bg, bm);
     }
+    if (i < chunks) reduce(ldnt16(g + 8 * i), ldnt8(mq + 8 * i));
     if (blockIdx.x == 0)
         for (int64_t i = chunks * 8 + threadIdx.x; i < n; i += ATHREADS) {
             float m, v;
@@ -135,12 +144,9 @@ __global__ __launch_bounds__(ATHREADS) void adam_update_kernel(float* __restrict
     const float inv_s = consts[0], s_new = consts[1];
     const int64_t chunks = n / 8;
     const int64_t stride = (int64_t)gridDim.x * ATHREADS;
-    for (int64_t i = (int64_t)blockIdx.x * ATHREADS + threadIdx.x; i < chunks; i += stride) {
-        const uint4 t0 = ldnt16(master + 8 * i);
-        const uint4 t1 = ldnt16(master + 8 * i + 4);
-        const uint4 gv = ldnt16(g + 8 * i);
-        const uint2 mv = ldnt8(mq + 8 * i);
-        const uint4 vv = ldnt16(v16 + 8 * i);
+    // Two chunks per trip (the second one stride further on), all loads issued before any arithmetic, so twice as
+    // many 16-byte accesses are in flight per thread.
+    auto process = [&](int64_t i, const uint4& t0, const uint4& t1, const uint4& gv, const uint2& mv, const uint4& vv) {
         const uint32_t th[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
         const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
         const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
@@ -163,7 +169,24 @@ __global__ __launch_bounds__(ATHREADS) void adam_update_kernel(float* __restrict
         stnt8(mq + 8 * i, make_uint2(mo[0], mo[1]));
         stnt16(v16 + 8 * i, make_uint4(vo[0], vo[1], vo[2], vo[3]));
         if (w) stnt16(w + 8 * i, make_uint4(wo[0], wo[1], wo[2], wo[3]));
+    };
+    int64_t i = (int64_t)blockIdx.x * ATHREADS + threadIdx.x;
+    for (; i + stride < chunks; i += 2 * stride) {
+        const int64_t j = i + stride;
+        const uint4 a0 = ldnt16(master + 8 * i), a1 = ldnt16(master + 8 * i + 4);
+        const uint4 ag = ldnt16(g + 8 * i);
+        const uint2 am = ldnt8(mq + 8 * i);
+        const uint4 av = ldnt16(v16 + 8 * i);
+        const uint4 b0 = ldnt16(master + 8 * j), b1 = ldnt16(master + 8 * j + 4);
+        const uint4 bg = ldnt16(g + 8 * j);
+        const uint2 bm = ldnt8(mq + 8 * j);
+        const uint4 bv = ldnt16(v16 + 8 * j);
+        process(i, a0, a1, ag, am, av);
+        process(j, b0, b1, bg, bm, bv);
     }
+    if (i < chunks)
+        process(i, ldnt16(master + 8 * i), ldnt16(master + 8 * i + 4), ldnt16(g + 8 * i), ldnt8(mq + 8 * i),
+                ldnt16(v16 + 8 * i));
     if (blockIdx.x == 0)
         for (int64_t i = chunks * 8 + threadIdx.x; i < n; i += ATHREADS) {
             float t_out;
