@@ -62,6 +62,12 @@ def lib():
         L.orc_adam_step.argtypes = [P, P, P, P, P, P, I64, P, I]
         L.orc_adam_amax.restype = F
         L.orc_adam_amax.argtypes = [P, P, P, F, I64, P, I]
+        L.orc_delayed_scale.restype = F
+        L.orc_delayed_scale.argtypes = [P, I64, I, F]
+        L.orc_history_push.argtypes = [P, I64, P, F]
+        L.orc_pertensor_quantize_delayed.argtypes = [P, I64, I64, I, F, P, I64, P, P, P, P, P, I]
+        L.orc_adam_step_delayed.restype = F
+        L.orc_adam_step_delayed.argtypes = [P, P, P, P, P, P, I64, P, P, I64, P, I]
         L.orc_adam_elements.argtypes = [P, P, P, P, F, F, P, I64, P, P, P, P, P]
         _lib = L
     return _lib
@@ -157,6 +163,29 @@ def pertensor_quantize(x_bf16, fmt: int = E4M3, margin: float = 1.0, scale_in: f
     return float(amax[0]), np.float32(scale[0]), q, qt
 
 
+def delayed_scale(history, fmt: int = E4M3, margin: float = 1.0) -> np.float32:
+    """Scale of a delayed-scaling cast: FMAX / max(max(history), 1e-12) * margin (fp32)."""
+    h = _c(history, np.float32)
+    return np.float32(lib().orc_delayed_scale(_p(h), h.size, fmt, C.c_float(margin)))
+
+
+def pertensor_quantize_delayed(x_bf16, history, pos, fmt: int = E4M3, margin: float = 1.0, want_q: bool = True,
+                               want_qt: bool = True, nthreads: int | None = None):
+    """One delayed-scaling cast. history (float32[H]) and pos (int32[1]) are updated in place.
+    Returns (amax, scale, q, q_t)."""
+    assert history.dtype == np.float32 and history.flags.c_contiguous
+    assert pos.dtype == np.int32 and pos.size == 1
+    x = _c(x_bf16, np.uint16)
+    R, Ccols = x.shape
+    amax = np.zeros(1, np.float32)
+    scale = np.zeros(1, np.float32)
+    q = np.empty((R, Ccols), np.uint8) if want_q else None
+    qt = np.empty((Ccols, R), np.uint8) if want_qt else None
+    lib().orc_pertensor_quantize_delayed(_p(x), R, Ccols, fmt, C.c_float(margin), _p(history), history.size, _p(pos),
+                                         _p(amax), _p(scale), _p(q), _p(qt), nthreads or default_threads())
+    return float(amax[0]), np.float32(scale[0]), q, qt
+
+
 # ---------------------------------------------------------------- GEMM references
 def gemm_ref(a_q, a_scale, a_fmt, b_q, b_scale, b_fmt, scaling, rows=None, cols=None, nthreads=None):
     """y, S over rows x cols of C = A B^T (fp64). a_q [M][K], b_q [N][K]; scales are E8M0 grids (MX) or fp32 scalars."""
@@ -206,6 +235,20 @@ def adam_step(master, grad_bf16, m_q, m_scale, v16, hp: AdamHP, want_w=True, nth
     w = np.empty(n, np.uint16) if want_w else None
     amax = lib().orc_adam_step(_p(master), _p(g), _p(m_q), _p(m_scale), _p(v16), _p(w), n, C.byref(hp),
                                nthreads or default_threads())
+    return float(amax), w
+
+
+def adam_step_delayed(master, grad_bf16, m_q, m_scale, v16, hp: AdamHP, history, pos, want_w=True, nthreads=None):
+    """Adam step whose m scale comes from the amax history (float32[H], int32[1] position; both updated in place).
+    In place on master, m_q, m_scale, v16 as adam_step. Returns (amax_m, w_bf16)."""
+    for a, dt in ((master, np.float32), (m_q, np.uint8), (m_scale, np.float32), (v16, np.uint16),
+                  (history, np.float32), (pos, np.int32)):
+        assert a.dtype == dt and a.flags.c_contiguous
+    g = _c(grad_bf16, np.uint16)
+    n = master.size
+    w = np.empty(n, np.uint16) if want_w else None
+    amax = lib().orc_adam_step_delayed(_p(master), _p(g), _p(m_q), _p(m_scale), _p(v16), _p(w), n, C.byref(hp),
+                                       _p(history), history.size, _p(pos), nthreads or default_threads())
     return float(amax), w
 
 

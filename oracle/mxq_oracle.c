@@ -319,6 +319,45 @@ void orc_pertensor_quantize(const uint16_t* x, int64_t rows, int64_t cols, int f
 }
 
 /* ------------------------------------------------------------------------------------------------------
+ * Delayed per-tensor scaling ([LLMSB] "Per-tensor scaling and the delayed-scaling recipe", the DelayedScale
+ * sketch; [FP8-LM] Section 3.4, delayed scaling): a rolling history of the amax of past calls; this call's scale
+ * is FMAX over the history's maximum (clamped below at 1e-12) times the margin; the tensor is cast with it; then
+ * this call's own amax is written at the history's current position, which advances cyclically.
+ * ------------------------------------------------------------------------------------------------------ */
+
+/* max over the history (a NaN entry makes it NaN), clamped at 1e-12, FMAX / that, times margin; all fp32. */
+float orc_delayed_scale(const float* history, int64_t H, int fmt, float margin)
+{
+    float m = 0.0f;
+    for (int64_t i = 0; i < H; ++i) {
+        float h = history[i];
+        if (isnan(h) || isnan(m)) m = NAN;
+        else if (h > m) m = h;
+    }
+    float fmax = (fmt == ORC_E4M3) ? 448.0f : 57344.0f;
+    float a = (m < 1e-12f) ? 1e-12f : m;
+    float s = fmax / a;
+    return s * margin;
+}
+
+void orc_history_push(float* history, int64_t H, int32_t* pos, float amax)
+{
+    history[*pos] = amax;
+    *pos = (int32_t)((*pos + 1) % H);
+}
+
+void orc_pertensor_quantize_delayed(const uint16_t* x, int64_t rows, int64_t cols, int fmt, float margin,
+                                    float* history, int64_t H, int32_t* pos, float* amax_out, float* scale_out,
+                                    uint8_t* q, uint8_t* q_t, int nthreads)
+{
+    float s = orc_delayed_scale(history, H, fmt, margin);
+    float amax = 0.0f;
+    orc_pertensor_quantize(x, rows, cols, fmt, margin, &s, &amax, scale_out, q, q_t, nthreads);
+    if (amax_out) *amax_out = amax;
+    orc_history_push(history, H, pos, amax);
+}
+
+/* ------------------------------------------------------------------------------------------------------
  * GEMM reference: C = A * B^T with A given as [M][K] qdata and B as [N][K] qdata (both K-contiguous).
  *   MX_BLOCK32: a_hat[i][k] = val(qa[i][k]) * 2^(sa[i][k/32] - 127), likewise b_hat; y = sum_k a_hat * b_hat.
  *   PER_TENSOR: y = (sum_k val(qa) * val(qb)) / (s_a * s_b)     ([LLMSB] Exercise 6: de-scale by 1/(s_x s_w)).
@@ -538,6 +577,40 @@ float orc_adam_step(float* master, const uint16_t* grad_bf16, uint8_t* m_q, floa
     }
     for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
     m_scale[0] = k.s_new;
+    return amax;
+}
+
+/* Adam with a delayed first-moment scale: the scale that encodes this step's m_t is E4M3's 448 over the maximum of
+ * the amax history of m from earlier steps (clamped at 1e-12); the amax of this step's m_t is then pushed into the
+ * history. Every other operation is the one of orc_adam_step. Returns the amax of m_t. */
+float orc_adam_step_delayed(float* master, const uint16_t* grad_bf16, uint8_t* m_q, float* m_scale, uint16_t* v16,
+                            uint16_t* w_bf16, int64_t n, const orc_adam_hp* hp, float* history, int64_t H,
+                            int32_t* pos, int nthreads)
+{
+    tables();
+    nthreads = clamp_threads(nthreads);
+    adam_consts k = adam_setup(hp, m_scale[0]);
+    k.s_new = orc_delayed_scale(history, H, ORC_E4M3, 1.0f);
+    pthread_t th[256];
+    adam_job jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (adam_job){master, grad_bf16, m_q, v16, w_bf16, n, &k, 0.0f, 1, nthreads, t};
+        pthread_create(&th[t], NULL, adam_worker, &jobs[t]);          /* amax of m_t, from the old state */
+    }
+    float amax = 0.0f;
+    for (int t = 0; t < nthreads; ++t) {
+        pthread_join(th[t], NULL);
+        float a = jobs[t].amax;
+        if (isnan(a) || isnan(amax)) amax = NAN;
+        else if (a > amax) amax = a;
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t].pass = 2;
+        pthread_create(&th[t], NULL, adam_worker, &jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+    m_scale[0] = k.s_new;
+    orc_history_push(history, H, pos, amax);
     return amax;
 }
 
