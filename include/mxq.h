@@ -88,6 +88,25 @@ mxq_status fp8_quantize_pertensor(const uint16_t* x_bf16, int64_t rows, int64_t 
                                   hipStream_t stream);
 
 /*
+ * Delayed per-tensor scaling: one pass over x instead of two ([LLMSB] "Per-tensor scaling and the delayed-scaling
+ * recipe", the DelayedScale sketch; [FP8-LM] Section 3.4, delayed scaling).
+ *   amax_history: device float[history_len] (in/out), hist_pos: device int32[1] (in/out, 0 <= pos < history_len),
+ *   1 <= history_len <= 2^20.
+ *   scale_out[0] = (FMAX / max(max(amax_history), 1e-12)) * margin, from the history as it was before this call
+ *                  (fp32 division and product; a NaN entry gives a NaN scale);
+ *   q[rows][cols] = FP8(fp32(x * scale)) and q_t[cols][rows] its transpose; either or both may be NULL;
+ *   amax_out[0] = max |x| of this call, which is then stored at amax_history[pos], and pos = (pos + 1) % history_len.
+ * All of this happens on the device, in stream order; the host never sees the scale. An all-zero history gives the
+ * scale FMAX / 1e-12, which saturates every nonzero value: seed the history (for example with the amax of a
+ * current-scaling call) before relying on it. workspace: at least mxq_workspace_bytes("pertensor_delayed", n) bytes,
+ * clobbered.
+ */
+mxq_status fp8_quantize_pertensor_delayed(const uint16_t* x_bf16, int64_t rows, int64_t cols, mxq_fp8 fmt,
+                                          float margin, float* amax_history, int32_t* hist_pos, int64_t history_len,
+                                          float* amax_out, float* scale_out, uint8_t* q, uint8_t* q_t,
+                                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Scaled FP8 GEMM with fp32 accumulation and a bf16 epilogue ([OLMO11] Figure 47 and Section 11.2.3:
  * block scales applied inside the matrix operation, BF16 output; [LLMSB] Exercise 6: de-scale by 1/(s_a s_b)):
  *   C[M][N] (row-major, leading dimension ldc >= N, in elements) = bf16_rne( A[M][K] * B[N][K]^T ).
@@ -144,7 +163,22 @@ mxq_status fp8_adam_step(float* master, const uint16_t* grad_bf16, uint8_t* m_q,
                          uint16_t* v_fp16, uint16_t* w_bf16, int64_t n, const mxq_adam_hparams* hp,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes needed by op ("pertensor" or "adam") for n elements; 0 for an unknown op. op is a host string. */
+/*
+ * The same AdamW step with a delayed first-moment scale, in one pass over the state (no amax pre-pass; [FP8-LM]
+ * Section 3.4, tensor-scaled first moment with delayed scaling):
+ *   s_new = 448 / max(max(m_history), 1e-12) from the amax of m of earlier steps encodes this step's m_t;
+ *   m_scale[0] <- s_new; the amax of this step's m_t is stored at m_history[pos], and pos = (pos + 1) % history_len.
+ * m_history: device float[history_len], hist_pos: device int32[1], both in/out (1 <= history_len <= 2^20). Every
+ * other output is computed exactly as in fp8_adam_step. An all-zero history saturates m (seed it, for example with the
+ * amax one current-scaling step reports). workspace: mxq_workspace_bytes("adam_delayed", n) bytes, clobbered.
+ */
+mxq_status fp8_adam_step_delayed(float* master, const uint16_t* grad_bf16, uint8_t* m_q, float* m_scale,
+                                 uint16_t* v_fp16, uint16_t* w_bf16, int64_t n, const mxq_adam_hparams* hp,
+                                 float* m_history, int32_t* hist_pos, int64_t history_len, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by op ("pertensor", "adam", "pertensor_delayed" or "adam_delayed") for n elements; 0 for an
+ * unknown op. op is a host string. */
 size_t mxq_workspace_bytes(const char* op, int64_t n);
 
 #ifdef __cplusplus

@@ -96,6 +96,27 @@ def pertensor_quantize(x: torch.Tensor, fmt: int = E4M3, margin: float = 1.0, sc
     return PerTensorFP8(q, qt, amax, scale)
 
 
+def pertensor_quantize_delayed(x: torch.Tensor, amax_history: torch.Tensor, hist_pos: torch.Tensor, fmt: int = E4M3,
+                               margin: float = 1.0, want_q: bool = True, want_qt: bool = True,
+                               workspace: Optional[torch.Tensor] = None) -> PerTensorFP8:
+    """Delayed-scaling cast: scale from the amax history (float32[H], updated in place with this call's amax at
+    hist_pos, an int32[1] that advances)."""
+    _dev(x, torch.bfloat16, "x"); _dev(amax_history, torch.float32, "amax_history"); _dev(hist_pos, torch.int32, "hist_pos")
+    rows, cols = x.shape
+    dev = x.device
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev) if want_q else None
+    qt = torch.empty((cols, rows), dtype=torch.uint8, device=dev) if want_qt else None
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes("pertensor_delayed", rows * cols), dtype=torch.uint8, device=dev)
+    st = _lib.load().fp8_quantize_pertensor_delayed(_ptr(x), rows, cols, fmt, C.c_float(margin), _ptr(amax_history),
+                                                    _ptr(hist_pos), amax_history.numel(), _ptr(amax), _ptr(scale),
+                                                    _ptr(q), _ptr(qt), _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check("fp8_quantize_pertensor_delayed", st)
+    return PerTensorFP8(q, qt, amax, scale)
+
+
 def scaled_gemm(a_q: torch.Tensor, a_scale: torch.Tensor, b_q: torch.Tensor, b_scale: torch.Tensor,
                 scaling: int = MX_BLOCK32, a_fmt: int = E4M3, b_fmt: int = E4M3,
                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -141,3 +162,19 @@ def fp8_adam_step(master: torch.Tensor, grad: torch.Tensor, m_q: torch.Tensor, m
     st = _lib.load().fp8_adam_step(_ptr(master), _ptr(grad), _ptr(m_q), _ptr(m_scale), _ptr(v), _ptr(w), n,
                                    C.byref(hp), _ptr(workspace), workspace.numel(), _stream(master.device))
     _lib.check("fp8_adam_step", st)
+
+
+def fp8_adam_step_delayed(master: torch.Tensor, grad: torch.Tensor, m_q: torch.Tensor, m_scale: torch.Tensor,
+                          v: torch.Tensor, w: Optional[torch.Tensor], hp: AdamHParams, m_history: torch.Tensor,
+                          hist_pos: torch.Tensor, workspace: Optional[torch.Tensor] = None) -> None:
+    """fp8_adam_step with the first-moment scale from the amax history (one pass over the state)."""
+    _dev(master, torch.float32, "master"); _dev(grad, torch.bfloat16, "grad"); _dev(m_q, torch.uint8, "m_q")
+    _dev(m_scale, torch.float32, "m_scale"); _dev(v, torch.float16, "v")
+    _dev(m_history, torch.float32, "m_history"); _dev(hist_pos, torch.int32, "hist_pos")
+    n = master.numel()
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes("adam_delayed", n), dtype=torch.uint8, device=master.device)
+    st = _lib.load().fp8_adam_step_delayed(_ptr(master), _ptr(grad), _ptr(m_q), _ptr(m_scale), _ptr(v), _ptr(w), n,
+                                           C.byref(hp), _ptr(m_history), _ptr(hist_pos), m_history.numel(),
+                                           _ptr(workspace), workspace.numel(), _stream(master.device))
+    _lib.check("fp8_adam_step_delayed", st)

@@ -16,8 +16,31 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 size_t pertensor_ws(int64_t n) { return round_up((size_t)mxq::pertensor_amax_parts(n) * 4u, 256); }
 size_t adam_ws(int64_t n) { return round_up((size_t)mxq::adam_parts(n) * 4u, 256) + 256; }
+constexpr size_t kDelayedWs = 256;   // delayed modes: the atomic amax word (and Adam's three constants)
+constexpr int64_t kMaxHistory = 1 << 20;
 
 constexpr int64_t kMaxGridY = 65535;
+
+// Adam's host scalars in double, each rounded once to float. beta^t is the product of t factors (it reaches 0 long
+// before t is large, after which further factors change nothing).
+mxq::AdamConsts adam_consts(const mxq_adam_hparams& hp) {
+    double p1 = 1.0, p2 = 1.0;
+    for (int64_t t = 0; t < hp.step && (p1 != 0.0 || p2 != 0.0); ++t) {
+        p1 *= (double)hp.beta1;
+        p2 *= (double)hp.beta2;
+    }
+    mxq::AdamConsts k;
+    k.b1 = hp.beta1;
+    k.ob1 = (float)(1.0 - (double)hp.beta1);
+    k.b2 = hp.beta2;
+    k.ob2 = (float)(1.0 - (double)hp.beta2);
+    k.c1 = (float)(1.0 / (1.0 - p1));
+    k.c2 = (float)(1.0 / (1.0 - p2));
+    k.lr = hp.lr;
+    k.eps = hp.eps;
+    k.wd = hp.weight_decay;
+    return k;
+}
 
 }  // namespace
 
@@ -42,6 +65,7 @@ size_t mxq_workspace_bytes(const char* op, int64_t n) {
     if (!op || n < 0) return 0;
     if (strcmp(op, "pertensor") == 0) return pertensor_ws(n);
     if (strcmp(op, "adam") == 0) return adam_ws(n);
+    if (strcmp(op, "pertensor_delayed") == 0 || strcmp(op, "adam_delayed") == 0) return kDelayedWs;
     return 0;
 }
 
@@ -76,6 +100,26 @@ mxq_status fp8_quantize_pertensor(const uint16_t* x_bf16, int64_t rows, int64_t 
     if (!al16(workspace)) return MXQ_ERR_ALIGN;
     return hip_status(mxq::launch_pertensor_quantize(x_bf16, rows, cols, (int)fmt, margin, scale_in, amax_out,
                                                      scale_out, q, q_t, static_cast<uint32_t*>(workspace), stream));
+}
+
+mxq_status fp8_quantize_pertensor_delayed(const uint16_t* x_bf16, int64_t rows, int64_t cols, mxq_fp8 fmt,
+                                          float margin, float* amax_history, int32_t* hist_pos, int64_t history_len,
+                                          float* amax_out, float* scale_out, uint8_t* q, uint8_t* q_t,
+                                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!amax_out || !scale_out || !amax_history || !hist_pos) return MXQ_ERR_NULL;
+    if (fmt != MXQ_E4M3 && fmt != MXQ_E5M2) return MXQ_ERR_UNSUPPORTED;
+    if (rows < 0 || cols < 0 || cols % 8 != 0) return MXQ_ERR_SHAPE;
+    if (q_t && rows % 32 != 0) return MXQ_ERR_SHAPE;
+    if ((rows + 127) / 128 > kMaxGridY) return MXQ_ERR_SHAPE;
+    if (history_len < 1 || history_len > kMaxHistory) return MXQ_ERR_SHAPE;
+    if (rows * cols > 0 && !x_bf16) return MXQ_ERR_NULL;
+    if (!al16(x_bf16) || (q && !al16(q)) || (q_t && !al16(q_t))) return MXQ_ERR_ALIGN;
+    if (!al4(amax_out) || !al4(scale_out) || !al4(amax_history) || !al4(hist_pos)) return MXQ_ERR_ALIGN;
+    if (!workspace || workspace_bytes < kDelayedWs) return MXQ_ERR_WORKSPACE;
+    if (!al16(workspace)) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_pertensor_quantize_delayed(x_bf16, rows, cols, (int)fmt, margin, amax_history,
+                                                             hist_pos, (int)history_len, amax_out, scale_out, q, q_t,
+                                                             static_cast<uint32_t*>(workspace), stream));
 }
 
 mxq_status scaled_gemm(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fmt, const uint8_t* b_q,
@@ -118,27 +162,31 @@ mxq_status fp8_adam_step(float* master, const uint16_t* grad_bf16, uint8_t* m_q,
         return MXQ_ERR_ALIGN;
     if (!workspace || workspace_bytes < adam_ws(n)) return MXQ_ERR_WORKSPACE;
     if (!al16(workspace)) return MXQ_ERR_ALIGN;
-    // Host scalars in double, each rounded once to float. beta^t is the product of t factors (it reaches 0 long
-    // before t is large, after which further factors change nothing).
-    double p1 = 1.0, p2 = 1.0;
-    for (int64_t t = 0; t < hp->step && (p1 != 0.0 || p2 != 0.0); ++t) {
-        p1 *= (double)hp->beta1;
-        p2 *= (double)hp->beta2;
-    }
-    mxq::AdamConsts k;
-    k.b1 = hp->beta1;
-    k.ob1 = (float)(1.0 - (double)hp->beta1);
-    k.b2 = hp->beta2;
-    k.ob2 = (float)(1.0 - (double)hp->beta2);
-    k.c1 = (float)(1.0 / (1.0 - p1));
-    k.c2 = (float)(1.0 / (1.0 - p2));
-    k.lr = hp->lr;
-    k.eps = hp->eps;
-    k.wd = hp->weight_decay;
+    const mxq::AdamConsts k = adam_consts(*hp);
     const size_t part_bytes = round_up((size_t)mxq::adam_parts(n) * 4u, 256);
     uint32_t* partial = static_cast<uint32_t*>(workspace);
     float* consts = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + part_bytes);
     return hip_status(mxq::launch_adam(master, grad_bf16, m_q, m_scale, v_fp16, w_bf16, n, k, partial, consts, stream));
+}
+
+mxq_status fp8_adam_step_delayed(float* master, const uint16_t* grad_bf16, uint8_t* m_q, float* m_scale,
+                                 uint16_t* v_fp16, uint16_t* w_bf16, int64_t n, const mxq_adam_hparams* hp,
+                                 float* m_history, int32_t* hist_pos, int64_t history_len, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    if (!hp) return MXQ_ERR_NULL;
+    if (n < 0 || hp->step < 1 || history_len < 1 || history_len > kMaxHistory) return MXQ_ERR_SHAPE;
+    if (n == 0) return MXQ_OK;
+    if (!master || !grad_bf16 || !m_q || !m_scale || !v_fp16 || !m_history || !hist_pos) return MXQ_ERR_NULL;
+    if (!al16(master) || !al16(grad_bf16) || !al16(m_q) || !al16(v_fp16) || (w_bf16 && !al16(w_bf16)) ||
+        !al4(m_scale) || !al4(m_history) || !al4(hist_pos))
+        return MXQ_ERR_ALIGN;
+    if (!workspace || workspace_bytes < kDelayedWs) return MXQ_ERR_WORKSPACE;
+    if (!al16(workspace)) return MXQ_ERR_ALIGN;
+    const mxq::AdamConsts k = adam_consts(*hp);
+    uint32_t* amax_word = static_cast<uint32_t*>(workspace);
+    float* consts = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + 16);
+    return hip_status(mxq::launch_adam_delayed(master, grad_bf16, m_q, m_scale, v_fp16, w_bf16, n, k, m_history,
+                                               hist_pos, (int)history_len, consts, amax_word, stream));
 }
 
 }  // extern "C"

@@ -118,9 +118,10 @@ __global__ __launch_bounds__(ATHREADS) void adam_finalize_kernel(const uint32_t*
 
 __device__ __forceinline__ void adam_one(const AdamConsts& k, float inv_s, float s_new, float theta, uint32_t g16,
                                          uint32_t mq, uint32_t v16, float& theta_out, uint32_t& m_code, uint32_t& v_out,
-                                         uint32_t& w_out) {
+                                         uint32_t& w_out, uint32_t& m_abs) {
     float m, v;
     adam_moments(k, inv_s, g16, mq, v16, m, v);
+    m_abs = __float_as_uint(m) & 0x7FFFFFFFu;
     const float mh = m * k.c1;
     const float vh = v * k.c2;
     const float den = __builtin_sqrtf(vh) + k.eps;
@@ -137,11 +138,16 @@ __device__ __forceinline__ void adam_one(const AdamConsts& k, float inv_s, float
     w_out = __builtin_bit_cast(uint16_t, (__bf16)theta_out);
 }
 
+// AMAX (delayed first-moment scale): also the max of |m_t| (fp32 magnitude bits) into *amax_word, one atomic
+// per workgroup.
+template <bool AMAX>
 __global__ __launch_bounds__(ATHREADS) void adam_update_kernel(float* __restrict__ master, const uint16_t* __restrict__ g,
                                                               uint8_t* __restrict__ mq, uint16_t* __restrict__ v16,
                                                               uint16_t* __restrict__ w, int64_t n, AdamConsts k,
-                                                              const float* __restrict__ consts) {
+                                                              const float* __restrict__ consts,
+                                                              uint32_t* __restrict__ amax_word) {
     const float inv_s = consts[0], s_new = consts[1];
+    uint32_t mx = 0;
     const int64_t chunks = n / 8;
     const int64_t stride = (int64_t)gridDim.x * ATHREADS;
     // Two chunks per trip (the second one stride further on), all loads issued before any arithmetic, so twice as
@@ -157,8 +163,9 @@ __global__ __launch_bounds__(ATHREADS) void adam_update_kernel(float* __restrict
             const uint32_t v_16 = (vw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
             const uint32_t m8 = ((e < 4 ? mv.x : mv.y) >> (8 * (e & 3))) & 0xFFu;
             float t_out;
-            uint32_t mc, vout, wout;
-            adam_one(k, inv_s, s_new, __uint_as_float(th[e]), g16, m8, v_16, t_out, mc, vout, wout);
+            uint32_t mc, vout, wout, mabs;
+            adam_one(k, inv_s, s_new, __uint_as_float(th[e]), g16, m8, v_16, t_out, mc, vout, wout, mabs);
+            if (AMAX) mx = max(mx, mabs);
             th_o[e] = __float_as_uint(t_out);
             mo[e >> 2] |= mc << (8 * (e & 3));
             vo[e >> 1] |= vout << (16 * (e & 1));
@@ -190,13 +197,65 @@ __global__ __launch_bounds__(ATHREADS) void adam_update_kernel(float* __restrict
     if (blockIdx.x == 0)
         for (int64_t i = chunks * 8 + threadIdx.x; i < n; i += ATHREADS) {
             float t_out;
-            uint32_t mc, vout, wout;
-            adam_one(k, inv_s, s_new, master[i], g[i], mq[i], v16[i], t_out, mc, vout, wout);
+            uint32_t mc, vout, wout, mabs;
+            adam_one(k, inv_s, s_new, master[i], g[i], mq[i], v16[i], t_out, mc, vout, wout, mabs);
+            if (AMAX) mx = max(mx, mabs);
             master[i] = t_out;
             mq[i] = (uint8_t)mc;
             v16[i] = (uint16_t)vout;
             if (w) w[i] = (uint16_t)wout;
         }
+    if constexpr (AMAX) {
+        mx = block_max_u32(mx);
+        if (threadIdx.x == 0) atomicMax(amax_word, mx);
+    }
+}
+
+// Delayed first-moment scale: s_new = 448 / max(max(history), 1e-12) from earlier steps' amax of m; consts[0] =
+// 1 / s_old (decodes the stored m), consts[1] = s_new (encodes m_t), m_scale <- s_new; clears the amax word.
+__global__ __launch_bounds__(ATHREADS) void adam_delayed_prep_kernel(const float* __restrict__ hist, int H,
+                                                                    float* __restrict__ m_scale,
+                                                                    float* __restrict__ consts,
+                                                                    uint32_t* __restrict__ amax_word) {
+    __shared__ float shm[ATHREADS / 64];
+    __shared__ int shn[ATHREADS / 64];
+    float m = 0.0f;
+    int nan = 0;
+    for (int i = threadIdx.x; i < H; i += ATHREADS) {
+        const float h = hist[i];
+        if (h != h) nan = 1;
+        else if (h > m) m = h;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        m = fmaxf(m, __shfl_xor(m, off, 64));
+        nan |= __shfl_xor(nan, off, 64);
+    }
+    if ((threadIdx.x & 63) == 0) { shm[threadIdx.x >> 6] = m; shn[threadIdx.x >> 6] = nan; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < ATHREADS / 64; ++w) { m = fmaxf(m, shm[w]); nan |= shn[w]; }
+        float a = nan ? __uint_as_float(0x7FC00000u) : m;
+        a = a < 1e-12f ? 1e-12f : a;
+        const float s_new = 448.0f / a;
+        consts[0] = 1.0f / m_scale[0];
+        consts[1] = s_new;
+        m_scale[0] = s_new;
+        *amax_word = 0u;
+    }
+}
+
+// This step's amax of m_t goes to the history at the ring position, which then advances.
+__global__ void adam_delayed_finalize_kernel(const uint32_t* __restrict__ amax_word, float* __restrict__ hist,
+                                             int32_t* __restrict__ pos, int H, float* __restrict__ consts) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        const float amax = __uint_as_float(*amax_word);
+        consts[2] = amax;
+        int p = *pos;
+        p = ((p % H) + H) % H;
+        hist[p] = amax;
+        *pos = (p + 1) % H;
+    }
 }
 
 int adam_parts(int64_t n) {
@@ -212,8 +271,21 @@ hipError_t launch_adam(float* master, const uint16_t* grad, uint8_t* m_q, float*
     const int parts = adam_parts(n);
     hipLaunchKernelGGL(adam_amax_kernel, dim3(parts), dim3(ATHREADS), 0, stream, grad, m_q, m_scale, n, k, partial);
     hipLaunchKernelGGL(adam_finalize_kernel, dim3(1), dim3(ATHREADS), 0, stream, partial, parts, m_scale, consts);
-    hipLaunchKernelGGL(adam_update_kernel, dim3(parts), dim3(ATHREADS), 0, stream, master, grad, m_q, v16, w, n, k,
-                       (const float*)consts);
+    hipLaunchKernelGGL(adam_update_kernel<false>, dim3(parts), dim3(ATHREADS), 0, stream, master, grad, m_q, v16, w, n, k,
+                       (const float*)consts, (uint32_t*)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_adam_delayed(float* master, const uint16_t* grad, uint8_t* m_q, float* m_scale, uint16_t* v16,
+                               uint16_t* w, int64_t n, const AdamConsts& k, float* hist, int32_t* pos, int H,
+                               float* consts, uint32_t* amax_word, hipStream_t stream) {
+    const int parts = adam_parts(n);
+    hipLaunchKernelGGL(adam_delayed_prep_kernel, dim3(1), dim3(ATHREADS), 0, stream, (const float*)hist, H, m_scale,
+                       consts, amax_word);
+    hipLaunchKernelGGL(adam_update_kernel<true>, dim3(parts), dim3(ATHREADS), 0, stream, master, grad, m_q, v16, w, n, k,
+                       (const float*)consts, amax_word);
+    hipLaunchKernelGGL(adam_delayed_finalize_kernel, dim3(1), dim3(64), 0, stream, (const uint32_t*)amax_word, hist, pos,
+                       H, consts);
     return hipGetLastError();
 }
 

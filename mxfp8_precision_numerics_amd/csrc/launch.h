@@ -18,6 +18,10 @@ hipError_t launch_pertensor_quantize(const uint16_t* x, int64_t rows, int64_t co
                                      const float* scale_in, float* amax_out, float* scale_out, uint8_t* q,
                                      uint8_t* q_t, uint32_t* partial, hipStream_t stream);
 
+hipError_t launch_pertensor_quantize_delayed(const uint16_t* x, int64_t rows, int64_t cols, int fmt, float margin,
+                                             float* hist, int32_t* pos, int H, float* amax_out, float* scale_out,
+                                             uint8_t* q, uint8_t* q_t, uint32_t* amax_word, hipStream_t stream);
+
 hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt, const uint8_t* b_q,
                               const void* b_scale, int b_fmt, int64_t M, int64_t N, int64_t K, int mx,
                               uint16_t* c, int64_t ldc, hipStream_t stream);
@@ -29,5 +33,8 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int
 int adam_parts(int64_t n);
 hipError_t launch_adam(float* master, const uint16_t* grad, uint8_t* m_q, float* m_scale, uint16_t* v16, uint16_t* w,
                        int64_t n, const AdamConsts& k, uint32_t* partial, float* consts, hipStream_t stream);
+hipError_t launch_adam_delayed(float* master, const uint16_t* grad, uint8_t* m_q, float* m_scale, uint16_t* v16,
+                               uint16_t* w, int64_t n, const AdamConsts& k, float* hist, int32_t* pos, int H,
+                               float* consts, uint32_t* amax_word, hipStream_t stream);
 
 }  // namespace mxq

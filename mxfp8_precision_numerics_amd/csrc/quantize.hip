@@ -30,6 +30,7 @@ struct QuantArgs {
     const float* scale; // per-tensor only
     int srow_words;     // s_row rows hold whole 4-byte words per 128-column tile (cols % 128 == 0, 4-aligned)
     int scol_words;     // s_col likewise (rows % 128 == 0, 4-aligned)
+    uint32_t* amax_word;  // AMAX: running max of |x| as a bf16 magnitude pattern (atomic max, one per workgroup)
 };
 
 template <int MODE>
@@ -41,7 +42,7 @@ __device__ __forceinline__ uint32_t pt_cvt_quad(float s, uint32_t p0, uint32_t p
     return cvt_f32_pair<FMT, true>(cvt_f32_pair<FMT, false>(0u, a, b), c, d);
 }
 
-template <int MODE, bool ROW, bool COL>
+template <int MODE, bool ROW, bool COL, bool AMAX = false>
 __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
     constexpr bool MX = MODE == QM_MX_RCEIL || MODE == QM_MX_FLOOR;
     constexpr int RULE = MODE == QM_MX_FLOOR ? RULE_FLOOR : RULE_RCEIL;
@@ -64,6 +65,22 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
             v[j] = ldnt16(a.x + gr * a.cols + gc);
         else
             v[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    if constexpr (AMAX) {
+        // max |x| of the tile (bf16 magnitude patterns; NaN patterns sort above infinity; padding loaded as 0)
+        __shared__ uint32_t red[QTHREADS / 64];
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = max(m, amax_bits8(v[j]));
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+        if ((tid & 63) == 0) red[tid >> 6] = m;
+        __syncthreads();
+        if (tid == 0) {
+            m = max(max(red[0], red[1]), max(red[2], red[3]));
+            atomicMax(a.amax_word, m);
+        }
     }
 
     if constexpr (COL) {
@@ -210,7 +227,7 @@ static hipError_t launch_quant_mode(const QuantArgs& a, bool row, bool col, hipS
 
 hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
                               uint8_t* q_col, uint8_t* s_col, int rule, hipStream_t stream) {
-    QuantArgs a{x, rows, cols, q_row, s_row, q_col, s_col, nullptr, 0, 0};
+    QuantArgs a{x, rows, cols, q_row, s_row, q_col, s_col, nullptr, 0, 0, nullptr};
     a.srow_words = cols % QT == 0 && (reinterpret_cast<uintptr_t>(s_row) & 3) == 0;
     a.scol_words = rows % QT == 0 && (reinterpret_cast<uintptr_t>(s_col) & 3) == 0;
     bool row = q_row != nullptr, col = q_col != nullptr;
@@ -300,9 +317,84 @@ hipError_t launch_pertensor_quantize(const uint16_t* x, int64_t rows, int64_t co
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (!q && !q_t) return hipSuccess;
-    QuantArgs a{x, rows, cols, q, nullptr, q_t, nullptr, scale_out, 0, 0};
+    QuantArgs a{x, rows, cols, q, nullptr, q_t, nullptr, scale_out, 0, 0, nullptr};
     return fmt == FMT_E4M3 ? launch_quant_mode<QM_PT_E4M3>(a, q != nullptr, q_t != nullptr, stream)
                            : launch_quant_mode<QM_PT_E5M2>(a, q != nullptr, q_t != nullptr, stream);
+}
+
+// ---------------------------------------------------------------------------------------- delayed scaling
+// Scale from the amax history of earlier calls ("3.8 Mixed Precision, bf16 & FP8 Training", delayed-scaling recipe):
+// max over the history (any NaN entry makes it NaN), clamped below at 1e-12, FMAX over it, times the margin. Also
+// clears the word the cast kernel's workgroups take the atomic max of |x| into.
+__global__ __launch_bounds__(AMAX_THREADS) void pt_delayed_prep_kernel(const float* __restrict__ hist, int H, float fmax,
+                                                                      float margin, float* __restrict__ scale_out,
+                                                                      uint32_t* __restrict__ amax_word) {
+    __shared__ float shm[AMAX_THREADS / 64];
+    __shared__ int shn[AMAX_THREADS / 64];
+    float m = 0.0f;
+    int nan = 0;
+    for (int i = threadIdx.x; i < H; i += AMAX_THREADS) {
+        const float h = hist[i];
+        if (h != h) nan = 1;
+        else if (h > m) m = h;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        m = fmaxf(m, __shfl_xor(m, off, 64));
+        nan |= __shfl_xor(nan, off, 64);
+    }
+    if ((threadIdx.x & 63) == 0) { shm[threadIdx.x >> 6] = m; shn[threadIdx.x >> 6] = nan; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < AMAX_THREADS / 64; ++w) { m = fmaxf(m, shm[w]); nan |= shn[w]; }
+        float a = nan ? __uint_as_float(0x7FC00000u) : m;
+        a = a < 1e-12f ? 1e-12f : a;                 // a NaN stays NaN
+        float s = fmax / a;
+        s = s * margin;
+        *scale_out = s;
+        *amax_word = 0u;
+    }
+}
+
+// amax_out = max |x| of this call; it goes to the history at the ring position, which then advances.
+__global__ void pt_delayed_finalize_kernel(const uint32_t* __restrict__ amax_word, float* __restrict__ hist,
+                                           int32_t* __restrict__ pos, int H, float* __restrict__ amax_out) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        const float amax = __uint_as_float(*amax_word << 16);
+        *amax_out = amax;
+        int p = *pos;
+        p = ((p % H) + H) % H;                        // an out-of-range position never writes outside the history
+        hist[p] = amax;
+        *pos = (p + 1) % H;
+    }
+}
+
+template <int MODE>
+static hipError_t launch_quant_delayed_mode(const QuantArgs& a, bool row, bool col, hipStream_t stream) {
+    dim3 grid((unsigned)((a.cols + QT - 1) / QT), (unsigned)((a.rows + QT - 1) / QT));
+    if (row && col) hipLaunchKernelGGL((quant_tile_kernel<MODE, true, true, true>), grid, dim3(QTHREADS), 0, stream, a);
+    else if (row) hipLaunchKernelGGL((quant_tile_kernel<MODE, true, false, true>), grid, dim3(QTHREADS), 0, stream, a);
+    else if (col) hipLaunchKernelGGL((quant_tile_kernel<MODE, false, true, true>), grid, dim3(QTHREADS), 0, stream, a);
+    else hipLaunchKernelGGL((quant_tile_kernel<MODE, false, false, true>), grid, dim3(QTHREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pertensor_quantize_delayed(const uint16_t* x, int64_t rows, int64_t cols, int fmt, float margin,
+                                             float* hist, int32_t* pos, int H, float* amax_out, float* scale_out,
+                                             uint8_t* q, uint8_t* q_t, uint32_t* amax_word, hipStream_t stream) {
+    hipLaunchKernelGGL(pt_delayed_prep_kernel, dim3(1), dim3(AMAX_THREADS), 0, stream, (const float*)hist, H,
+                       fmt == FMT_E4M3 ? 448.0f : 57344.0f, margin, scale_out, amax_word);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (rows > 0 && cols > 0) {
+        QuantArgs a{x, rows, cols, q, nullptr, q_t, nullptr, scale_out, 0, 0, amax_word};
+        e = fmt == FMT_E4M3 ? launch_quant_delayed_mode<QM_PT_E4M3>(a, q != nullptr, q_t != nullptr, stream)
+                            : launch_quant_delayed_mode<QM_PT_E5M2>(a, q != nullptr, q_t != nullptr, stream);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(pt_delayed_finalize_kernel, dim3(1), dim3(64), 0, stream, (const uint32_t*)amax_word, hist, pos,
+                       H, amax_out);
+    return hipGetLastError();
 }
 
 }  // namespace mxq

@@ -169,6 +169,12 @@ def delayed_scale(history, fmt: int = E4M3, margin: float = 1.0) -> np.float32:
     return np.float32(lib().orc_delayed_scale(_p(h), h.size, fmt, C.c_float(margin)))
 
 
+def history_push(history, pos, amax: float) -> None:
+    """Write amax at the ring position and advance it (history float32[H], pos int32[1], in place)."""
+    assert history.dtype == np.float32 and pos.dtype == np.int32
+    lib().orc_history_push(_p(history), history.size, _p(pos), C.c_float(amax))
+
+
 def pertensor_quantize_delayed(x_bf16, history, pos, fmt: int = E4M3, margin: float = 1.0, want_q: bool = True,
                                want_qt: bool = True, nthreads: int | None = None):
     """One delayed-scaling cast. history (float32[H]) and pos (int32[1]) are updated in place.

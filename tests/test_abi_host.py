@@ -100,3 +100,22 @@ def test_grouped_and_adam_validation():
     assert a(P, P, P, P, P, None, 1024, None, P, ws, None) == 1
     assert a(P, P, P, P, P, None, 1024, C.byref(hp), P, ws - 1, None) == 5
     assert a(P, MIS, P, P, P, None, 1024, C.byref(hp), P, ws, None) == 3
+
+
+def test_delayed_validation():
+    lib = _lib.load()
+    f = lib.fp8_quantize_pertensor_delayed
+    ws = lib.mxq_workspace_bytes(b"pertensor_delayed", 64 * 64)
+    assert ws >= 4
+    assert f(P, 64, 64, 0, C.c_float(1.0), None, P, 4, P, P, P, P, P, ws, None) == 1     # no history
+    assert f(P, 64, 64, 0, C.c_float(1.0), P, P, 0, P, P, P, P, P, ws, None) == 2        # history_len >= 1
+    assert f(P, 64, 64, 3, C.c_float(1.0), P, P, 4, P, P, P, P, P, ws, None) == 4
+    assert f(P, 64, 64, 0, C.c_float(1.0), P, P, 4, P, P, P, P, None, ws, None) == 5
+    assert f(P, 64, 64, 0, C.c_float(1.0), P + 2, P, 4, P, P, P, P, P, ws, None) == 3    # history 4-aligned
+    g = lib.fp8_adam_step_delayed
+    hp = _lib.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.0, 1)
+    wsa = lib.mxq_workspace_bytes(b"adam_delayed", 1024)
+    assert g(P, P, P, P, P, None, 1024, C.byref(hp), None, P, 4, P, wsa, None) == 1
+    assert g(P, P, P, P, P, None, 1024, C.byref(hp), P, P, 0, P, wsa, None) == 2
+    assert g(P, P, P, P, P, None, 1024, C.byref(hp), P, P, 4, P, wsa - 1, None) == 5
+    assert g(P, P, P, P, P, None, 0, C.byref(hp), None, None, 4, None, 0, None) == 0     # empty

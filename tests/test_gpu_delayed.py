@@ -1,0 +1,102 @@
+"""GPU parity of the delayed-scaling entry points (fp8_quantize_pertensor_delayed, fp8_adam_step_delayed) against
+the oracle, bit for bit, over sequences of calls that exercise the amax history ring: the scale each call uses, its
+codes (and transposed codes), its amax, and the history and position it leaves behind."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_precision_numerics_amd as mxq
+import oracle
+from gpu_util import DEV, need_gpu, say, u16, u8
+from mxfp8_precision_numerics_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("rows,cols,fmt,margin", [(64, 96, mxq.E4M3, 1.0), (200 - 8, 328, mxq.E5M2, 1.0),
+                                                  (1024, 1032, mxq.E4M3, 0.5), (4096, 12288, mxq.E4M3, 1.0)])
+def test_delayed_cast_sequence(rows, cols, fmt, margin):
+    need_gpu()
+    say("delayed cast", rows, cols, fmt, margin)
+    H = 3
+    hist = torch.zeros(H, dtype=torch.float32, device=DEV)
+    pos = torch.zeros(1, dtype=torch.int32, device=DEV)
+    o_hist = np.zeros(H, np.float32)
+    o_pos = np.zeros(1, np.int32)
+    want_qt = rows % 32 == 0
+    ws = torch.empty(mxq.workspace_bytes("pertensor_delayed", rows * cols), dtype=torch.uint8, device=DEV)
+    for call, std in enumerate((1.0, 4.0, 0.5, 2.0, 3.0)):
+        x = workloads.normal_bf16((rows, cols), std, 2, 10 + call, DEV)
+        r = mxq.pertensor_quantize_delayed(x, hist, pos, fmt, margin, want_qt=want_qt, workspace=ws)
+        torch.cuda.synchronize()
+        a, s, q, qt = oracle.pertensor_quantize_delayed(u16(x), o_hist, o_pos, fmt, margin, want_qt=want_qt)
+        assert np.float32(r.amax.item()) == np.float32(a), f"amax call {call}"
+        assert _bits(r.scale)[0] == np.float32(s).view(np.uint32), f"scale call {call}"
+        assert np.array_equal(u8(r.q), q), f"q call {call}"
+        if want_qt:
+            assert np.array_equal(u8(r.q_t), qt), f"q_t call {call}"
+        assert np.array_equal(_bits(hist), o_hist.view(np.uint32)), f"history call {call}"
+        assert int(pos.item()) == int(o_pos[0]), f"pos call {call}"
+
+
+def test_delayed_cast_outputs_optional_and_position_wraps():
+    need_gpu()
+    rows, cols = 96, 256
+    x = workloads.normal_bf16((rows, cols), 1.0, 2, 30, DEV)
+    hist = torch.tensor([0.25, 7.0], dtype=torch.float32, device=DEV)
+    pos = torch.tensor([1], dtype=torch.int32, device=DEV)
+    o_hist = np.array([0.25, 7.0], np.float32)
+    o_pos = np.array([1], np.int32)
+    full = mxq.pertensor_quantize_delayed(x, hist.clone(), pos.clone(), mxq.E4M3)
+    only_q = mxq.pertensor_quantize_delayed(x, hist.clone(), pos.clone(), mxq.E4M3, want_qt=False)
+    only_t = mxq.pertensor_quantize_delayed(x, hist.clone(), pos.clone(), mxq.E4M3, want_q=False)
+    none = mxq.pertensor_quantize_delayed(x, hist, pos, mxq.E4M3, want_q=False, want_qt=False)
+    torch.cuda.synchronize()
+    a, s, q, qt = oracle.pertensor_quantize_delayed(u16(x), o_hist, o_pos, mxq.E4M3)
+    assert np.array_equal(u8(full.q), q) and np.array_equal(u8(full.q_t), qt)
+    assert np.array_equal(u8(only_q.q), q) and np.array_equal(u8(only_t.q_t), qt)
+    assert np.float32(none.amax.item()) == np.float32(a)
+    assert np.array_equal(_bits(hist), o_hist.view(np.uint32)) and int(pos.item()) == int(o_pos[0]) == 0
+
+
+@pytest.mark.parametrize("n", [1, 7, 1000, 100_003])
+def test_delayed_adam_sequence(n):
+    need_gpu()
+    say("delayed adam", n)
+    H = 2
+    theta = workloads.workload5_params(n, DEV)
+    m_q = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    m_scale = torch.ones(1, dtype=torch.float32, device=DEV)
+    v = torch.zeros(n, dtype=torch.float16, device=DEV)
+    w = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    hist = torch.zeros(H, dtype=torch.float32, device=DEV)
+    pos = torch.zeros(1, dtype=torch.int32, device=DEV)
+    o_theta = theta.cpu().numpy().copy()
+    o_mq = np.zeros(n, np.uint8); o_ms = np.ones(1, np.float32); o_v = np.zeros(n, np.uint16)
+    o_hist = np.zeros(H, np.float32); o_pos = np.zeros(1, np.int32)
+    for t in (1, 2, 3, 4):
+        g = workloads.workload5_grad(n, t, DEV)
+        hp = mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.0, t)
+        ohp = oracle.AdamHP(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, step=t)
+        if t == 1:
+            # seed the history the way a user would: one current-scaling step reports the amax of m
+            mxq.fp8_adam_step(theta, g, m_q, m_scale, v, w, hp)
+            a, o_w = oracle.adam_step(o_theta, u16(g), o_mq, o_ms, o_v, ohp)
+            oracle.history_push(o_hist, o_pos, a)
+            hist[0] = a
+            pos[0] = 1
+        else:
+            mxq.fp8_adam_step_delayed(theta, g, m_q, m_scale, v, w, hp, hist, pos)
+            _, o_w = oracle.adam_step_delayed(o_theta, u16(g), o_mq, o_ms, o_v, ohp, o_hist, o_pos)
+        torch.cuda.synchronize()
+        assert np.array_equal(theta.cpu().numpy().view(np.uint32), o_theta.view(np.uint32)), f"theta t={t}"
+        assert np.array_equal(u8(m_q), o_mq), f"m_q t={t}"
+        assert _bits(m_scale)[0] == o_ms.view(np.uint32)[0], f"m_scale t={t}"
+        assert np.array_equal(u16(v), o_v), f"v t={t}"
+        assert np.array_equal(u16(w), o_w), f"w t={t}"
+        assert np.array_equal(_bits(hist), o_hist.view(np.uint32)), f"history t={t}"
+        assert int(pos.item()) == int(o_pos[0]), f"pos t={t}"
