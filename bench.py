@@ -9,6 +9,8 @@ One step is one pass over every row of the hot path, on seeded synthetic inputs 
                 1024->2048), including the row quantize of both activations (expert weights quantized once)
   adam          precision-decoupled FP8 Adam step over 1.3e9 parameters (2 passes)
   small         MX quantize + 256^3 block-scaled GEMM
+  pt_quant_delayed  the per-tensor casts of X, W, dY with delayed scaling (16-slot amax histories): one pass each
+  adam_delayed  the Adam step with a delayed first-moment scale: one pass over the state (18 B/param)
 The headline value is the MXFP8 linear layer's GEMM FLOPs (11.13 TFLOP) divided by the device time of its quantize
 and GEMM launches ("MXFP8 GEMM TFLOP/s incl. quantize"). Device times come from events on the stream the kernels
 run on; the JSON line also carries every part's rate, the MX GEMM's roofline and the CPU oracle baseline.
@@ -100,11 +102,26 @@ def main():
     C_up = torch.empty((rows4, d_ff), dtype=torch.bfloat16, device=dev)
     C_dn = torch.empty((rows4, d_model), dtype=torch.bfloat16, device=dev)
     hp = mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.0, 2)
+    # delayed scaling: amax histories (16 slots) seeded with one current-scaling call each
+    hists, hpos = {}, {}
+    for name, t, fmt in (("X", X, mxq.E4M3), ("W", W, mxq.E4M3), ("dY", dY, mxq.E5M2)):
+        r = mxq.pertensor_quantize(t, fmt, want_q=False, want_qt=False, workspace=ws_pt)
+        hists[name] = torch.zeros(16, dtype=torch.float32, device=dev)
+        hists[name][0] = r.amax[0]
+        hpos[name] = torch.ones(1, dtype=torch.int32, device=dev)
+    m_hist = torch.zeros(16, dtype=torch.float32, device=dev)
+    m_pos = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws_del = torch.empty(mxq.workspace_bytes("pertensor_delayed", N * K), dtype=torch.uint8, device=dev)
+    ws_adel = torch.empty(mxq.workspace_bytes("adam_delayed", n_adam), dtype=torch.uint8, device=dev)
+    mxq.fp8_adam_step(theta, grad, m_q, m_scale, v16, w16, hp, workspace=adam_ws)
+    m_hist[0] = 448.0 / m_scale[0]           # the amax that step's scale came from
+    m_pos[0] = 1
     torch.cuda.synchronize()
 
     Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     parts = ["mx_quant_XWdY", "mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "pt_quant", "pt_gemms", "mx_quant_act",
-             "grouped", "adam", "small"]
+             "grouped", "adam", "small", "pt_quant_delayed", "adam_delayed"]
+    NEV = len(parts) + 1
 
     def step(ev):
         ev[0].record(stream)
@@ -141,14 +158,20 @@ def main():
         qb = mxq.mx_quantize(B1, rowwise=False)
         mxq.scaled_gemm(qa.q_row, qa.s_row, qb.q_col, qb.s_col, mxq.MX_BLOCK32)
         ev[10].record(stream)
+        mxq.pertensor_quantize_delayed(X, hists["X"], hpos["X"], mxq.E4M3, workspace=ws_del)
+        mxq.pertensor_quantize_delayed(W, hists["W"], hpos["W"], mxq.E4M3, workspace=ws_del)
+        mxq.pertensor_quantize_delayed(dY, hists["dY"], hpos["dY"], mxq.E5M2, workspace=ws_del)
+        ev[11].record(stream)
+        mxq.fp8_adam_step_delayed(theta, grad, m_q, m_scale, v16, w16, hp, m_hist, m_pos, workspace=ws_adel)
+        ev[12].record(stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
-        step([Ev() for _ in range(11)])
+        step([Ev() for _ in range(NEV)])
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
-    evs = [[Ev() for _ in range(11)] for _ in range(args.steps)]
+    evs = [[Ev() for _ in range(NEV)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -157,7 +180,7 @@ def main():
     wall = time.perf_counter() - t0
     ms = {p: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
           for i, p in enumerate(parts)}
-    step_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][10]) for s in range(args.steps)]))
+    step_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][NEV - 1]) for s in range(args.steps)]))
     log("per-part ms:", json.dumps({k: round(v, 4) for k, v in ms.items()}))
 
     # ------------------------------------------------------------------ rates
@@ -187,6 +210,8 @@ def main():
         "grouped_tflops_incl_act_quant": grouped_flop / (ms["grouped"] * 1e-3) / 1e12,
         "adam_gbs": adam_bytes / (ms["adam"] * 1e-3) / 1e9,
         "small_us": ms["small"] * 1e3,
+        "pt_quant_delayed_gbs": sum(4 * r * c for r, c in ((M, K), (N, K), (M, N))) / (ms["pt_quant_delayed"] * 1e-3) / 1e9,
+        "adam_delayed_gbs": 18 * n_adam / (ms["adam_delayed"] * 1e-3) / 1e9,
     }
     for k, v in rate.items():
         rate[k] = round(v, 3)
