@@ -62,6 +62,7 @@ def lib():
         L.orc_adam_step.argtypes = [P, P, P, P, P, P, I64, P, I]
         L.orc_adam_amax.restype = F
         L.orc_adam_amax.argtypes = [P, P, P, F, I64, P, I]
+        L.orc_mx_quantize_f32.argtypes = [P, I64, I64, I, P, P, P, P, I]
         L.orc_delayed_scale.restype = F
         L.orc_delayed_scale.argtypes = [P, I64, I, F]
         L.orc_history_push.argtypes = [P, I64, P, F]
@@ -145,6 +146,19 @@ def mx_quantize(x_bf16, rule: int = RCEIL, rowwise: bool = True, colwise: bool =
     s_col = np.empty((Ccols, R // 32), np.uint8) if colwise else None
     lib().orc_mx_quantize(_p(x), R, Ccols, rule, _p(q_row), _p(s_row), _p(q_col), _p(s_col),
                           nthreads or default_threads())
+    return q_row, s_row, q_col, s_col
+
+
+def mx_quantize_f32(x_f32, rule: int = RCEIL, rowwise: bool = True, colwise: bool = True, nthreads=None):
+    """MXFP8 quantize of an fp32 [rows][cols] matrix. Returns (q_row, s_row, q_col, s_col) (None where not asked)."""
+    x = _c(x_f32, np.float32)
+    R, Ccols = x.shape
+    q_row = np.empty((R, Ccols), np.uint8) if rowwise else None
+    s_row = np.empty((R, Ccols // 32), np.uint8) if rowwise else None
+    q_col = np.empty((Ccols, R), np.uint8) if colwise else None
+    s_col = np.empty((Ccols, R // 32), np.uint8) if colwise else None
+    lib().orc_mx_quantize_f32(_p(x), R, Ccols, rule, _p(q_row), _p(s_row), _p(q_col), _p(s_col),
+                              nthreads or default_threads())
     return q_row, s_row, q_col, s_col
 
 

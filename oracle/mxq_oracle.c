@@ -203,10 +203,28 @@ static uint8_t mx_block(const uint16_t* src, int64_t stride, int rule, uint8_t* 
     return (e == 128) ? 0xFF : (uint8_t)(e + 127);
 }
 
+/* The same block rule for fp32 values (the weight-cache refresh quantizes the fp32 master weight directly: one
+ * rounding from fp32 to E4M3; [OLMO11] Section 11.3.2, Figure 55: caches derived from the FP32 main weight). */
+static uint8_t mx_block_f32(const float* src, int64_t stride, int rule, uint8_t* q)
+{
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) {
+        double a = fabs((double)src[i * stride]);
+        if (isnan(a) || isnan(amax)) amax = NAN;
+        else if (a > amax) amax = a;
+    }
+    int e = orc_mx_scale_exp(amax, rule);
+    int eq = (e == 128) ? 127 : e;
+    for (int i = 0; i < 32; ++i)
+        q[i] = orc_fp8_encode(ldexp((double)src[i * stride], -eq), ORC_E4M3);
+    return (e == 128) ? 0xFF : (uint8_t)(e + 127);
+}
+
 typedef struct {
     const uint16_t* x; int64_t rows, cols; int rule;
     uint8_t *q_row, *s_row, *q_col, *s_col;
     int nthreads, tid;
+    const float* xf;            /* fp32 input instead of x when not NULL */
 } mxq_job;
 
 static void* mx_worker(void* p)
@@ -215,14 +233,16 @@ static void* mx_worker(void* p)
     if (j->q_row) {
         for (int64_t r = j->tid; r < j->rows; r += j->nthreads)
             for (int64_t b = 0; b < j->cols / 32; ++b)
-                j->s_row[r * (j->cols / 32) + b] =
-                    mx_block(j->x + r * j->cols + 32 * b, 1, j->rule, j->q_row + r * j->cols + 32 * b);
+                j->s_row[r * (j->cols / 32) + b] = j->xf
+                    ? mx_block_f32(j->xf + r * j->cols + 32 * b, 1, j->rule, j->q_row + r * j->cols + 32 * b)
+                    : mx_block(j->x + r * j->cols + 32 * b, 1, j->rule, j->q_row + r * j->cols + 32 * b);
     }
     if (j->q_col) {
         for (int64_t c = j->tid; c < j->cols; c += j->nthreads)
             for (int64_t b = 0; b < j->rows / 32; ++b)
-                j->s_col[c * (j->rows / 32) + b] =
-                    mx_block(j->x + (32 * b) * j->cols + c, j->cols, j->rule, j->q_col + c * j->rows + 32 * b);
+                j->s_col[c * (j->rows / 32) + b] = j->xf
+                    ? mx_block_f32(j->xf + (32 * b) * j->cols + c, j->cols, j->rule, j->q_col + c * j->rows + 32 * b)
+                    : mx_block(j->x + (32 * b) * j->cols + c, j->cols, j->rule, j->q_col + c * j->rows + 32 * b);
     }
     return NULL;
 }
@@ -240,7 +260,22 @@ void orc_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int rule, ui
     pthread_t th[256];
     mxq_job jobs[256];
     for (int t = 0; t < nthreads; ++t) {
-        jobs[t] = (mxq_job){x, rows, cols, rule, q_row, s_row, q_col, s_col, nthreads, t};
+        jobs[t] = (mxq_job){x, rows, cols, rule, q_row, s_row, q_col, s_col, nthreads, t, NULL};
+        pthread_create(&th[t], NULL, mx_worker, &jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+}
+
+/* MXFP8 quantize of an fp32 matrix (same layouts and rules as orc_mx_quantize). */
+void orc_mx_quantize_f32(const float* x, int64_t rows, int64_t cols, int rule, uint8_t* q_row, uint8_t* s_row,
+                         uint8_t* q_col, uint8_t* s_col, int nthreads)
+{
+    tables();
+    nthreads = clamp_threads(nthreads);
+    pthread_t th[256];
+    mxq_job jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (mxq_job){NULL, rows, cols, rule, q_row, s_row, q_col, s_col, nthreads, t, x};
         pthread_create(&th[t], NULL, mx_worker, &jobs[t]);
     }
     for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
