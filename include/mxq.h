@@ -164,6 +164,22 @@ mxq_status fp8_adam_step(float* master, const uint16_t* grad_bf16, uint8_t* m_q,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The AdamW step of fp8_adam_step fused with the refresh of the weight's MXFP8 caches ([OLMO11] Section 11.3.2 and
+ * Figure 55: the cached operand orientations derive from the FP32 main weight and are rebuilt after every update).
+ * The n = rows * cols parameters are the weight matrix W[rows][cols] (row-major). After the update:
+ *   row orientation:    q_row[rows][cols], s_row[rows][cols/32]   (needs cols % 32 == 0), the forward operand;
+ *   column orientation: q_col[cols][rows], s_col[cols][rows/32]   (needs rows % 32 == 0), the dgrad operand;
+ * each 32-value block of the updated fp32 master weight quantized as mxq_quantize does (rule = rceil or floor, one
+ * rounding from fp32 to E4M3). Either orientation pair may be NULL, not both. All Adam outputs are bit-identical to
+ * fp8_adam_step's; w_bf16 may be NULL. Requires cols % 8 == 0. workspace: mxq_workspace_bytes("adam", rows * cols).
+ */
+mxq_status fp8_adam_step_mx_cache(float* master, const uint16_t* grad_bf16, uint8_t* m_q, float* m_scale,
+                                  uint16_t* v_fp16, uint16_t* w_bf16, int64_t rows, int64_t cols, uint8_t* q_row,
+                                  uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, mxq_scale_rule rule,
+                                  const mxq_adam_hparams* hp, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
  * The same AdamW step with a delayed first-moment scale, in one pass over the state (no amax pre-pass; [FP8-LM]
  * Section 3.4, tensor-scaled first moment with delayed scaling):
  *   s_new = 448 / max(max(m_history), 1e-12) from the amax of m of earlier steps encodes this step's m_t;

@@ -178,3 +178,25 @@ def fp8_adam_step_delayed(master: torch.Tensor, grad: torch.Tensor, m_q: torch.T
                                            C.byref(hp), _ptr(m_history), _ptr(hist_pos), m_history.numel(),
                                            _ptr(workspace), workspace.numel(), _stream(master.device))
     _lib.check("fp8_adam_step_delayed", st)
+
+
+def fp8_adam_step_mx_cache(master: torch.Tensor, grad: torch.Tensor, m_q: torch.Tensor, m_scale: torch.Tensor,
+                           v: torch.Tensor, w: Optional[torch.Tensor], hp: AdamHParams, rows: int, cols: int,
+                           rowwise: bool = True, colwise: bool = True, rule: int = RCEIL,
+                           out: Optional[MXTensor] = None, workspace: Optional[torch.Tensor] = None) -> MXTensor:
+    """fp8_adam_step on a [rows][cols] weight that also rebuilds its MXFP8 caches from the updated fp32 master."""
+    _dev(master, torch.float32, "master"); _dev(grad, torch.bfloat16, "grad"); _dev(m_q, torch.uint8, "m_q")
+    _dev(m_scale, torch.float32, "m_scale"); _dev(v, torch.float16, "v")
+    dev = master.device
+    if out is None:
+        e = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+        out = MXTensor(e(rows, cols) if rowwise else None, e(rows, cols // 32) if rowwise else None,
+                       e(cols, rows) if colwise else None, e(cols, rows // 32) if colwise else None)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes("adam", rows * cols), dtype=torch.uint8, device=dev)
+    st = _lib.load().fp8_adam_step_mx_cache(_ptr(master), _ptr(grad), _ptr(m_q), _ptr(m_scale), _ptr(v), _ptr(w),
+                                            rows, cols, _ptr(out.q_row), _ptr(out.s_row), _ptr(out.q_col),
+                                            _ptr(out.s_col), rule, C.byref(hp), _ptr(workspace), workspace.numel(),
+                                            _stream(dev))
+    _lib.check("fp8_adam_step_mx_cache", st)
+    return out

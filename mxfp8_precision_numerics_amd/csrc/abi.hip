@@ -169,6 +169,35 @@ mxq_status fp8_adam_step(float* master, const uint16_t* grad_bf16, uint8_t* m_q,
     return hip_status(mxq::launch_adam(master, grad_bf16, m_q, m_scale, v_fp16, w_bf16, n, k, partial, consts, stream));
 }
 
+mxq_status fp8_adam_step_mx_cache(float* master, const uint16_t* grad_bf16, uint8_t* m_q, float* m_scale,
+                                  uint16_t* v_fp16, uint16_t* w_bf16, int64_t rows, int64_t cols, uint8_t* q_row,
+                                  uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, mxq_scale_rule rule,
+                                  const mxq_adam_hparams* hp, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    if (!hp) return MXQ_ERR_NULL;
+    if ((q_row == nullptr) != (s_row == nullptr) || (q_col == nullptr) != (s_col == nullptr)) return MXQ_ERR_NULL;
+    const bool row = q_row != nullptr, col = q_col != nullptr;
+    if (!row && !col) return MXQ_ERR_NULL;
+    if (rule != MXQ_SCALE_RCEIL && rule != MXQ_SCALE_FLOOR) return MXQ_ERR_UNSUPPORTED;
+    if (rows < 0 || cols < 0 || cols % 8 != 0 || hp->step < 1) return MXQ_ERR_SHAPE;
+    if ((row && cols % 32 != 0) || (col && rows % 32 != 0)) return MXQ_ERR_SHAPE;
+    if ((rows + 63) / 64 > kMaxGridY) return MXQ_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!master || !grad_bf16 || !m_q || !m_scale || !v_fp16) return MXQ_ERR_NULL;
+    if (!al16(master) || !al16(grad_bf16) || !al16(m_q) || !al16(v_fp16) || (w_bf16 && !al16(w_bf16)) ||
+        !al4(m_scale) || (row && !al16(q_row)) || (col && !al16(q_col)))
+        return MXQ_ERR_ALIGN;
+    const int64_t n = rows * cols;
+    if (!workspace || workspace_bytes < adam_ws(n)) return MXQ_ERR_WORKSPACE;
+    if (!al16(workspace)) return MXQ_ERR_ALIGN;
+    const mxq::AdamConsts k = adam_consts(*hp);
+    const size_t part_bytes = round_up((size_t)mxq::adam_parts(n) * 4u, 256);
+    uint32_t* partial = static_cast<uint32_t*>(workspace);
+    float* consts = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + part_bytes);
+    return hip_status(mxq::launch_adam_weight_cache(master, grad_bf16, m_q, m_scale, v_fp16, w_bf16, rows, cols, q_row,
+                                                    s_row, q_col, s_col, (int)rule, k, partial, consts, stream));
+}
+
 mxq_status fp8_adam_step_delayed(float* master, const uint16_t* grad_bf16, uint8_t* m_q, float* m_scale,
                                  uint16_t* v_fp16, uint16_t* w_bf16, int64_t n, const mxq_adam_hparams* hp,
                                  float* m_history, int32_t* hist_pos, int64_t history_len, void* workspace,

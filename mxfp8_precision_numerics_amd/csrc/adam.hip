@@ -258,6 +258,133 @@ __global__ void adam_delayed_finalize_kernel(const uint32_t* __restrict__ amax_w
     }
 }
 
+// ---------------------------------------------------------------------------------------- weight-cache refresh
+// The update fused with the MXFP8 quantize of the updated fp32 master weight, viewed as a [rows][cols] matrix, into
+// both orientations ("OLMo-core MoE, Section 11: MXFP8 Training", Section 11.3.2 and Figure 55: the cached operand
+// orientations are derived from the FP32 main weight after every update). One workgroup owns a 64 x 128 tile:
+// each thread updates 8 consecutive elements in 4 rows exactly as adam_update_kernel does, encodes the row
+// orientation from registers (a 32-value block spans 4 lanes) and leaves the fp32 tile in LDS for the column
+// orientation (32-row blocks, stored transposed).
+constexpr int WT_ROWS = 64, WT_COLS = 128;
+
+struct WeightCacheArgs {
+    float* master; const uint16_t* g; uint8_t* mq; uint16_t* v16; uint16_t* w;
+    int64_t rows, cols;
+    uint8_t *q_row, *s_row, *q_col, *s_col;
+    const float* consts;
+};
+
+template <int RULE, bool ROW, bool COL>
+__global__ __launch_bounds__(ATHREADS) void adam_mx_tile_kernel(WeightCacheArgs a, AdamConsts k) {
+    __shared__ __attribute__((aligned(16))) float tile[COL ? WT_ROWS * WT_COLS : 1];
+    const float inv_s = a.consts[0], s_new = a.consts[1];
+    const int tid = threadIdx.x;
+    const int ch = tid & 15, rr = tid >> 4;
+    const int64_t r0 = (int64_t)blockIdx.y * WT_ROWS, c0 = (int64_t)blockIdx.x * WT_COLS;
+    const int64_t gc = c0 + 8 * ch;
+    const bool col_ok = gc < a.cols;                     // cols % 8 == 0: a chunk is all in or all out
+    float th_new[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t gr = r0 + rr + 16 * j;
+        const bool ok = col_ok && gr < a.rows;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) th_new[j][e] = 0.0f;
+        if (ok) {
+            const int64_t i = gr * a.cols + gc;
+            const uint4 t0 = ldnt16(a.master + i), t1 = ldnt16(a.master + i + 4);
+            const uint4 gv = ldnt16(a.g + i);
+            const uint2 mv = ldnt8(a.mq + i);
+            const uint4 vv = ldnt16(a.v16 + i);
+            const uint32_t th[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+            const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+            const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+            uint32_t vo[4] = {0, 0, 0, 0}, wo[4] = {0, 0, 0, 0}, mo[2] = {0, 0};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t g16 = (gw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                const uint32_t v_16 = (vw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                const uint32_t m8 = ((e < 4 ? mv.x : mv.y) >> (8 * (e & 3))) & 0xFFu;
+                float t_out;
+                uint32_t mc, vout, wout, mabs;
+                adam_one(k, inv_s, s_new, __uint_as_float(th[e]), g16, m8, v_16, t_out, mc, vout, wout, mabs);
+                th_new[j][e] = t_out;
+                mo[e >> 2] |= mc << (8 * (e & 3));
+                vo[e >> 1] |= vout << (16 * (e & 1));
+                wo[e >> 1] |= wout << (16 * (e & 1));
+            }
+            stnt16(a.master + i, make_uint4(__float_as_uint(th_new[j][0]), __float_as_uint(th_new[j][1]),
+                                            __float_as_uint(th_new[j][2]), __float_as_uint(th_new[j][3])));
+            stnt16(a.master + i + 4, make_uint4(__float_as_uint(th_new[j][4]), __float_as_uint(th_new[j][5]),
+                                                __float_as_uint(th_new[j][6]), __float_as_uint(th_new[j][7])));
+            stnt8(a.mq + i, make_uint2(mo[0], mo[1]));
+            stnt16(a.v16 + i, make_uint4(vo[0], vo[1], vo[2], vo[3]));
+            if (a.w) stnt16(a.w + i, make_uint4(wo[0], wo[1], wo[2], wo[3]));
+        }
+    }
+
+    if constexpr (ROW) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t gr = r0 + rr + 16 * j;
+            uint32_t m = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = max(m, __float_as_uint(th_new[j][e]) & 0x7FFFFFFFu);
+            m = quad_max(m);                            // the 4 lanes of a 32-value block
+            const uint32_t byte = mx_scale_byte_f32(m, RULE);
+            const float f = mx_inv_scale_f32(byte);
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = clamp_keep_nan(th_new[j][e] * f, 448.0f);
+            const uint32_t lo = cvt_f32_pair<FMT_E4M3, true>(cvt_f32_pair<FMT_E4M3, false>(0u, y[0], y[1]), y[2], y[3]);
+            const uint32_t hi = cvt_f32_pair<FMT_E4M3, true>(cvt_f32_pair<FMT_E4M3, false>(0u, y[4], y[5]), y[6], y[7]);
+            if (col_ok && gr < a.rows) {
+                *reinterpret_cast<uint2*>(a.q_row + gr * a.cols + gc) = make_uint2(lo, hi);
+                if ((ch & 3) == 0) a.s_row[gr * (a.cols / 32) + gc / 32] = (uint8_t)byte;
+            }
+        }
+    }
+
+    if constexpr (COL) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float* dst = &tile[(rr + 16 * j) * WT_COLS + 8 * ch];
+            *reinterpret_cast<float4*>(dst) = make_float4(th_new[j][0], th_new[j][1], th_new[j][2], th_new[j][3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(th_new[j][4], th_new[j][5], th_new[j][6], th_new[j][7]);
+        }
+        __syncthreads();
+        const int c = tid & (WT_COLS - 1), b = tid >> 7;           // column, 32-row block
+        const int64_t gcol = c0 + c, grow = r0 + 32 * b;
+        float d[32];
+        uint32_t m = 0;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            d[r] = tile[(32 * b + r) * WT_COLS + c];
+            m = max(m, __float_as_uint(d[r]) & 0x7FFFFFFFu);
+        }
+        const uint32_t byte = mx_scale_byte_f32(m, RULE);
+        const float f = mx_inv_scale_f32(byte);
+        uint32_t out[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float y0 = clamp_keep_nan(d[4 * q] * f, 448.0f), y1 = clamp_keep_nan(d[4 * q + 1] * f, 448.0f);
+            const float y2 = clamp_keep_nan(d[4 * q + 2] * f, 448.0f), y3 = clamp_keep_nan(d[4 * q + 3] * f, 448.0f);
+            out[q] = cvt_f32_pair<FMT_E4M3, true>(cvt_f32_pair<FMT_E4M3, false>(0u, y0, y1), y2, y3);
+        }
+        if (gcol < a.cols && grow + 32 <= a.rows) {               // rows % 32 == 0: a block is whole or absent
+            uint4* q = reinterpret_cast<uint4*>(a.q_col + gcol * a.rows + grow);
+            q[0] = make_uint4(out[0], out[1], out[2], out[3]);
+            q[1] = make_uint4(out[4], out[5], out[6], out[7]);
+            a.s_col[gcol * (a.rows / 32) + grow / 32] = (uint8_t)byte;
+        }
+    }
+}
+
+hipError_t launch_adam_weight_cache(float* master, const uint16_t* grad, uint8_t* m_q, float* m_scale, uint16_t* v16,
+                                    uint16_t* w, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
+                                    uint8_t* q_col, uint8_t* s_col, int rule, const AdamConsts& k, uint32_t* partial,
+                                    float* consts, hipStream_t stream);
+
 int adam_parts(int64_t n) {
     int64_t chunks = (n + 7) / 8;
     int64_t parts = (chunks + ATHREADS * 4 - 1) / (ATHREADS * 4);
@@ -273,6 +400,32 @@ hipError_t launch_adam(float* master, const uint16_t* grad, uint8_t* m_q, float*
     hipLaunchKernelGGL(adam_finalize_kernel, dim3(1), dim3(ATHREADS), 0, stream, partial, parts, m_scale, consts);
     hipLaunchKernelGGL(adam_update_kernel<false>, dim3(parts), dim3(ATHREADS), 0, stream, master, grad, m_q, v16, w, n, k,
                        (const float*)consts, (uint32_t*)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_adam_weight_cache(float* master, const uint16_t* grad, uint8_t* m_q, float* m_scale, uint16_t* v16,
+                                    uint16_t* w, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
+                                    uint8_t* q_col, uint8_t* s_col, int rule, const AdamConsts& k, uint32_t* partial,
+                                    float* consts, hipStream_t stream) {
+    const int64_t n = rows * cols;
+    const int parts = adam_parts(n);
+    hipLaunchKernelGGL(adam_amax_kernel, dim3(parts), dim3(ATHREADS), 0, stream, grad, m_q, m_scale, n, k, partial);
+    hipLaunchKernelGGL(adam_finalize_kernel, dim3(1), dim3(ATHREADS), 0, stream, partial, parts, m_scale, consts);
+    WeightCacheArgs a{master, grad, m_q, v16, w, rows, cols, q_row, s_row, q_col, s_col, consts};
+    dim3 grid((unsigned)((cols + WT_COLS - 1) / WT_COLS), (unsigned)((rows + WT_ROWS - 1) / WT_ROWS));
+    const bool row = q_row != nullptr, col = q_col != nullptr;
+#define MXQ_WC_LAUNCH(R, RW, CL) \
+    hipLaunchKernelGGL((adam_mx_tile_kernel<R, RW, CL>), grid, dim3(ATHREADS), 0, stream, a, k)
+    if (rule == RULE_FLOOR) {
+        if (row && col) MXQ_WC_LAUNCH(RULE_FLOOR, true, true);
+        else if (row) MXQ_WC_LAUNCH(RULE_FLOOR, true, false);
+        else MXQ_WC_LAUNCH(RULE_FLOOR, false, true);
+    } else {
+        if (row && col) MXQ_WC_LAUNCH(RULE_RCEIL, true, true);
+        else if (row) MXQ_WC_LAUNCH(RULE_RCEIL, true, false);
+        else MXQ_WC_LAUNCH(RULE_RCEIL, false, true);
+    }
+#undef MXQ_WC_LAUNCH
     return hipGetLastError();
 }
 

@@ -33,6 +33,10 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int
 int adam_parts(int64_t n);
 hipError_t launch_adam(float* master, const uint16_t* grad, uint8_t* m_q, float* m_scale, uint16_t* v16, uint16_t* w,
                        int64_t n, const AdamConsts& k, uint32_t* partial, float* consts, hipStream_t stream);
+hipError_t launch_adam_weight_cache(float* master, const uint16_t* grad, uint8_t* m_q, float* m_scale, uint16_t* v16,
+                                    uint16_t* w, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
+                                    uint8_t* q_col, uint8_t* s_col, int rule, const AdamConsts& k, uint32_t* partial,
+                                    float* consts, hipStream_t stream);
 hipError_t launch_adam_delayed(float* master, const uint16_t* grad, uint8_t* m_q, float* m_scale, uint16_t* v16,
                                uint16_t* w, int64_t n, const AdamConsts& k, float* hist, int32_t* pos, int H,
                                float* consts, uint32_t* amax_word, hipStream_t stream);

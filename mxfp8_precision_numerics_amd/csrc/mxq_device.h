@@ -72,6 +72,21 @@ __device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits, int rule) 
     return b < 0 ? 0u : (uint32_t)b;
 }
 
+// The same rule for an fp32 block maximum (magnitude bits): NaN -> 0xFF, +inf -> 254 (e = 127), otherwise
+// E - 8 (+1 under rceil when the mantissa exceeds 0.75, i.e. amax > 448 * 2^(E-135)), clamped at 0.
+__device__ __forceinline__ uint32_t mx_scale_byte_f32(uint32_t abs_bits, int rule) {
+    if (abs_bits >= 0x7F800000u) return abs_bits == 0x7F800000u ? 254u : 255u;
+    int E = (int)(abs_bits >> 23), mant = (int)(abs_bits & 0x7FFFFF);
+    int b = E - 8 + ((rule == RULE_RCEIL && mant > 0x600000) ? 1 : 0);
+    return b < 0 ? 0u : (uint32_t)b;
+}
+
+// 2^-(e) for the block exponent e = byte - 127 as an fp32 multiplier; byte 254 (and NaN's 255, encoded as if
+// e = 127) give the subnormal 2^-127. Multiplying by it scales exactly wherever the result can reach E4M3's range.
+__device__ __forceinline__ float mx_inv_scale_f32(uint32_t byte) {
+    return byte < 254u ? __uint_as_float((254u - byte) << 23) : __uint_as_float(0x00400000u);
+}
+
 // fp32 scale operand for v_cvt_scalef32_*: only its exponent field is read, so byte -> exponent bits
 // (a mantissa bit is set so the byte-0 pattern is a subnormal rather than zero).
 __device__ __forceinline__ float scale_operand(uint32_t byte) {

@@ -119,3 +119,18 @@ def test_delayed_validation():
     assert g(P, P, P, P, P, None, 1024, C.byref(hp), P, P, 0, P, wsa, None) == 2
     assert g(P, P, P, P, P, None, 1024, C.byref(hp), P, P, 4, P, wsa - 1, None) == 5
     assert g(P, P, P, P, P, None, 0, C.byref(hp), None, None, 4, None, 0, None) == 0     # empty
+
+
+def test_weight_cache_validation():
+    lib = _lib.load()
+    f = lib.fp8_adam_step_mx_cache
+    hp = _lib.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.0, 1)
+    ws = lib.mxq_workspace_bytes(b"adam", 64 * 64)
+    assert f(P, P, P, P, P, None, 64, 64, None, None, None, None, 0, C.byref(hp), P, ws, None) == 1   # no cache
+    assert f(P, P, P, P, P, None, 64, 64, P, None, None, None, 0, C.byref(hp), P, ws, None) == 1      # q without s
+    assert f(P, P, P, P, P, None, 64, 48, P, P, None, None, 0, C.byref(hp), P, ws, None) == 2         # cols % 32
+    assert f(P, P, P, P, P, None, 48, 64, None, None, P, P, 0, C.byref(hp), P, ws, None) == 2         # rows % 32
+    assert f(P, P, P, P, P, None, 64, 64, P, P, P, P, 9, C.byref(hp), P, ws, None) == 4
+    assert f(P, P, P, P, P, None, 64, 64, P, P, P, P, 0, C.byref(hp), P, ws - 1, None) == 5
+    assert f(P, P, P, P, P, None, 64, 64, MIS, P, P, P, 0, C.byref(hp), P, ws, None) == 3
+    assert f(P, P, P, P, P, None, 0, 64, P, P, P, P, 0, C.byref(hp), None, 0, None) == 0              # empty

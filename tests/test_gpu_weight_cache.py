@@ -1,0 +1,63 @@
+"""GPU parity of fp8_adam_step_mx_cache: the Adam outputs must equal the oracle's Adam step bit for bit, and the
+two MXFP8 cache orientations must equal the oracle's fp32-input MX quantize of the updated master weight (viewed as
+[rows][cols]), byte for byte, over consecutive steps."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_precision_numerics_amd as mxq
+import oracle
+from gpu_util import DEV, need_gpu, say, u16, u8
+from mxfp8_precision_numerics_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("rows,cols,rule,wd", [(64, 128, mxq.RCEIL, 0.0), (96, 160, mxq.FLOOR, 0.1),
+                                               (320, 1056, mxq.RCEIL, 0.1), (2048, 4096, mxq.RCEIL, 0.0)])
+def test_weight_cache_steps(rows, cols, rule, wd):
+    need_gpu()
+    say("weight cache", rows, cols, rule, wd)
+    n = rows * cols
+    theta = workloads.workload5_params(n, DEV)
+    m_q = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    m_scale = torch.ones(1, dtype=torch.float32, device=DEV)
+    v = torch.zeros(n, dtype=torch.float16, device=DEV)
+    w = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    o_theta = theta.cpu().numpy().copy()
+    o_mq = np.zeros(n, np.uint8); o_ms = np.ones(1, np.float32); o_v = np.zeros(n, np.uint16)
+    for t in (1, 2):
+        g = workloads.workload5_grad(n, t, DEV)
+        hp = mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, wd, t)
+        ohp = oracle.AdamHP(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=wd, step=t)
+        cache = mxq.fp8_adam_step_mx_cache(theta, g, m_q, m_scale, v, w, hp, rows, cols, rule=rule)
+        torch.cuda.synchronize()
+        _, o_w = oracle.adam_step(o_theta, u16(g), o_mq, o_ms, o_v, ohp)
+        qr, sr, qc, sc = oracle.mx_quantize_f32(o_theta.reshape(rows, cols), rule)
+        assert np.array_equal(theta.cpu().numpy().view(np.uint32), o_theta.view(np.uint32)), f"theta t={t}"
+        assert np.array_equal(u8(m_q), o_mq) and np.float32(m_scale.item()) == o_ms[0], f"m t={t}"
+        assert np.array_equal(u16(v), o_v) and np.array_equal(u16(w), o_w), f"v/w t={t}"
+        assert np.array_equal(u8(cache.s_row), sr) and np.array_equal(u8(cache.q_row), qr), f"row cache t={t}"
+        assert np.array_equal(u8(cache.s_col), sc) and np.array_equal(u8(cache.q_col), qc), f"col cache t={t}"
+
+
+def test_weight_cache_single_orientation_and_no_weight_copy():
+    need_gpu()
+    rows, cols = 128, 256
+    n = rows * cols
+    base = workloads.workload5_params(n, DEV)
+    g = workloads.workload5_grad(n, 1, DEV)
+    hp = mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.0, 1)
+    outs = []
+    for rowwise, colwise in ((True, True), (True, False), (False, True)):
+        theta = base.clone()
+        m_q = torch.zeros(n, dtype=torch.uint8, device=DEV)
+        ms = torch.ones(1, dtype=torch.float32, device=DEV)
+        v = torch.zeros(n, dtype=torch.float16, device=DEV)
+        c = mxq.fp8_adam_step_mx_cache(theta, g, m_q, ms, v, None, hp, rows, cols, rowwise, colwise)
+        outs.append((theta, c))
+    torch.cuda.synchronize()
+    full = outs[0][1]
+    assert torch.equal(outs[1][0], outs[0][0]) and torch.equal(outs[2][0], outs[0][0])
+    assert torch.equal(outs[1][1].q_row, full.q_row) and torch.equal(outs[1][1].s_row, full.s_row)
+    assert torch.equal(outs[2][1].q_col, full.q_col) and torch.equal(outs[2][1].s_col, full.s_col)
