@@ -11,6 +11,8 @@ One step is one pass over every row of the hot path, on seeded synthetic inputs 
   small         MX quantize + 256^3 block-scaled GEMM
   pt_quant_delayed  the per-tensor casts of X, W, dY with delayed scaling (16-slot amax histories): one pass each
   adam_delayed  the Adam step with a delayed first-moment scale: one pass over the state (18 B/param)
+  wcache_fused  Adam on W's 36864 x 12288 state fused with the refresh of W's two MXFP8 caches from the fp32 master
+  wcache_unfused  the same as two calls: Adam writing a bf16 copy, then MX quantize of that copy
 The headline value is the MXFP8 linear layer's GEMM FLOPs (11.13 TFLOP) divided by the device time of its quantize
 and GEMM launches ("MXFP8 GEMM TFLOP/s incl. quantize"). Device times come from events on the stream the kernels
 run on; the JSON line also carries every part's rate, the MX GEMM's roofline and the CPU oracle baseline.
@@ -116,11 +118,21 @@ def main():
     mxq.fp8_adam_step(theta, grad, m_q, m_scale, v16, w16, hp, workspace=adam_ws)
     m_hist[0] = 448.0 / m_scale[0]           # the amax that step's scale came from
     m_pos[0] = 1
+    # weight-cache refresh on W's shape: Adam state of a 36864 x 12288 weight and its two MX caches
+    nw = N * K
+    th_w = W.float().reshape(-1).clone()
+    g_w = workloads.normal_bf16((nw,), 1e-3, 5, 7, dev)
+    mq_w = torch.zeros(nw, dtype=torch.uint8, device=dev)
+    ms_w = torch.ones(1, dtype=torch.float32, device=dev)
+    v_w = torch.zeros(nw, dtype=torch.float16, device=dev)
+    wb_w = torch.empty(nw, dtype=torch.bfloat16, device=dev)
+    cache_w = mxq.MXTensor(u8(N, K), u8(N, K // 32), u8(K, N), u8(K, N // 32))
+    ws_w = torch.empty(mxq.workspace_bytes("adam", nw), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     parts = ["mx_quant_XWdY", "mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "pt_quant", "pt_gemms", "mx_quant_act",
-             "grouped", "adam", "small", "pt_quant_delayed", "adam_delayed"]
+             "grouped", "adam", "small", "pt_quant_delayed", "adam_delayed", "wcache_fused", "wcache_unfused"]
     NEV = len(parts) + 1
 
     def step(ev):
@@ -164,6 +176,11 @@ def main():
         ev[11].record(stream)
         mxq.fp8_adam_step_delayed(theta, grad, m_q, m_scale, v16, w16, hp, m_hist, m_pos, workspace=ws_adel)
         ev[12].record(stream)
+        mxq.fp8_adam_step_mx_cache(th_w, g_w, mq_w, ms_w, v_w, None, hp, N, K, out=cache_w, workspace=ws_w)
+        ev[13].record(stream)
+        mxq.fp8_adam_step(th_w, g_w, mq_w, ms_w, v_w, wb_w, hp, workspace=ws_w)
+        mxq.mx_quantize(wb_w.view(N, K), out=cache_w)
+        ev[14].record(stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -212,6 +229,8 @@ def main():
         "small_us": ms["small"] * 1e3,
         "pt_quant_delayed_gbs": sum(4 * r * c for r, c in ((M, K), (N, K), (M, N))) / (ms["pt_quant_delayed"] * 1e-3) / 1e9,
         "adam_delayed_gbs": 18 * n_adam / (ms["adam_delayed"] * 1e-3) / 1e9,
+        "wcache_fused_gbs": (21 + 2 / 32) * N * K / (ms["wcache_fused"] * 1e-3) / 1e9,
+        "wcache_fused_speedup_vs_unfused": ms["wcache_unfused"] / ms["wcache_fused"],
     }
     for k, v in rate.items():
         rate[k] = round(v, 3)
