@@ -63,6 +63,9 @@ def lib():
         L.orc_adam_amax.restype = F
         L.orc_adam_amax.argtypes = [P, P, P, F, I64, P, I]
         L.orc_mx_quantize_f32.argtypes = [P, I64, I64, I, P, P, P, P, I]
+        L.orc_exp_f32.restype = F; L.orc_exp_f32.argtypes = [F]
+        L.orc_swiglu_f32.restype = F; L.orc_swiglu_f32.argtypes = [F, F]
+        L.orc_swiglu_mx_quantize.argtypes = [P, I64, I64, I, P, P, P]
         L.orc_delayed_scale.restype = F
         L.orc_delayed_scale.argtypes = [P, I64, I, F]
         L.orc_history_push.argtypes = [P, I64, P, F]
@@ -160,6 +163,26 @@ def mx_quantize_f32(x_f32, rule: int = RCEIL, rowwise: bool = True, colwise: boo
     lib().orc_mx_quantize_f32(_p(x), R, Ccols, rule, _p(q_row), _p(s_row), _p(q_col), _p(s_col),
                               nthreads or default_threads())
     return q_row, s_row, q_col, s_col
+
+
+def exp_f32(x: float) -> np.float32:
+    return np.float32(lib().orc_exp_f32(C.c_float(x)))
+
+
+def swiglu_f32(g: float, u: float) -> np.float32:
+    return np.float32(lib().orc_swiglu_f32(C.c_float(g), C.c_float(u)))
+
+
+def swiglu_mx_quantize(c_bf16, rule: int = RCEIL, want_h: bool = False):
+    """c_bf16: [rows][2F] (gate | up). Returns (q[rows][F], s[rows][F/32], h fp32 or None)."""
+    c = _c(c_bf16, np.uint16)
+    R, F2 = c.shape
+    F = F2 // 2
+    q = np.empty((R, F), np.uint8)
+    s = np.empty((R, F // 32), np.uint8)
+    h = np.empty((R, F), np.float32) if want_h else None
+    lib().orc_swiglu_mx_quantize(_p(c), R, F, rule, _p(q), _p(s), _p(h))
+    return q, s, h
 
 
 def pertensor_quantize(x_bf16, fmt: int = E4M3, margin: float = 1.0, scale_in: float | None = None,

@@ -282,6 +282,66 @@ void orc_mx_quantize_f32(const float* x, int64_t rows, int64_t cols, int rule, u
 }
 
 /* ------------------------------------------------------------------------------------------------------
+ * Fused SwiGLU + MX row quantize ([OLMO11] Section 11.4.1: the hidden representation of the routed experts is
+ * produced by a fused SwiGLU-plus-quantization step, straight into the down projection's MXFP8 operand).
+ * Reading: the up/gate GEMM output C[rows][2F] holds the gate in columns [0, F) and up in [F, 2F);
+ * h = silu(g) * u with silu(g) = g / (1 + exp(-g)), every operation one fp32 rounding, and h is quantized from fp32
+ * (one rounding to E4M3) in 32-value blocks along each row.
+ * exp is evaluated by a fixed fp32 sequence both implementations follow: Cody-Waite reduction x = k ln2 + r
+ * (k = rint(x log2 e), ln2 split into a high part with few significant bits and a low part), the degree-6 Taylor
+ * polynomial of e^r in Horner form, then the exact scaling by 2^k. Its error against the true exponential is a few
+ * ulp; it is fixed so that both sides produce the same fp32 value.
+ * ------------------------------------------------------------------------------------------------------ */
+float orc_exp_f32(float x)
+{
+    if (x != x) return x;
+    if (x > 88.75f) return INFINITY;
+    if (x < -104.0f) return 0.0f;
+    const float log2e = 1.44269504f;
+    const float ln2_hi = 0.693145751953125f;          /* 0x3F317200: ln 2 to 16 significant bits */
+    const float ln2_lo = 1.42860677e-06f;             /* ln 2 - ln2_hi */
+    float t = x * log2e;
+    float k = rintf(t);
+    float a = k * ln2_hi;                             /* exact: k has at most 8 significant bits */
+    float r = x - a;
+    float b = k * ln2_lo;
+    r = r - b;
+    float p = 1.0f / 720.0f;
+    p = p * r; p = p + 1.0f / 120.0f;
+    p = p * r; p = p + 1.0f / 24.0f;
+    p = p * r; p = p + 1.0f / 6.0f;
+    p = p * r; p = p + 0.5f;
+    p = p * r; p = p + 1.0f;
+    p = p * r; p = p + 1.0f;
+    return ldexpf(p, (int)k);
+}
+
+float orc_swiglu_f32(float g, float u)
+{
+    float e = orc_exp_f32(-g);
+    float d = 1.0f + e;
+    float silu = g / d;
+    return silu * u;
+}
+
+void orc_swiglu_mx_quantize(const uint16_t* c, int64_t rows, int64_t F, int rule, uint8_t* q, uint8_t* s,
+                            float* h_out)
+{
+    tables();
+    float* h = (float*)malloc(sizeof(float) * (size_t)F);
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* row = c + r * 2 * F;
+        for (int64_t j = 0; j < F; ++j) {
+            h[j] = orc_swiglu_f32(orc_bf16_to_f32(row[j]), orc_bf16_to_f32(row[F + j]));
+            if (h_out) h_out[r * F + j] = h[j];
+        }
+        for (int64_t b = 0; b < F / 32; ++b)
+            s[r * (F / 32) + b] = mx_block_f32(h + 32 * b, 1, rule, q + r * F + 32 * b);
+    }
+    free(h);
+}
+
+/* ------------------------------------------------------------------------------------------------------
  * Per-tensor current scaling ([FP8-LM] tensor scaling; [LLMSB] per-tensor scaling and Exercise 6).
  *   amax = max |x|;  s = (FMAX / max(amax, 1e-12)) * margin  (fp32);  q = FP8(fp32(x * s));  x ~ q / s.
  * With scale_in given (delayed scaling) s = *scale_in and amax is still reported.
