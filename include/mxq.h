@@ -73,6 +73,19 @@ mxq_status mxq_quantize(const uint16_t* x_bf16, int64_t rows, int64_t cols,
                         mxq_scale_rule rule, hipStream_t stream);
 
 /*
+ * Fused SwiGLU + MXFP8 row quantize of the routed experts' hidden representation ([OLMO11] Section 11.4.1: a fused
+ * SwiGLU-plus-quantization step produces the down projection's operand with no separate BF16-to-MXFP8 pass).
+ *   c_bf16[rows][2F]: the up/gate GEMM output, gate in columns [0, F), up in [F, 2F);
+ *   h = silu(g) * u in fp32 with silu(g) = g / (1 + exp(-g)), each operation rounded on its own; exp is a fixed fp32
+ *   sequence (Cody-Waite reduction by k ln2, degree-6 Taylor polynomial, exact scaling by 2^k; within a few ulp of the
+ *   true exponential), so the result is reproducible bit for bit;
+ *   q[rows][F], s[rows][F/32]: h quantized from fp32 in 32-value blocks along each row (rule as in mxq_quantize).
+ * Requires F % 32 == 0.
+ */
+mxq_status swiglu_mx_quantize(const uint16_t* c_bf16, int64_t rows, int64_t F, uint8_t* q, uint8_t* s,
+                              mxq_scale_rule rule, hipStream_t stream);
+
+/*
  * Per-tensor current scaling ([FP8-LM] tensor scaling FP8(x) = cast(s x), x ~ FP8(x) / s; [LLMSB] per-tensor
  * scaling and Exercise 6's to_fp8_e4m3):
  *   amax_out[0] = max |x|   (fp32, device);

@@ -68,6 +68,19 @@ def mx_quantize(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, rul
     return out
 
 
+def swiglu_mx_quantize(c: torch.Tensor, rule: int = RCEIL, out: Optional[MXTensor] = None) -> MXTensor:
+    """c: bf16 [rows][2F] (gate | up) -> MXFP8 row orientation of silu(gate) * up: MXTensor(q_row, s_row, None, None)."""
+    _dev(c, torch.bfloat16, "c")
+    rows, f2 = c.shape
+    F = f2 // 2
+    if out is None:
+        out = MXTensor(torch.empty((rows, F), dtype=torch.uint8, device=c.device),
+                       torch.empty((rows, F // 32), dtype=torch.uint8, device=c.device), None, None)
+    st = _lib.load().swiglu_mx_quantize(_ptr(c), rows, F, _ptr(out.q_row), _ptr(out.s_row), rule, _stream(c.device))
+    _lib.check("swiglu_mx_quantize", st)
+    return out
+
+
 class PerTensorFP8(NamedTuple):
     q: Optional[torch.Tensor]       # [rows][cols] uint8
     q_t: Optional[torch.Tensor]     # [cols][rows] uint8

@@ -84,6 +84,16 @@ mxq_status mxq_quantize(const uint16_t* x_bf16, int64_t rows, int64_t cols, uint
     return hip_status(mxq::launch_mx_quantize(x_bf16, rows, cols, q_row, s_row, q_col, s_col, (int)rule, stream));
 }
 
+mxq_status swiglu_mx_quantize(const uint16_t* c_bf16, int64_t rows, int64_t F, uint8_t* q, uint8_t* s,
+                              mxq_scale_rule rule, hipStream_t stream) {
+    if (rule != MXQ_SCALE_RCEIL && rule != MXQ_SCALE_FLOOR) return MXQ_ERR_UNSUPPORTED;
+    if (rows < 0 || F < 0 || F % 32 != 0) return MXQ_ERR_SHAPE;
+    if (rows == 0 || F == 0) return MXQ_OK;
+    if (!c_bf16 || !q || !s) return MXQ_ERR_NULL;
+    if (!al16(c_bf16) || !al16(q)) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_swiglu_mx_quantize(c_bf16, rows, F, q, s, (int)rule, stream));
+}
+
 mxq_status fp8_quantize_pertensor(const uint16_t* x_bf16, int64_t rows, int64_t cols, mxq_fp8 fmt, float margin,
                                   const float* scale_in, float* amax_out, float* scale_out, uint8_t* q, uint8_t* q_t,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {

@@ -22,6 +22,9 @@ hipError_t launch_pertensor_quantize_delayed(const uint16_t* x, int64_t rows, in
                                              float* hist, int32_t* pos, int H, float* amax_out, float* scale_out,
                                              uint8_t* q, uint8_t* q_t, uint32_t* amax_word, hipStream_t stream);
 
+hipError_t launch_swiglu_mx_quantize(const uint16_t* c, int64_t rows, int64_t F, uint8_t* q, uint8_t* s, int rule,
+                                     hipStream_t stream);
+
 hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt, const uint8_t* b_q,
                               const void* b_scale, int b_fmt, int64_t M, int64_t N, int64_t K, int mx,
                               uint16_t* c, int64_t ldc, hipStream_t stream);

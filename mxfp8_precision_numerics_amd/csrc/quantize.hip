@@ -397,4 +397,84 @@ hipError_t launch_pertensor_quantize_delayed(const uint16_t* x, int64_t rows, in
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------- fused SwiGLU + MX
+// The routed experts' hidden representation ("OLMo-core MoE, Section 11: MXFP8 Training", Section 11.4.1: a fused
+// SwiGLU-plus-quantization step feeds the down projection without a separate BF16-to-MXFP8 pass). C[rows][2F]
+// holds the gate in columns [0, F) and up in [F, 2F); h = silu(g) * u in fp32, quantized from fp32 in 32-value
+// blocks along each row. exp is the fixed fp32 sequence below (Cody-Waite reduction by k ln2, ln2 in a 16-bit
+// high part and a low part, the degree-6 Taylor polynomial of e^r in Horner form, exact scaling by 2^k), every
+// operation rounded on its own, so that any implementation following it computes the same value.
+__device__ __forceinline__ float exp_fixed(float x) {
+    if (x != x) return x;
+    if (x > 88.75f) return __uint_as_float(0x7F800000u);
+    if (x < -104.0f) return 0.0f;
+    const float t = x * 1.44269504f;
+    const float k = __builtin_rintf(t);
+    const float a = k * 0.693145751953125f;
+    float r = x - a;
+    const float b = k * 1.42860677e-06f;
+    r = r - b;
+    float p = 1.0f / 720.0f;
+    p = p * r; p = p + 1.0f / 120.0f;
+    p = p * r; p = p + 1.0f / 24.0f;
+    p = p * r; p = p + 1.0f / 6.0f;
+    p = p * r; p = p + 0.5f;
+    p = p * r; p = p + 1.0f;
+    p = p * r; p = p + 1.0f;
+    return __builtin_ldexpf(p, (int)k);
+}
+
+__device__ __forceinline__ float swiglu_f32(float g, float u) {
+    const float e = exp_fixed(-g);
+    const float d = 1.0f + e;
+    const float silu = g / d;
+    return silu * u;
+}
+
+// One thread per 8 consecutive outputs of a row; the 4 lanes of a quad cover one 32-value block (F % 32 == 0, so
+// quads never straddle rows and the chunk count is a multiple of 4).
+template <int RULE>
+__global__ __launch_bounds__(256) void swiglu_mx_kernel(const uint16_t* __restrict__ c, int64_t rows, int64_t F,
+                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+    const int64_t per_row = F / 8, total = rows * per_row;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+        const int64_t r = i / per_row, j = (i - r * per_row) * 8;
+        const uint4 gv = ldnt16(c + r * 2 * F + j);
+        const uint4 uv = ldnt16(c + r * 2 * F + F + j);
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+        float h[8];
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float g = (e & 1) ? bf16_hi(gw[e >> 1]) : bf16_lo(gw[e >> 1]);
+            const float u = (e & 1) ? bf16_hi(uw[e >> 1]) : bf16_lo(uw[e >> 1]);
+            h[e] = swiglu_f32(g, u);
+            m = max(m, __float_as_uint(h[e]) & 0x7FFFFFFFu);
+        }
+        m = quad_max(m);
+        const uint32_t byte = mx_scale_byte_f32(m, RULE);
+        const float f = mx_inv_scale_f32(byte);
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = clamp_keep_nan(h[e] * f, 448.0f);
+        const uint32_t lo = cvt_f32_pair<FMT_E4M3, true>(cvt_f32_pair<FMT_E4M3, false>(0u, y[0], y[1]), y[2], y[3]);
+        const uint32_t hi = cvt_f32_pair<FMT_E4M3, true>(cvt_f32_pair<FMT_E4M3, false>(0u, y[4], y[5]), y[6], y[7]);
+        *reinterpret_cast<uint2*>(q + r * F + j) = make_uint2(lo, hi);
+        if ((j & 31) == 0) s[r * (F / 32) + j / 32] = (uint8_t)byte;
+    }
+}
+
+hipError_t launch_swiglu_mx_quantize(const uint16_t* c, int64_t rows, int64_t F, uint8_t* q, uint8_t* s, int rule,
+                                     hipStream_t stream) {
+    const int64_t total = rows * (F / 8);
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (rule == RULE_FLOOR)
+        hipLaunchKernelGGL(swiglu_mx_kernel<RULE_FLOOR>, dim3((unsigned)blocks), dim3(256), 0, stream, c, rows, F, q, s);
+    else
+        hipLaunchKernelGGL(swiglu_mx_kernel<RULE_RCEIL>, dim3((unsigned)blocks), dim3(256), 0, stream, c, rows, F, q, s);
+    return hipGetLastError();
+}
+
 }  // namespace mxq

@@ -134,3 +134,12 @@ def test_weight_cache_validation():
     assert f(P, P, P, P, P, None, 64, 64, P, P, P, P, 0, C.byref(hp), P, ws - 1, None) == 5
     assert f(P, P, P, P, P, None, 64, 64, MIS, P, P, P, 0, C.byref(hp), P, ws, None) == 3
     assert f(P, P, P, P, P, None, 0, 64, P, P, P, P, 0, C.byref(hp), None, 0, None) == 0              # empty
+
+
+def test_swiglu_validation():
+    f = _lib.load().swiglu_mx_quantize
+    assert f(P, 64, 48, P, P, 0, None) == 2          # F % 32
+    assert f(P, 64, 64, P, P, 3, None) == 4
+    assert f(None, 64, 64, P, P, 0, None) == 1
+    assert f(MIS, 64, 64, P, P, 0, None) == 3
+    assert f(None, 0, 64, None, None, 0, None) == 0   # empty
