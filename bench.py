@@ -13,6 +13,9 @@ One step is one pass over every row of the hot path, on seeded synthetic inputs 
   adam_delayed  the Adam step with a delayed first-moment scale: one pass over the state (18 B/param)
   wcache_fused  Adam on W's 36864 x 12288 state fused with the refresh of W's two MXFP8 caches from the fp32 master
   wcache_unfused  the same as two calls: Adam writing a bf16 copy, then MX quantize of that copy
+  moe_swiglu_mlp  the routed MLP of the grouped workload with SwiGLU: activation quantize, up/gate grouped GEMM
+                (2048 -> 2 x 1024), fused SwiGLU + MX quantize, down grouped GEMM (1024 -> 2048)
+  swiglu_quant  the fused SwiGLU + MX quantize alone (132,160 x 2048 bf16 in, 132,160 x 1024 MXFP8 out)
 The headline value is the MXFP8 linear layer's GEMM FLOPs (11.13 TFLOP) divided by the device time of its quantize
 and GEMM launches ("MXFP8 GEMM TFLOP/s incl. quantize"). Device times come from events on the stream the kernels
 run on; the JSON line also carries every part's rate, the MX GEMM's roofline and the CPU oracle baseline.
@@ -103,6 +106,13 @@ def main():
     mx_dn = mxq.MXTensor(u8(rows4, d_ff), u8(rows4, d_ff // 32), None, None)
     C_up = torch.empty((rows4, d_ff), dtype=torch.bfloat16, device=dev)
     C_dn = torch.empty((rows4, d_model), dtype=torch.bfloat16, device=dev)
+    # routed MLP with SwiGLU: gate|up expert weights [G][2 d_ff][d_model] (seeded N(0,1), quantized once), the fused
+    # SwiGLU + MX quantize between the up/gate and down grouped GEMMs
+    w_gu = workloads.normal_bf16((G * 2 * d_ff, d_model), 1.0, 4, 5, dev)
+    qwgu = mxq.mx_quantize(w_gu, colwise=False)
+    del w_gu
+    C_gu = torch.empty((rows4, 2 * d_ff), dtype=torch.bfloat16, device=dev)
+    mx_h = mxq.MXTensor(u8(rows4, d_ff), u8(rows4, d_ff // 32), None, None)
     hp = mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.0, 2)
     # delayed scaling: amax histories (16 slots) seeded with one current-scaling call each
     hists, hpos = {}, {}
@@ -132,7 +142,8 @@ def main():
 
     Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     parts = ["mx_quant_XWdY", "mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "pt_quant", "pt_gemms", "mx_quant_act",
-             "grouped", "adam", "small", "pt_quant_delayed", "adam_delayed", "wcache_fused", "wcache_unfused"]
+             "grouped", "adam", "small", "pt_quant_delayed", "adam_delayed", "wcache_fused", "wcache_unfused",
+             "moe_swiglu_mlp", "swiglu_quant"]
     NEV = len(parts) + 1
 
     def step(ev):
@@ -181,6 +192,15 @@ def main():
         mxq.fp8_adam_step(th_w, g_w, mq_w, ms_w, v_w, wb_w, hp, workspace=ws_w)
         mxq.mx_quantize(wb_w.view(N, K), out=cache_w)
         ev[14].record(stream)
+        mxq.mx_quantize(wl4["a_up"], colwise=False, out=mx_up)
+        mxq.grouped_scaled_gemm(mx_up.q_row, mx_up.s_row, off4, qwgu.q_row.view(G, 2 * d_ff, d_model),
+                                qwgu.s_row.view(G, 2 * d_ff, d_model // 32), out=C_gu)
+        mxq.swiglu_mx_quantize(C_gu, out=mx_h)
+        mxq.grouped_scaled_gemm(mx_h.q_row, mx_h.s_row, off4, qwd.q_row.view(G, d_model, d_ff),
+                                qwd.s_row.view(G, d_model, d_ff // 32), out=C_dn)
+        ev[15].record(stream)
+        mxq.swiglu_mx_quantize(C_gu, out=mx_h)
+        ev[16].record(stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -231,6 +251,9 @@ def main():
         "adam_delayed_gbs": 18 * n_adam / (ms["adam_delayed"] * 1e-3) / 1e9,
         "wcache_fused_gbs": (21 + 2 / 32) * N * K / (ms["wcache_fused"] * 1e-3) / 1e9,
         "wcache_fused_speedup_vs_unfused": ms["wcache_unfused"] / ms["wcache_fused"],
+        "moe_swiglu_mlp_tflops_incl_quant": 2.0 * rows_valid * (2 * d_ff * d_model + d_ff * d_model)
+                                            / (ms["moe_swiglu_mlp"] * 1e-3) / 1e12,
+        "swiglu_quant_gbs": rows4 * (4 * d_ff + d_ff + d_ff // 32) / (ms["swiglu_quant"] * 1e-3) / 1e9,
     }
     for k, v in rate.items():
         rate[k] = round(v, 3)
