@@ -66,6 +66,9 @@ def lib():
         L.orc_exp_f32.restype = F; L.orc_exp_f32.argtypes = [F]
         L.orc_swiglu_f32.restype = F; L.orc_swiglu_f32.argtypes = [F, F]
         L.orc_swiglu_mx_quantize.argtypes = [P, I64, I64, I, P, P, P]
+        L.orc_autoscale_cast.argtypes = [P, I64, I, P, P, P, P]
+        L.orc_min_scale.restype = F; L.orc_min_scale.argtypes = [P, I64]
+        L.orc_requantize_shared.argtypes = [P, I64, I, F, F, I, P]
         L.orc_delayed_scale.restype = F
         L.orc_delayed_scale.argtypes = [P, I64, I, F]
         L.orc_history_push.argtypes = [P, I64, P, F]
@@ -183,6 +186,29 @@ def swiglu_mx_quantize(c_bf16, rule: int = RCEIL, want_h: bool = False):
     h = np.empty((R, F), np.float32) if want_h else None
     lib().orc_swiglu_mx_quantize(_p(c), R, F, rule, _p(q), _p(s), _p(h))
     return q, s, h
+
+
+def autoscale_cast(g_bf16, mu: float, fmt: int = E4M3):
+    """Returns (q, overflow_count, scale used (= mu), mu for the next step)."""
+    g = _c(g_bf16, np.uint16).reshape(-1)
+    m = np.array([mu], np.float32)
+    q = np.empty(g.size, np.uint8)
+    cnt = np.zeros(1, np.uint64)
+    sc = np.zeros(1, np.float32)
+    lib().orc_autoscale_cast(_p(g), g.size, fmt, _p(m), _p(q), _p(cnt), _p(sc))
+    return q, int(cnt[0]), np.float32(sc[0]), np.float32(m[0])
+
+
+def min_scale(scales) -> np.float32:
+    s = _c(scales, np.float32)
+    return np.float32(lib().orc_min_scale(_p(s), s.size))
+
+
+def requantize_shared(q_in, fmt_in: int, s_in: float, s_g: float, fmt_out: int):
+    q = _c(q_in, np.uint8).reshape(-1)
+    out = np.empty(q.size, np.uint8)
+    lib().orc_requantize_shared(_p(q), q.size, fmt_in, C.c_float(s_in), C.c_float(s_g), fmt_out, _p(out))
+    return out
 
 
 def pertensor_quantize(x_bf16, fmt: int = E4M3, margin: float = 1.0, scale_in: float | None = None,

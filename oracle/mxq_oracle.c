@@ -342,6 +342,59 @@ void orc_swiglu_mx_quantize(const uint16_t* c, int64_t rows, int64_t F, int rule
 }
 
 /* ------------------------------------------------------------------------------------------------------
+ * FP8 gradient all-reduce, the parts one GPU runs ([FP8-LM] Section 3.4, automatic scaling (Eq. 3) and the shared
+ * scaling factor of Eq. 4-6).
+ * Auto-scaled cast: g' = mu * g (one fp32 rounding), q = FP8(g') with saturation; the tensor's scale is mu
+ * (g ~ val(q) / mu). The overflow ratio is the fraction of codes at the format's maximum magnitude; if it exceeds
+ * 0.001 % (ratio > 1e-5, evaluated in double) mu is halved for the next step, otherwise multiplied by 2^(1/1000)
+ * (that factor rounded once to fp32; the product rounded in fp32).
+ * Shared-scale requantize: s_g = the minimum of the gathered per-rank scales; each value is decoded, divided by its
+ * own scale s_i, multiplied by s_g (each an fp32 rounding) and re-encoded; the sum of N such tensors carries the
+ * scale N * s_g.
+ * ------------------------------------------------------------------------------------------------------ */
+void orc_autoscale_cast(const uint16_t* g, int64_t n, int fmt, float* mu, uint8_t* q, uint64_t* overflow,
+                        float* scale_out)
+{
+    tables();
+    const float m = *mu;
+    const uint8_t maxcode = (fmt == ORC_E4M3) ? 0x7E : 0x7B;
+    uint64_t count = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        float p = m * orc_bf16_to_f32(g[i]);
+        uint8_t c = orc_fp8_encode((double)p, fmt);
+        q[i] = c;
+        if ((c & 0x7F) == maxcode) ++count;
+    }
+    const float up = (float)exp2(1.0 / 1000.0);
+    double ratio = (n > 0) ? (double)count / (double)n : 0.0;
+    *overflow = count;
+    if (scale_out) *scale_out = m;
+    *mu = (ratio > 1e-5) ? m * 0.5f : m * up;
+}
+
+float orc_min_scale(const float* scales, int64_t N)
+{
+    float m = scales[0];
+    for (int64_t i = 1; i < N; ++i) {
+        if (isnan(scales[i]) || isnan(m)) m = NAN;
+        else if (scales[i] < m) m = scales[i];
+    }
+    return m;
+}
+
+void orc_requantize_shared(const uint8_t* q_in, int64_t n, int fmt_in, float s_in, float s_g, int fmt_out,
+                           uint8_t* q_out)
+{
+    tables();
+    for (int64_t i = 0; i < n; ++i) {
+        float v = (float)orc_fp8_value(q_in[i], fmt_in);        /* every FP8 value is exact in fp32 */
+        float t = v / s_in;
+        float u = s_g * t;
+        q_out[i] = orc_fp8_encode((double)u, fmt_out);
+    }
+}
+
+/* ------------------------------------------------------------------------------------------------------
  * Per-tensor current scaling ([FP8-LM] tensor scaling; [LLMSB] per-tensor scaling and Exercise 6).
  *   amax = max |x|;  s = (FMAX / max(amax, 1e-12)) * margin  (fp32);  q = FP8(fp32(x * s));  x ~ q / s.
  * With scale_in given (delayed scaling) s = *scale_in and amax is still reported.
