@@ -16,6 +16,9 @@ One step is one pass over every row of the hot path, on seeded synthetic inputs 
   moe_swiglu_mlp  the routed MLP of the grouped workload with SwiGLU: activation quantize, up/gate grouped GEMM
                 (2048 -> 2 x 1024), fused SwiGLU + MX quantize, down grouped GEMM (1024 -> 2048)
   swiglu_quant  the fused SwiGLU + MX quantize alone (132,160 x 2048 bf16 in, 132,160 x 1024 MXFP8 out)
+  grad_cast     the auto-scaled FP8 cast of the weight gradient dW (36864 x 12288 bf16 -> E4M3, overflow count, mu
+                update): the part of the FP8 all-reduce that runs before the scales are gathered
+  grad_requant  the re-quantize of those codes to the shared scale (the min over 8 gathered scales)
 The headline value is the MXFP8 linear layer's GEMM FLOPs (11.13 TFLOP) divided by the device time of its quantize
 and GEMM launches ("MXFP8 GEMM TFLOP/s incl. quantize"). Device times come from events on the stream the kernels
 run on; the JSON line also carries every part's rate, the MX GEMM's roofline and the CPU oracle baseline.
@@ -138,12 +141,18 @@ def main():
     wb_w = torch.empty(nw, dtype=torch.bfloat16, device=dev)
     cache_w = mxq.MXTensor(u8(N, K), u8(N, K // 32), u8(K, N), u8(K, N // 32))
     ws_w = torch.empty(mxq.workspace_bytes("adam", nw), dtype=torch.uint8, device=dev)
+    # FP8 all-reduce pieces on dW: mu, the codes, and 8 gathered scales (this rank's and 7 seeded others)
+    mu_g = torch.ones(1, dtype=torch.float32, device=dev)
+    ws_g = torch.empty(mxq.workspace_bytes("autoscale", nw), dtype=torch.uint8, device=dev)
+    others = 2.0 ** torch.arange(-3, 4, dtype=torch.float32, device=dev)
+    gathered = torch.empty(8, dtype=torch.float32, device=dev)
+    q_req = torch.empty(nw, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     parts = ["mx_quant_XWdY", "mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "pt_quant", "pt_gemms", "mx_quant_act",
              "grouped", "adam", "small", "pt_quant_delayed", "adam_delayed", "wcache_fused", "wcache_unfused",
-             "moe_swiglu_mlp", "swiglu_quant"]
+             "moe_swiglu_mlp", "swiglu_quant", "grad_cast", "grad_requant"]
     NEV = len(parts) + 1
 
     def step(ev):
@@ -201,6 +210,12 @@ def main():
         ev[15].record(stream)
         mxq.swiglu_mx_quantize(C_gu, out=mx_h)
         ev[16].record(stream)
+        gc = mxq.fp8_autoscale_cast(dW, mu_g, mxq.E4M3, workspace=ws_g)
+        ev[17].record(stream)
+        gathered[:1] = gc.scale
+        gathered[1:] = others
+        mxq.fp8_requantize_shared(gc.q, mxq.E4M3, gc.scale, gathered, mxq.E4M3, out=q_req)
+        ev[18].record(stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -254,6 +269,8 @@ def main():
         "moe_swiglu_mlp_tflops_incl_quant": 2.0 * rows_valid * (2 * d_ff * d_model + d_ff * d_model)
                                             / (ms["moe_swiglu_mlp"] * 1e-3) / 1e12,
         "swiglu_quant_gbs": rows4 * (4 * d_ff + d_ff + d_ff // 32) / (ms["swiglu_quant"] * 1e-3) / 1e9,
+        "grad_cast_gbs": 3 * nw / (ms["grad_cast"] * 1e-3) / 1e9,
+        "grad_requant_gbs": 2 * nw / (ms["grad_requant"] * 1e-3) / 1e9,
     }
     for k, v in rate.items():
         rate[k] = round(v, 3)

@@ -120,6 +120,31 @@ mxq_status fp8_quantize_pertensor_delayed(const uint16_t* x_bf16, int64_t rows, 
                                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Auto-scaled FP8 gradient cast, the per-GPU half of the FP8 all-reduce ([FP8-LM] Section 3.4, automatic scaling
+ * factor mu, Eq. 3):
+ *   q[i] = FP8(fp32(mu * g[i])) with saturation; the scale of q is mu (g ~ val(q) / mu), reported in scale_out[0]
+ *   (may be NULL); overflow_count[0] (device uint64) = the number of codes at the format's maximum magnitude;
+ *   then mu[0] (device, in/out) <- mu / 2 if overflow_count / n > 1e-5 (0.001 %), else mu * 2^(1/1000) (the factor
+ *   rounded to fp32; each product one fp32 rounding), for the next step.
+ * workspace: mxq_workspace_bytes("autoscale", n) bytes, clobbered.
+ */
+mxq_status fp8_autoscale_cast(const uint16_t* g_bf16, int64_t n, mxq_fp8 fmt, float* mu, uint8_t* q,
+                              float* scale_out, uint64_t* overflow_count, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
+ * Re-quantize to the shared scaling factor before an FP8 all-reduce ([FP8-LM] Section 3.4, Eq. 4-6):
+ *   shared_scale_out[0] = s_g = min(gathered_scales[0 .. nranks)) (the scales every rank reported for this tensor;
+ *   a NaN entry gives NaN), sum_scale_out[0] = nranks * s_g (the scale of the sum of the ranks' tensors; may be NULL);
+ *   q_out[i] = FP8_out(s_g * (val_in(q_in[i]) / scale_in[0])), each operation one fp32 rounding, saturating; a NaN
+ *   gives the NaN code (E4M3 S.1111.111, E5M2 S.11111.10).
+ * All scalars are device pointers. 1 <= nranks <= 2^24.
+ */
+mxq_status fp8_requantize_shared(const uint8_t* q_in, int64_t n, mxq_fp8 fmt_in, const float* scale_in,
+                                 const float* gathered_scales, int64_t nranks, mxq_fp8 fmt_out, uint8_t* q_out,
+                                 float* shared_scale_out, float* sum_scale_out, hipStream_t stream);
+
+/*
  * Scaled FP8 GEMM with fp32 accumulation and a bf16 epilogue ([OLMO11] Figure 47 and Section 11.2.3:
  * block scales applied inside the matrix operation, BF16 output; [LLMSB] Exercise 6: de-scale by 1/(s_a s_b)):
  *   C[M][N] (row-major, leading dimension ldc >= N, in elements) = bf16_rne( A[M][K] * B[N][K]^T ).
@@ -206,8 +231,8 @@ mxq_status fp8_adam_step_delayed(float* master, const uint16_t* grad_bf16, uint8
                                  float* m_history, int32_t* hist_pos, int64_t history_len, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes needed by op ("pertensor", "adam", "pertensor_delayed" or "adam_delayed") for n elements; 0 for an
- * unknown op. op is a host string. */
+/* Workspace bytes needed by op ("pertensor", "adam", "pertensor_delayed", "adam_delayed" or "autoscale") for n
+ * elements; 0 for an unknown op. op is a host string. */
 size_t mxq_workspace_bytes(const char* op, int64_t n);
 
 #ifdef __cplusplus

@@ -213,3 +213,47 @@ def fp8_adam_step_mx_cache(master: torch.Tensor, grad: torch.Tensor, m_q: torch.
                                             _stream(dev))
     _lib.check("fp8_adam_step_mx_cache", st)
     return out
+
+
+class AutoScaled(NamedTuple):
+    q: torch.Tensor                 # uint8 codes
+    scale: torch.Tensor             # float32[1]: the mu these codes carry
+    overflow: torch.Tensor          # int64[1]: codes at the maximum magnitude
+
+
+def fp8_autoscale_cast(g: torch.Tensor, mu: torch.Tensor, fmt: int = E4M3,
+                       workspace: Optional[torch.Tensor] = None) -> AutoScaled:
+    """q = FP8(mu * g); mu (float32[1], device) is updated in place for the next step."""
+    _dev(g, torch.bfloat16, "g"); _dev(mu, torch.float32, "mu")
+    dev = g.device
+    n = g.numel()
+    q = torch.empty(g.shape, dtype=torch.uint8, device=dev)
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    overflow = torch.empty(1, dtype=torch.int64, device=dev)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes("autoscale", n), dtype=torch.uint8, device=dev)
+    st = _lib.load().fp8_autoscale_cast(_ptr(g), n, fmt, _ptr(mu), _ptr(q), _ptr(scale), _ptr(overflow),
+                                        _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check("fp8_autoscale_cast", st)
+    return AutoScaled(q, scale, overflow)
+
+
+def fp8_requantize_shared(q: torch.Tensor, fmt_in: int, scale_in: torch.Tensor, gathered_scales: torch.Tensor,
+                          fmt_out: int = E4M3, out: Optional[torch.Tensor] = None):
+    """Returns (q_out, shared scale s_g, sum scale N * s_g), all on the device."""
+    _dev(q, torch.uint8, "q"); _dev(scale_in, torch.float32, "scale_in")
+    _dev(gathered_scales, torch.float32, "gathered_scales")
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, torch.uint8, "out")
+        if out.numel() != q.numel():
+            raise ValueError("out must hold as many codes as q")
+    sg = torch.empty(1, dtype=torch.float32, device=dev)
+    ssum = torch.empty(1, dtype=torch.float32, device=dev)
+    st = _lib.load().fp8_requantize_shared(_ptr(q), q.numel(), fmt_in, _ptr(scale_in), _ptr(gathered_scales),
+                                           gathered_scales.numel(), fmt_out, _ptr(out), _ptr(sg), _ptr(ssum),
+                                           _stream(dev))
+    _lib.check("fp8_requantize_shared", st)
+    return out, sg, ssum

@@ -65,7 +65,8 @@ size_t mxq_workspace_bytes(const char* op, int64_t n) {
     if (!op || n < 0) return 0;
     if (strcmp(op, "pertensor") == 0) return pertensor_ws(n);
     if (strcmp(op, "adam") == 0) return adam_ws(n);
-    if (strcmp(op, "pertensor_delayed") == 0 || strcmp(op, "adam_delayed") == 0) return kDelayedWs;
+    if (strcmp(op, "pertensor_delayed") == 0 || strcmp(op, "adam_delayed") == 0 || strcmp(op, "autoscale") == 0)
+        return kDelayedWs;
     return 0;
 }
 
@@ -130,6 +131,38 @@ mxq_status fp8_quantize_pertensor_delayed(const uint16_t* x_bf16, int64_t rows, 
     return hip_status(mxq::launch_pertensor_quantize_delayed(x_bf16, rows, cols, (int)fmt, margin, amax_history,
                                                              hist_pos, (int)history_len, amax_out, scale_out, q, q_t,
                                                              static_cast<uint32_t*>(workspace), stream));
+}
+
+mxq_status fp8_autoscale_cast(const uint16_t* g_bf16, int64_t n, mxq_fp8 fmt, float* mu, uint8_t* q,
+                              float* scale_out, uint64_t* overflow_count, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    if (!mu || !overflow_count) return MXQ_ERR_NULL;
+    if (fmt != MXQ_E4M3 && fmt != MXQ_E5M2) return MXQ_ERR_UNSUPPORTED;
+    if (n < 0) return MXQ_ERR_SHAPE;
+    if (n > 0 && (!g_bf16 || !q)) return MXQ_ERR_NULL;
+    if (!al16(g_bf16) || !al16(q) || !al4(mu) || (scale_out && !al4(scale_out)) ||
+        (reinterpret_cast<uintptr_t>(overflow_count) & 7u))
+        return MXQ_ERR_ALIGN;
+    if (!workspace || workspace_bytes < kDelayedWs) return MXQ_ERR_WORKSPACE;
+    if (!al16(workspace)) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_autoscale_cast(g_bf16, n, (int)fmt, mu, q, scale_out,
+                                                 reinterpret_cast<unsigned long long*>(overflow_count),
+                                                 static_cast<unsigned long long*>(workspace), stream));
+}
+
+mxq_status fp8_requantize_shared(const uint8_t* q_in, int64_t n, mxq_fp8 fmt_in, const float* scale_in,
+                                 const float* gathered_scales, int64_t nranks, mxq_fp8 fmt_out, uint8_t* q_out,
+                                 float* shared_scale_out, float* sum_scale_out, hipStream_t stream) {
+    if ((fmt_in != MXQ_E4M3 && fmt_in != MXQ_E5M2) || (fmt_out != MXQ_E4M3 && fmt_out != MXQ_E5M2))
+        return MXQ_ERR_UNSUPPORTED;
+    if (n < 0 || nranks < 1 || nranks > (int64_t(1) << 24)) return MXQ_ERR_SHAPE;
+    if (!scale_in || !gathered_scales || !shared_scale_out) return MXQ_ERR_NULL;
+    if (n > 0 && (!q_in || !q_out)) return MXQ_ERR_NULL;
+    if (!al16(q_in) || !al16(q_out) || !al4(scale_in) || !al4(gathered_scales) || !al4(shared_scale_out) ||
+        (sum_scale_out && !al4(sum_scale_out)))
+        return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_requantize_shared(q_in, n, (int)fmt_in, scale_in, gathered_scales, (int)nranks,
+                                                    (int)fmt_out, q_out, shared_scale_out, sum_scale_out, stream));
 }
 
 mxq_status scaled_gemm(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fmt, const uint8_t* b_q,

@@ -33,6 +33,12 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int
                                int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s, int64_t N, int64_t K,
                                uint16_t* c, hipStream_t stream);
 
+hipError_t launch_autoscale_cast(const uint16_t* g, int64_t n, int fmt, float* mu, uint8_t* q, float* scale_out,
+                                 unsigned long long* overflow, unsigned long long* count, hipStream_t stream);
+hipError_t launch_requantize_shared(const uint8_t* q_in, int64_t n, int fmt_in, const float* scale_in,
+                                    const float* scales, int nranks, int fmt_out, uint8_t* q_out, float* shared_out,
+                                    float* sum_out, hipStream_t stream);
+
 int adam_parts(int64_t n);
 hipError_t launch_adam(float* master, const uint16_t* grad, uint8_t* m_q, float* m_scale, uint16_t* v16, uint16_t* w,
                        int64_t n, const AdamConsts& k, uint32_t* partial, float* consts, hipStream_t stream);

@@ -16,6 +16,9 @@ Workloads (sizes are those of the five configurations; the tests also use smalle
      rank^-1.1 (Gumbel top-k), each group padded to a multiple of 32 rows (zero rows at the group's end);
      A_up [rows][2048], A_down [rows][1024], W_up [64][1024][2048], W_down [64][2048][1024], all N(0,1).
   5  Adam step over n parameters: theta fp32 N(0,0.02), gradient bf16 N(0,1e-3) for step t drawn with index t.
+  6  FP8 gradient all-reduce pieces: per rank r of 8, the weight gradient of workload 2's W (36864 x 12288 values),
+     N(0, 1e-3 * 2^(r/4)) with round(2e-5 n) positions multiplied by 1000 before the bf16 cast (step t: index
+     16 t + 2 r, positions 16 t + 2 r + 1).
 """
 from __future__ import annotations
 
@@ -126,3 +129,8 @@ def workload5_params(n: int, device="cpu") -> torch.Tensor:
 
 def workload5_grad(n: int, t: int, device="cpu") -> torch.Tensor:
     return normal_bf16((n,), 1e-3, 5, t, device)
+
+
+def workload6_grad(n: int, rank: int, t: int = 0, device="cpu") -> torch.Tensor:
+    k = 16 * int(t) + 2 * int(rank)
+    return normal_bf16_with_outliers((n,), 1e-3 * 2.0 ** (rank / 4), 2e-5, 1000.0, 6, k, k + 1, device)

@@ -143,3 +143,22 @@ def test_swiglu_validation():
     assert f(None, 64, 64, P, P, 0, None) == 1
     assert f(MIS, 64, 64, P, P, 0, None) == 3
     assert f(None, 0, 64, None, None, 0, None) == 0   # empty
+
+
+def test_gradcomm_validation():
+    lib = _lib.load()
+    f = lib.fp8_autoscale_cast
+    assert f(P, 64, 2, P, P, P, P, P, 256, None) == 4           # unsupported format
+    assert f(P, -1, 0, P, P, P, P, P, 256, None) == 2
+    assert f(P, 64, 0, None, P, P, P, P, 256, None) == 1        # mu
+    assert f(None, 64, 0, P, P, P, P, P, 256, None) == 1
+    assert f(P, 64, 0, P, P, P, P, P, 8, None) == 5             # workspace too small
+    assert f(P, 64, 0, P, P, P, P + 4, P, 256, None) == 3       # overflow counter not 8-byte aligned
+    assert f(MIS, 64, 0, P, P, P, P, P, 256, None) == 3
+    assert lib.mxq_workspace_bytes(b"autoscale", 1 << 20) >= 8
+    r = lib.fp8_requantize_shared
+    assert r(P, 64, 0, P, P, 0, 0, P, P, P, None) == 2          # no ranks
+    assert r(P, 64, 0, P, P, 8, 5, P, P, P, None) == 4
+    assert r(P, 64, 0, None, P, 8, 0, P, P, P, None) == 1
+    assert r(None, 64, 0, P, P, 8, 0, P, P, P, None) == 1
+    assert r(P, 64, 0, P, P, 8, 0, MIS, P, P, None) == 3
