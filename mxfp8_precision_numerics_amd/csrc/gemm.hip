@@ -336,9 +336,11 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------------------------------------------
 // Large-tile kernel: a 256 x 256 output tile per workgroup, one workgroup per CU (4 waves, 2 x 2, each 128 x 128 as
 // 4 x 4 tiles of 32 x 32 matrix instructions). K advances 64 bytes per stage. A ring of NST = 4 LDS stage buffers
-// (16 KiB per operand each) is filled straight from global memory by buffer_load_dwordx4 ... lds, three stages ahead
-// of the stage being multiplied, and the next stage's fragments are read into registers while the current stage's
-// matrix instructions run, so neither the copy latency nor the LDS latency sits between two stages.
+// (16 KiB per operand each) is filled straight from global memory by buffer_load_dwordx4 ... lds, four stages ahead
+// of the stage being multiplied (whose fragments already sit in registers, so its buffer is free), and the next
+// stage's fragments are read into registers while the current stage's matrix instructions run, so neither the copy
+// latency nor the LDS latency sits between two stages. The copy stream is bound by bytes in flight over memory
+// latency, so the ring keeps three stages in flight.
 // One copy instruction of one wave fills a 16-row slab (1 KiB): lane l writes 16-byte slot l (row l / 4, position
 // l % 4) and fetches global chunk (l % 4) ^ swz4(row), so position p of a row holds chunk p ^ swz4(row); the fragment
 // reads of 16 consecutive rows (one chunk each) then land on distinct banks. Rows past the end of an operand are
@@ -377,11 +379,11 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 template <int BYTES>
 __device__ __forceinline__ void dma_to_lds(v4i rsrc, uint32_t lds, int voff, int soff) {
     if constexpr (BYTES == 16)
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                     :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+        asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+                     :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds) : "memory");
     else
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                     :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+        asm volatile("buffer_load_dword %0, %1, %2 offen lds"
+                     :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds) : "memory");
 }
 
 // Wait until at most N of this wave's copies are still outstanding (vector-memory counter, which retires in issue
@@ -594,53 +596,109 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     };
 
     const int nk = (int)(K / KS);
-    const int pre = nk < 3 ? nk : 3;
+    const int pre = nk < NST ? nk : NST;
     for (int st = 0; st < pre; ++st) load_stage(st);
-    if (nk > 2) wait_copies_barrier<8>();                       // stages 0 and 1 have landed
+    if (nk > 3) wait_copies_barrier<16>();                      // stages 0 and 1 have landed
+    else if (nk > 2) wait_copies_barrier<8>();
     else wait_copies_barrier<0>();
     v8i fa[4], fb[4];
     uint32_t sa[4], sb[4];
     read_stage(std::integral_constant<int, 0>{}, 0, fa, fb, sa, sb);
+    // Stage 0's buffer is refilled (stage 4) by the first trip: every wave's reads of it must have returned.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // The asm waits are invisible to the compiler; this visible lgkmcnt(0) (vmcnt 63 and expcnt 7: no wait) tells it
     // that the fragment reads so far have returned, so it does not hold matrix instructions for them later.
     __builtin_amdgcn_s_waitcnt(0xC07F);
 
-    // Steady state: copy stage kt + 3 into the buffer stage kt - 1 used, read stage kt + 1's fragments (landed at the
-    // end of kt - 1), multiply stage kt, then wait until stage kt + 2 has landed (only kt + 3's 8 slabs may remain).
-    // Two stages per trip, ping-ponging between two fragment register sets (no copies between iterations).
+    // Steady state, trip kt: stage kt's fragments are in registers (read during trip kt - 1), so its LDS buffer is
+    // free and receives the copy of stage kt + 4; stage kt + 1's fragments are read (landed by the end of trip
+    // kt - 1) while stage kt is multiplied; then wait until stage kt + 2 has landed, leaving the copies of stages
+    // kt + 3 and kt + 4 (16 per wave) in flight. Three stages are always in flight. Two fragment register sets
+    // ping-pong between trips (no copies between iterations).
     v8i fa2[4], fb2[4];
     uint32_t sa2[4], sb2[4];
     // PH_C: kt % 4 as a std::integral_constant when known, else -1.
     auto steady = [&](auto ph_c, int kt, v8i* ca, v8i* cb, uint32_t* csa, uint32_t* csb, v8i* na, v8i* nb,
                       uint32_t* nsa, uint32_t* nsb) {
         constexpr int PH = decltype(ph_c)::value;
-        load_stage(kt + 3);
-        read_stage(std::integral_constant<int, PH < 0 ? -1 : (PH + 1) % NST>{}, kt + 1, na, nb, nsa, nsb);
-        mma_stage(std::integral_constant<int, PH < 0 ? -1 : PH % 2>{}, kt, ca, cb, csa, csb);
-        interleave_reads();
+        if constexpr (MF == 1) {
+            // FP8 path: 16 issue slots, each one matrix instruction and one 16-byte fragment read of stage kt + 1
+            // (MX: plus one scale read in the first 8), and every second slot one copy instruction of stage kt + 4.
+            // Spreading the copies keeps a wave that finds the memory queue full from stalling its matrix
+            // instructions behind a burst of copy issues. The scheduling barriers keep the slots in this order.
+            constexpr int RB = PH < 0 ? -1 : (PH + 1) % NST;
+            const int rb = RB < 0 ? (kt + 1) % NST : RB;
+            const int odd = PH < 0 ? (kt & 1) : (PH & 1);
+            const int sh = 8 * (2 * odd + fg);
+            const int ls = kt + 4, k0 = ls * KS;
+            const uint32_t la = lds_offset(&sA[ls % NST][1024 * wave]);
+            const uint32_t lb = lds_offset(&sB[ls % NST][1024 * wave]);
+            const uint32_t* cSA = sSA[((kt + 1) / SG) & 1];
+            const uint32_t* cSB = sSB[((kt + 1) / SG) & 1];
+            const int sw = ((kt + 1) % SG) >> 1;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int i = q >> 2, j = q & 3;
+                acc16[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    cb[i], ca[j], acc16[i][j], FB, FA, 0, (int)(csb[i] >> sh), 0, (int)(csa[j] >> sh));
+                {
+                    const int f = q >> 1, h = q & 1;
+                    const uint8_t* base = f < 4 ? sA[rb] : sB[rb];
+                    const int row = (f < 4 ? wm : wn) * 128 + 32 * (f & 3) + fr;
+                    const uint4 x = *reinterpret_cast<const uint4*>(base + row * KS + 16 * ((2 * h + fg) ^ fsw));
+                    v8i& d = f < 4 ? na[f & 3] : nb[f & 3];
+                    d[4 * h] = (int)x.x; d[4 * h + 1] = (int)x.y; d[4 * h + 2] = (int)x.z; d[4 * h + 3] = (int)x.w;
+                }
+                if constexpr (MX) {
+                    if (q < 4) nsa[q] = cSA[(wm * 128 + 32 * q + fr) * 4 + sw];
+                    else if (q < 8) nsb[q - 4] = cSB[(wn * 128 + 32 * (q - 4) + fr) * 4 + sw];
+                } else if (q == 0) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { nsa[e] = 0x7F7F7F7Fu; nsb[e] = 0x7F7F7F7Fu; }
+                }
+                if (q & 1) {
+                    const int c = q >> 1;
+                    if constexpr (MX) {
+                        if (c == 0 && ls % SG == 0) {       // a scale group's copies go first (see load_stage)
+                            const int gb = (ls / SG) & 1;
+                            dma_to_lds<16>(rSA, lds_offset(&sSA[gb][256 * wave]), sa_off, k0 / 32);
+                            dma_to_lds<16>(rSB, lds_offset(&sSB[gb][256 * wave]), sb_off, k0 / 32);
+                        }
+                    }
+                    if (c < 4) dma_to_lds<16>(rA, la + 4096 * c, a_off[c], k0);
+                    else dma_to_lds<16>(rB, lb + 4096 * (c - 4), b_off[c - 4], k0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            load_stage(kt + 4);
+            read_stage(std::integral_constant<int, PH < 0 ? -1 : (PH + 1) % NST>{}, kt + 1, na, nb, nsa, nsb);
+            mma_stage(std::integral_constant<int, PH < 0 ? -1 : PH % 2>{}, kt, ca, cb, csa, csb);
+            interleave_reads();
+        }
         pin_accumulators();
-        wait_copies_barrier<8>();
+        wait_copies_barrier<16>();
         __builtin_amdgcn_s_waitcnt(0xC07F);
     };
     using dyn = std::integral_constant<int, -1>;
     int kt = 0;
-    for (; kt + 6 < nk; kt += 4) {                               // kt % 4 == 0 on entry
+    for (; kt + 7 < nk; kt += 4) {                               // kt % 4 == 0 on entry
         steady(std::integral_constant<int, 0>{}, kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
         steady(std::integral_constant<int, 1>{}, kt + 1, fa2, fb2, sa2, sb2, fa, fb, sa, sb);
         steady(std::integral_constant<int, 2>{}, kt + 2, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
         steady(std::integral_constant<int, 3>{}, kt + 3, fa2, fb2, sa2, sb2, fa, fb, sa, sb);
     }
-    for (; kt + 4 < nk; kt += 2) {
+    for (; kt + 5 < nk; kt += 2) {
         steady(dyn{}, kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
         steady(dyn{}, kt + 1, fa2, fb2, sa2, sb2, fa, fb, sa, sb);
     }
-    if (kt + 3 < nk) {
+    if (kt + 4 < nk) {
         steady(dyn{}, kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
         ++kt;
 #pragma unroll
         for (int j = 0; j < 4; ++j) { fa[j] = fa2[j]; fb[j] = fb2[j]; sa[j] = sa2[j]; sb[j] = sb2[j]; }
     }
-    // Last (at most three) stages: everything has been issued; wait for all of it.
+    // Last (at most four) stages: everything has been issued; wait for all of it.
     for (; kt < nk; ++kt) {
         v8i na[4], nb[4];
         uint32_t nsa[4], nsb[4];
