@@ -335,26 +335,31 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
 
 // ---------------------------------------------------------------------------------------------------------------
 // Large-tile kernel: a 256 x 256 output tile per workgroup, one workgroup per CU (4 waves, 2 x 2, each 128 x 128 as
-// 4 x 4 tiles of 32 x 32 matrix instructions). K advances 64 bytes per stage. A ring of NST = 4 LDS stage buffers
-// (16 KiB per operand each) is filled straight from global memory by buffer_load_dwordx4 ... lds, four stages ahead
-// of the stage being multiplied (whose fragments already sit in registers, so its buffer is free), and the next
-// stage's fragments are read into registers while the current stage's matrix instructions run, so neither the copy
-// latency nor the LDS latency sits between two stages. The copy stream is bound by bytes in flight over memory
-// latency, so the ring keeps three stages in flight.
-// One copy instruction of one wave fills a 16-row slab (1 KiB): lane l writes 16-byte slot l (row l / 4, position
-// l % 4) and fetches global chunk (l % 4) ^ swz4(row), so position p of a row holds chunk p ^ swz4(row); the fragment
-// reads of 16 consecutive rows (one chunk each) then land on distinct banks. Rows past the end of an operand are
-// clamped to its last row (their outputs are never stored), so every access stays inside the caller's buffers.
-// MX scales: one 16-byte lane per row covers SG = 8 stages (16 blocks); the groups are double-buffered.
+// 4 x 4 tiles of 32 x 32 matrix instructions). K advances 64 bytes per stage; trip t multiplies stage t from
+// fragments read into registers during trip t - 1, while reading stage t + 1's fragments.
+// LDS: per operand two 32 KiB regions of two stages each, as 32 blocks of 1 KiB: block b holds rows 8b .. 8b+7 of the
+// region's first stage in its first 512 bytes and of its second stage in the last 512 (64 bytes per row).
+// Copies go straight from global memory to LDS (buffer_load_dwordx4 ... lds) and every copy instruction fetches whole
+// 128-byte lines: 8 rows x 128 bytes of K, the same rows of two consecutive stages (lanes 0-31 the first stage,
+// lanes 32-63 the second), half the cache-line requests of 64-byte rows. A's stage pairs are (2q, 2q+1) and B's
+// (2q+1, 2q+2); trip t copies one pair, A's (t+3, t+4) on odd t and B's on even t, into the region whose two stages
+// were read by the end of trip t - 1. Stage t + 2 must have landed at the end of trip t, so only the current trip's
+// copies stay in flight across that wait, and every stage has one to two trips to land.
+// Within a block, position p of a row holds chunk p ^ swz8(row), so the 16-byte fragment reads of 16 consecutive
+// rows hit distinct banks. Rows past the end of an operand are clamped to its last row (their outputs are never
+// stored), so every access stays inside the caller's buffers.
+// MX scales: one 16-byte lane per row covers SG = 8 stages (16 blocks); the groups are double-buffered and a group's
+// copies are issued four trips before its first stage is read.
 // Tile order: each XCD (which receives every eighth workgroup) walks a contiguous run of a grouped-M order, so its
 // resident workgroups share A and B tiles in its L2.
 constexpr int TB = 256;
 constexpr int KS = 64;
-constexpr int NST = 4;
 constexpr int SG = 8;
 constexpr int GROUP_M2 = 4;
+// Issue slot (of the 16 matrix instructions of a stage) after which each of a trip's 8 copy instructions goes.
+constexpr int kCopySlot[8] = {1, 3, 5, 7, 9, 11, 13, 15};
 
-__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int swz8(int row) { return (row >> 2) & 3; }
 
 // Raw buffer resource (base, stride 0, 2^31 - 1 bytes, raw untyped access) for a workgroup-uniform address. The
 // address is moved to scalar registers explicitly: values derived from the tile index are computed with vector
@@ -396,8 +401,8 @@ __device__ __forceinline__ void wait_copies_barrier() {
 
 template <bool MX, int FA, int FB, bool GROUPED, int MF>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint8_t sA[NST][TB * KS];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[NST][TB * KS];
+    __shared__ __attribute__((aligned(16))) uint8_t sA[2][2 * TB * KS];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][2 * TB * KS];
     // MX scales: [row][4 words] = 16 blocks = SG stages per row, double-buffered by group.
     __shared__ __attribute__((aligned(16))) uint32_t sSA[2][MX ? TB * 4 : 1];
     __shared__ __attribute__((aligned(16))) uint32_t sSB[2][MX ? TB * 4 : 1];
@@ -448,22 +453,23 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     const int64_t n_end = (n0 + TB < g.N) ? n0 + TB : g.N;
 
     // ------------------------------------------------------------------ copies global -> LDS
-    // One resource per operand based at the tile's first row; 32-bit per-lane row offsets (row * K + chunk, below
-    // 2^31 because the host requires 256 K < 2^31); the stage's k offset goes in the scalar offset.
-    const int lq = lane >> 2;                  // row within the wave's 16-row slab
-    // Global chunk this lane fetches. swz4 reads row bits 1..4; the slabs of a wave are 16 * (4 i + wave), so bit 4
-    // of the row is wave & 1 for every slab of the wave.
-    const int lc = (lane & 3) ^ swz4(16 * wave + lq);
+    // One resource per operand based at the tile's first row; 32-bit per-lane offsets (row * K + byte, below 2^31
+    // because the host requires 256 K < 2^31); a pair's k offset goes in the scalar offset. Copy instruction c of a
+    // wave fills block 4c + wave of a region.
+    const int half_lane = lane >> 5;                       // which stage of a pair this lane carries
+    const int brow = (lane & 31) >> 2;                     // row within the 8-row block
+    // chunk this lane fetches: its position ^ swz8(row); rows 8 (4c + wave) + brow have swz8 = (2 wave + brow / 4) & 3
+    const int bchunk = (lane & 3) ^ ((2 * wave + (brow >> 2)) & 3);
     const v4i rA = buffer_rsrc(g.a + m0 * K);
     const v4i rB = buffer_rsrc(Bq + n0 * K);
-    int a_off[4], b_off[4];
+    int a_off[8], b_off[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 16 * (4 * i + wave) + lq;
+    for (int c = 0; c < 8; ++c) {
+        const int row = 8 * (4 * c + wave) + brow;
         const int ar = (m0 + row < m_end) ? row : (int)(m_end - 1 - m0);
         const int br = (n0 + row < n_end) ? row : (int)(n_end - 1 - n0);
-        a_off[i] = ar * (int)K + 16 * lc;
-        b_off[i] = br * (int)K + 16 * lc;
+        a_off[c] = ar * (int)K + KS * half_lane + 16 * bchunk;
+        b_off[c] = br * (int)K + KS * half_lane + 16 * bchunk;
     }
     v4i rSA = rA, rSB = rB;
     int sa_off = 0, sb_off = 0;
@@ -476,25 +482,50 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         sa_off = ar * (int)kblocks;
         sb_off = br * (int)kblocks;
     }
-    // Copies of one stage: on the first stage of a scale group (MX) the group's scales (64 rows per wave of 16
-    // bytes), then 4 slabs per operand per wave. The scales are issued first so that, copies retiring in issue order,
-    // "at most 8 copies outstanding" always means: everything but the newest stage's slabs has landed.
-    auto load_stage = [&](int st) {
-        const int k0 = st * KS;
+    const int nk = (int)(K / KS);
+    // Region of stage s: A (s / 2) % 2, B ((s + 1) / 2) % 2; its half: A s % 2, B (s + 1) % 2.
+    // Copy instruction c of the pair of operand A (IS_A) or B whose first stage is s0, into region `region`. When the
+    // pair's second stage lies past K only the first-stage lanes copy.
+    // WHOLE: the pair is known at compile time to lie inside K.
+    auto copy_pair = [&](auto is_a, auto whole_c, int region, int s0, int c) {
+        constexpr bool IS_A = decltype(is_a)::value;
+        const uint32_t lds = lds_offset(IS_A ? &sA[region][1024 * wave] : &sB[region][1024 * wave]) + 4096 * c;
+        if (decltype(whole_c)::value || s0 + 1 < nk)
+            dma_to_lds<16>(IS_A ? rA : rB, lds, IS_A ? a_off[c] : b_off[c], s0 * KS);
+        else if (half_lane == 0)
+            dma_to_lds<16>(IS_A ? rA : rB, lds, IS_A ? a_off[c] : b_off[c], s0 * KS);
+    };
+    auto copy_scales = [&](int s) {                       // the scale group whose first stage is s
+        const int gb = (s / SG) & 1;
+        dma_to_lds<16>(rSA, lds_offset(&sSA[gb][256 * wave]), sa_off, s * KS / 32);
+        dma_to_lds<16>(rSB, lds_offset(&sSB[gb][256 * wave]), sb_off, s * KS / 32);
+    };
+    // Copy instruction c of trip t: the pair starting at stage t + 3 (A on odd t, B on even t), if any. PH = t % 4 when
+    // known at compile time (then the pair exists in full), else -1.
+    auto trip_copy = [&](auto ph_c, int t, int c) {
+        constexpr int PH = decltype(ph_c)::value;
+        const int s0 = t + 3;
+        if constexpr (PH >= 0) {
+            if constexpr (PH & 1) copy_pair(std::true_type{}, std::true_type{}, ((PH + 3) >> 1) & 1, s0, c);
+            else copy_pair(std::false_type{}, std::true_type{}, ((PH + 4) >> 1) & 1, s0, c);
+        } else if (s0 < nk) {
+            if (t & 1) copy_pair(std::true_type{}, std::false_type{}, (s0 >> 1) & 1, s0, c);
+            else copy_pair(std::false_type{}, std::false_type{}, ((s0 + 1) >> 1) & 1, s0, c);
+        }
+    };
+    // Scale copies of trip t (issued after its pair): the group starting at stage t + 4. Returns whether issued.
+    auto trip_scales = [&](int t) -> bool {
         if constexpr (MX) {
-            if (st % SG == 0) {
-                const int gb = (st / SG) & 1;
-                dma_to_lds<16>(rSA, lds_offset(&sSA[gb][256 * wave]), sa_off, k0 / 32);
-                dma_to_lds<16>(rSB, lds_offset(&sSB[gb][256 * wave]), sb_off, k0 / 32);
-            }
+            const int s = t + 4;
+            if (s % SG == 0 && s < nk) { copy_scales(s); return true; }
         }
-        const uint32_t la = lds_offset(&sA[st % NST][1024 * wave]);
-        const uint32_t lb = lds_offset(&sB[st % NST][1024 * wave]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            dma_to_lds<16>(rA, la + 4096 * i, a_off[i], k0);
-            dma_to_lds<16>(rB, lb + 4096 * i, b_off[i], k0);
-        }
+        return false;
+    };
+    // Wait at the end of trip t: only the copies issued in trip t may remain in flight.
+    auto trip_wait = [&](int t, bool scales) {
+        if (t + 3 >= nk) wait_copies_barrier<0>();
+        else if (scales) wait_copies_barrier<10>();
+        else wait_copies_barrier<8>();
     };
 
     // ------------------------------------------------------------------ fragments
@@ -502,22 +533,27 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     // i.e. k = 16g .. 16g+15 and 32+16g .. 32+16g+15. Its scale operand is the scale of (row, block g), stage word
     // (st % SG) / 2, byte 2 (st % 2) + g.
     const int fr = lane & 31, fg = lane >> 5;
-    const int fsw = swz4(fr);                  // rows wm*128 + 32j + fr share bits 1..3 with fr
-    auto frag = [&](const uint8_t* base, int row) {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(base + row * KS + 16 * (fg ^ fsw));
-        const uint4 x1 = *reinterpret_cast<const uint4*>(base + row * KS + 16 * ((2 + fg) ^ fsw));
+    const int fsw = swz8(fr);                  // rows wm*128 + 32j + fr share bits 2..3 with fr
+    const int frow = (fr >> 3) * 1024 + (fr & 7) * KS;   // lane's row within its 32-row group (block, row in block)
+    const int fch0 = 16 * (fg ^ fsw), fch1 = 16 * ((2 + fg) ^ fsw);
+    // Byte offset, within an operand's LDS, of chunk half h (0: chunk g, 1: chunk 2 + g) of the lane's row in 32-row
+    // group `grp` (0..7) of stage s. SP = s % 4 when known at compile time, else -1.
+    auto frag_off = [&](auto is_a, auto sp_c, int s, int grp, int h) {
+        constexpr bool IS_A = decltype(is_a)::value;
+        constexpr int SP = decltype(sp_c)::value;
+        const int sp = SP < 0 ? (s & 3) : SP;
+        const int region = IS_A ? ((sp >> 1) & 1) : (((sp + 1) >> 1) & 1);
+        const int half = IS_A ? (sp & 1) : ((sp + 1) & 1);
+        return region * (2 * TB * KS) + grp * 4096 + half * 512 + frow + (h ? fch1 : fch0);
+    };
+    auto frag = [&](auto is_a, auto sp_c, int s, int grp) {
+        constexpr bool IS_A = decltype(is_a)::value;
+        const uint8_t* base = IS_A ? &sA[0][0] : &sB[0][0];
+        const uint4 x0 = *reinterpret_cast<const uint4*>(base + frag_off(is_a, sp_c, s, grp, 0));
+        const uint4 x1 = *reinterpret_cast<const uint4*>(base + frag_off(is_a, sp_c, s, grp, 1));
         return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     };
-    // BUF_C: std::integral_constant with the stage's ring buffer when it is known at compile time (then every LDS
-    // offset is an immediate), or -1.
-    auto read_stage = [&](auto buf_c, int st, v8i* fa, v8i* fb, uint32_t* sa, uint32_t* sb) {
-        constexpr int BUF = decltype(buf_c)::value;
-        const uint8_t* cA = sA[BUF < 0 ? st % NST : BUF];
-        const uint8_t* cB = sB[BUF < 0 ? st % NST : BUF];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fa[j] = frag(cA, wm * 128 + 32 * j + fr);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fb[i] = frag(cB, wn * 128 + 32 * i + fr);
+    auto read_scales = [&](int st, uint32_t* sa, uint32_t* sb) {
         if constexpr (MX) {
             const uint32_t* cSA = sSA[(st / SG) & 1];
             const uint32_t* cSB = sSB[(st / SG) & 1];
@@ -530,6 +566,13 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) { sa[j] = 0x7F7F7F7Fu; sb[j] = 0x7F7F7F7Fu; }
         }
+    };
+    auto read_stage = [&](auto sp_c, int st, v8i* fa, v8i* fb, uint32_t* sa, uint32_t* sb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fa[j] = frag(std::true_type{}, sp_c, st, 4 * wm + j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fb[i] = frag(std::false_type{}, sp_c, st, 4 * wn + i);
+        read_scales(st, sa, sb);
     };
 
     v16f acc16[4][4];
@@ -585,54 +628,63 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
                            "a"(acc16[3][0]), "a"(acc16[3][1]), "a"(acc16[3][2]), "a"(acc16[3][3]));
     };
 
-    // Scheduling pattern for a stage: one matrix instruction, then the next LDS read (MX: two), so the next
-    // stage's fragment reads trickle out between the matrix instructions instead of queueing ahead of them.
+    // Scheduling pattern for a stage of the exact path: four matrix instructions, then the next LDS read (MX: two),
+    // so the next stage's fragment reads trickle out between the matrix instructions instead of queueing ahead.
     auto interleave_reads = [&]() {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, MF == 1 ? 1 : 4, 0);   // matrix instructions
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                // matrix instructions
             __builtin_amdgcn_sched_group_barrier(0x100, MX ? 2 : 1, 0);        // LDS reads
         }
     };
 
-    const int nk = (int)(K / KS);
-    const int pre = nk < NST ? nk : NST;
-    for (int st = 0; st < pre; ++st) load_stage(st);
-    if (nk > 3) wait_copies_barrier<16>();                      // stages 0 and 1 have landed
-    else if (nk > 2) wait_copies_barrier<8>();
-    else wait_copies_barrier<0>();
+    // ------------------------------------------------------------------ prologue: stages 0 .. 3
+    if constexpr (MX) copy_scales(0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) copy_pair(std::true_type{}, std::false_type{}, 0, 0, c);       // A (0, 1)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {                                                       // B (-1, 0): stage 0 only
+        const uint32_t lds = lds_offset(&sB[0][1024 * wave]) + 4096 * c;
+        if (half_lane == 1) dma_to_lds<16>(rB, lds, b_off[c] - KS, 0);
+    }
+    if (nk > 1) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) copy_pair(std::false_type{}, std::false_type{}, 1, 1, c);  // B (1, 2)
+    }
+    if (nk > 2) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) copy_pair(std::true_type{}, std::false_type{}, 1, 2, c);   // A (2, 3)
+        wait_copies_barrier<8>();                               // stages 0 and 1 have landed
+    } else {
+        wait_copies_barrier<0>();
+    }
     v8i fa[4], fb[4];
     uint32_t sa[4], sb[4];
     read_stage(std::integral_constant<int, 0>{}, 0, fa, fb, sa, sb);
-    // Stage 0's buffer is refilled (stage 4) by the first trip: every wave's reads of it must have returned.
+    // Stage 0's regions are refilled by the first trips: every wave's reads of them must have returned.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // The asm waits are invisible to the compiler; this visible lgkmcnt(0) (vmcnt 63 and expcnt 7: no wait) tells it
     // that the fragment reads so far have returned, so it does not hold matrix instructions for them later.
     __builtin_amdgcn_s_waitcnt(0xC07F);
 
-    // Steady state, trip kt: stage kt's fragments are in registers (read during trip kt - 1), so its LDS buffer is
-    // free and receives the copy of stage kt + 4; stage kt + 1's fragments are read (landed by the end of trip
-    // kt - 1) while stage kt is multiplied; then wait until stage kt + 2 has landed, leaving the copies of stages
-    // kt + 3 and kt + 4 (16 per wave) in flight. Three stages are always in flight. Two fragment register sets
-    // ping-pong between trips (no copies between iterations).
+    // ------------------------------------------------------------------ trips
+    // Trip kt (kt + 1 < nk): copy the trip's pair, read stage kt + 1's fragments, multiply stage kt, then wait until
+    // stage kt + 2 has landed. Two fragment register sets ping-pong between trips (no copies between iterations).
     v8i fa2[4], fb2[4];
     uint32_t sa2[4], sb2[4];
-    // PH_C: kt % 4 as a std::integral_constant when known, else -1.
+    // PH_C: kt % 4 as a std::integral_constant when known (then the trip's pair exists in full), else -1.
     auto steady = [&](auto ph_c, int kt, v8i* ca, v8i* cb, uint32_t* csa, uint32_t* csb, v8i* na, v8i* nb,
                       uint32_t* nsa, uint32_t* nsb) {
         constexpr int PH = decltype(ph_c)::value;
+        using SP = std::integral_constant<int, PH < 0 ? -1 : (PH + 1) % 4>;     // stage kt + 1 mod 4
+        bool scales = false;
         if constexpr (MF == 1) {
             // FP8 path: 16 issue slots, each one matrix instruction and one 16-byte fragment read of stage kt + 1
-            // (MX: plus one scale read in the first 8), and every second slot one copy instruction of stage kt + 4.
+            // (MX: plus one scale read in the first 8), the trip's 8 copy instructions in the slots kCopySlot names.
             // Spreading the copies keeps a wave that finds the memory queue full from stalling its matrix
             // instructions behind a burst of copy issues. The scheduling barriers keep the slots in this order.
-            constexpr int RB = PH < 0 ? -1 : (PH + 1) % NST;
-            const int rb = RB < 0 ? (kt + 1) % NST : RB;
             const int odd = PH < 0 ? (kt & 1) : (PH & 1);
             const int sh = 8 * (2 * odd + fg);
-            const int ls = kt + 4, k0 = ls * KS;
-            const uint32_t la = lds_offset(&sA[ls % NST][1024 * wave]);
-            const uint32_t lb = lds_offset(&sB[ls % NST][1024 * wave]);
             const uint32_t* cSA = sSA[((kt + 1) / SG) & 1];
             const uint32_t* cSB = sSB[((kt + 1) / SG) & 1];
             const int sw = ((kt + 1) % SG) >> 1;
@@ -643,9 +695,13 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
                     cb[i], ca[j], acc16[i][j], FB, FA, 0, (int)(csb[i] >> sh), 0, (int)(csa[j] >> sh));
                 {
                     const int f = q >> 1, h = q & 1;
-                    const uint8_t* base = f < 4 ? sA[rb] : sB[rb];
-                    const int row = (f < 4 ? wm : wn) * 128 + 32 * (f & 3) + fr;
-                    const uint4 x = *reinterpret_cast<const uint4*>(base + row * KS + 16 * ((2 * h + fg) ^ fsw));
+                    uint4 x;
+                    if (f < 4)
+                        x = *reinterpret_cast<const uint4*>(&sA[0][0] +
+                                                            frag_off(std::true_type{}, SP{}, kt + 1, 4 * wm + f, h));
+                    else
+                        x = *reinterpret_cast<const uint4*>(&sB[0][0] +
+                                                            frag_off(std::false_type{}, SP{}, kt + 1, 4 * wn + f - 4, h));
                     v8i& d = f < 4 ? na[f & 3] : nb[f & 3];
                     d[4 * h] = (int)x.x; d[4 * h + 1] = (int)x.y; d[4 * h + 2] = (int)x.z; d[4 * h + 3] = (int)x.w;
                 }
@@ -656,61 +712,50 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) { nsa[e] = 0x7F7F7F7Fu; nsb[e] = 0x7F7F7F7Fu; }
                 }
-                if (q & 1) {
-                    const int c = q >> 1;
-                    if constexpr (MX) {
-                        if (c == 0 && ls % SG == 0) {       // a scale group's copies go first (see load_stage)
-                            const int gb = (ls / SG) & 1;
-                            dma_to_lds<16>(rSA, lds_offset(&sSA[gb][256 * wave]), sa_off, k0 / 32);
-                            dma_to_lds<16>(rSB, lds_offset(&sSB[gb][256 * wave]), sb_off, k0 / 32);
-                        }
-                    }
-                    if (c < 4) dma_to_lds<16>(rA, la + 4096 * c, a_off[c], k0);
-                    else dma_to_lds<16>(rB, lb + 4096 * (c - 4), b_off[c - 4], k0);
-                }
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    if (q == kCopySlot[c]) trip_copy(ph_c, kt, c);
+                if (q == 15) scales = trip_scales(kt);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
-            load_stage(kt + 4);
-            read_stage(std::integral_constant<int, PH < 0 ? -1 : (PH + 1) % NST>{}, kt + 1, na, nb, nsa, nsb);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) trip_copy(ph_c, kt, c);
+            scales = trip_scales(kt);
+            read_stage(SP{}, kt + 1, na, nb, nsa, nsb);
             mma_stage(std::integral_constant<int, PH < 0 ? -1 : PH % 2>{}, kt, ca, cb, csa, csb);
             interleave_reads();
         }
         pin_accumulators();
-        wait_copies_barrier<16>();
+        if constexpr (PH >= 0) {
+            if (scales) wait_copies_barrier<10>();
+            else wait_copies_barrier<8>();
+        } else {
+            trip_wait(kt, scales);
+        }
         __builtin_amdgcn_s_waitcnt(0xC07F);
     };
     using dyn = std::integral_constant<int, -1>;
     int kt = 0;
-    for (; kt + 7 < nk; kt += 4) {                               // kt % 4 == 0 on entry
+    for (; kt + 7 < nk; kt += 4) {                               // kt % 4 == 0; every pair of these trips is whole
         steady(std::integral_constant<int, 0>{}, kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
         steady(std::integral_constant<int, 1>{}, kt + 1, fa2, fb2, sa2, sb2, fa, fb, sa, sb);
         steady(std::integral_constant<int, 2>{}, kt + 2, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
         steady(std::integral_constant<int, 3>{}, kt + 3, fa2, fb2, sa2, sb2, fa, fb, sa, sb);
     }
-    for (; kt + 5 < nk; kt += 2) {
+    for (; kt + 2 < nk; kt += 2) {
         steady(dyn{}, kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
         steady(dyn{}, kt + 1, fa2, fb2, sa2, sb2, fa, fb, sa, sb);
     }
-    if (kt + 4 < nk) {
+    if (kt + 1 < nk) {
         steady(dyn{}, kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
         ++kt;
 #pragma unroll
         for (int j = 0; j < 4; ++j) { fa[j] = fa2[j]; fb[j] = fb2[j]; sa[j] = sa2[j]; sb[j] = sb2[j]; }
     }
-    // Last (at most four) stages: everything has been issued; wait for all of it.
-    for (; kt < nk; ++kt) {
-        v8i na[4], nb[4];
-        uint32_t nsa[4], nsb[4];
-        if (kt + 1 < nk) read_stage(std::integral_constant<int, -1>{}, kt + 1, na, nb, nsa, nsb);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_stage(std::integral_constant<int, -1>{}, kt, fa, fb, sa, sb);
-        pin_accumulators();
-        wait_copies_barrier<0>();
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { fa[j] = na[j]; fb[j] = nb[j]; sa[j] = nsa[j]; sb[j] = nsb[j]; }
-    }
+    // Last stage (kt == nk - 1): its fragments are in registers and no copy is outstanding.
+    __builtin_amdgcn_sched_barrier(0);
+    mma_stage(dyn{}, kt, fa, fb, sa, sb);
 
     // ------------------------------------------------------------------ epilogue
     float post = 1.0f;
