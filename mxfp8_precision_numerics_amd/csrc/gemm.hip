@@ -596,19 +596,28 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         } else {
             // Exact path: dequantize to bf16 and use the bf16 instruction. k-step s takes bytes 8s .. 8s+7 of each
             // lane's 32 (A and B lanes hold the same k values, so the product sums every k of the stage once);
-            // steps 0, 1 lie in the stage's first 32-block, steps 2, 3 in its second.
+            // steps 0, 1 lie in the stage's first 32-block, steps 2, 3 in its second, so each block's scale operands
+            // are formed once.
+            float xa[2][4], xb[2][4];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const int sh = 8 * (2 * odd + blk);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) xa[blk][j] = scale_operand((sa[j] >> sh) & 0xFFu);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xb[blk][i] = scale_operand((sb[i] >> sh) & 0xFFu);
+            }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const int sh = 8 * (2 * odd + (s >> 1));
                 v8bf da[4], db[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     da[j] = dequant8_bf16<FA>(make_uint2((uint32_t)fa[j][2 * s], (uint32_t)fa[j][2 * s + 1]),
-                                              scale_operand((sa[j] >> sh) & 0xFFu));
+                                              xa[s >> 1][j]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     db[i] = dequant8_bf16<FB>(make_uint2((uint32_t)fb[i][2 * s], (uint32_t)fb[i][2 * s + 1]),
-                                              scale_operand((sb[i] >> sh) & 0xFFu));
+                                              xb[s >> 1][i]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll

@@ -90,8 +90,7 @@ __device__ __forceinline__ float mx_inv_scale_f32(uint32_t byte) {
 // fp32 scale operand for v_cvt_scalef32_*: only its exponent field is read, so byte -> exponent bits
 // (a mantissa bit is set so the byte-0 pattern is a subnormal rather than zero).
 __device__ __forceinline__ float scale_operand(uint32_t byte) {
-    uint32_t b = byte > 254u ? 254u : byte;
-    return __uint_as_float((b << 23) | 0x00400000u);
+    return __uint_as_float((__builtin_elementwise_min(byte, 254u) << 23) | 0x00400000u);
 }
 
 // ------------------------------------------------------------------ conversions
