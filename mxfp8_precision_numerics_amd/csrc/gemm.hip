@@ -688,8 +688,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         using SP = std::integral_constant<int, PH < 0 ? -1 : (PH + 1) % 4>;     // stage kt + 1 mod 4
         bool scales = false;
         if constexpr (MF == 1) {
-            // FP8 path: 16 issue slots, each one matrix instruction and one 16-byte fragment read of stage kt + 1
-            // (MX: plus one scale read in the first 8), the trip's 8 copy instructions in the slots kCopySlot names.
+            // FP8 path: 16 issue slots, each one matrix instruction; the 16 fragment reads of stage kt + 1 go two per
+            // slot in the first 8 slots and (MX) its 8 scale reads two per slot in the next 4, so they have returned
+            // well before the wait that ends the trip; the trip's 8 copy instructions go in the slots kCopySlot names.
             // Spreading the copies keeps a wave that finds the memory queue full from stalling its matrix
             // instructions behind a burst of copy issues. The scheduling barriers keep the slots in this order.
             const int odd = PH < 0 ? (kt & 1) : (PH & 1);
@@ -702,8 +703,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
                 const int i = q >> 2, j = q & 3;
                 acc16[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     cb[i], ca[j], acc16[i][j], FB, FA, 0, (int)(csb[i] >> sh), 0, (int)(csa[j] >> sh));
-                {
-                    const int f = q >> 1, h = q & 1;
+#pragma unroll
+                for (int pc = 2 * q; pc < 2 * q + 2; ++pc) {
+                    if (pc >= 16) break;
+                    const int f = pc >> 1, h = pc & 1;
                     uint4 x;
                     if (f < 4)
                         x = *reinterpret_cast<const uint4*>(&sA[0][0] +
@@ -715,8 +718,20 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
                     d[4 * h] = (int)x.x; d[4 * h + 1] = (int)x.y; d[4 * h + 2] = (int)x.z; d[4 * h + 3] = (int)x.w;
                 }
                 if constexpr (MX) {
-                    if (q < 4) nsa[q] = cSA[(wm * 128 + 32 * q + fr) * 4 + sw];
-                    else if (q < 8) nsb[q - 4] = cSB[(wn * 128 + 32 * (q - 4) + fr) * 4 + sw];
+                    // A scale word holds the bytes of two stages: an odd stage reuses its even neighbour's words.
+                    constexpr bool REUSE = PH >= 0 && ((PH + 1) & 1) == 1;
+                    if constexpr (REUSE) {
+                        if (q == 8) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) { nsa[e] = csa[e]; nsb[e] = csb[e]; }
+                        }
+                    } else if (q >= 8 && q < 12) {
+#pragma unroll
+                        for (int e = 2 * (q - 8); e < 2 * (q - 8) + 2; ++e) {
+                            if (e < 4) nsa[e] = cSA[(wm * 128 + 32 * e + fr) * 4 + sw];
+                            else nsb[e - 4] = cSB[(wn * 128 + 32 * (e - 4) + fr) * 4 + sw];
+                        }
+                    }
                 } else if (q == 0) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) { nsa[e] = 0x7F7F7F7Fu; nsb[e] = 0x7F7F7F7Fu; }
