@@ -782,37 +782,51 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     mma_stage(dyn{}, kt, fa, fb, sa, sb);
 
     // ------------------------------------------------------------------ epilogue
+    // Lane l holds, for output row m (l % 32), the columns 8q + 4g + 0..3 (g = l / 32) of each 32-column block in
+    // accumulator registers 4q .. 4q+3. After rounding to bf16 pairs, swapping register sets q = 2p + 1 of the lower
+    // half-wave with q = 2p of the upper (v_permlane32_swap) leaves lane l with the 8 consecutive columns
+    // 16p + 8g .. 16p + 8g + 7, stored as one 16-byte write.
     float post = 1.0f;
     if constexpr (!MX) post = 1.0f / (g.pa[0] * g.pb[0]);
-    const bool vec_ok = (g.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 7) == 0;
-    auto store4 = [&](int64_t m, int64_t n, float v0, float v1, float v2, float v3) {
-        if (m >= m_end) return;
-        float v[4] = {v0, v1, v2, v3};
-        uint16_t h4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float x = v[e];
-            if constexpr (!MX) x = x * post;
-            h4[e] = __builtin_bit_cast(uint16_t, (__bf16)x);
-        }
-        uint16_t* dst = g.c + m * g.ldc + n;
-        if (vec_ok && n + 4 <= n_end) {
-            *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)h4[0] | ((uint32_t)h4[1] << 16),
-                                                        (uint32_t)h4[2] | ((uint32_t)h4[3] << 16));
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (n + e < n_end) dst[e] = h4[e];
-        }
+    const bool vec_ok = (g.ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 15) == 0;
+    auto pack2 = [&](float x0, float x1) {
+        if constexpr (!MX) { x0 = x0 * post; x1 = x1 * post; }
+        return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x0) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x1) << 16);
     };
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+            uint32_t w[4][2];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                store4(m0 + wm * 128 + j * 32 + fr, n0 + wn * 128 + i * 32 + 8 * q + 4 * fg, acc16[i][j][4 * q],
-                       acc16[i][j][4 * q + 1], acc16[i][j][4 * q + 2], acc16[i][j][4 * q + 3]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) w[q][h] = pack2(acc16[i][j][4 * q + 2 * h], acc16[i][j][4 * q + 2 * h + 1]);
+#pragma unroll
+            for (int pq = 0; pq < 2; ++pq)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pq][h], w[2 * pq + 1][h], false, false);
+                    w[2 * pq][h] = r[0];
+                    w[2 * pq + 1][h] = r[1];
+                }
+            const int64_t m = m0 + wm * 128 + j * 32 + fr;
+            if (m >= m_end) continue;
+#pragma unroll
+            for (int pq = 0; pq < 2; ++pq) {
+                const int64_t n = n0 + wn * 128 + i * 32 + 16 * pq + 8 * fg;
+                uint16_t* dst = g.c + m * g.ldc + n;
+                const uint32_t v4[4] = {w[2 * pq][0], w[2 * pq][1], w[2 * pq + 1][0], w[2 * pq + 1][1]};
+                if (vec_ok && n + 8 <= n_end) {
+                    *reinterpret_cast<uint4*>(dst) = make_uint4(v4[0], v4[1], v4[2], v4[3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < n_end) dst[e] = (uint16_t)(v4[e >> 1] >> (16 * (e & 1)));
+                }
+            }
+        }
 }
 
 // Path selection. The FP8 matrix instructions (v_mfma_*_f8f6f4 and the older *_fp8_fp8 forms) sum the products of
