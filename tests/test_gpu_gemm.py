@@ -116,6 +116,61 @@ def test_gemm_leading_dimension():
     assert torch.all(big[:, :4] == 7.0) and torch.all(big[:, 44:] == 7.0)
 
 
+@pytest.mark.parametrize("K", [64, 128, 192, 320, 576, 4160])
+@pytest.mark.parametrize("N", [776, 1030])
+def test_large_tile_stage_counts_pertensor(K, N):
+    """The large-tile kernel (M, N >= 512) at 1, 2, 3, 5, 9 and 65 stages of 64 bytes: the copy tails (a last stage
+    without its pair partner), the dynamic trips and the last-stage drain; partial tiles in M and N, and an output
+    whose rows are not 16-byte multiples (N = 1030) next to one that is (N = 776)."""
+    need_gpu()
+    M = 520
+    say("large-tile per-tensor", M, N, K)
+    A = workloads.normal_bf16((M, K), 1.0, 25, K, DEV)
+    B = workloads.normal_bf16((N, K), 0.02, 25, 7 * K + N, DEV)
+    pa = mxq.pertensor_quantize(A, mxq.E4M3, want_qt=False)
+    pb = mxq.pertensor_quantize(B, mxq.E4M3, want_qt=False)
+    C = mxq.scaled_gemm(pa.q, pa.scale, pb.q, pb.scale, mxq.PER_TENSOR, mxq.E4M3, mxq.E4M3)
+    torch.cuda.synchronize()
+    y, S = oracle.gemm_ref(u8(pa.q), np.float32(pa.scale.item()), oracle.E4M3, u8(pb.q), np.float32(pb.scale.item()),
+                           oracle.E4M3, oracle.PER_TENSOR)
+    _bound_check(C.float().cpu().numpy(), y, S, f"large-tile per-tensor {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("K", [512, 1536])
+def test_large_tile_stage_counts_mx(K):
+    """MX operands on the large-tile kernel with 8 and 24 stages (one and three scale groups)."""
+    need_gpu()
+    M, N = 600, 520
+    say("large-tile mx", M, N, K)
+    A = workloads.normal_bf16((M, K), 1.0, 26, K, DEV)
+    B = workloads.normal_bf16((N, K), 1.0, 26, 3 * K + 1, DEV)
+    qa, sa, qb, sb = _mx_operands(A, B)
+    C = mxq.scaled_gemm(qa, sa, qb, sb, mxq.MX_BLOCK32)
+    torch.cuda.synchronize()
+    y, S = oracle.gemm_ref(u8(qa), u8(sa), oracle.E4M3, u8(qb), u8(sb), oracle.E4M3, oracle.MX_BLOCK32)
+    _bound_check(C.float().cpu().numpy(), y, S, f"large-tile mx {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("col0", [4, 8])
+def test_large_tile_leading_dimension(col0):
+    """Output as a column window of a wider matrix on the large-tile kernel: 8-byte (col0 = 4) and 16-byte (col0 = 8)
+    aligned windows, a width (516) that ends inside an 8-column group; the rest of the matrix stays untouched."""
+    need_gpu()
+    M, N, K = 512, 516, 1024
+    A = workloads.normal_bf16((M, K), 1.0, 27, 0, DEV)
+    B = workloads.normal_bf16((N, K), 1.0, 27, 1, DEV)
+    qa, sa, qb, sb = _mx_operands(A, B)
+    big = torch.full((M, 528), 7.0, dtype=torch.bfloat16, device=DEV)
+    view = big[:, col0:col0 + N]
+    C = mxq.scaled_gemm(qa, sa, qb, sb, mxq.MX_BLOCK32, out=view)
+    ref = mxq.scaled_gemm(qa, sa, qb, sb, mxq.MX_BLOCK32)
+    torch.cuda.synchronize()
+    assert torch.equal(C, ref)
+    assert torch.all(big[:, :col0] == 7.0) and torch.all(big[:, col0 + N:] == 7.0)
+    y, S = oracle.gemm_ref(u8(qa), u8(sa), oracle.E4M3, u8(qb), u8(sb), oracle.E4M3, oracle.MX_BLOCK32)
+    _bound_check(ref.float().cpu().numpy(), y, S, f"large-tile ld {M}x{N}x{K}")
+
+
 def _sampled(C, y_rows, S_rows, y_cols, S_cols, rows, cols, what):
     Ch = C.float().cpu().numpy() if not isinstance(C, np.ndarray) else C
     w1 = _bound_check(Ch[rows, :], y_rows, S_rows, what + " rows")
