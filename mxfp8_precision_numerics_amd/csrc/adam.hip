@@ -207,7 +207,9 @@ __global__ __launch_bounds__(ATHREADS) void adam_update_kernel(float* __restrict
         }
     if constexpr (AMAX) {
         mx = block_max_u32(mx);
-        if (threadIdx.x == 0) atomicMax(amax_word, mx);
+        // the running maximum only grows: most workgroups find theirs already covered and skip the atomic
+        if (threadIdx.x == 0 && mx > __hip_atomic_load(amax_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            atomicMax(amax_word, mx);
     }
 }
 

@@ -67,20 +67,12 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
             v[j] = make_uint4(0u, 0u, 0u, 0u);
     }
 
+    // AMAX: this thread's max |x| (bf16 magnitude patterns; NaN patterns sort above infinity; padding loaded as 0);
+    // the workgroup's reduction waits until its stores are issued, so no wave stalls on it before converting.
+    uint32_t amax_local = 0;
     if constexpr (AMAX) {
-        // max |x| of the tile (bf16 magnitude patterns; NaN patterns sort above infinity; padding loaded as 0)
-        __shared__ uint32_t red[QTHREADS / 64];
-        uint32_t m = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) m = max(m, amax_bits8(v[j]));
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-        if ((tid & 63) == 0) red[tid >> 6] = m;
-        __syncthreads();
-        if (tid == 0) {
-            m = max(max(red[0], red[1]), max(red[2], red[3]));
-            atomicMax(a.amax_word, m);
-        }
+        for (int j = 0; j < 8; ++j) amax_local = max(amax_local, amax_bits8(v[j]));
     }
 
     if constexpr (COL) {
@@ -212,6 +204,19 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
                     }
                 }
             }
+        }
+    }
+    if constexpr (AMAX) {
+        __shared__ uint32_t red[QTHREADS / 64];
+        uint32_t m = amax_local;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+        if ((tid & 63) == 0) red[tid >> 6] = m;
+        __syncthreads();
+        if (tid == 0) {
+            m = max(max(red[0], red[1]), max(red[2], red[3]));
+            // the running maximum only grows: most tiles find theirs already covered and skip the atomic
+            if (m > __hip_atomic_load(a.amax_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(a.amax_word, m);
         }
     }
 }
