@@ -6,7 +6,8 @@ One step is one pass over every row of the hot path, on seeded synthetic inputs 
   pt_linear     the same layer with per-tensor current scaling (E4M3 X and W, E5M2 dY; q and q^T) and three GEMMs
   mx_quant      MX quantize of a 16384x8192 activation with 0.1% x100 outliers, row and column orientation
   grouped       64-expert grouped MX GEMM (Zipf(1.1) top-8 routing of 16384 tokens, up 2048->1024 and down
-                1024->2048), including the row quantize of both activations (expert weights quantized once)
+                1024->2048), including the row quantize of both activations (expert weights quantized once); the
+                activation quantizes and the two grouped GEMMs are timed separately as well
   adam          precision-decoupled FP8 Adam step over 1.3e9 parameters (2 passes)
   small         MX quantize + 256^3 block-scaled GEMM
   pt_quant_delayed  the per-tensor casts of X, W, dY with delayed scaling (16-slot amax histories): one pass each
@@ -21,7 +22,8 @@ One step is one pass over every row of the hot path, on seeded synthetic inputs 
   grad_requant  the re-quantize of those codes to the shared scale (the min over 8 gathered scales)
 The headline value is the MXFP8 linear layer's GEMM FLOPs (11.13 TFLOP) divided by the device time of its quantize
 and GEMM launches ("MXFP8 GEMM TFLOP/s incl. quantize"). Device times come from events on the stream the kernels
-run on; the JSON line also carries every part's rate, the MX GEMM's roofline and the CPU oracle baseline.
+run on; the JSON line also carries every part's rate, the MX GEMM's roofline, the ceilings this part attains
+(a 1 GiB device copy, an MFMA-only loop), measured after the timed steps, and the CPU oracle baseline.
 """
 from __future__ import annotations
 
@@ -151,8 +153,9 @@ def main():
 
     Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     parts = ["mx_quant_XWdY", "mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "pt_quant", "pt_gemms", "mx_quant_act",
-             "grouped", "adam", "small", "pt_quant_delayed", "adam_delayed", "wcache_fused", "wcache_unfused",
-             "moe_swiglu_mlp", "swiglu_quant", "grad_cast", "grad_requant"]
+             "grouped_q_up", "grouped_gemm_up", "grouped_q_down", "grouped_gemm_down", "adam", "small",
+             "pt_quant_delayed", "adam_delayed", "wcache_fused", "wcache_unfused", "moe_swiglu_mlp", "swiglu_quant",
+             "grad_cast", "grad_requant"]
     NEV = len(parts) + 1
 
     def step(ev):
@@ -178,44 +181,47 @@ def main():
         mxq.mx_quantize(act3, out=mx3)
         ev[7].record(stream)
         mxq.mx_quantize(wl4["a_up"], colwise=False, out=mx_up)
+        ev[8].record(stream)
         mxq.grouped_scaled_gemm(mx_up.q_row, mx_up.s_row, off4, qwu.q_row.view(G, d_ff, d_model),
                                 qwu.s_row.view(G, d_ff, d_model // 32), out=C_up)
+        ev[9].record(stream)
         mxq.mx_quantize(wl4["a_down"], colwise=False, out=mx_dn)
+        ev[10].record(stream)
         mxq.grouped_scaled_gemm(mx_dn.q_row, mx_dn.s_row, off4, qwd.q_row.view(G, d_model, d_ff),
                                 qwd.s_row.view(G, d_model, d_ff // 32), out=C_dn)
-        ev[8].record(stream)
+        ev[11].record(stream)
         mxq.fp8_adam_step(theta, grad, m_q, m_scale, v16, w16, hp, workspace=adam_ws)
-        ev[9].record(stream)
+        ev[12].record(stream)
         qa = mxq.mx_quantize(A1, colwise=False)
         qb = mxq.mx_quantize(B1, rowwise=False)
         mxq.scaled_gemm(qa.q_row, qa.s_row, qb.q_col, qb.s_col, mxq.MX_BLOCK32)
-        ev[10].record(stream)
+        ev[13].record(stream)
         mxq.pertensor_quantize_delayed(X, hists["X"], hpos["X"], mxq.E4M3, workspace=ws_del)
         mxq.pertensor_quantize_delayed(W, hists["W"], hpos["W"], mxq.E4M3, workspace=ws_del)
         mxq.pertensor_quantize_delayed(dY, hists["dY"], hpos["dY"], mxq.E5M2, workspace=ws_del)
-        ev[11].record(stream)
+        ev[14].record(stream)
         mxq.fp8_adam_step_delayed(theta, grad, m_q, m_scale, v16, w16, hp, m_hist, m_pos, workspace=ws_adel)
-        ev[12].record(stream)
+        ev[15].record(stream)
         mxq.fp8_adam_step_mx_cache(th_w, g_w, mq_w, ms_w, v_w, None, hp, N, K, out=cache_w, workspace=ws_w)
-        ev[13].record(stream)
+        ev[16].record(stream)
         mxq.fp8_adam_step(th_w, g_w, mq_w, ms_w, v_w, wb_w, hp, workspace=ws_w)
         mxq.mx_quantize(wb_w.view(N, K), out=cache_w)
-        ev[14].record(stream)
+        ev[17].record(stream)
         mxq.mx_quantize(wl4["a_up"], colwise=False, out=mx_up)
         mxq.grouped_scaled_gemm(mx_up.q_row, mx_up.s_row, off4, qwgu.q_row.view(G, 2 * d_ff, d_model),
                                 qwgu.s_row.view(G, 2 * d_ff, d_model // 32), out=C_gu)
         mxq.swiglu_mx_quantize(C_gu, out=mx_h)
         mxq.grouped_scaled_gemm(mx_h.q_row, mx_h.s_row, off4, qwd.q_row.view(G, d_model, d_ff),
                                 qwd.s_row.view(G, d_model, d_ff // 32), out=C_dn)
-        ev[15].record(stream)
+        ev[18].record(stream)
         mxq.swiglu_mx_quantize(C_gu, out=mx_h)
-        ev[16].record(stream)
+        ev[19].record(stream)
         gc = mxq.fp8_autoscale_cast(dW, mu_g, mxq.E4M3, workspace=ws_g)
-        ev[17].record(stream)
+        ev[20].record(stream)
         gathered[:1] = gc.scale
         gathered[1:] = others
         mxq.fp8_requantize_shared(gc.q, mxq.E4M3, gc.scale, gathered, mxq.E4M3, out=q_req)
-        ev[18].record(stream)
+        ev[21].record(stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -233,6 +239,8 @@ def main():
     ms = {p: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
           for i, p in enumerate(parts)}
     step_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][NEV - 1]) for s in range(args.steps)]))
+    ms["grouped"] = sum(ms[p] for p in ("grouped_q_up", "grouped_gemm_up", "grouped_q_down", "grouped_gemm_down"))
+    grouped_gemm_ms = ms["grouped_gemm_up"] + ms["grouped_gemm_down"]
     log("per-part ms:", json.dumps({k: round(v, 4) for k, v in ms.items()}))
 
     # ------------------------------------------------------------------ rates
@@ -260,7 +268,9 @@ def main():
         "pt_quant_gbs": pt_bytes / (ms["pt_quant"] * 1e-3) / 1e9,
         "mx_quant_act_gbs": act_bytes / (ms["mx_quant_act"] * 1e-3) / 1e9,
         "grouped_tflops_incl_act_quant": grouped_flop / (ms["grouped"] * 1e-3) / 1e12,
+        "grouped_gemm_only_tflops": grouped_flop / (grouped_gemm_ms * 1e-3) / 1e12,
         "adam_gbs": adam_bytes / (ms["adam"] * 1e-3) / 1e9,
+        "adam_gbs_vs_18B_ideal": 18 * n_adam / (ms["adam"] * 1e-3) / 1e9,
         "small_us": ms["small"] * 1e3,
         "pt_quant_delayed_gbs": sum(4 * r * c for r, c in ((M, K), (N, K), (M, N))) / (ms["pt_quant_delayed"] * 1e-3) / 1e9,
         "adam_delayed_gbs": 18 * n_adam / (ms["adam_delayed"] * 1e-3) / 1e9,
@@ -276,10 +286,13 @@ def main():
         rate[k] = round(v, 3)
     log("rates:", json.dumps(rate))
 
+    attainable = measure_attainable(mxq, mxX.q_row, dev, stream)
+    log("attainable:", json.dumps(attainable))
     fwd_tflops = rate["mx_gemm_fwd_tflops"]
     roofline = {"kernel": "scaled_gemm MX_BLOCK32 fwd 4096x36864x12288 (gemm_big_kernel, block-scaled FP8 MFMA)",
                 "bound": "mfma", "achieved": fwd_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(fwd_tflops / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic(),
+                "frac_of_attainable": round(fwd_tflops / attainable["mfma_fp8_tflops"], 4),
                 "algorithmic_flop_per_launch": flop_gemm, "avg_launch_ms": round(ms["mx_gemm_fwd"], 4)}
 
     cpu = None
@@ -299,6 +312,7 @@ def main():
         "parts_ms": {k: round(v, 4) for k, v in ms.items()},
         "rates": rate,
         "roofline": roofline,
+        "attainable": attainable,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -359,6 +373,48 @@ def profile_kernel(name, dev):
     print(json.dumps({"profile_kernel": name, "avg_ms": round(e0.elapsed_time(e1) / 10, 4)}), flush=True)
 
 
+def measure_attainable(mxq, operand_bytes, dev, stream):
+    """What this part sustains, measured in the same run beside the spec peaks: the library's streaming copy of 1 GiB
+    (HBM read + write; best of four grid sizes) and the MFMA-only loop of the block-scaled FP8 instruction on real
+    quantized operand bytes."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.empty(256 * 256, dtype=torch.float32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    mxq.probe_mfma_fp8(operand_bytes, 200, 256, sink)
+    torch.cuda.synchronize()
+    copy_gbs = 0.0
+    for blocks in (1024, 2048, 4096, 8192):
+        mxq.probe_copy(src, dst, blocks)
+        ev[0].record(stream)
+        for _ in range(10):
+            moved = mxq.probe_copy(src, dst, blocks)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        copy_gbs = max(copy_gbs, 10 * moved / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9)
+    ev[2].record(stream)
+    flop = mxq.probe_mfma_fp8(operand_bytes, 8000, 256, sink)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    mfma_tflops = flop / (ev[2].elapsed_time(ev[3]) * 1e-3) / 1e12
+    del src, dst
+    return {"hbm_copy_gbs": round(copy_gbs, 1), "hbm_copy_frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
+            "mfma_fp8_tflops": round(mfma_tflops, 1), "mfma_fp8_frac_of_peak": round(mfma_tflops / PEAK_FP8_TFLOPS, 4)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(X, W, rows):
     """The oracle (unchanged) on the host cores: MX quantize of `rows` rows of X and all of W, then the fp64 GEMM
     of those rows against W (the forward GEMM of the MX linear layer), as TFLOP/s of the sample."""
@@ -379,6 +435,7 @@ def cpu_baseline(X, W, rows):
     flop = 2.0 * rows * W.shape[0] * W.shape[1]
     log(f"cpu oracle: quantize {t1 - t0:.2f}s, gemm {t2 - t1:.2f}s on {threads} threads")
     return {"value": round(flop / (t2 - t0) / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
             "sample": f"forward GEMM of the MX linear layer for {rows} of 4096 rows of X (2*{rows}*36864*12288 FLOP) "
                       f"in fp64, including MX quantize of those rows and of all of W ({t2 - t0:.1f} s)"}
 

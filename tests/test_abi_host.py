@@ -162,3 +162,19 @@ def test_gradcomm_validation():
     assert r(P, 64, 0, None, P, 8, 0, P, P, P, None) == 1
     assert r(None, 64, 0, P, P, 8, 0, P, P, P, None) == 1
     assert r(P, 64, 0, P, P, 8, 0, MIS, P, P, None) == 3
+
+
+def test_probe_validation():
+    f = _lib.load().mxq_probe_mfma_fp8
+    assert f(None, 10, 4, P, None) == 1
+    assert f(P, 10, 4, None, None) == 1
+    assert f(P, 0, 4, P, None) == 2
+    assert f(P, 10, 0, P, None) == 2
+    assert f(P, 10, 70000, P, None) == 2
+    assert f(MIS, 10, 4, P, None) == 3
+    c = _lib.load().mxq_probe_copy
+    assert c(P, P, 24, 4, None) == 2                 # bytes % 16
+    assert c(P, P, 32, 0, None) == 2
+    assert c(None, P, 32, 4, None) == 1
+    assert c(MIS, P, 32, 4, None) == 3
+    assert c(None, None, 0, 4, None) == 0            # empty
