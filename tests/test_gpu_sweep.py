@@ -1,0 +1,99 @@
+"""Seeded sweeps of random shapes against the oracle, beyond the hand-picked shapes of the other GPU tests: tiles cut
+at every edge (rows and columns that are not multiples of the 128-wide quantize tiles or the 128/256-wide GEMM tiles),
+both scale rules and both orientations, both FP8 formats, and GEMM shapes on either side of the small/large-tile and
+exact/FP8 path thresholds. Quantizers must match byte for byte; GEMMs must satisfy
+|C - y| <= 2^-7 |y| + 2^-20 sum|a b| on every element. Each case prints its seed and shape before it runs."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_precision_numerics_amd as mxq
+import oracle
+from gpu_util import DEV, need_gpu, say, u16, u8
+from mxfp8_precision_numerics_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _shapes(seed, n, rmult, cmult, rmax, cmax):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, rmax // rmult + 1)) * rmult, int(rng.integers(1, cmax // cmult + 1)) * cmult)
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_mx_quantize_random_shapes(case):
+    need_gpu()
+    rows, cols = _shapes(100 + case, 1, 32, 32, 700, 900)[0]
+    rule = mxq.RCEIL if case % 2 == 0 else mxq.FLOOR
+    say("sweep mx quantize", case, rows, cols, rule)
+    x = workloads.normal_bf16((rows, cols), 10.0 ** (case % 5 - 2), 30, case, DEV)
+    r = mxq.mx_quantize(x, rule=rule)
+    torch.cuda.synchronize()
+    qr, sr, qc, sc = oracle.mx_quantize(u16(x), rule)
+    assert np.array_equal(u8(r.s_row), sr) and np.array_equal(u8(r.q_row), qr)
+    assert np.array_equal(u8(r.s_col), sc) and np.array_equal(u8(r.q_col), qc)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_pertensor_quantize_random_shapes(case):
+    need_gpu()
+    rows, cols = _shapes(200 + case, 1, 32, 8, 700, 900)[0]
+    fmt = mxq.E4M3 if case % 2 == 0 else mxq.E5M2
+    margin = (1.0, 0.5, 2.0 ** -3)[case % 3]
+    say("sweep per-tensor quantize", case, rows, cols, fmt, margin)
+    x = workloads.normal_bf16((rows, cols), 10.0 ** (case % 4 - 3), 31, case, DEV)
+    r = mxq.pertensor_quantize(x, fmt, margin)
+    torch.cuda.synchronize()
+    a, s, q, qt = oracle.pertensor_quantize(u16(x), fmt, margin)
+    assert np.float32(r.amax.item()) == np.float32(a)
+    assert r.scale.cpu().numpy().view(np.uint32)[0] == np.float32(s).view(np.uint32)
+    assert np.array_equal(u8(r.q), q) and np.array_equal(u8(r.q_t), qt)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_swiglu_quantize_random_shapes(case):
+    need_gpu()
+    rows, F = _shapes(300 + case, 1, 1, 32, 500, 640)[0]
+    rule = mxq.RCEIL if case % 2 == 0 else mxq.FLOOR
+    say("sweep swiglu", case, rows, F, rule)
+    c = workloads.normal_bf16((rows, 2 * F), 2.0 ** (case % 4), 32, case, DEV)
+    r = mxq.swiglu_mx_quantize(c, rule)
+    torch.cuda.synchronize()
+    q, s, _ = oracle.swiglu_mx_quantize(u16(c), rule)
+    assert np.array_equal(u8(r.s_row), s) and np.array_equal(u8(r.q_row), q)
+
+
+# (M, N, K) around the kernel thresholds: large tiles need M, N >= 512 and K % 64 (per-tensor) or K % 512 (MX); the
+# FP8 instruction is used from K = 12288
+GEMM_SHAPES = [(511, 700, 512), (512, 512, 512), (513, 640, 1024), (700, 513, 1536), (600, 777, 96), (520, 530, 12288),
+               (300, 1100, 12320), (1030, 516, 2048)]
+
+
+@pytest.mark.parametrize("shape", GEMM_SHAPES)
+@pytest.mark.parametrize("scaling", ["mx", "pt"])
+def test_gemm_threshold_shapes(shape, scaling):
+    need_gpu()
+    M, N, K = shape
+    if scaling == "pt" and K % 8:
+        pytest.skip("per-tensor rows need K % 8 == 0")
+    say("sweep gemm", scaling, M, N, K)
+    A = workloads.normal_bf16((M, K), 1.0, 33, M + K, DEV)
+    B = workloads.normal_bf16((N, K), 1.0, 33, 7 * N + K, DEV)
+    if scaling == "mx":
+        qa = mxq.mx_quantize(A, colwise=False)
+        qb = mxq.mx_quantize(B, colwise=False)
+        C = mxq.scaled_gemm(qa.q_row, qa.s_row, qb.q_row, qb.s_row, mxq.MX_BLOCK32)
+        torch.cuda.synchronize()
+        y, S = oracle.gemm_ref(u8(qa.q_row), u8(qa.s_row), oracle.E4M3, u8(qb.q_row), u8(qb.s_row), oracle.E4M3,
+                               oracle.MX_BLOCK32)
+    else:
+        pa = mxq.pertensor_quantize(A, mxq.E4M3, want_qt=False)
+        pb = mxq.pertensor_quantize(B, mxq.E5M2, want_qt=False)
+        C = mxq.scaled_gemm(pa.q, pa.scale, pb.q, pb.scale, mxq.PER_TENSOR, mxq.E4M3, mxq.E5M2)
+        torch.cuda.synchronize()
+        y, S = oracle.gemm_ref(u8(pa.q), np.float32(pa.scale.item()), oracle.E4M3, u8(pb.q),
+                               np.float32(pb.scale.item()), oracle.E5M2, oracle.PER_TENSOR)
+    err = np.abs(C.float().cpu().numpy().astype(np.float64) - y)
+    lim = 2.0 ** -7 * np.abs(y) + 2.0 ** -20 * S
+    assert np.all(err <= lim), f"{int((err > lim).sum())} elements outside the bound"
