@@ -104,7 +104,7 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
                 const uint32_t b8 = (uint32_t)__shfl_down((int)byte, 8, 16);
                 const uint32_t b12 = (uint32_t)__shfl_down((int)byte, 12, 16);
                 if (col_ok && gr < a.rows) {
-                    *reinterpret_cast<uint2*>(a.q_row + gr * a.cols + gc) = make_uint2(lo, hi);
+                    stnt8(a.q_row + gr * a.cols + gc, make_uint2(lo, hi));
                     if (a.srow_words) {
                         if (ch == 0)
                             *reinterpret_cast<uint32_t*>(a.s_row + gr * (a.cols / 32) + c0 / 32) =
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
             } else {
                 lo = pt_cvt_quad<MODE>(pt_scale, v[j].x, v[j].y);
                 hi = pt_cvt_quad<MODE>(pt_scale, v[j].z, v[j].w);
-                if (col_ok && gr < a.rows) *reinterpret_cast<uint2*>(a.q_row + gr * a.cols + gc) = make_uint2(lo, hi);
+                if (col_ok && gr < a.rows) stnt8(a.q_row + gr * a.cols + gc, make_uint2(lo, hi));
             }
         }
     }
