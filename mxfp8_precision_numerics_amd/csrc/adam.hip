@@ -341,7 +341,7 @@ __global__ __launch_bounds__(ATHREADS) void adam_mx_tile_kernel(WeightCacheArgs 
             const uint32_t lo = cvt_f32_pair<FMT_E4M3, true>(cvt_f32_pair<FMT_E4M3, false>(0u, y[0], y[1]), y[2], y[3]);
             const uint32_t hi = cvt_f32_pair<FMT_E4M3, true>(cvt_f32_pair<FMT_E4M3, false>(0u, y[4], y[5]), y[6], y[7]);
             if (col_ok && gr < a.rows) {
-                *reinterpret_cast<uint2*>(a.q_row + gr * a.cols + gc) = make_uint2(lo, hi);
+                stnt8(a.q_row + gr * a.cols + gc, make_uint2(lo, hi));
                 if ((ch & 3) == 0) a.s_row[gr * (a.cols / 32) + gc / 32] = (uint8_t)byte;
             }
         }

@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256) void swiglu_mx_kernel(const uint16_t* __restri
         for (int e = 0; e < 8; ++e) y[e] = clamp_keep_nan(h[e] * f, 448.0f);
         const uint32_t lo = cvt_f32_pair<FMT_E4M3, true>(cvt_f32_pair<FMT_E4M3, false>(0u, y[0], y[1]), y[2], y[3]);
         const uint32_t hi = cvt_f32_pair<FMT_E4M3, true>(cvt_f32_pair<FMT_E4M3, false>(0u, y[4], y[5]), y[6], y[7]);
-        *reinterpret_cast<uint2*>(q + r * F + j) = make_uint2(lo, hi);
+        stnt8(q + r * F + j, make_uint2(lo, hi));
         if ((j & 31) == 0) s[r * (F / 32) + j / 32] = (uint8_t)byte;
     }
 }
