@@ -57,8 +57,8 @@ def main():
                     help="run only this kernel (10 launches) for hardware-counter passes, print its timing, exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (multi-GPU sharding is a design "
-                                   "note, not implemented)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1 (sharding across GPUs is not "
+                                   "implemented)", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np
