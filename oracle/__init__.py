@@ -76,6 +76,10 @@ def lib():
         L.orc_adam_step_delayed.restype = F
         L.orc_adam_step_delayed.argtypes = [P, P, P, P, P, P, I64, P, P, I64, P, I]
         L.orc_adam_elements.argtypes = [P, P, P, P, F, F, P, I64, P, P, P, P, P]
+        L.orc_route_weighted_mx_quantize.argtypes = [P, P, I64, I64, I, P, P, P, P, P, I]
+        L.orc_swiglu_bwd_f32.argtypes = [F, F, F, P, P]
+        L.orc_swiglu_bwd_mx_quantize.argtypes = [P, P, I64, I64, I, P, P, P, P, P, I]
+        L.orc_grouped_wgrad_ref.argtypes = [P, P, P, P, P, I64, P, I64, P, I64, P, I64, P, P]
         _lib = L
     return _lib
 
@@ -186,6 +190,69 @@ def swiglu_mx_quantize(c_bf16, rule: int = RCEIL, want_h: bool = False):
     h = np.empty((R, F), np.float32) if want_h else None
     lib().orc_swiglu_mx_quantize(_p(c), R, F, rule, _p(q), _p(s), _p(h))
     return q, s, h
+
+
+# ---------------------------------------------------------------- routed-expert backward
+def route_weighted_mx_quantize(dy_bf16, p_f32, rule: int = RCEIL, rowwise: bool = True, colwise: bool = True,
+                               want_x: bool = False, nthreads=None):
+    """x = fp32(p[r] * dy[r][c]) quantized to MXFP8. Returns (q_row, s_row, q_col, s_col, x or None)."""
+    dy = _c(dy_bf16, np.uint16)
+    p = _c(p_f32, np.float32)
+    R, Ccols = dy.shape
+    q_row = np.empty((R, Ccols), np.uint8) if rowwise else None
+    s_row = np.empty((R, Ccols // 32), np.uint8) if rowwise else None
+    q_col = np.empty((Ccols, R), np.uint8) if colwise else None
+    s_col = np.empty((Ccols, R // 32), np.uint8) if colwise else None
+    x = np.empty((R, Ccols), np.float32) if want_x else None
+    lib().orc_route_weighted_mx_quantize(_p(dy), _p(p), R, Ccols, rule, _p(q_row), _p(s_row), _p(q_col), _p(s_col),
+                                         _p(x), nthreads or default_threads())
+    return q_row, s_row, q_col, s_col, x
+
+
+def swiglu_bwd_f32(g: float, u: float, dh: float):
+    """(d_gate, d_up) of h = silu(g) u for the incoming gradient dh, in the oracle's fp32 operation order."""
+    dg = C.c_float(); du = C.c_float()
+    lib().orc_swiglu_bwd_f32(C.c_float(g), C.c_float(u), C.c_float(dh), C.byref(dg), C.byref(du))
+    return np.float32(dg.value), np.float32(du.value)
+
+
+def swiglu_bwd_mx_quantize(c_bf16, dh_bf16, rule: int = RCEIL, rowwise: bool = True, colwise: bool = True,
+                           want_dc: bool = False, nthreads=None):
+    """c_bf16 [rows][2F] (gate | up), dh_bf16 [rows][F]. dc = (d_gate | d_up) [rows][2F] quantized to MXFP8.
+    Returns (q_row, s_row, q_col, s_col, dc fp32 or None)."""
+    c = _c(c_bf16, np.uint16)
+    dh = _c(dh_bf16, np.uint16)
+    R, F2 = c.shape
+    F = F2 // 2
+    assert dh.shape == (R, F)
+    q_row = np.empty((R, F2), np.uint8) if rowwise else None
+    s_row = np.empty((R, F2 // 32), np.uint8) if rowwise else None
+    q_col = np.empty((F2, R), np.uint8) if colwise else None
+    s_col = np.empty((F2, R // 32), np.uint8) if colwise else None
+    dc = np.empty((R, F2), np.float32) if want_dc else None
+    lib().orc_swiglu_bwd_mx_quantize(_p(c), _p(dh), R, F, rule, _p(q_row), _p(s_row), _p(q_col), _p(s_col), _p(dc),
+                                     nthreads or default_threads())
+    return q_row, s_row, q_col, s_col, dc
+
+
+def grouped_wgrad_ref(a_q, a_s, b_q, b_s, offsets, groups=None, rows=None, cols=None):
+    """Per-expert contraction over token ranges: y[g][m][n] = sum_{k in group g} a_hat[m][k] b_hat[n][k] (fp64),
+    with a_q [M][Kt], b_q [N][Kt] and scales [.][Kt/32]. Returns (y, S) of shape [groups][rows][cols]."""
+    aq = _c(a_q, np.uint8); as_ = _c(a_s, np.uint8)
+    bq = _c(b_q, np.uint8); bs = _c(b_s, np.uint8)
+    off = _c(offsets, np.int64)
+    M, Kt = aq.shape
+    N = bq.shape[0]
+    assert bq.shape[1] == Kt and as_.shape == (M, Kt // 32) and bs.shape == (N, Kt // 32)
+    G = off.size - 1
+    groups = np.arange(G, dtype=np.int64) if groups is None else _c(groups, np.int64)
+    rows = np.arange(M, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    cols = np.arange(N, dtype=np.int64) if cols is None else _c(cols, np.int64)
+    y = np.empty((groups.size, rows.size, cols.size), np.float64)
+    S = np.empty((groups.size, rows.size, cols.size), np.float64)
+    lib().orc_grouped_wgrad_ref(_p(aq), _p(as_), _p(bq), _p(bs), _p(off), Kt, _p(groups), groups.size, _p(rows),
+                                rows.size, _p(cols), cols.size, _p(y), _p(S))
+    return y, S
 
 
 def autoscale_cast(g_bf16, mu: float, fmt: int = E4M3):

@@ -342,6 +342,71 @@ void orc_swiglu_mx_quantize(const uint16_t* c, int64_t rows, int64_t F, int rule
 }
 
 /* ------------------------------------------------------------------------------------------------------
+ * Routed-expert backward ([OLMO11] Section 11.4.1, backward of the routed experts; Section 11.4.4, Table 25).
+ *
+ * Combine backward: the route weight of each routed row multiplies that row's output gradient, and the product
+ * is quantized straight to MXFP8 (the fused route-weighting + gradient Q of Table 25). Reading: the product is one
+ * fp32 rounding of p * float(dy); both orientations follow the fp32 MX block rule (mx_block_f32), the row
+ * orientation for the down projection's dgrad, the column orientation (blocks of 32 routed rows) for its Wgrad.
+ * ------------------------------------------------------------------------------------------------------ */
+void orc_route_weighted_mx_quantize(const uint16_t* dy, const float* p, int64_t rows, int64_t cols, int rule,
+                                    uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, float* x_out,
+                                    int nthreads)
+{
+    tables();
+    float* x = x_out ? x_out : (float*)malloc(sizeof(float) * (size_t)(rows * cols));
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            float v = orc_bf16_to_f32(dy[r * cols + c]);
+            x[r * cols + c] = p[r] * v;
+        }
+    orc_mx_quantize_f32(x, rows, cols, rule, q_row, s_row, q_col, s_col, nthreads);
+    if (!x_out) free(x);
+}
+
+/* SwiGLU backward. Forward h = silu(g) u with silu(g) = g sigma(g), sigma(g) = 1 / (1 + e^-g). Its partial
+ * derivatives: dh/du = silu(g); dh/dg = u silu'(g) with silu'(g) = sigma(g) (1 + g (1 - sigma(g))).
+ * Given the incoming gradient dh: d_gate = (dh u) silu'(g), d_up = dh silu(g).
+ * Reading (the pages fix only that SwiGLU feeds the down projection and that backward follows the forward's data
+ * dependencies in reverse): every step is one fp32 operation in the order written below, with the forward's fixed
+ * exponential and the forward's silu = g / (1 + e^-g), so the d_up factor equals the forward's silu bit for bit. */
+void orc_swiglu_bwd_f32(float g, float u, float dh, float* d_gate, float* d_up)
+{
+    float e = orc_exp_f32(-g);
+    float d = 1.0f + e;
+    float silu = g / d;
+    float sig = 1.0f / d;
+    float one_m = 1.0f - sig;
+    float t = g * one_m;
+    t = 1.0f + t;
+    float ds = sig * t;
+    float du = dh * u;
+    *d_gate = du * ds;
+    *d_up = dh * silu;
+}
+
+/* The fused backward step between the down projection's dgrad and the up/gate projection's dgrad and Wgrad:
+ * c[rows][2F] is the forward's up/gate output (gate in columns [0, F), up in [F, 2F)), dh[rows][F] the gradient
+ * of h. dc[rows][2F] = (d_gate | d_up) is quantized in both orientations with the fp32 MX block rule: row blocks
+ * along 2F feed the up/gate dgrad (K = 2F), column blocks of 32 routed rows feed its Wgrad (K = routed rows). */
+void orc_swiglu_bwd_mx_quantize(const uint16_t* c, const uint16_t* dh, int64_t rows, int64_t F, int rule,
+                                uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, float* dc_out,
+                                int nthreads)
+{
+    tables();
+    float* dc = dc_out ? dc_out : (float*)malloc(sizeof(float) * (size_t)(rows * 2 * F));
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < F; ++j) {
+            float g = orc_bf16_to_f32(c[r * 2 * F + j]);
+            float u = orc_bf16_to_f32(c[r * 2 * F + F + j]);
+            float h = orc_bf16_to_f32(dh[r * F + j]);
+            orc_swiglu_bwd_f32(g, u, h, &dc[r * 2 * F + j], &dc[r * 2 * F + F + j]);
+        }
+    orc_mx_quantize_f32(dc, rows, 2 * F, rule, q_row, s_row, q_col, s_col, nthreads);
+    if (!dc_out) free(dc);
+}
+
+/* ------------------------------------------------------------------------------------------------------
  * FP8 gradient all-reduce, the parts one GPU runs ([FP8-LM] Section 3.4, automatic scaling (Eq. 3) and the shared
  * scaling factor of Eq. 4-6).
  * Auto-scaled cast: g' = mu * g (one fp32 rounding), q = FP8(g') with saturation; the tensor's scale is mu
@@ -606,6 +671,47 @@ void orc_grouped_gemm_ref(const uint8_t* aq, const uint8_t* as, const int64_t* o
                   y + r * nc, S + r * nc, nthreads);
     }
     free(arow);
+}
+
+/* Routed Wgrad as a contraction over tokens ([OLMO11] Section 11.4.1 and Section 11.4.4: the reduction dimension of
+ * the routed Wgrad is the expert's token rows). A[M][Kt] and B[N][Kt] are column-orientation MX operands (blocks of 32
+ * along the token dimension, scales [M][Kt/32] and [N][Kt/32]); expert g owns tokens [offsets[g], offsets[g+1]), each
+ * offset a multiple of 32. y_g[m][n] = sum over those k, ascending, of a_hat[m][k] b_hat[n][k] in double, with
+ * a_hat = val(q) 2^(byte - 127); S_g = the same sum of |products|. Computes the requested groups, rows and columns
+ * into y[ng][nr][nc] and S[ng][nr][nc]. An empty group gives 0. */
+void orc_grouped_wgrad_ref(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                           const int64_t* offsets, int64_t Kt, const int64_t* groups, int64_t ng, const int64_t* rows,
+                           int64_t nr, const int64_t* cols, int64_t nc, double* y, double* S)
+{
+    tables();
+    for (int64_t gi = 0; gi < ng; ++gi) {
+        int64_t g = groups[gi];
+        int64_t k0 = offsets[g], Kg = offsets[g + 1] - offsets[g];
+        size_t len = (size_t)(Kg > 0 ? Kg : 1);
+        double* a = (double*)malloc(sizeof(double) * len * (size_t)nr);
+        double* b = (double*)malloc(sizeof(double) * len * (size_t)nc);
+        for (int64_t i = 0; i < nr; ++i)
+            dequant_row(aq + rows[i] * Kt + k0, as + rows[i] * (Kt / 32) + k0 / 32, ORC_E4M3, ORC_MX_BLOCK32, Kg,
+                        a + (size_t)i * len);
+        for (int64_t j = 0; j < nc; ++j)
+            dequant_row(bq + cols[j] * Kt + k0, bs + cols[j] * (Kt / 32) + k0 / 32, ORC_E4M3, ORC_MX_BLOCK32, Kg,
+                        b + (size_t)j * len);
+        for (int64_t i = 0; i < nr; ++i)
+            for (int64_t j = 0; j < nc; ++j) {
+                const double* ai = a + (size_t)i * len;
+                const double* bj = b + (size_t)j * len;
+                double acc = 0.0, sabs = 0.0;
+                for (int64_t k = 0; k < Kg; ++k) {
+                    double prod = ai[k] * bj[k];
+                    acc += prod;
+                    sabs += fabs(prod);
+                }
+                y[(gi * nr + i) * nc + j] = acc;
+                S[(gi * nr + i) * nc + j] = sabs;
+            }
+        free(a);
+        free(b);
+    }
 }
 
 /* ------------------------------------------------------------------------------------------------------
