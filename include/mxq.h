@@ -86,6 +86,49 @@ mxq_status swiglu_mx_quantize(const uint16_t* c_bf16, int64_t rows, int64_t F, u
                               mxq_scale_rule rule, hipStream_t stream);
 
 /*
+ * swiglu_mx_quantize with both orientations, for a forward that saves the hidden representation for the down
+ * projection's Wgrad ([OLMO11] Section 11.3.2: an activation saved in MXFP8 for Wgrad is produced explicitly in the
+ * right-hand-operand layout; Section 11.4.1, fused SwiGLU plus quantization).
+ *   h[r][j] = silu(c[r][j]) c[r][F + j] in fp32 exactly as swiglu_mx_quantize computes it, quantized from fp32:
+ *   row: q_row[rows][F], s_row[rows][F/32] (equal to swiglu_mx_quantize's q and s);
+ *   col: q_col[F][rows], s_col[F][rows/32] (blocks of 32 routed rows, stored transposed).
+ * Either orientation may be NULL (not both). Requires F % 32 == 0 and rows % 32 == 0.
+ */
+mxq_status swiglu_mx_quantize_oriented(const uint16_t* c_bf16, int64_t rows, int64_t F, uint8_t* q_row,
+                                       uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, mxq_scale_rule rule,
+                                       hipStream_t stream);
+
+/*
+ * Combine backward of the routed experts: the route weighting fused with the gradient's MXFP8 quantize ([OLMO11]
+ * Section 11.4.1, combine backward; Section 11.4.4 / Table 25, route weighting + gradient Q as one fusion).
+ *   dy_bf16[rows][cols]: the output gradient of each routed row (in expert order); route_w: device fp32[rows], the
+ *   route weight of each routed row (0 for padding rows).
+ *   x[r][c] = fp32(route_w[r] * dy[r][c]) (one rounding), quantized from fp32 like mxq_quantize:
+ *   row: q_row[rows][cols], s_row[rows][cols/32] (the down projection's dgrad operand);
+ *   col: q_col[cols][rows], s_col[cols][rows/32] (its Wgrad operand, blocks of 32 routed rows).
+ * Either orientation may be NULL (not both). Requires cols % 32 == 0 and rows % 32 == 0.
+ */
+mxq_status route_weighted_mx_quantize(const uint16_t* dy_bf16, const float* route_w, int64_t rows, int64_t cols,
+                                      uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                                      mxq_scale_rule rule, hipStream_t stream);
+
+/*
+ * SwiGLU backward fused with the MXFP8 quantize of its gradients ([OLMO11] Section 11.4.1: qdata and scales pass
+ * directly between adjacent backward stages that agree on layout, with no DQ-Q cycle).
+ *   c_bf16[rows][2F]: the forward up/gate GEMM output (gate in [0, F), up in [F, 2F)); dh_bf16[rows][F]: the
+ *   gradient of h = silu(g) u (the down projection's dgrad output).
+ *   With sigma = 1 / (1 + e^-g), silu = g / (1 + e^-g) (the forward's value) and silu' = sigma (1 + g (1 - sigma)):
+ *   dc[r][j] = (dh u) silu'(g), dc[r][F + j] = dh silu(g); every fp32 operation rounded on its own, in the order
+ *   written, with swiglu_mx_quantize's fixed exponential.
+ *   row: q_row[rows][2F], s_row[rows][2F/32] (the up/gate dgrad operand, K = 2F);
+ *   col: q_col[2F][rows], s_col[2F][rows/32] (its Wgrad operand). Either orientation may be NULL (not both).
+ * Requires F % 32 == 0 and rows % 32 == 0.
+ */
+mxq_status swiglu_backward_mx_quantize(const uint16_t* c_bf16, const uint16_t* dh_bf16, int64_t rows, int64_t F,
+                                       uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                                       mxq_scale_rule rule, hipStream_t stream);
+
+/*
  * Per-tensor current scaling ([FP8-LM] tensor scaling FP8(x) = cast(s x), x ~ FP8(x) / s; [LLMSB] per-tensor
  * scaling and Exercise 6's to_fp8_e4m3):
  *   amax_out[0] = max |x|   (fp32, device);
@@ -178,6 +221,41 @@ mxq_status scaled_gemm(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fmt,
 mxq_status grouped_scaled_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* group_offsets, int64_t G,
                                int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s,
                                int64_t N, int64_t K, uint16_t* c_bf16, hipStream_t stream);
+
+/*
+ * The same grouped MX GEMM with a strided B operand, so the routed experts' dgrad reads the column-orientation weight
+ * cache in place ([OLMO11] Section 11.4.1: dgrad uses the orientation-specific MXFP8 weight caches). Expert g's B row
+ * n (n < N) is the K bytes at b_q + g*b_group_stride + n*ldb, its scales the K/32 bytes at
+ * b_s + g*bs_group_stride + n*ldbs; C rows have stride ldc (bf16 elements).
+ * Example: W[G][D][F] refreshed as one [G*D][F] matrix by fp8_adam_step_mx_cache has q_col[F][G*D]; the dgrad
+ * dX = dY W_g takes b_q = q_col, ldb = G*D, b_group_stride = D, b_s = s_col, ldbs = G*D/32, bs_group_stride = D/32,
+ * N = F, K = D.
+ * Requires everything grouped_scaled_gemm requires, plus ldb >= K, ldbs >= K/32, ldc >= N, non-negative group
+ * strides, and ldb and b_group_stride multiples of 16 (16-byte rows). Fastest when ldbs and bs_group_stride are
+ * multiples of 16 as well.
+ */
+mxq_status grouped_scaled_gemm_strided(const uint8_t* a_q, const uint8_t* a_s, const int64_t* group_offsets,
+                                       int64_t G, int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s,
+                                       int64_t ldb, int64_t b_group_stride, int64_t ldbs, int64_t bs_group_stride,
+                                       int64_t N, int64_t K, uint16_t* c_bf16, int64_t ldc, hipStream_t stream);
+
+/*
+ * Routed Wgrad: one MX contraction per expert over that expert's token rows ([OLMO11] Section 11.4.1 and
+ * Section 11.4.4 / Table 25: the routed Wgrad's reduction dimension is the expert's tokens). The operands are
+ * column-orientation MXFP8 tensors whose 32-value blocks run along the token dimension (mxq_quantize's q_col / s_col
+ * of the token-major activations and gradients, or route_weighted_mx_quantize's and swiglu_backward_mx_quantize's):
+ *   a_q[M][Kt], a_s[M][Kt/32], b_q[N][Kt], b_s[N][Kt/32]; group_offsets: device int64[G+1], offsets[0] = 0,
+ *   non-decreasing, multiples of 32, offsets[G] = Kt.
+ *   For each expert g: C_g[m][n] = sum over k in [offsets[g], offsets[g+1]) of a_hat[m][k] b_hat[n][k] (fp32
+ *   accumulation of exactly dequantized operands: equal to dequantizing to BF16 and running a BF16 grouped GEMM).
+ *   Output, exactly one of: c_bf16[G][M][N] (bf16 RNE of C_g; an empty expert gives zeros), or
+ *   c_f32[G][M][N] (in/out: c_f32 += C_g, one fp32 rounding per element; the high-precision gradient sink).
+ * Requires M, N >= 1, Kt >= 0 and Kt % 32 == 0, 1 <= G <= 4096. As for grouped_scaled_gemm, the offsets are read on
+ * the device only; offsets outside [0, Kt] are clamped.
+ */
+mxq_status grouped_wgrad_mx(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
+                            const int64_t* group_offsets, int64_t G, int64_t M, int64_t N, int64_t Kt,
+                            uint16_t* c_bf16, float* c_f32, hipStream_t stream);
 
 /* Adam hyper-parameters, passed by HOST pointer. step is the 1-based step count t. */
 typedef struct {

@@ -6,8 +6,11 @@ outputs, and call the C ABI of libmxq.so with raw pointers. All arithmetic happe
   mx_quantize            MXFP8 row/column quantization (E4M3 payload, E8M0 scale per 32 values)
   pertensor_quantize     per-tensor current/delayed scaling to E4M3 or E5M2 (+ transposed copy)
   scaled_gemm            C = A B^T with FP8 operands (per-tensor or MX block scales), fp32 accumulate, bf16 out
-  grouped_scaled_gemm    the MX GEMM over ragged expert row groups
+  grouped_scaled_gemm    the MX GEMM over ragged expert row groups (and a strided-B form for the routed dgrad)
+  grouped_wgrad_mx       the routed Wgrad: one MX contraction per expert over its token rows
   fp8_adam_step          precision-decoupled FP8 AdamW step (fp32 master, E4M3 m + scale, fp16 v, bf16 copy)
+  swiglu_mx_quantize(_oriented), swiglu_backward_mx_quantize, route_weighted_mx_quantize
+                         the routed MLP's fused elementwise + MX quantize steps (forward and backward)
 """
 from __future__ import annotations
 
@@ -20,6 +23,8 @@ from . import _lib
 from ._lib import E4M3, E5M2, FLOOR, MX_BLOCK32, PER_TENSOR, RCEIL, AdamHParams, MXQError  # noqa: F401
 
 __all__ = ["mx_quantize", "pertensor_quantize", "scaled_gemm", "grouped_scaled_gemm", "fp8_adam_step",
+           "swiglu_mx_quantize", "swiglu_mx_quantize_oriented", "swiglu_backward_mx_quantize", "route_weighted_mx_quantize",
+           "grouped_scaled_gemm_strided", "grouped_wgrad_mx",
            "workspace_bytes", "MXTensor", "AdamHParams", "MXQError", "E4M3", "E5M2", "RCEIL", "FLOOR",
            "PER_TENSOR", "MX_BLOCK32"]
 
@@ -78,6 +83,61 @@ def swiglu_mx_quantize(c: torch.Tensor, rule: int = RCEIL, out: Optional[MXTenso
                        torch.empty((rows, F // 32), dtype=torch.uint8, device=c.device), None, None)
     st = _lib.load().swiglu_mx_quantize(_ptr(c), rows, F, _ptr(out.q_row), _ptr(out.s_row), rule, _stream(c.device))
     _lib.check("swiglu_mx_quantize", st)
+    return out
+
+
+def _mx_out(rows: int, cols: int, rowwise: bool, colwise: bool, dev) -> MXTensor:
+    e = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+    return MXTensor(e(rows, cols) if rowwise else None, e(rows, cols // 32) if rowwise else None,
+                    e(cols, rows) if colwise else None, e(cols, rows // 32) if colwise else None)
+
+
+def swiglu_mx_quantize_oriented(c: torch.Tensor, rowwise: bool = True, colwise: bool = True, rule: int = RCEIL,
+                                out: Optional[MXTensor] = None) -> MXTensor:
+    """c: bf16 [rows][2F] (gate | up) -> MXFP8 of silu(gate) * up [rows][F] in the requested orientations (the
+    column one is the down projection's Wgrad operand)."""
+    _dev(c, torch.bfloat16, "c")
+    rows, f2 = c.shape
+    F = f2 // 2
+    if out is None:
+        out = _mx_out(rows, F, rowwise, colwise, c.device)
+    st = _lib.load().swiglu_mx_quantize_oriented(_ptr(c), rows, F, _ptr(out.q_row), _ptr(out.s_row), _ptr(out.q_col),
+                                                 _ptr(out.s_col), rule, _stream(c.device))
+    _lib.check("swiglu_mx_quantize_oriented", st)
+    return out
+
+
+def route_weighted_mx_quantize(dy: torch.Tensor, route_w: torch.Tensor, rowwise: bool = True, colwise: bool = True,
+                               rule: int = RCEIL, out: Optional[MXTensor] = None) -> MXTensor:
+    """dy: bf16 [rows][cols] (routed rows in expert order), route_w: float32[rows] -> MXFP8 of route_w[r] * dy[r][c]
+    in the requested orientations (the down projection's dgrad and Wgrad operands)."""
+    _dev(dy, torch.bfloat16, "dy"); _dev(route_w, torch.float32, "route_w")
+    rows, cols = dy.shape
+    if route_w.numel() != rows:
+        raise ValueError("route_w must hold one weight per row of dy")
+    if out is None:
+        out = _mx_out(rows, cols, rowwise, colwise, dy.device)
+    st = _lib.load().route_weighted_mx_quantize(_ptr(dy), _ptr(route_w), rows, cols, _ptr(out.q_row),
+                                                _ptr(out.s_row), _ptr(out.q_col), _ptr(out.s_col), rule,
+                                                _stream(dy.device))
+    _lib.check("route_weighted_mx_quantize", st)
+    return out
+
+
+def swiglu_backward_mx_quantize(c: torch.Tensor, dh: torch.Tensor, rowwise: bool = True, colwise: bool = True,
+                                rule: int = RCEIL, out: Optional[MXTensor] = None) -> MXTensor:
+    """c: bf16 [rows][2F] (gate | up, the forward up/gate GEMM output), dh: bf16 [rows][F] (gradient of
+    silu(gate) * up) -> MXFP8 of (d_gate | d_up) [rows][2F] in the requested orientations."""
+    _dev(c, torch.bfloat16, "c"); _dev(dh, torch.bfloat16, "dh")
+    rows, f2 = c.shape
+    F = f2 // 2
+    if tuple(dh.shape) != (rows, F) or f2 != 2 * F:
+        raise ValueError("dh must be [rows][F] for c of shape [rows][2F]")
+    if out is None:
+        out = _mx_out(rows, f2, rowwise, colwise, c.device)
+    st = _lib.load().swiglu_backward_mx_quantize(_ptr(c), _ptr(dh), rows, F, _ptr(out.q_row), _ptr(out.s_row),
+                                                 _ptr(out.q_col), _ptr(out.s_col), rule, _stream(c.device))
+    _lib.check("swiglu_backward_mx_quantize", st)
     return out
 
 
@@ -161,6 +221,62 @@ def grouped_scaled_gemm(a_q: torch.Tensor, a_s: torch.Tensor, offsets: torch.Ten
                                          _ptr(out), _stream(a_q.device))
     _lib.check("grouped_scaled_gemm", st)
     return out
+
+
+def grouped_scaled_gemm_strided(a_q: torch.Tensor, a_s: torch.Tensor, offsets: torch.Tensor, b_q: torch.Tensor,
+                                b_s: torch.Tensor, G: int, N: int, K: int, ldb: int, b_group_stride: int, ldbs: int,
+                                bs_group_stride: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The grouped MX GEMM with expert g's B row n at b_q[g * b_group_stride + n * ldb] (K bytes) and its scales at
+    b_s[g * bs_group_stride + n * ldbs] (K/32 bytes): e.g. a column-orientation weight cache read in place."""
+    _dev(a_q, torch.uint8, "a_q"); _dev(b_q, torch.uint8, "b_q"); _dev(offsets, torch.int64, "offsets")
+    _dev(a_s, torch.uint8, "a_s"); _dev(b_s, torch.uint8, "b_s")
+    total, Ka = a_q.shape
+    if Ka != K or offsets.numel() != G + 1:
+        raise ValueError("shape mismatch")
+    last = (G - 1) * b_group_stride + (N - 1) * ldb + K
+    last_s = (G - 1) * bs_group_stride + (N - 1) * ldbs + K // 32
+    if b_q.numel() < last or b_s.numel() < last_s:
+        raise ValueError("b_q / b_s do not hold every expert's rows at the given strides")
+    if out is None:
+        out = torch.empty((total, N), dtype=torch.bfloat16, device=a_q.device)
+    elif out.dtype != torch.bfloat16 or out.shape[0] != total or out.shape[1] < N or out.stride(1) != 1:
+        raise ValueError("out must be bf16 [total_rows][>= N] with unit column stride")
+    st = _lib.load().grouped_scaled_gemm_strided(_ptr(a_q), _ptr(a_s), _ptr(offsets), G, total, _ptr(b_q), _ptr(b_s),
+                                                 ldb, b_group_stride, ldbs, bs_group_stride, N, K, _ptr(out),
+                                                 out.stride(0), _stream(a_q.device))
+    _lib.check("grouped_scaled_gemm_strided", st)
+    return out
+
+
+def grouped_wgrad_mx(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Tensor,
+                     offsets: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     accumulate: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-expert contraction over token ranges: C_g = A[:, off_g:off_g+1] B[:, off_g:off_g+1]^T for column-
+    orientation operands a_q [M][Kt], b_q [N][Kt]. Returns bf16 [G][M][N], or adds into `accumulate` (float32
+    [G][M][N]) and returns it."""
+    _dev(a_q, torch.uint8, "a_q"); _dev(b_q, torch.uint8, "b_q"); _dev(offsets, torch.int64, "offsets")
+    _dev(a_s, torch.uint8, "a_s"); _dev(b_s, torch.uint8, "b_s")
+    M, Kt = a_q.shape
+    N = b_q.shape[0]
+    G = offsets.numel() - 1
+    if b_q.shape[1] != Kt or tuple(a_s.shape) != (M, Kt // 32) or tuple(b_s.shape) != (N, Kt // 32):
+        raise ValueError("shape mismatch")
+    if accumulate is not None:
+        _dev(accumulate, torch.float32, "accumulate")
+        if tuple(accumulate.shape) != (G, M, N):
+            raise ValueError("accumulate must be float32 [G][M][N]")
+        c_bf16, c_f32, res = None, accumulate, accumulate
+    else:
+        if out is None:
+            out = torch.empty((G, M, N), dtype=torch.bfloat16, device=a_q.device)
+        _dev(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (G, M, N):
+            raise ValueError("out must be bf16 [G][M][N]")
+        c_bf16, c_f32, res = out, None, out
+    st = _lib.load().grouped_wgrad_mx(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(offsets), G, M, N, Kt,
+                                      _ptr(c_bf16), _ptr(c_f32), _stream(a_q.device))
+    _lib.check("grouped_wgrad_mx", st)
+    return res
 
 
 def fp8_adam_step(master: torch.Tensor, grad: torch.Tensor, m_q: torch.Tensor, m_scale: torch.Tensor,

@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmxq.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["quantize.hip", "gemm.hip", "adam.hip", "gradcomm.hip", "probe.hip", "abi.hip"]
+SOURCES = ["quantize.hip", "gemm.hip", "adam.hip", "gradcomm.hip", "moe.hip", "probe.hip", "abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -43,6 +43,12 @@ SIGNATURES = {
     "fp8_adam_step_mx_cache": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _I, C.POINTER(AdamHParams),
                                     _P, _SZ, _P]),
     "fp8_adam_step_delayed": (_I, [_P, _P, _P, _P, _P, _P, _I64, C.POINTER(AdamHParams), _P, _P, _I64, _P, _SZ, _P]),
+    "swiglu_mx_quantize_oriented": (_I, [_P, _I64, _I64, _P, _P, _P, _P, _I, _P]),
+    "route_weighted_mx_quantize": (_I, [_P, _P, _I64, _I64, _P, _P, _P, _P, _I, _P]),
+    "swiglu_backward_mx_quantize": (_I, [_P, _P, _I64, _I64, _P, _P, _P, _P, _I, _P]),
+    "grouped_scaled_gemm_strided": (_I, [_P, _P, _P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P,
+                                         _I64, _P]),
+    "grouped_wgrad_mx": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P]),
 }
 
 _lib = None

@@ -111,6 +111,51 @@ mxq_status swiglu_mx_quantize(const uint16_t* c_bf16, int64_t rows, int64_t F, u
     return hip_status(mxq::launch_swiglu_mx_quantize(c_bf16, rows, F, q, s, (int)rule, stream));
 }
 
+mxq_status swiglu_mx_quantize_oriented(const uint16_t* c_bf16, int64_t rows, int64_t F, uint8_t* q_row,
+                                       uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, mxq_scale_rule rule,
+                                       hipStream_t stream) {
+    if ((q_row == nullptr) != (s_row == nullptr) || (q_col == nullptr) != (s_col == nullptr)) return MXQ_ERR_NULL;
+    if (q_row == nullptr && q_col == nullptr) return MXQ_ERR_NULL;
+    if (rule != MXQ_SCALE_RCEIL && rule != MXQ_SCALE_FLOOR) return MXQ_ERR_UNSUPPORTED;
+    if (rows < 0 || F < 0 || F % 32 != 0 || rows % 32 != 0) return MXQ_ERR_SHAPE;
+    if ((rows + 63) / 64 > kMaxGridY) return MXQ_ERR_SHAPE;
+    if (rows == 0 || F == 0) return MXQ_OK;
+    if (!c_bf16) return MXQ_ERR_NULL;
+    if (!al16(c_bf16) || (q_row && !al16(q_row)) || (q_col && !al16(q_col))) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_swiglu_mx_quantize_oriented(c_bf16, rows, F, q_row, s_row, q_col, s_col, (int)rule,
+                                                              stream));
+}
+
+mxq_status route_weighted_mx_quantize(const uint16_t* dy_bf16, const float* route_w, int64_t rows, int64_t cols,
+                                      uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                                      mxq_scale_rule rule, hipStream_t stream) {
+    if ((q_row == nullptr) != (s_row == nullptr) || (q_col == nullptr) != (s_col == nullptr)) return MXQ_ERR_NULL;
+    if (q_row == nullptr && q_col == nullptr) return MXQ_ERR_NULL;
+    if (rule != MXQ_SCALE_RCEIL && rule != MXQ_SCALE_FLOOR) return MXQ_ERR_UNSUPPORTED;
+    if (rows < 0 || cols < 0 || cols % 32 != 0 || rows % 32 != 0) return MXQ_ERR_SHAPE;
+    if ((rows + 63) / 64 > kMaxGridY) return MXQ_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!dy_bf16 || !route_w) return MXQ_ERR_NULL;
+    if (!al16(dy_bf16) || !al4(route_w) || (q_row && !al16(q_row)) || (q_col && !al16(q_col))) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_route_weighted_mx_quantize(dy_bf16, route_w, rows, cols, q_row, s_row, q_col, s_col,
+                                                             (int)rule, stream));
+}
+
+mxq_status swiglu_backward_mx_quantize(const uint16_t* c_bf16, const uint16_t* dh_bf16, int64_t rows, int64_t F,
+                                       uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                                       mxq_scale_rule rule, hipStream_t stream) {
+    if ((q_row == nullptr) != (s_row == nullptr) || (q_col == nullptr) != (s_col == nullptr)) return MXQ_ERR_NULL;
+    if (q_row == nullptr && q_col == nullptr) return MXQ_ERR_NULL;
+    if (rule != MXQ_SCALE_RCEIL && rule != MXQ_SCALE_FLOOR) return MXQ_ERR_UNSUPPORTED;
+    if (rows < 0 || F < 0 || F % 32 != 0 || rows % 32 != 0) return MXQ_ERR_SHAPE;
+    if ((rows + 63) / 64 > kMaxGridY) return MXQ_ERR_SHAPE;
+    if (rows == 0 || F == 0) return MXQ_OK;
+    if (!c_bf16 || !dh_bf16) return MXQ_ERR_NULL;
+    if (!al16(c_bf16) || !al16(dh_bf16) || (q_row && !al16(q_row)) || (q_col && !al16(q_col))) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_swiglu_bwd_mx_quantize(c_bf16, dh_bf16, rows, F, q_row, s_row, q_col, s_col,
+                                                         (int)rule, stream));
+}
+
 mxq_status fp8_quantize_pertensor(const uint16_t* x_bf16, int64_t rows, int64_t cols, mxq_fp8 fmt, float margin,
                                   const float* scale_in, float* amax_out, float* scale_out, uint8_t* q, uint8_t* q_t,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -207,7 +252,39 @@ mxq_status grouped_scaled_gemm(const uint8_t* a_q, const uint8_t* a_s, const int
     if (!al16(a_q) || !al16(a_s) || !al16(b_q) || !al16(b_s) || (reinterpret_cast<uintptr_t>(c_bf16) & 1u) ||
         (reinterpret_cast<uintptr_t>(group_offsets) & 7u))
         return MXQ_ERR_ALIGN;
-    return hip_status(mxq::launch_grouped_gemm(a_q, a_s, group_offsets, G, total_rows, b_q, b_s, N, K, c_bf16, stream));
+    return hip_status(mxq::launch_grouped_gemm(a_q, a_s, group_offsets, G, total_rows, b_q, b_s, K, N * K, K / 32,
+                                               N * (K / 32), N, K, c_bf16, N, stream));
+}
+
+mxq_status grouped_scaled_gemm_strided(const uint8_t* a_q, const uint8_t* a_s, const int64_t* group_offsets,
+                                       int64_t G, int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s,
+                                       int64_t ldb, int64_t b_group_stride, int64_t ldbs, int64_t bs_group_stride,
+                                       int64_t N, int64_t K, uint16_t* c_bf16, int64_t ldc, hipStream_t stream) {
+    if (G < 1 || G > 4096 || total_rows < 0 || N < 1 || K <= 0 || K % 32 != 0) return MXQ_ERR_SHAPE;
+    if (ldb < K || ldbs < K / 32 || ldc < N || b_group_stride < 0 || bs_group_stride < 0) return MXQ_ERR_SHAPE;
+    if (ldb % 16 != 0 || b_group_stride % 16 != 0) return MXQ_ERR_ALIGN;
+    if (!group_offsets || !b_q || !b_s) return MXQ_ERR_NULL;
+    if (total_rows == 0) return MXQ_OK;
+    if (!a_q || !a_s || !c_bf16) return MXQ_ERR_NULL;
+    if (!al16(a_q) || !al16(a_s) || !al16(b_q) || !al16(b_s) || (reinterpret_cast<uintptr_t>(c_bf16) & 1u) ||
+        (reinterpret_cast<uintptr_t>(group_offsets) & 7u))
+        return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_grouped_gemm(a_q, a_s, group_offsets, G, total_rows, b_q, b_s, ldb, b_group_stride,
+                                               ldbs, bs_group_stride, N, K, c_bf16, ldc, stream));
+}
+
+mxq_status grouped_wgrad_mx(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
+                            const int64_t* group_offsets, int64_t G, int64_t M, int64_t N, int64_t Kt,
+                            uint16_t* c_bf16, float* c_f32, hipStream_t stream) {
+    if (G < 1 || G > 4096 || M < 1 || N < 1 || Kt < 0 || Kt % 32 != 0) return MXQ_ERR_SHAPE;
+    if ((c_bf16 == nullptr) == (c_f32 == nullptr)) return MXQ_ERR_NULL;       // exactly one output
+    if (!group_offsets) return MXQ_ERR_NULL;
+    if (Kt > 0 && (!a_q || !a_s || !b_q || !b_s)) return MXQ_ERR_NULL;
+    if (!al16(a_q) || !al16(a_s) || !al16(b_q) || !al16(b_s) || (c_bf16 && !al16(c_bf16)) ||
+        (c_f32 && !al16(c_f32)) || (reinterpret_cast<uintptr_t>(group_offsets) & 7u))
+        return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_grouped_wgrad(a_q, a_s, b_q, b_s, group_offsets, G, M, N, Kt, c_bf16, c_f32,
+                                                stream));
 }
 
 mxq_status fp8_adam_step(float* master, const uint16_t* grad_bf16, uint8_t* m_q, float* m_scale, uint16_t* v_fp16,

@@ -27,16 +27,24 @@ constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int GTHREADS = 256;
 constexpr int GROUP_M = 8;
 
+// Group modes: none; expert groups of A rows, each against its own B (forward and dgrad of routed experts); expert
+// ranges of K, each with its own output (routed Wgrad: the contraction runs over the expert's token rows).
+enum : int { GM_NONE = 0, GM_ROWS = 1, GM_TOKENS = 2 };
+
 struct GemmArgs {
     const uint8_t* a;
     const uint8_t* b;
-    const uint8_t* sa;   // MX: [rows][K/32]
-    const uint8_t* sb;   // MX: [N][K/32] (per group when grouped)
+    const uint8_t* sa;   // MX: E8M0 per 32 values of K, row stride ldsa
+    const uint8_t* sb;   // MX: likewise for B, row stride ldsb
     const float* pa;     // per-tensor scales
     const float* pb;
-    uint16_t* c;
+    uint16_t* c;         // bf16 output, row stride ldc
+    float* cf;           // token groups only: fp32 output that the result is added to (when c is null)
     int64_t M, N, K, ldc;
-    const int64_t* offsets;   // grouped only: [G+1]
+    int64_t lda, ldb, ldsa, ldsb;      // operand row strides in bytes (qdata) and scale bytes
+    int64_t b_gstride, sb_gstride;     // row groups: distance from one expert's B (and B scales) to the next
+    int64_t c_gstride;                 // token groups: distance from one expert's output to the next
+    const int64_t* offsets;            // grouped only: [G+1]
     int64_t G;
 };
 
@@ -65,7 +73,7 @@ __device__ __forceinline__ v8bf dequant8_bf16(uint2 x, float scale) {
     return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-template <bool MX, int FA, int FB, bool GROUPED, int MF>
+template <bool MX, int FA, int FB, int GM, int MF>
 __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * BK];
     __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * BK];
@@ -75,15 +83,18 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    const int64_t K = g.K;
-    const int64_t kblocks = K / 32;
     const int tiles_n = (int)((g.N + BN - 1) / BN);
 
-    // ------------------------------------------------------------------ tile -> (rows, n0)
+    // ------------------------------------------------------------------ tile -> (rows, n0, K range)
     int64_t m0, m_end, n0;
+    int64_t K = g.K;                                  // this tile's contraction length
+    const uint8_t* Aq = g.a;
+    const uint8_t* As = g.sa;
     const uint8_t* Bq = g.b;
     const uint8_t* Bs = g.sb;
-    if constexpr (GROUPED) {
+    uint16_t* Cb = g.c;
+    float* Cf = g.cf;
+    if constexpr (GM == GM_ROWS) {
         const int64_t bid = blockIdx.x;
         const int64_t t = bid / tiles_n;
         n0 = (bid % tiles_n) * BN;
@@ -99,25 +110,41 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
         if (grp < 0) return;                          // more workgroups than tiles: nothing to do
         m0 = lo;
         m_end = (lo + BM < hi) ? lo + BM : hi;
-        Bq = g.b + grp * g.N * K;
-        Bs = MX ? g.sb + grp * g.N * kblocks : nullptr;
+        Bq = g.b + grp * g.b_gstride;
+        Bs = MX ? g.sb + grp * g.sb_gstride : nullptr;
     } else {
         const int tiles_m = (int)((g.M + BM - 1) / BM);
-        const int bid = blockIdx.x;
+        int64_t bid = blockIdx.x;
+        if constexpr (GM == GM_TOKENS) {
+            // expert-major order: every expert's tiles share its K range; its A and B columns are read once per tile
+            const int64_t per = (int64_t)tiles_m * tiles_n;
+            const int64_t grp = bid / per;
+            bid -= grp * per;
+            int64_t k0 = g.offsets[grp], k1 = g.offsets[grp + 1];
+            k0 = k0 < 0 ? 0 : (k0 > g.K ? g.K : k0);
+            k1 = k1 < k0 ? k0 : (k1 > g.K ? g.K : k1);
+            K = k1 - k0;
+            Aq = g.a + k0;
+            Bq = g.b + k0;
+            As = g.sa + k0 / 32;
+            Bs = g.sb + k0 / 32;
+            if (Cb) Cb += grp * g.c_gstride;
+            if (Cf) Cf += grp * g.c_gstride;
+        }
         const int per_group = GROUP_M * tiles_n;
-        const int first_m = (bid / per_group) * GROUP_M;
+        const int first_m = ((int)bid / per_group) * GROUP_M;
         const int gm = min(GROUP_M, tiles_m - first_m);
-        const int r = bid % per_group;
+        const int r = (int)bid % per_group;
         m0 = (int64_t)(first_m + r % gm) * BM;
         n0 = (int64_t)(r / gm) * BN;
         m_end = (m0 + BM < g.M) ? m0 + BM : g.M;
     }
+    const int64_t kblocks = K / 32;
     const int64_t n_end = (n0 + BN < g.N) ? n0 + BN : g.N;
 
     // ------------------------------------------------------------------ global -> registers (one stage)
     uint4 ra[4], rb[4];
     uint32_t rs = 0x7F7F7F7Fu;
-    const bool scale_dword = (kblocks & 3) == 0;
 
     auto load_stage = [&](int64_t k0) {
 #pragma unroll
@@ -125,23 +152,23 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
             const int row = (tid >> 3) + 32 * j, ch = tid & 7;
             const int64_t kk = k0 + ch * 16;
             const int64_t ar = m0 + row, br = n0 + row;
-            ra[j] = (ar < m_end && kk < K) ? *reinterpret_cast<const uint4*>(g.a + ar * K + kk) : make_uint4(0, 0, 0, 0);
-            rb[j] = (br < n_end && kk < K) ? *reinterpret_cast<const uint4*>(Bq + br * K + kk) : make_uint4(0, 0, 0, 0);
+            ra[j] = (ar < m_end && kk < K) ? *reinterpret_cast<const uint4*>(Aq + ar * g.lda + kk) : make_uint4(0, 0, 0, 0);
+            rb[j] = (br < n_end && kk < K) ? *reinterpret_cast<const uint4*>(Bq + br * g.ldb + kk) : make_uint4(0, 0, 0, 0);
         }
         if constexpr (MX) {
             const int row = tid & 127;
             const bool isA = tid < 128;
             const int64_t rr = isA ? m0 + row : n0 + row;
             const bool ok = isA ? rr < m_end : rr < n_end;
-            const uint8_t* sp = isA ? g.sa : Bs;
+            const uint8_t* sp = isA ? As + rr * g.ldsa : Bs + rr * g.ldsb;    // this row's scales
             const int64_t kb = k0 / 32;
-            if (ok && scale_dword && kb + 4 <= kblocks) {
-                rs = *reinterpret_cast<const uint32_t*>(sp + rr * kblocks + kb);
+            if (ok && kb + 4 <= kblocks && (reinterpret_cast<uintptr_t>(sp + kb) & 3) == 0) {
+                rs = *reinterpret_cast<const uint32_t*>(sp + kb);
             } else {
                 uint32_t v = 0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    uint32_t byte = (ok && kb + i < kblocks) ? sp[rr * kblocks + kb + i] : 127u;
+                    uint32_t byte = (ok && kb + i < kblocks) ? sp[kb + i] : 127u;
                     v |= byte << (8 * i);
                 }
                 rs = v;
@@ -289,10 +316,25 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
     // ------------------------------------------------------------------ epilogue: fp32 -> bf16, store
     float post = 1.0f;
     if constexpr (!MX) post = 1.0f / (g.pa[0] * g.pb[0]);
-    const bool vec_ok = (g.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 7) == 0;
+    const bool vec_ok = (g.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(Cb) & 7) == 0;
+    const bool vec_ok_f = (g.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(Cf) & 15) == 0;
     auto store4 = [&](int64_t m, int64_t n, float v0, float v1, float v2, float v3) {
         if (m >= m_end) return;
         float v[4] = {v0, v1, v2, v3};
+        if constexpr (GM == GM_TOKENS) {
+            if (Cb == nullptr) {                      // add to the fp32 output: one rounding of old + sum
+                float* dst = Cf + m * g.ldc + n;
+                if (vec_ok_f && n + 4 <= n_end) {
+                    const float4 o = *reinterpret_cast<const float4*>(dst);
+                    *reinterpret_cast<float4*>(dst) = make_float4(o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < n_end) dst[e] = dst[e] + v[e];
+                }
+                return;
+            }
+        }
         uint16_t h4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -300,7 +342,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
             if constexpr (!MX) x = x * post;
             h4[e] = __builtin_bit_cast(uint16_t, (__bf16)x);
         }
-        uint16_t* dst = g.c + m * g.ldc + n;
+        uint16_t* dst = Cb + m * g.ldc + n;
         if (vec_ok && n + 4 <= n_end) {
             *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)h4[0] | ((uint32_t)h4[1] << 16),
                                                         (uint32_t)h4[2] | ((uint32_t)h4[3] << 16));
@@ -399,8 +441,9 @@ __device__ __forceinline__ void wait_copies_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
-template <bool MX, int FA, int FB, bool GROUPED, int MF>
+template <bool MX, int FA, int FB, int GM, int MF>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
+    static_assert(GM != GM_TOKENS, "token-grouped contractions run on the register-staged kernel");
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][2 * TB * KS];
     __shared__ __attribute__((aligned(16))) uint8_t sB[2][2 * TB * KS];
     // MX scales: [row][4 words] = 16 blocks = SG stages per row, double-buffered by group.
@@ -412,13 +455,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS copy bases go to M0
     const int wm = wave & 1, wn = wave >> 1;
     const int64_t K = g.K;
-    const int64_t kblocks = K / 32;
     const int tiles_n = (int)((g.N + TB - 1) / TB);
 
     int64_t m0, m_end, n0;
     const uint8_t* Bq = g.b;
     const uint8_t* Bs = g.sb;
-    if constexpr (GROUPED) {
+    if constexpr (GM == GM_ROWS) {
         const int64_t bid = blockIdx.x;
         const int64_t t = bid / tiles_n;
         n0 = (bid % tiles_n) * TB;
@@ -434,8 +476,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         if (grp < 0) return;
         m0 = lo;
         m_end = (lo + TB < hi) ? lo + TB : hi;
-        Bq = g.b + grp * g.N * K;
-        Bs = MX ? g.sb + grp * g.N * kblocks : nullptr;
+        Bq = g.b + grp * g.b_gstride;
+        Bs = MX ? g.sb + grp * g.sb_gstride : nullptr;
     } else {
         const int tiles_m = (int)((g.M + TB - 1) / TB);
         const int T = tiles_m * tiles_n;
@@ -460,16 +502,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     const int brow = (lane & 31) >> 2;                     // row within the 8-row block
     // chunk this lane fetches: its position ^ swz8(row); rows 8 (4c + wave) + brow have swz8 = (2 wave + brow / 4) & 3
     const int bchunk = (lane & 3) ^ ((2 * wave + (brow >> 2)) & 3);
-    const v4i rA = buffer_rsrc(g.a + m0 * K);
-    const v4i rB = buffer_rsrc(Bq + n0 * K);
+    const v4i rA = buffer_rsrc(g.a + m0 * g.lda);
+    const v4i rB = buffer_rsrc(Bq + n0 * g.ldb);
     int a_off[8], b_off[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const int row = 8 * (4 * c + wave) + brow;
         const int ar = (m0 + row < m_end) ? row : (int)(m_end - 1 - m0);
         const int br = (n0 + row < n_end) ? row : (int)(n_end - 1 - n0);
-        a_off[c] = ar * (int)K + KS * half_lane + 16 * bchunk;
-        b_off[c] = br * (int)K + KS * half_lane + 16 * bchunk;
+        a_off[c] = ar * (int)g.lda + KS * half_lane + 16 * bchunk;
+        b_off[c] = br * (int)g.ldb + KS * half_lane + 16 * bchunk;
     }
     v4i rSA = rA, rSB = rB;
     int sa_off = 0, sb_off = 0;
@@ -477,10 +519,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         const int row = 64 * wave + lane;
         const int ar = (m0 + row < m_end) ? row : (int)(m_end - 1 - m0);
         const int br = (n0 + row < n_end) ? row : (int)(n_end - 1 - n0);
-        rSA = buffer_rsrc(g.sa + m0 * kblocks);
-        rSB = buffer_rsrc(Bs + n0 * kblocks);
-        sa_off = ar * (int)kblocks;
-        sb_off = br * (int)kblocks;
+        rSA = buffer_rsrc(g.sa + m0 * g.ldsa);
+        rSB = buffer_rsrc(Bs + n0 * g.ldsb);
+        sa_off = ar * (int)g.ldsa;
+        sb_off = br * (int)g.ldsb;
     }
     const int nk = (int)(K / KS);
     // Region of stage s: A (s / 2) % 2, B ((s + 1) / 2) % 2; its half: A s % 2, B (s + 1) % 2.
@@ -839,21 +881,32 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
 constexpr int64_t kFp8MinK = 12288;
 
 // Large tiles when K is a whole number of 64-byte stages, the output spans at least a few tiles, and a tile's
-// 256 rows of K bytes stay below 2^31 (the kernel's 32-bit buffer offsets). MX operands also need K to be a whole
-// number of scale groups (SG stages, 16 scale bytes per row).
-static bool use_big(const GemmArgs& a, bool mx) {
-    return a.K % (mx ? KS * SG : KS) == 0 && a.M >= 512 && a.N >= 512 && a.K <= (int64_t(1) << 22);
+// 256 rows stay below 2^31 bytes (the kernel's 32-bit buffer offsets). Its copies move 16-byte pieces, so operand row
+// strides (and, for row groups, the distance between experts) are multiples of 16 bytes. MX operands also need K to
+// be a whole number of scale groups (SG stages, 16 scale bytes per row) and 16-byte scale rows.
+static bool use_big(const GemmArgs& a, bool mx, bool grouped) {
+    constexpr int64_t kLim = int64_t(1) << 23;                  // 256 rows x stride < 2^31
+    if (a.K % (mx ? KS * SG : KS) != 0 || a.M < 512 || a.N < 512 || a.K > (int64_t(1) << 22)) return false;
+    if (a.lda % 16 || a.ldb % 16 || a.lda >= kLim || a.ldb >= kLim) return false;
+    if (mx && (a.ldsa % 16 || a.ldsb % 16)) return false;
+    if (grouped && (a.b_gstride % 16 || (mx && a.sb_gstride % 16))) return false;
+    return true;
 }
 
-template <bool MX, int FA, int FB, bool GROUPED>
+template <bool MX, int FA, int FB, int GM>
 static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks_small, unsigned blocks_big, hipStream_t stream) {
-    const bool fp8 = a.K >= kFp8MinK;
-    if (use_big(a, MX)) {
-        if (fp8) hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GROUPED, 1>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
-        else hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GROUPED, 2>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
+    if constexpr (GM == GM_TOKENS) {
+        // Expert K ranges differ, so every expert runs the exact path (which meets the bound at any K).
+        hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GM, 2>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
     } else {
-        if (fp8) hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GROUPED, 1>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
-        else hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GROUPED, 2>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
+        const bool fp8 = a.K >= kFp8MinK;
+        if (use_big(a, MX, GM == GM_ROWS)) {
+            if (fp8) hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GM, 1>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
+            else hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GM, 2>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
+        } else {
+            if (fp8) hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GM, 1>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
+            else hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GM, 2>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
+        }
     }
     return hipGetLastError();
 }
@@ -863,30 +916,45 @@ hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt
                               uint16_t* c, int64_t ldc, hipStream_t stream) {
     GemmArgs a{};
     a.a = a_q; a.b = b_q; a.c = c; a.M = M; a.N = N; a.K = K; a.ldc = ldc;
+    a.lda = K; a.ldb = K; a.ldsa = K / 32; a.ldsb = K / 32;
     if (mx) { a.sa = (const uint8_t*)a_scale; a.sb = (const uint8_t*)b_scale; }
     else { a.pa = (const float*)a_scale; a.pb = (const float*)b_scale; }
     const int64_t small = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int64_t big = ((M + TB - 1) / TB) * ((N + TB - 1) / TB);
     if (small > 0x7FFFFFFF) return hipErrorInvalidValue;
     const unsigned bs = (unsigned)small, bb = (unsigned)big;
-    if (mx) return launch_gemm_t<true, 0, 0, false>(a, bs, bb, stream);
-    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 0, 0, false>(a, bs, bb, stream);
-    if (a_fmt == FMT_E5M2 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 1, 0, false>(a, bs, bb, stream);
-    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E5M2) return launch_gemm_t<false, 0, 1, false>(a, bs, bb, stream);
-    return launch_gemm_t<false, 1, 1, false>(a, bs, bb, stream);
+    if (mx) return launch_gemm_t<true, 0, 0, GM_NONE>(a, bs, bb, stream);
+    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 0, 0, GM_NONE>(a, bs, bb, stream);
+    if (a_fmt == FMT_E5M2 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 1, 0, GM_NONE>(a, bs, bb, stream);
+    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E5M2) return launch_gemm_t<false, 0, 1, GM_NONE>(a, bs, bb, stream);
+    return launch_gemm_t<false, 1, 1, GM_NONE>(a, bs, bb, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* offsets, int64_t G,
-                               int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s, int64_t N, int64_t K,
-                               uint16_t* c, hipStream_t stream) {
+                               int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s, int64_t ldb,
+                               int64_t b_gstride, int64_t ldsb, int64_t sb_gstride, int64_t N, int64_t K,
+                               uint16_t* c, int64_t ldc, hipStream_t stream) {
     GemmArgs a{};
     a.a = a_q; a.sa = a_s; a.b = b_q; a.sb = b_s; a.c = c;
-    a.M = total_rows; a.N = N; a.K = K; a.ldc = N; a.offsets = offsets; a.G = G;
+    a.M = total_rows; a.N = N; a.K = K; a.ldc = ldc; a.offsets = offsets; a.G = G;
+    a.lda = K; a.ldsa = K / 32; a.ldb = ldb; a.ldsb = ldsb; a.b_gstride = b_gstride; a.sb_gstride = sb_gstride;
     // each group adds at most one partial row tile
     const int64_t small = ((total_rows + BM - 1) / BM + G) * ((N + BN - 1) / BN);
     const int64_t big = ((total_rows + TB - 1) / TB + G) * ((N + TB - 1) / TB);
     if (small > 0x7FFFFFFF) return hipErrorInvalidValue;
-    return launch_gemm_t<true, 0, 0, true>(a, (unsigned)small, (unsigned)big, stream);
+    return launch_gemm_t<true, 0, 0, GM_ROWS>(a, (unsigned)small, (unsigned)big, stream);
+}
+
+hipError_t launch_grouped_wgrad(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
+                                const int64_t* offsets, int64_t G, int64_t M, int64_t N, int64_t Kt, uint16_t* c,
+                                float* cf, hipStream_t stream) {
+    GemmArgs a{};
+    a.a = a_q; a.sa = a_s; a.b = b_q; a.sb = b_s; a.c = c; a.cf = cf;
+    a.M = M; a.N = N; a.K = Kt; a.ldc = N; a.offsets = offsets; a.G = G;
+    a.lda = Kt; a.ldb = Kt; a.ldsa = Kt / 32; a.ldsb = Kt / 32; a.c_gstride = M * N;
+    const int64_t blocks = G * ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    return launch_gemm_t<true, 0, 0, GM_TOKENS>(a, (unsigned)blocks, 0u, stream);
 }
 
 }  // namespace mxq

@@ -30,8 +30,22 @@ hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt
                               uint16_t* c, int64_t ldc, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* offsets, int64_t G,
-                               int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s, int64_t N, int64_t K,
-                               uint16_t* c, hipStream_t stream);
+                               int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s, int64_t ldb,
+                               int64_t b_gstride, int64_t ldsb, int64_t sb_gstride, int64_t N, int64_t K,
+                               uint16_t* c, int64_t ldc, hipStream_t stream);
+hipError_t launch_grouped_wgrad(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
+                                const int64_t* offsets, int64_t G, int64_t M, int64_t N, int64_t Kt, uint16_t* c,
+                                float* cf, hipStream_t stream);
+
+hipError_t launch_route_weighted_mx_quantize(const uint16_t* dy, const float* p, int64_t rows, int64_t cols,
+                                             uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, int rule,
+                                             hipStream_t stream);
+hipError_t launch_swiglu_mx_quantize_oriented(const uint16_t* c, int64_t rows, int64_t F, uint8_t* q_row,
+                                              uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, int rule,
+                                              hipStream_t stream);
+hipError_t launch_swiglu_bwd_mx_quantize(const uint16_t* c, const uint16_t* dh, int64_t rows, int64_t F,
+                                         uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, int rule,
+                                         hipStream_t stream);
 
 hipError_t launch_autoscale_cast(const uint16_t* g, int64_t n, int fmt, float* mu, uint8_t* q, float* scale_out,
                                  unsigned long long* overflow, unsigned long long* count, hipStream_t stream);

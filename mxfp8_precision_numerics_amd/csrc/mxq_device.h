@@ -142,4 +142,37 @@ __device__ __forceinline__ uint32_t mx_sat_threshold(uint32_t byte) {
     return expf >= 255u ? 0x7F80u : ((expf << 7) | 0x68u);
 }
 
+// ------------------------------------------------------------------ exponential for SwiGLU and its backward
+// A fixed fp32 sequence: Cody-Waite reduction by k ln2 (k = rint(x log2 e), ln2 split into a 16-bit high part and a
+// low part), the degree-6 Taylor polynomial of e^r in Horner form, exact scaling by 2^k. Every operation is rounded
+// on its own (callers build without contraction), so any implementation following it computes the same value; its
+// error against the true exponential is a few ulp.
+__device__ __forceinline__ float exp_fixed(float x) {
+    if (x != x) return x;
+    if (x > 88.75f) return __uint_as_float(0x7F800000u);
+    if (x < -104.0f) return 0.0f;
+    const float t = x * 1.44269504f;
+    const float k = __builtin_rintf(t);
+    const float a = k * 0.693145751953125f;
+    float r = x - a;
+    const float b = k * 1.42860677e-06f;
+    r = r - b;
+    float p = 1.0f / 720.0f;
+    p = p * r; p = p + 1.0f / 120.0f;
+    p = p * r; p = p + 1.0f / 24.0f;
+    p = p * r; p = p + 1.0f / 6.0f;
+    p = p * r; p = p + 0.5f;
+    p = p * r; p = p + 1.0f;
+    p = p * r; p = p + 1.0f;
+    return __builtin_ldexpf(p, (int)k);
+}
+
+// h = silu(g) u with silu(g) = g / (1 + e^-g): one rounding per operation, in this order.
+__device__ __forceinline__ float swiglu_f32(float g, float u) {
+    const float e = exp_fixed(-g);
+    const float d = 1.0f + e;
+    const float silu = g / d;
+    return silu * u;
+}
+
 }  // namespace mxq

@@ -405,36 +405,8 @@ hipError_t launch_pertensor_quantize_delayed(const uint16_t* x, int64_t rows, in
 // ---------------------------------------------------------------------------------------- fused SwiGLU + MX
 // The routed experts' hidden representation ("OLMo-core MoE, Section 11: MXFP8 Training", Section 11.4.1: a fused
 // SwiGLU-plus-quantization step feeds the down projection without a separate BF16-to-MXFP8 pass). C[rows][2F]
-// holds the gate in columns [0, F) and up in [F, 2F); h = silu(g) * u in fp32, quantized from fp32 in 32-value
-// blocks along each row. exp is the fixed fp32 sequence below (Cody-Waite reduction by k ln2, ln2 in a 16-bit
-// high part and a low part, the degree-6 Taylor polynomial of e^r in Horner form, exact scaling by 2^k), every
-// operation rounded on its own, so that any implementation following it computes the same value.
-__device__ __forceinline__ float exp_fixed(float x) {
-    if (x != x) return x;
-    if (x > 88.75f) return __uint_as_float(0x7F800000u);
-    if (x < -104.0f) return 0.0f;
-    const float t = x * 1.44269504f;
-    const float k = __builtin_rintf(t);
-    const float a = k * 0.693145751953125f;
-    float r = x - a;
-    const float b = k * 1.42860677e-06f;
-    r = r - b;
-    float p = 1.0f / 720.0f;
-    p = p * r; p = p + 1.0f / 120.0f;
-    p = p * r; p = p + 1.0f / 24.0f;
-    p = p * r; p = p + 1.0f / 6.0f;
-    p = p * r; p = p + 0.5f;
-    p = p * r; p = p + 1.0f;
-    p = p * r; p = p + 1.0f;
-    return __builtin_ldexpf(p, (int)k);
-}
-
-__device__ __forceinline__ float swiglu_f32(float g, float u) {
-    const float e = exp_fixed(-g);
-    const float d = 1.0f + e;
-    const float silu = g / d;
-    return silu * u;
-}
+// holds the gate in columns [0, F) and up in [F, 2F); h = silu(g) * u in fp32 (exp_fixed), quantized from fp32 in
+// 32-value blocks along each row.
 
 // One thread per 8 consecutive outputs of a row; the 4 lanes of a quad cover one 32-value block (F % 32 == 0, so
 // quads never straddle rows and the chunk count is a multiple of 4).

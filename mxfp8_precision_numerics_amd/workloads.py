@@ -14,7 +14,8 @@ Workloads (sizes are those of the five configurations; the tests also use smalle
      multiplied by 100 before the bf16 cast.
   4  Grouped expert GEMM: 16384 tokens routed to 8 distinct experts of 64, expert weights proportional to
      rank^-1.1 (Gumbel top-k), each group padded to a multiple of 32 rows (zero rows at the group's end);
-     A_up [rows][2048], A_down [rows][1024], W_up [64][1024][2048], W_down [64][2048][1024], all N(0,1).
+     A_up [rows][2048], A_down [rows][1024], W_up [64][1024][2048], W_down [64][2048][1024], all N(0,1); route
+     weights (backward of the routed MLP) uniform in [0.01, 1), 0 on padding rows.
   5  Adam step over n parameters: theta fp32 N(0,0.02), gradient bf16 N(0,1e-3) for step t drawn with index t.
   6  FP8 gradient all-reduce pieces: per rank r of 8, the weight gradient of workload 2's W (36864 x 12288 values),
      N(0, 1e-3 * 2^(r/4)) with round(2e-5 n) positions multiplied by 1000 before the bf16 cast (step t: index
@@ -42,6 +43,11 @@ def normal_f32(shape, std: float, workload: int, k: int, device="cpu") -> torch.
     if std != 1.0:
         x.mul_(std)
     return x
+
+
+def uniform_f32(shape, lo: float, hi: float, workload: int, k: int, device="cpu") -> torch.Tensor:
+    g = _gen(workload, k, device)
+    return torch.rand(tuple(shape), generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo
 
 
 def normal_bf16(shape, std: float, workload: int, k: int, device="cpu") -> torch.Tensor:
@@ -83,6 +89,12 @@ def zipf_routing(tokens: int = 16384, experts: int = 64, topk: int = 8, alpha: f
     offsets = np.zeros(experts + 1, np.int64)
     offsets[1:] = np.cumsum(padded)
     return counts, padded, offsets
+
+
+def route_weights(counts, padded, offsets, workload: int = 4, k: int = 5, device="cpu") -> torch.Tensor:
+    """One fp32 route weight per routed row (expert order), uniform in [0.01, 1); padding rows get 0."""
+    p = uniform_f32((int(offsets[-1]),), 0.01, 1.0, workload, k, device)
+    return zero_padding_rows(p, counts, padded, offsets)
 
 
 def zero_padding_rows(a: torch.Tensor, counts, padded, offsets) -> torch.Tensor:

@@ -178,3 +178,53 @@ def test_probe_validation():
     assert c(None, P, 32, 4, None) == 1
     assert c(MIS, P, 32, 4, None) == 3
     assert c(None, None, 0, 4, None) == 0            # empty
+
+
+def test_routed_backward_validation():
+    lib = _lib.load()
+    for f in (lib.route_weighted_mx_quantize, lib.swiglu_backward_mx_quantize):
+        assert f(P, P, 64, 64, None, None, None, None, 0, None) == 1          # no orientation
+        assert f(P, P, 64, 64, P, None, None, None, 0, None) == 1             # q_row without s_row
+        assert f(P, P, 64, 48, P, P, None, None, 0, None) == 2                # cols / F % 32
+        assert f(P, P, 48, 64, P, P, None, None, 0, None) == 2                # rows % 32, also for the row orientation
+        assert f(P, P, 64, 64, P, P, P, P, 5, None) == 4
+        assert f(P, None, 64, 64, P, P, P, P, 0, None) == 1
+        assert f(MIS, P, 64, 64, P, P, P, P, 0, None) == 3
+        assert f(P, P, 64, 64, P, P, MIS, P, 0, None) == 3
+        assert f(None, None, 0, 64, P, P, P, P, 0, None) == 0                 # empty: nothing enqueued
+    assert lib.route_weighted_mx_quantize(P, P + 2, 64, 64, P, P, P, P, 0, None) == 3   # weights 4-byte aligned
+    s = lib.swiglu_mx_quantize_oriented
+    assert s(P, 64, 64, None, None, None, None, 0, None) == 1
+    assert s(P, 64, 48, P, P, P, P, 0, None) == 2
+    assert s(P, 48, 64, P, P, P, P, 0, None) == 2
+    assert s(P, 64, 64, P, P, P, P, 2, None) == 4
+    assert s(None, 64, 64, P, P, P, P, 0, None) == 1
+    assert s(MIS, 64, 64, P, P, P, P, 0, None) == 3
+    assert s(None, 0, 64, P, P, P, P, 0, None) == 0
+
+
+def test_grouped_strided_and_wgrad_validation():
+    lib = _lib.load()
+    g = lib.grouped_scaled_gemm_strided
+    #        a_q a_s off G  rows b_q b_s ldb  bgs  ldbs bsgs N   K   c  ldc
+    assert g(P, P, None, 4, 128, P, P, 256, 64, 8, 2, 64, 64, P, 64, None) == 1
+    assert g(P, P, P, 4, 128, P, P, 32, 64, 8, 2, 64, 64, P, 64, None) == 2             # ldb < K
+    assert g(P, P, P, 4, 128, P, P, 256, 64, 1, 2, 64, 64, P, 64, None) == 2            # ldbs < K/32
+    assert g(P, P, P, 4, 128, P, P, 256, 64, 8, 2, 64, 64, P, 32, None) == 2            # ldc < N
+    assert g(P, P, P, 4, 128, P, P, 256, -64, 8, 2, 64, 64, P, 64, None) == 2           # negative group stride
+    assert g(P, P, P, 4, 128, P, P, 264, 64, 8, 2, 64, 64, P, 64, None) == 3            # ldb % 16
+    assert g(P, P, P, 4, 128, P, P, 256, 72, 8, 2, 64, 64, P, 64, None) == 3            # group stride % 16
+    assert g(P, P, P, 4, 128, P, P, 256, 64, 8, 2, 64, 40, P, 64, None) == 2            # K % 32
+    assert g(P, P, P + 4, 4, 128, P, P, 256, 64, 8, 2, 64, 64, P, 64, None) == 3
+    assert g(P, P, P, 4, 0, P, P, 256, 64, 8, 2, 64, 64, P, 64, None) == 0              # no rows: nothing enqueued
+    w = lib.grouped_wgrad_mx
+    #        a_q a_s b_q b_s off G  M   N   Kt   c     cf
+    assert w(P, P, P, P, P, 4, 64, 64, 128, None, None, None) == 1                      # no output
+    assert w(P, P, P, P, P, 4, 64, 64, 128, P, P, None) == 1                            # two outputs
+    assert w(P, P, P, P, None, 4, 64, 64, 128, P, None, None) == 1
+    assert w(P, P, P, P, P, 0, 64, 64, 128, P, None, None) == 2
+    assert w(P, P, P, P, P, 4, 0, 64, 128, P, None, None) == 2
+    assert w(P, P, P, P, P, 4, 64, 64, 48, P, None, None) == 2                          # Kt % 32
+    assert w(None, P, P, P, P, 4, 64, 64, 128, P, None, None) == 1
+    assert w(MIS, P, P, P, P, 4, 64, 64, 128, P, None, None) == 3
+    assert w(P, P, P, P, P + 4, 4, 64, 64, 128, P, None, None) == 3
