@@ -20,6 +20,12 @@ One step is one pass over every row of the hot path, on seeded synthetic inputs 
   grad_cast     the auto-scaled FP8 cast of the weight gradient dW (36864 x 12288 bf16 -> E4M3, overflow count, mu
                 update): the part of the FP8 all-reduce that runs before the scales are gathered
   grad_requant  the re-quantize of those codes to the shared scale (the min over 8 gathered scales)
+  moe_fwd_train the routed MLP's forward as training runs it: the activation quantized in both orientations, the
+                up/gate grouped GEMM, SwiGLU + MX quantize saving h in both orientations, the down grouped GEMM
+  moe_bwd       its backward (seeded output gradient N(0,1e-3), route weights uniform): route weighting fused with
+                the gradient's MX quantize (both orientations), down dgrad over W_down's column cache, SwiGLU
+                backward fused with the MX quantize of (d_gate | d_up), up/gate dgrad over W_gu's column cache, and
+                the two routed Wgrad contractions over each expert's tokens into fp32 gradient sinks
 The headline value is the MXFP8 linear layer's GEMM FLOPs (11.13 TFLOP) divided by the device time of its quantize
 and GEMM launches ("MXFP8 GEMM TFLOP/s incl. quantize"). Device times come from events on the stream the kernels
 run on; the JSON line also carries every part's rate, the MX GEMM's roofline, the ceilings this part attains
@@ -114,10 +120,24 @@ def main():
     # routed MLP with SwiGLU: gate|up expert weights [G][2 d_ff][d_model] (seeded N(0,1), quantized once), the fused
     # SwiGLU + MX quantize between the up/gate and down grouped GEMMs
     w_gu = workloads.normal_bf16((G * 2 * d_ff, d_model), 1.0, 4, 5, dev)
-    qwgu = mxq.mx_quantize(w_gu, colwise=False)
+    qwgu = mxq.mx_quantize(w_gu, colwise=True)             # row cache (forward) and column cache (dgrad)
     del w_gu
+    qwd_c = mxq.mx_quantize(wl4["w_down"].reshape(G * d_model, d_ff), rowwise=False, colwise=True)
     C_gu = torch.empty((rows4, 2 * d_ff), dtype=torch.bfloat16, device=dev)
     mx_h = mxq.MXTensor(u8(rows4, d_ff), u8(rows4, d_ff // 32), None, None)
+    # routed MLP training forward (saved operands in both orientations) and backward
+    mx_x2 = mxq.MXTensor(u8(rows4, d_model), u8(rows4, d_model // 32), u8(d_model, rows4), u8(d_model, rows4 // 32))
+    mx_h2 = mxq.MXTensor(u8(rows4, d_ff), u8(rows4, d_ff // 32), u8(d_ff, rows4), u8(d_ff, rows4 // 32))
+    dy4 = workloads.zero_padding_rows(workloads.normal_bf16((rows4, d_model), 1e-3, 4, 6, dev), wl4["counts"],
+                                      wl4["padded"], wl4["offsets"])
+    p4 = workloads.route_weights(wl4["counts"], wl4["padded"], wl4["offsets"], device=dev)
+    mx_dyw = mxq.MXTensor(u8(rows4, d_model), u8(rows4, d_model // 32), u8(d_model, rows4), u8(d_model, rows4 // 32))
+    mx_dc = mxq.MXTensor(u8(rows4, 2 * d_ff), u8(rows4, 2 * d_ff // 32), u8(2 * d_ff, rows4),
+                         u8(2 * d_ff, rows4 // 32))
+    dh4 = torch.empty((rows4, d_ff), dtype=torch.bfloat16, device=dev)
+    dx4 = torch.empty((rows4, d_model), dtype=torch.bfloat16, device=dev)
+    sink_wd = torch.zeros((G, d_model, d_ff), dtype=torch.float32, device=dev)
+    sink_wgu = torch.zeros((G, 2 * d_ff, d_model), dtype=torch.float32, device=dev)
     hp = mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.0, 2)
     # delayed scaling: amax histories (16 slots) seeded with one current-scaling call each
     hists, hpos = {}, {}
@@ -155,7 +175,8 @@ def main():
     parts = ["mx_quant_XWdY", "mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "pt_quant", "pt_gemms", "mx_quant_act",
              "grouped_q_up", "grouped_gemm_up", "grouped_q_down", "grouped_gemm_down", "adam", "small",
              "pt_quant_delayed", "adam_delayed", "wcache_fused", "wcache_unfused", "moe_swiglu_mlp", "swiglu_quant",
-             "grad_cast", "grad_requant"]
+             "grad_cast", "grad_requant", "moe_fwd_train", "bwd_rw_quant", "bwd_dgrad_down", "bwd_swiglu_quant",
+             "bwd_dgrad_up", "bwd_wgrad_down", "bwd_wgrad_up"]
     NEV = len(parts) + 1
 
     def step(ev):
@@ -222,6 +243,29 @@ def main():
         gathered[1:] = others
         mxq.fp8_requantize_shared(gc.q, mxq.E4M3, gc.scale, gathered, mxq.E4M3, out=q_req)
         ev[21].record(stream)
+        mxq.mx_quantize(wl4["a_up"], out=mx_x2)
+        mxq.grouped_scaled_gemm(mx_x2.q_row, mx_x2.s_row, off4, qwgu.q_row.view(G, 2 * d_ff, d_model),
+                                qwgu.s_row.view(G, 2 * d_ff, d_model // 32), out=C_gu)
+        mxq.swiglu_mx_quantize_oriented(C_gu, out=mx_h2)
+        mxq.grouped_scaled_gemm(mx_h2.q_row, mx_h2.s_row, off4, qwd.q_row.view(G, d_model, d_ff),
+                                qwd.s_row.view(G, d_model, d_ff // 32), out=C_dn)
+        ev[22].record(stream)
+        mxq.route_weighted_mx_quantize(dy4, p4, out=mx_dyw)
+        ev[23].record(stream)
+        mxq.grouped_scaled_gemm_strided(mx_dyw.q_row, mx_dyw.s_row, off4, qwd_c.q_col, qwd_c.s_col, G, d_ff, d_model,
+                                        ldb=G * d_model, b_group_stride=d_model, ldbs=G * d_model // 32,
+                                        bs_group_stride=d_model // 32, out=dh4)
+        ev[24].record(stream)
+        mxq.swiglu_backward_mx_quantize(C_gu, dh4, out=mx_dc)
+        ev[25].record(stream)
+        mxq.grouped_scaled_gemm_strided(mx_dc.q_row, mx_dc.s_row, off4, qwgu.q_col, qwgu.s_col, G, d_model,
+                                        2 * d_ff, ldb=G * 2 * d_ff, b_group_stride=2 * d_ff,
+                                        ldbs=G * 2 * d_ff // 32, bs_group_stride=2 * d_ff // 32, out=dx4)
+        ev[26].record(stream)
+        mxq.grouped_wgrad_mx(mx_dyw.q_col, mx_dyw.s_col, mx_h2.q_col, mx_h2.s_col, off4, accumulate=sink_wd)
+        ev[27].record(stream)
+        mxq.grouped_wgrad_mx(mx_dc.q_col, mx_dc.s_col, mx_x2.q_col, mx_x2.s_col, off4, accumulate=sink_wgu)
+        ev[28].record(stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -241,6 +285,9 @@ def main():
     step_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][NEV - 1]) for s in range(args.steps)]))
     ms["grouped"] = sum(ms[p] for p in ("grouped_q_up", "grouped_gemm_up", "grouped_q_down", "grouped_gemm_down"))
     grouped_gemm_ms = ms["grouped_gemm_up"] + ms["grouped_gemm_down"]
+    bwd_parts = ("bwd_rw_quant", "bwd_dgrad_down", "bwd_swiglu_quant", "bwd_dgrad_up", "bwd_wgrad_down",
+                 "bwd_wgrad_up")
+    ms["moe_bwd"] = sum(ms[p] for p in bwd_parts)
     log("per-part ms:", json.dumps({k: round(v, 4) for k, v in ms.items()}))
 
     # ------------------------------------------------------------------ rates
@@ -281,6 +328,14 @@ def main():
         "swiglu_quant_gbs": rows4 * (4 * d_ff + d_ff + d_ff // 32) / (ms["swiglu_quant"] * 1e-3) / 1e9,
         "grad_cast_gbs": 3 * nw / (ms["grad_cast"] * 1e-3) / 1e9,
         "grad_requant_gbs": 2 * nw / (ms["grad_requant"] * 1e-3) / 1e9,
+        "moe_fwd_train_tflops_incl_quant": 2.0 * rows_valid * 3 * d_ff * d_model / (ms["moe_fwd_train"] * 1e-3) / 1e12,
+        "moe_bwd_tflops_incl_quant": 2.0 * rows_valid * 6 * d_ff * d_model / (ms["moe_bwd"] * 1e-3) / 1e12,
+        "bwd_rw_quant_gbs": rows4 * (d_model * (2 + 2 * 33 / 32) + 4) / (ms["bwd_rw_quant"] * 1e-3) / 1e9,
+        "bwd_swiglu_quant_gbs": rows4 * d_ff * (4 + 2 + 2 * 2 * 33 / 32) / (ms["bwd_swiglu_quant"] * 1e-3) / 1e9,
+        "bwd_dgrad_down_tflops": 2.0 * rows_valid * d_ff * d_model / (ms["bwd_dgrad_down"] * 1e-3) / 1e12,
+        "bwd_dgrad_up_tflops": 2.0 * rows_valid * 2 * d_ff * d_model / (ms["bwd_dgrad_up"] * 1e-3) / 1e12,
+        "bwd_wgrad_down_tflops": 2.0 * rows_valid * d_ff * d_model / (ms["bwd_wgrad_down"] * 1e-3) / 1e12,
+        "bwd_wgrad_up_tflops": 2.0 * rows_valid * 2 * d_ff * d_model / (ms["bwd_wgrad_up"] * 1e-3) / 1e12,
     }
     for k, v in rate.items():
         rate[k] = round(v, 3)
