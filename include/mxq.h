@@ -249,7 +249,8 @@ mxq_status grouped_scaled_gemm_strided(const uint8_t* a_q, const uint8_t* a_s, c
  *   For each expert g: C_g[m][n] = sum over k in [offsets[g], offsets[g+1]) of a_hat[m][k] b_hat[n][k] (fp32
  *   accumulation of exactly dequantized operands: equal to dequantizing to BF16 and running a BF16 grouped GEMM).
  *   Output, exactly one of: c_bf16[G][M][N] (bf16 RNE of C_g; an empty expert gives zeros), or
- *   c_f32[G][M][N] (in/out: c_f32 += C_g, one fp32 rounding per element; the high-precision gradient sink).
+ *   c_f32[G][M][N] (in/out: c_f32 += C_g, one fp32 rounding per element; the FP32 gradient buffer that Wgrad
+ *   outputs accumulate into, [OLMO11] Sections 11.3.4 and 11.4).
  * Requires M, N >= 1, Kt >= 0 and Kt % 32 == 0, 1 <= G <= 4096. As for grouped_scaled_gemm, the offsets are read on
  * the device only; offsets outside [0, Kt] are clamped.
  */
