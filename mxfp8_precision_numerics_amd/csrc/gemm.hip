@@ -406,11 +406,13 @@ __device__ __forceinline__ int swz8(int row) { return (row >> 2) & 3; }
 // Raw buffer resource (base, stride 0, 2^31 - 1 bytes, raw untyped access) for a workgroup-uniform address. The
 // address is moved to scalar registers explicitly: values derived from the tile index are computed with vector
 // instructions, and the descriptor must live in scalar registers.
-__device__ __forceinline__ v4i buffer_rsrc(const void* p) {
+// With `records` set, accesses at or past that many bytes from the base are out of range: loads return zero and
+// nothing outside the buffer is touched.
+__device__ __forceinline__ v4i buffer_rsrc(const void* p, uint32_t records = 0x7FFFFFFFu) {
     const uint64_t a = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    return v4i{(int)lo, (int)(hi & 0xFFFFu), 0x7FFFFFFF, 0x00020000};
+    return v4i{(int)lo, (int)(hi & 0xFFFFu), (int)__builtin_amdgcn_readfirstlane(records), 0x00020000};
 }
 
 // LDS offset (the low 32 bits of a shared-aperture address) of an LDS location, made wave-uniform.
@@ -443,24 +445,57 @@ __device__ __forceinline__ void wait_copies_barrier() {
 
 template <bool MX, int FA, int FB, int GM, int MF>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
-    static_assert(GM != GM_TOKENS, "token-grouped contractions run on the register-staged kernel");
+    // Token groups: every expert has its own K range (a multiple of 32, not of the 64-byte stage) and scale rows of
+    // any byte alignment; they run the exact path only.
+    constexpr bool TOK = GM == GM_TOKENS;
+    static_assert(!TOK || (MX && MF == 2), "token-grouped contractions are MX on the exact path");
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][2 * TB * KS];
     __shared__ __attribute__((aligned(16))) uint8_t sB[2][2 * TB * KS];
-    // MX scales: [row][4 words] = 16 blocks = SG stages per row, double-buffered by group.
-    __shared__ __attribute__((aligned(16))) uint32_t sSA[2][MX ? TB * 4 : 1];
-    __shared__ __attribute__((aligned(16))) uint32_t sSB[2][MX ? TB * 4 : 1];
+    // MX scales, double-buffered by group of SG stages (16 blocks per row). Rows: [row][4 words]. Token groups:
+    // [word][row], 5 words from the 4-byte-aligned address at or below the row's first scale byte of the group.
+    constexpr int SCW = TOK ? 5 : 4;
+    __shared__ __attribute__((aligned(16))) uint32_t sSA[2][MX ? TB * SCW : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t sSB[2][MX ? TB * SCW : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS copy bases go to M0
     const int wm = wave & 1, wn = wave >> 1;
-    const int64_t K = g.K;
+    int64_t K = g.K;                                   // this tile's contraction length
     const int tiles_n = (int)((g.N + TB - 1) / TB);
 
     int64_t m0, m_end, n0;
+    int64_t k0 = 0;                                    // token groups: first column of the expert's K range
+    const uint8_t* Aq = g.a;
     const uint8_t* Bq = g.b;
     const uint8_t* Bs = g.sb;
-    if constexpr (GM == GM_ROWS) {
+    uint16_t* Cb = g.c;
+    float* Cf = g.cf;
+    if constexpr (TOK) {
+        // Expert-major order in workgroup order (no XCD remap: consecutive workgroups go to different XCDs, so every
+        // XCD shares the large experts at the front), grouped by GROUP_M2 row tiles of one expert.
+        const int tiles_m = (int)((g.M + TB - 1) / TB);
+        const int tiles_mm = (int)g.G * tiles_m;
+        const int v = blockIdx.x;
+        const int per_group = GROUP_M2 * tiles_n;
+        const int first_m = (v / per_group) * GROUP_M2;
+        const int gm = min(GROUP_M2, tiles_mm - first_m);
+        const int r = v % per_group;
+        const int mt = first_m + r % gm;
+        const int64_t grp = mt / tiles_m;
+        m0 = (int64_t)(mt - grp * tiles_m) * TB;
+        n0 = (int64_t)(r / gm) * TB;
+        m_end = (m0 + TB < g.M) ? m0 + TB : g.M;
+        int64_t a0 = g.offsets[grp], a1 = g.offsets[grp + 1];
+        a0 = a0 < 0 ? 0 : (a0 > g.K ? g.K : a0);
+        a1 = a1 < a0 ? a0 : (a1 > g.K ? g.K : a1);
+        k0 = a0;
+        K = a1 - a0;
+        Aq = g.a + k0;
+        Bq = g.b + k0;
+        if (Cb) Cb += grp * g.c_gstride;
+        if (Cf) Cf += grp * g.c_gstride;
+    } else if constexpr (GM == GM_ROWS) {
         const int64_t bid = blockIdx.x;
         const int64_t t = bid / tiles_n;
         n0 = (bid % tiles_n) * TB;
@@ -502,8 +537,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     const int brow = (lane & 31) >> 2;                     // row within the 8-row block
     // chunk this lane fetches: its position ^ swz8(row); rows 8 (4c + wave) + brow have swz8 = (2 wave + brow / 4) & 3
     const int bchunk = (lane & 3) ^ ((2 * wave + (brow >> 2)) & 3);
-    const v4i rA = buffer_rsrc(g.a + m0 * g.lda);
-    const v4i rB = buffer_rsrc(Bq + n0 * g.ldb);
+    // Token groups: a half-filled last stage reads up to 32 bytes past the expert's range; the record counts end
+    // the resources at the operands' last byte, so such reads past the matrix return zero (and are never used).
+    const v4i rA = TOK ? buffer_rsrc(Aq + m0 * g.lda, (uint32_t)((g.M - m0) * g.lda - k0))
+                       : buffer_rsrc(Aq + m0 * g.lda);
+    const v4i rB = TOK ? buffer_rsrc(Bq + n0 * g.ldb, (uint32_t)((g.N - n0) * g.ldb - k0))
+                       : buffer_rsrc(Bq + n0 * g.ldb);
     int a_off[8], b_off[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -515,7 +554,18 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     }
     v4i rSA = rA, rSB = rB;
     int sa_off = 0, sb_off = 0;
-    if constexpr (MX) {
+    if constexpr (TOK) {
+        // Scale bytes of row r for the expert start at byte r * lds + k0 / 32 of the grid (any alignment). Each lane
+        // copies 4-byte words from the aligned address at or below it; a word holding a byte of the grid lies in
+        // the grid's last page, and words past the grid's rounded-up end read as zero.
+        const int row = 64 * wave + lane;
+        const int ar = (m0 + row < m_end) ? row : (int)(m_end - 1 - m0);
+        const int br = (n0 + row < n_end) ? row : (int)(n_end - 1 - n0);
+        rSA = buffer_rsrc(g.sa, (uint32_t)((g.M * g.ldsa + 3) & ~int64_t(3)));
+        rSB = buffer_rsrc(g.sb, (uint32_t)((g.N * g.ldsb + 3) & ~int64_t(3)));
+        sa_off = (int)(((m0 + ar) * g.ldsa + k0 / 32) & ~int64_t(3));
+        sb_off = (int)(((n0 + br) * g.ldsb + k0 / 32) & ~int64_t(3));
+    } else if constexpr (MX) {
         const int row = 64 * wave + lane;
         const int ar = (m0 + row < m_end) ? row : (int)(m_end - 1 - m0);
         const int br = (n0 + row < n_end) ? row : (int)(n_end - 1 - n0);
@@ -524,7 +574,26 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         sa_off = ar * (int)g.ldsa;
         sb_off = br * (int)g.ldsb;
     }
-    const int nk = (int)(K / KS);
+    // Token groups: a K range of 32 mod 64 ends in a half stage, of which only the first 32-value block is summed.
+    const int nk = TOK ? (int)((K + KS - 1) / KS) : (int)(K / KS);
+    const bool half_last = TOK && (K % KS) != 0;
+    // Byte shift of the fragment rows' scale words (token groups): the low two bits of each row's first scale byte,
+    // two bits per row, A rows j at bits 2j, B rows i at bits 8 + 2i (v_alignbyte reads only the low two bits).
+    uint32_t shifts = 0;
+    if constexpr (TOK) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = wm * 128 + 32 * j + (lane & 31);
+            const int ar = (m0 + row < m_end) ? row : (int)(m_end - 1 - m0);
+            shifts |= (uint32_t)(((m0 + ar) * g.ldsa + k0 / 32) & 3) << (2 * j);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = wn * 128 + 32 * i + (lane & 31);
+            const int br = (n0 + row < n_end) ? row : (int)(n_end - 1 - n0);
+            shifts |= (uint32_t)(((n0 + br) * g.ldsb + k0 / 32) & 3) << (8 + 2 * i);
+        }
+    }
     // Region of stage s: A (s / 2) % 2, B ((s + 1) / 2) % 2; its half: A s % 2, B (s + 1) % 2.
     // Copy instruction c of the pair of operand A (IS_A) or B whose first stage is s0, into region `region`. When the
     // pair's second stage lies past K only the first-stage lanes copy.
@@ -539,9 +608,18 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     };
     auto copy_scales = [&](int s) {                       // the scale group whose first stage is s
         const int gb = (s / SG) & 1;
-        dma_to_lds<16>(rSA, lds_offset(&sSA[gb][256 * wave]), sa_off, s * KS / 32);
-        dma_to_lds<16>(rSB, lds_offset(&sSB[gb][256 * wave]), sb_off, s * KS / 32);
+        if constexpr (TOK) {
+#pragma unroll
+            for (int w = 0; w < 5; ++w) {
+                dma_to_lds<4>(rSA, lds_offset(&sSA[gb][TB * w + 64 * wave]), sa_off, s * KS / 32 + 4 * w);
+                dma_to_lds<4>(rSB, lds_offset(&sSB[gb][TB * w + 64 * wave]), sb_off, s * KS / 32 + 4 * w);
+            }
+        } else {
+            dma_to_lds<16>(rSA, lds_offset(&sSA[gb][256 * wave]), sa_off, s * KS / 32);
+            dma_to_lds<16>(rSB, lds_offset(&sSB[gb][256 * wave]), sb_off, s * KS / 32);
+        }
     };
+    constexpr int kScaleCopies = TOK ? 10 : 2;
     // Copy instruction c of trip t: the pair starting at stage t + 3 (A on odd t, B on even t), if any. PH = t % 4 when
     // known at compile time (then the pair exists in full), else -1.
     auto trip_copy = [&](auto ph_c, int t, int c) {
@@ -566,7 +644,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     // Wait at the end of trip t: only the copies issued in trip t may remain in flight.
     auto trip_wait = [&](int t, bool scales) {
         if (t + 3 >= nk) wait_copies_barrier<0>();
-        else if (scales) wait_copies_barrier<10>();
+        else if (scales) wait_copies_barrier<8 + kScaleCopies>();
         else wait_copies_barrier<8>();
     };
 
@@ -596,7 +674,22 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     };
     auto read_scales = [&](int st, uint32_t* sa, uint32_t* sb) {
-        if constexpr (MX) {
+        if constexpr (TOK) {
+            // word w of the group = bytes 4w .. 4w+3 after the row's shift
+            const uint32_t* cSA = sSA[(st / SG) & 1];
+            const uint32_t* cSB = sSB[(st / SG) & 1];
+            const int w = (st % SG) >> 1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = wm * 128 + 32 * j + fr;
+                sa[j] = __builtin_amdgcn_alignbyte(cSA[TB * (w + 1) + row], cSA[TB * w + row], shifts >> (2 * j));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = wn * 128 + 32 * i + fr;
+                sb[i] = __builtin_amdgcn_alignbyte(cSB[TB * (w + 1) + row], cSB[TB * w + row], shifts >> (8 + 2 * i));
+            }
+        } else if constexpr (MX) {
             const uint32_t* cSA = sSA[(st / SG) & 1];
             const uint32_t* cSB = sSB[(st / SG) & 1];
             const int w = (st % SG) >> 1;
@@ -690,6 +783,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     };
 
     // ------------------------------------------------------------------ prologue: stages 0 .. 3
+    // (token groups: an expert without tokens skips straight to its zero output)
+    if (!TOK || nk > 0) {
     if constexpr (MX) copy_scales(0);
 #pragma unroll
     for (int c = 0; c < 8; ++c) copy_pair(std::true_type{}, std::false_type{}, 0, 0, c);       // A (0, 1)
@@ -794,7 +889,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         }
         pin_accumulators();
         if constexpr (PH >= 0) {
-            if (scales) wait_copies_barrier<10>();
+            if (scales) wait_copies_barrier<8 + kScaleCopies>();
             else wait_copies_barrier<8>();
         } else {
             trip_wait(kt, scales);
@@ -821,7 +916,27 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     }
     // Last stage (kt == nk - 1): its fragments are in registers and no copy is outstanding.
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (TOK) {
+        // A half last stage sums only its first block: the second block's codes become 0 and its scale bytes 2^0,
+        // so those k-steps add exact zeros whatever lies past the expert's range (selects, not branches, so the
+        // accumulators keep one path).
+        const uint32_t keep = half_last ? 0u : 0xFFFFFFFFu;
+        const int sh1 = 8 * (2 * (kt & 1) + 1);
+        const uint32_t smask = half_last ? (0xFFu << sh1) : 0u;
+        const uint32_t sset = half_last ? (127u << sh1) : 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int e = 4; e < 8; ++e) {
+                fa[j][e] = (int)((uint32_t)fa[j][e] & keep);
+                fb[j][e] = (int)((uint32_t)fb[j][e] & keep);
+            }
+            sa[j] = (sa[j] & ~smask) | sset;
+            sb[j] = (sb[j] & ~smask) | sset;
+        }
+    }
     mma_stage(dyn{}, kt, fa, fb, sa, sb);
+    }
 
     // ------------------------------------------------------------------ epilogue
     // Lane l holds, for output row m (l % 32), the columns 8q + 4g + 0..3 (g = l / 32) of each 32-column block in
@@ -830,7 +945,68 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     // 16p + 8g .. 16p + 8g + 7, stored as one 16-byte write.
     float post = 1.0f;
     if constexpr (!MX) post = 1.0f / (g.pa[0] * g.pb[0]);
-    const bool vec_ok = (g.ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 15) == 0;
+    if constexpr (TOK) {
+        if (Cb == nullptr) {
+            // fp32 gradient sink: c += sum, one rounding per element; lane l adds its 4 consecutive n of row m
+            const bool vec_f = (g.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(Cf) & 15) == 0;
+            if (vec_f && m_end - m0 == TB && n_end - n0 == TB) {
+                // whole tile, one column block i at a time: block i + 1's 16 loads are in flight while block i is
+                // added and stored
+                auto sink_ptr = [&](int i, int j, int q) {
+                    return Cf + (m0 + wm * 128 + j * 32 + fr) * g.ldc + n0 + wn * 128 + i * 32 + 8 * q + 4 * fg;
+                };
+                float4 o[2][4][4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) o[0][j][q] = *reinterpret_cast<const float4*>(sink_ptr(0, j, q));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (i + 1 < 4) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                o[(i + 1) & 1][j][q] = *reinterpret_cast<const float4*>(sink_ptr(i + 1, j, q));
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float4 v = o[i & 1][j][q];
+                            *reinterpret_cast<float4*>(sink_ptr(i, j, q)) =
+                                make_float4(v.x + acc16[i][j][4 * q], v.y + acc16[i][j][4 * q + 1],
+                                            v.z + acc16[i][j][4 * q + 2], v.w + acc16[i][j][4 * q + 3]);
+                        }
+                }
+                return;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t m = m0 + wm * 128 + j * 32 + fr;
+                    if (m >= m_end) continue;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int64_t n = n0 + wn * 128 + i * 32 + 8 * q + 4 * fg;
+                        float* dst = Cf + m * g.ldc + n;
+                        const float v[4] = {acc16[i][j][4 * q], acc16[i][j][4 * q + 1], acc16[i][j][4 * q + 2],
+                                            acc16[i][j][4 * q + 3]};
+                        if (vec_f && n + 4 <= n_end) {
+                            const float4 o = *reinterpret_cast<const float4*>(dst);
+                            *reinterpret_cast<float4*>(dst) = make_float4(o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < n_end) dst[e] = dst[e] + v[e];
+                        }
+                    }
+                }
+            return;
+        }
+    }
+    const bool vec_ok = (g.ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(Cb) & 15) == 0;
     auto pack2 = [&](float x0, float x1) {
         if constexpr (!MX) { x0 = x0 * post; x1 = x1 * post; }
         return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x0) |
@@ -858,7 +1034,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
 #pragma unroll
             for (int pq = 0; pq < 2; ++pq) {
                 const int64_t n = n0 + wn * 128 + i * 32 + 16 * pq + 8 * fg;
-                uint16_t* dst = g.c + m * g.ldc + n;
+                uint16_t* dst = Cb + m * g.ldc + n;
                 const uint32_t v4[4] = {w[2 * pq][0], w[2 * pq][1], w[2 * pq + 1][0], w[2 * pq + 1][1]};
                 if (vec_ok && n + 8 <= n_end) {
                     *reinterpret_cast<uint4*>(dst) = make_uint4(v4[0], v4[1], v4[2], v4[3]);
@@ -893,11 +1069,21 @@ static bool use_big(const GemmArgs& a, bool mx, bool grouped) {
     return true;
 }
 
+// Token groups on the large tiles: at least one whole tile each way, and every operand and scale byte offset of a
+// tile below 2^31 (32-bit buffer offsets and record counts).
+static bool use_big_tokens(const GemmArgs& a) {
+    constexpr int64_t kLim = int64_t(1) << 31;
+    return a.M >= TB && a.N >= TB && a.lda % 16 == 0 && a.ldb % 16 == 0 && a.M * a.lda < kLim && a.N * a.ldb < kLim;
+}
+
 template <bool MX, int FA, int FB, int GM>
 static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks_small, unsigned blocks_big, hipStream_t stream) {
     if constexpr (GM == GM_TOKENS) {
         // Expert K ranges differ, so every expert runs the exact path (which meets the bound at any K).
-        hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GM, 2>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
+        if (blocks_big > 0 && use_big_tokens(a))
+            hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GM, 2>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GM, 2>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
     } else {
         const bool fp8 = a.K >= kFp8MinK;
         if (use_big(a, MX, GM == GM_ROWS)) {
@@ -953,8 +1139,9 @@ hipError_t launch_grouped_wgrad(const uint8_t* a_q, const uint8_t* a_s, const ui
     a.M = M; a.N = N; a.K = Kt; a.ldc = N; a.offsets = offsets; a.G = G;
     a.lda = Kt; a.ldb = Kt; a.ldsa = Kt / 32; a.ldsb = Kt / 32; a.c_gstride = M * N;
     const int64_t blocks = G * ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t big = G * ((M + TB - 1) / TB) * ((N + TB - 1) / TB);
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    return launch_gemm_t<true, 0, 0, GM_TOKENS>(a, (unsigned)blocks, 0u, stream);
+    return launch_gemm_t<true, 0, 0, GM_TOKENS>(a, (unsigned)blocks, (unsigned)big, stream);
 }
 
 }  // namespace mxq

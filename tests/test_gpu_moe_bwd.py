@@ -287,6 +287,54 @@ def test_grouped_wgrad_all_elements(M, N, off):
             assert np.all(got[g] == 0) and np.all(f32[g] == 0)
 
 
+# Large-tile path (M, N >= 256): K ranges of 32 mod 64 end in a half stage, odd Kt/32 leaves scale rows unaligned,
+# the last expert ends at the operands' last byte, ranges span several 16-block scale groups.
+@pytest.mark.parametrize("M,N,off", [
+    (512, 320, [0, 32, 32, 96, 160, 1216, 1248, 1760, 1792]),
+    (296, 264, [0, 0, 64, 608, 640, 2784]),
+    (256, 256, [0, 32]),
+    (264, 512, [0, 544, 544, 1088, 1120, 1632, 1696, 2208]),
+])
+def test_grouped_wgrad_large_tiles_all_elements(M, N, off):
+    need_gpu()
+    offsets = np.array(off, np.int64)
+    G, kt = offsets.size - 1, int(offsets[-1])
+    say("grouped wgrad large tiles", M, N, offsets.tolist())
+    aq, as_ = _token_operand(kt, M, 80 + M)
+    bq, bs = _token_operand(kt, N, 81 + N, 0.3)
+    off_t = torch.from_numpy(offsets).to(DEV)
+    C = mxq.grouped_wgrad_mx(aq, as_, bq, bs, off_t)
+    acc0 = torch.zeros((G, M, N), dtype=torch.float32, device=DEV)
+    mxq.grouped_wgrad_mx(aq, as_, bq, bs, off_t, accumulate=acc0)
+    torch.cuda.synchronize()
+    y, S = oracle.grouped_wgrad_ref(u8(aq), u8(as_), u8(bq), u8(bs), offsets)
+    got = C.float().cpu().numpy()
+    f32 = acc0.cpu().numpy()
+    _bound_check(got, y, S, "grouped wgrad large tiles bf16")
+    _bound_check(f32, y, S, "grouped wgrad large tiles fp32")
+    assert np.array_equal(u16(C), oracle.bf16_from_f32(f32))
+    for g in range(G):
+        if offsets[g] == offsets[g + 1]:
+            assert np.all(got[g] == 0) and np.all(f32[g] == 0)
+
+
+def test_grouped_wgrad_large_tiles_accumulate():
+    need_gpu()
+    M, N = 256, 384
+    offsets = np.array([0, 96, 96, 672], np.int64)
+    kt = int(offsets[-1])
+    aq, as_ = _token_operand(kt, M, 90)
+    bq, bs = _token_operand(kt, N, 91)
+    off_t = torch.from_numpy(offsets).to(DEV)
+    base = workloads.normal_f32((3, M, N), 5.0, 4, 92, DEV)
+    sink = base.clone()
+    mxq.grouped_wgrad_mx(aq, as_, bq, bs, off_t, accumulate=sink)
+    fresh = torch.zeros_like(base)
+    mxq.grouped_wgrad_mx(aq, as_, bq, bs, off_t, accumulate=fresh)
+    torch.cuda.synchronize()
+    assert np.array_equal(sink.cpu().numpy(), (base.cpu().numpy() + fresh.cpu().numpy()).astype(np.float32))
+
+
 def test_grouped_wgrad_accumulates_into_fp32():
     """Two calls into one fp32 sink: each adds its sum with one rounding (the high-precision gradient sink)."""
     need_gpu()
