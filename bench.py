@@ -59,7 +59,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
-    ap.add_argument("--profile-kernel", choices=["mx_gemm_fwd", "copy"], default=None,
+    ap.add_argument("--profile-kernel", choices=["mx_gemm_fwd", "mx_gemm_wgrad", "copy"], default=None,
                     help="run only this kernel (10 launches) for hardware-counter passes, print its timing, exit")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -411,6 +411,12 @@ def profile_kernel(name, dev):
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         run = lambda: dst.copy_(src)  # noqa: E731
+    elif name == "mx_gemm_wgrad":                             # dW = dY^T X, K = 4096 (exact bf16 path)
+        X, _, dY = workloads.workload2(dev)
+        qx = mxq.mx_quantize(X, rowwise=False)
+        qd = mxq.mx_quantize(dY, rowwise=False)
+        dW = torch.empty((dY.shape[1], X.shape[1]), dtype=torch.bfloat16, device=dev)
+        run = lambda: mxq.scaled_gemm(qd.q_col, qd.s_col, qx.q_col, qx.s_col, mxq.MX_BLOCK32, out=dW)  # noqa: E731
     else:
         X, W, _ = workloads.workload2(dev)
         qx = mxq.mx_quantize(X, colwise=False)
