@@ -45,7 +45,7 @@ def _eq_mx(out, ref, what):
 
 # ----------------------------------------------------------------------------------------------- route weighting
 @pytest.mark.parametrize("rows,cols,rule", [(32, 32, mxq.RCEIL), (96, 160, mxq.FLOOR), (320, 1056, mxq.RCEIL),
-                                            (64, 4096, mxq.FLOOR)])
+                                            (64, 4096, mxq.FLOOR), (256, 384, mxq.RCEIL)])
 def test_route_weighted_quantize(rows, cols, rule):
     need_gpu()
     say("route weighted", rows, cols, rule)
@@ -111,7 +111,7 @@ def _compare_nan_tolerant(out, ref, x):
 
 # ----------------------------------------------------------------------------------------------- SwiGLU
 @pytest.mark.parametrize("rows,F,rule", [(32, 32, mxq.RCEIL), (96, 96, mxq.FLOOR), (320, 544, mxq.RCEIL),
-                                         (64, 1024, mxq.RCEIL)])
+                                         (64, 1024, mxq.RCEIL), (256, 256, mxq.FLOOR)])
 def test_swiglu_backward_quantize(rows, F, rule):
     need_gpu()
     say("swiglu backward", rows, F, rule)
@@ -162,7 +162,8 @@ def test_swiglu_backward_quantize_extremes():
     _compare_nan_tolerant(out, (qr, sr, qc, sc), dc)
 
 
-@pytest.mark.parametrize("rows,F,rule", [(32, 32, mxq.RCEIL), (96, 160, mxq.FLOOR), (132_160, 1024, mxq.RCEIL)])
+@pytest.mark.parametrize("rows,F,rule", [(32, 32, mxq.RCEIL), (96, 160, mxq.FLOOR), (384, 256, mxq.RCEIL),
+                                         (132_160, 1024, mxq.RCEIL)])
 def test_swiglu_forward_oriented(rows, F, rule):
     """Row orientation equals swiglu_mx_quantize; the column one is the fp32 MX quantize of the same h."""
     need_gpu()
