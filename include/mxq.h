@@ -253,6 +253,8 @@ mxq_status grouped_scaled_gemm_strided(const uint8_t* a_q, const uint8_t* a_s, c
  *   outputs accumulate into, [OLMO11] Sections 11.3.4 and 11.4).
  * Requires M, N >= 1, Kt >= 0 and Kt % 32 == 0, 1 <= G <= 4096. As for grouped_scaled_gemm, the offsets are read on
  * the device only; offsets outside [0, Kt] are clamped.
+ * Scale grids are read in aligned 4-byte words, so up to 3 bytes past the end of a_s or b_s (inside the word that
+ * holds their last byte) may be read; nothing outside the caller's buffers is ever written.
  */
 mxq_status grouped_wgrad_mx(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
                             const int64_t* group_offsets, int64_t G, int64_t M, int64_t N, int64_t Kt,
