@@ -495,10 +495,22 @@ def cpu_baseline(X, W, rows):
     t2 = time.perf_counter()
     flop = 2.0 * rows * W.shape[0] * W.shape[1]
     log(f"cpu oracle: quantize {t1 - t0:.2f}s, gemm {t2 - t1:.2f}s on {threads} threads")
+    # the same computation on one thread, on a smaller sample: 8 rows of X against the first 4096 rows of W
+    r1, n1 = 8, 4096
+    t3 = time.perf_counter()
+    q1, s1, _, _ = oracle.mx_quantize(xs[:r1], oracle.RCEIL, colwise=False, nthreads=1)
+    q2, s2, _, _ = oracle.mx_quantize(wh[:n1], oracle.RCEIL, colwise=False, nthreads=1)
+    oracle.gemm_ref(q1, s1, oracle.E4M3, q2, s2, oracle.E4M3, oracle.MX_BLOCK32, nthreads=1)
+    t4 = time.perf_counter()
+    flop1 = 2.0 * r1 * n1 * W.shape[1]
+    log(f"cpu oracle, one thread: {t4 - t3:.2f}s")
     return {"value": round(flop / (t2 - t0) / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "cpu_model": cpu_model(), "nproc": os.cpu_count(),
             "sample": f"forward GEMM of the MX linear layer for {rows} of 4096 rows of X (2*{rows}*36864*12288 FLOP) "
-                      f"in fp64, including MX quantize of those rows and of all of W ({t2 - t0:.1f} s)"}
+                      f"in fp64, including MX quantize of those rows and of all of W ({t2 - t0:.1f} s)",
+            "single_thread": {"value": round(flop1 / (t4 - t3) / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                              "sample": f"{r1} rows of X against the first {n1} rows of W (2*{r1}*{n1}*12288 FLOP), "
+                                        f"including MX quantize of both ({t4 - t3:.1f} s)"}}
 
 
 if __name__ == "__main__":
