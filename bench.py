@@ -4,7 +4,8 @@ One step is one pass over every row of the hot path, on seeded synthetic inputs 
   mx_linear     GPT-175B QKV linear (X 4096x12288, W 36864x12288, dY 4096x36864) in MXFP8: quantize X, W and dY in
                 both orientations, then Y = X W^T, dX = dY W, dW = dY^T X (block-scaled GEMMs, bf16 out)
   pt_linear     the same layer with per-tensor current scaling (E4M3 X and W, E5M2 dY; q and q^T) and three GEMMs
-  mx_quant      MX quantize of a 16384x8192 activation with 0.1% x100 outliers, row and column orientation
+  mx_quant      MX quantize of a 16384x8192 activation with 0.1% x100 outliers, row and column orientation (and,
+                timed as mx_quant_act_row, the row orientation alone: 406.8 MB)
   grouped       64-expert grouped MX GEMM (Zipf(1.1) top-8 routing of 16384 tokens, up 2048->1024 and down
                 1024->2048), including the row quantize of both activations (expert weights quantized once); the
                 activation quantizes and the two grouped GEMMs are timed separately as well
@@ -104,6 +105,7 @@ def main():
     mxD = mxq.MXTensor(u8(M, N), u8(M, N // 32), u8(N, M), u8(N, M // 32))
     mx3 = mxq.MXTensor(u8(*act3.shape), u8(act3.shape[0], act3.shape[1] // 32), u8(act3.shape[1], act3.shape[0]),
                        u8(act3.shape[1], act3.shape[0] // 32))
+    mx3_row = mxq.MXTensor(mx3.q_row, mx3.s_row, None, None)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
@@ -176,7 +178,7 @@ def main():
              "grouped_q_up", "grouped_gemm_up", "grouped_q_down", "grouped_gemm_down", "adam", "small",
              "pt_quant_delayed", "adam_delayed", "wcache_fused", "wcache_unfused", "moe_swiglu_mlp", "swiglu_quant",
              "grad_cast", "grad_requant", "moe_fwd_train", "bwd_rw_quant", "bwd_dgrad_down", "bwd_swiglu_quant",
-             "bwd_dgrad_up", "bwd_wgrad_down", "bwd_wgrad_up"]
+             "bwd_dgrad_up", "bwd_wgrad_down", "bwd_wgrad_up", "mx_quant_act_row"]
     NEV = len(parts) + 1
 
     def step(ev):
@@ -266,6 +268,8 @@ def main():
         ev[27].record(stream)
         mxq.grouped_wgrad_mx(mx_dc.q_col, mx_dc.s_col, mx_x2.q_col, mx_x2.s_col, off4, accumulate=sink_wgu)
         ev[28].record(stream)
+        mxq.mx_quantize(act3, colwise=False, out=mx3_row)
+        ev[29].record(stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -314,6 +318,7 @@ def main():
         "pt_gemms_tflops": 3 * flop_gemm / (ms["pt_gemms"] * 1e-3) / 1e12,
         "pt_quant_gbs": pt_bytes / (ms["pt_quant"] * 1e-3) / 1e9,
         "mx_quant_act_gbs": act_bytes / (ms["mx_quant_act"] * 1e-3) / 1e9,
+        "mx_quant_act_row_gbs": (2 + 33 / 32) * act3.numel() / (ms["mx_quant_act_row"] * 1e-3) / 1e9,
         "grouped_tflops_incl_act_quant": grouped_flop / (ms["grouped"] * 1e-3) / 1e12,
         "grouped_gemm_only_tflops": grouped_flop / (grouped_gemm_ms * 1e-3) / 1e12,
         "adam_gbs": adam_bytes / (ms["adam"] * 1e-3) / 1e9,
@@ -495,8 +500,9 @@ def cpu_baseline(X, W, rows):
     t2 = time.perf_counter()
     flop = 2.0 * rows * W.shape[0] * W.shape[1]
     log(f"cpu oracle: quantize {t1 - t0:.2f}s, gemm {t2 - t1:.2f}s on {threads} threads")
-    # the same computation on one thread, on a smaller sample: 8 rows of X against the first 4096 rows of W
-    r1, n1 = 8, 4096
+    # the same computation on one thread, on a smaller sample with the GEMM still dominant: 128 rows of X against
+    # the first 1024 rows of W
+    r1, n1 = 128, 1024
     t3 = time.perf_counter()
     q1, s1, _, _ = oracle.mx_quantize(xs[:r1], oracle.RCEIL, colwise=False, nthreads=1)
     q2, s2, _, _ = oracle.mx_quantize(wh[:n1], oracle.RCEIL, colwise=False, nthreads=1)
