@@ -1,7 +1,8 @@
 """Seeded sweeps of random shapes against the oracle, beyond the hand-picked shapes of the other GPU tests: tiles cut
 at every edge (rows and columns that are not multiples of the 128-wide quantize tiles or the 128/256-wide GEMM tiles),
-both scale rules and both orientations, both FP8 formats, and GEMM shapes on either side of the small/large-tile and
-exact/FP8 path thresholds. Quantizers must match byte for byte; GEMMs must satisfy
+both scale rules and both orientations, both FP8 formats, GEMM shapes on either side of the small/large-tile and
+exact/FP8 path thresholds, and random expert groupings (some empty) for the routed Wgrad over token ranges and the
+strided dgrad, on both tile kernels. Quantizers must match byte for byte; GEMMs must satisfy
 |C - y| <= 2^-7 |y| + 2^-20 sum|a b| on every element. Each case prints its seed and shape before it runs."""
 import numpy as np
 import pytest
@@ -97,3 +98,83 @@ def test_gemm_threshold_shapes(shape, scaling):
     err = np.abs(C.float().cpu().numpy().astype(np.float64) - y)
     lim = 2.0 ** -7 * np.abs(y) + 2.0 ** -20 * S
     assert np.all(err <= lim), f"{int((err > lim).sum())} elements outside the bound"
+
+
+def _random_groups(rng, G, max_blocks, empty_frac=0.2):
+    """Group sizes in 32-row blocks, some empty; returns int64 offsets[G + 1]."""
+    sizes = rng.integers(0, max_blocks + 1, G) * 32
+    sizes[rng.random(G) < empty_frac] = 0
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+
+
+def _bound(got, y, S, what):
+    err = np.abs(np.asarray(got, np.float64) - y)
+    lim = 2.0 ** -7 * np.abs(y) + 2.0 ** -20 * S
+    assert np.all(err <= lim), f"{what}: {int((err > lim).sum())} elements outside the bound"
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_routed_wgrad_random_shapes(case):
+    """Per-expert contraction over token ranges: random expert counts and sizes (multiples of 32, some empty, odd and
+    even numbers of blocks), M and N on both sides of the large-tile threshold (256)."""
+    need_gpu()
+    rng = np.random.default_rng(400 + case)
+    G = int(rng.integers(1, 7))
+    lo = 32 if case % 2 else 1                                         # odd cases: the large-tile kernel
+    M = int(rng.integers(lo, 76)) * 8
+    N = int(rng.integers(lo, 76)) * 8
+    off = _random_groups(rng, G, 24)
+    if off[-1] == 0:
+        off[-1] = 32
+        off = np.maximum.accumulate(off)
+    kt = int(off[-1])
+    say("sweep routed wgrad", case, G, M, N, off.tolist())
+    xa = workloads.normal_bf16((kt, M), 10.0 ** (case % 3 - 1), 34, case, DEV)
+    xb = workloads.normal_bf16((kt, N), 1.0, 34, 100 + case, DEV)
+    qa = mxq.mx_quantize(xa, rowwise=False)
+    qb = mxq.mx_quantize(xb, rowwise=False)
+    off_t = torch.from_numpy(off).to(DEV)
+    C = mxq.grouped_wgrad_mx(qa.q_col, qa.s_col, qb.q_col, qb.s_col, off_t)
+    sink = torch.zeros((G, M, N), dtype=torch.float32, device=DEV)
+    mxq.grouped_wgrad_mx(qa.q_col, qa.s_col, qb.q_col, qb.s_col, off_t, accumulate=sink)
+    torch.cuda.synchronize()
+    y, S = oracle.grouped_wgrad_ref(u8(qa.q_col), u8(qa.s_col), u8(qb.q_col), u8(qb.s_col), off)
+    _bound(C.float().cpu().numpy(), y, S, "bf16")
+    _bound(sink.cpu().numpy(), y, S, "fp32 sink")
+    assert np.array_equal(u16(C), oracle.bf16_from_f32(sink.cpu().numpy()))
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_routed_dgrad_strided_random_shapes(case):
+    """Grouped GEMM reading a column-orientation expert weight cache in place: random expert sizes (some empty),
+    D and F on both sides of the large-tile thresholds, outputs wider than N."""
+    need_gpu()
+    rng = np.random.default_rng(500 + case)
+    G = int(rng.integers(1, 6))
+    if case % 2:                                                       # odd cases: the large-tile kernel
+        D = int(rng.integers(1, 5)) * 512
+        F = int(rng.integers(64, 100)) * 8
+    else:
+        D = int(rng.integers(1, 40)) * 32
+        F = int(rng.integers(1, 80)) * 8
+    off = _random_groups(rng, G, 40)
+    total = int(off[-1])
+    extra = int(rng.integers(0, 3)) * 8
+    say("sweep routed dgrad", case, G, D, F, total, extra)
+    dY = workloads.normal_bf16((max(total, 1), D), 1.0, 35, case, DEV)[:total]
+    W = workloads.normal_bf16((G, D, F), 1.0, 35, 100 + case, DEV)
+    qa = mxq.mx_quantize(dY.contiguous(), colwise=False) if total else None
+    cache = mxq.mx_quantize(W.reshape(G * D, F), rowwise=False)
+    off_t = torch.from_numpy(off).to(DEV)
+    out = torch.full((total, F + extra), 3.0, dtype=torch.bfloat16, device=DEV)
+    if total == 0:
+        return
+    mxq.grouped_scaled_gemm_strided(qa.q_row, qa.s_row, off_t, cache.q_col, cache.s_col, G, F, D, ldb=G * D,
+                                    b_group_stride=D, ldbs=G * D // 32, bs_group_stride=D // 32, out=out)
+    torch.cuda.synchronize()
+    bq = u8(cache.q_col).reshape(F, G, D).transpose(1, 0, 2).copy()
+    bs = u8(cache.s_col).reshape(F, G, D // 32).transpose(1, 0, 2).copy()
+    y, S = oracle.grouped_gemm_ref(u8(qa.q_row), u8(qa.s_row), off, bq, bs)
+    got = out.float().cpu().numpy()
+    _bound(got[:, :F], y, S, "strided dgrad")
+    assert np.all(got[:, F:] == 3.0)
