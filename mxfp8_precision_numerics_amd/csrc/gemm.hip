@@ -3,8 +3,9 @@
 // MX_BLOCK32 applies one E8M0 scale per 32 values along K inside the matrix instruction ("OLMo-core MoE,
 // Section 11: MXFP8 Training", Figure 47 and Section 11.2.3: native block-scaled GEMM, BF16 operator output).
 // PER_TENSOR multiplies the fp32 accumulator by 1 / (s_a s_b) ("3.8 Mixed Precision, bf16 & FP8 Training",
-// Exercise 6: de-scale by 1/(s_x s_w)). The grouped variant runs the same tiles over ragged expert row groups
-// (Section 11.4.1, routed experts).
+// Exercise 6: de-scale by 1/(s_x s_w)). The grouped variants run the same tiles over ragged expert row groups
+// (Section 11.4.1, routed experts: forward, and dgrad with a strided expert operand) and over ragged expert ranges of
+// K with one output per expert (the routed Wgrad, whose contraction runs over each expert's tokens).
 //
 // Matrix instruction: v_mfma_scale_f32_32x32x64_f8f6f4. Operand layout (per lane l, g = l / 32): row l % 32;
 // bytes 0-15 hold k = 16g .. 16g+15 and bytes 16-31 hold k = 32+16g .. 32+16g+15 of the 64-wide K window. The
@@ -393,7 +394,8 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
 // MX scales: one 16-byte lane per row covers SG = 8 stages (16 blocks); the groups are double-buffered and a group's
 // copies are issued four trips before its first stage is read.
 // Tile order: each XCD (which receives every eighth workgroup) walks a contiguous run of a grouped-M order, so its
-// resident workgroups share A and B tiles in its L2.
+// resident workgroups share A and B tiles in its L2. Row groups take their tiles group by group; token groups run
+// expert-major in launch order (see the token-group notes in the kernel).
 constexpr int TB = 256;
 constexpr int KS = 64;
 constexpr int SG = 8;
