@@ -100,3 +100,62 @@ def test_delayed_adam_sequence(n):
         assert np.array_equal(u16(w), o_w), f"w t={t}"
         assert np.array_equal(_bits(hist), o_hist.view(np.uint32)), f"history t={t}"
         assert int(pos.item()) == int(o_pos[0]), f"pos t={t}"
+
+
+def test_delayed_cast_full_shape_of_w():
+    """Two delayed-scaling casts of the 36864 x 12288 weight (the shape the benchmark times), q and q^T byte for byte."""
+    need_gpu()
+    rows, cols = 36864, 12288
+    say("delayed cast full shape", rows, cols)
+    hist = torch.tensor([0.05, 0.2], dtype=torch.float32, device=DEV)
+    pos = torch.zeros(1, dtype=torch.int32, device=DEV)
+    o_hist = np.array([0.05, 0.2], np.float32)
+    o_pos = np.zeros(1, np.int32)
+    ws = torch.empty(mxq.workspace_bytes("pertensor_delayed", rows * cols), dtype=torch.uint8, device=DEV)
+    for call in range(2):
+        x = workloads.normal_bf16((rows, cols), 0.02, 2, 1 + 50 * call, DEV)
+        r = mxq.pertensor_quantize_delayed(x, hist, pos, mxq.E4M3, workspace=ws)
+        torch.cuda.synchronize()
+        a, s, q, qt = oracle.pertensor_quantize_delayed(u16(x), o_hist, o_pos, mxq.E4M3)
+        del x
+        assert np.float32(r.amax.item()) == np.float32(a), f"amax call {call}"
+        assert _bits(r.scale)[0] == np.float32(s).view(np.uint32), f"scale call {call}"
+        assert np.array_equal(u8(r.q), q) and np.array_equal(u8(r.q_t), qt), f"codes call {call}"
+        assert np.array_equal(_bits(hist), o_hist.view(np.uint32)) and int(pos.item()) == int(o_pos[0])
+        del r, q, qt
+
+
+def test_delayed_adam_full_size():
+    """The delayed-scaling Adam step over 1.3e9 parameters (the benchmark's size): a current-scaling step seeds the
+    history, then a delayed step; every output byte for byte."""
+    need_gpu()
+    n = 1_300_000_000
+    say("delayed adam full size", n)
+    theta = workloads.workload5_params(n, DEV)
+    m_q = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    m_scale = torch.ones(1, dtype=torch.float32, device=DEV)
+    v = torch.zeros(n, dtype=torch.float16, device=DEV)
+    hist = torch.zeros(2, dtype=torch.float32, device=DEV)
+    pos = torch.zeros(1, dtype=torch.int32, device=DEV)
+    o_theta = theta.cpu().numpy().copy()
+    o_mq = np.zeros(n, np.uint8); o_ms = np.ones(1, np.float32); o_v = np.zeros(n, np.uint16)
+    o_hist = np.zeros(2, np.float32); o_pos = np.zeros(1, np.int32)
+    for t in (1, 2):
+        g = workloads.workload5_grad(n, t, DEV)
+        hp = mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.0, t)
+        ohp = oracle.AdamHP(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, step=t)
+        if t == 1:
+            mxq.fp8_adam_step(theta, g, m_q, m_scale, v, None, hp)
+            a, _ = oracle.adam_step(o_theta, u16(g), o_mq, o_ms, o_v, ohp, want_w=False)
+            oracle.history_push(o_hist, o_pos, a)
+            hist[0] = a
+            pos[0] = 1
+        else:
+            mxq.fp8_adam_step_delayed(theta, g, m_q, m_scale, v, None, hp, hist, pos)
+            oracle.adam_step_delayed(o_theta, u16(g), o_mq, o_ms, o_v, ohp, o_hist, o_pos, want_w=False)
+        torch.cuda.synchronize()
+        del g
+        assert np.array_equal(theta.cpu().numpy().view(np.uint32), o_theta.view(np.uint32)), f"theta t={t}"
+        assert np.array_equal(u8(m_q), o_mq) and _bits(m_scale)[0] == o_ms.view(np.uint32)[0], f"m t={t}"
+        assert np.array_equal(u16(v), o_v), f"v t={t}"
+        assert np.array_equal(_bits(hist), o_hist.view(np.uint32)) and int(pos.item()) == int(o_pos[0])

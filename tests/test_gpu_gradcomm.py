@@ -133,3 +133,28 @@ def test_eight_rank_pipeline_on_one_gpu():
         assert _bits(sg) == _f32bits(o_sg) and _bits(ssum) == _f32bits(np.float32(8) * o_sg)
         want = oracle.requantize_shared(o_qs[r], mxq.E4M3, float(o_scales[r]), float(o_sg), mxq.E4M3)
         assert np.array_equal(u8(out), want), f"requantize rank {r}"
+
+
+def test_autoscale_and_requantize_full_size_of_dw():
+    """The FP8 all-reduce pieces on a weight gradient of W's shape (453M values, the size the benchmark times): an
+    auto-scaled cast, then the requantize of its codes to the shared scale, byte for byte."""
+    need_gpu()
+    n = 36864 * 12288
+    say("autoscale + requantize full size", n)
+    mu = torch.tensor([2000.0], dtype=torch.float32, device=DEV)
+    o_mu = np.float32(2000.0)
+    ws = torch.empty(mxq.workspace_bytes("autoscale", n), dtype=torch.uint8, device=DEV)
+    for t in range(1):
+        g = workloads.workload6_grad(n, 0, t, DEV)
+        r = mxq.fp8_autoscale_cast(g, mu, mxq.E4M3, workspace=ws)
+        torch.cuda.synchronize()
+        q, cnt, s, o_mu = oracle.autoscale_cast(u16(g), float(o_mu), mxq.E4M3)
+        del g
+        assert np.array_equal(u8(r.q), q), f"codes step {t}"
+        assert int(r.overflow.item()) == cnt and _bits(r.scale) == _f32bits(s) and _bits(mu) == _f32bits(o_mu)
+    gathered = torch.cat([r.scale, 2.0 ** torch.arange(-3, 4, dtype=torch.float32, device=DEV)])
+    rq, sg, _ = mxq.fp8_requantize_shared(r.q, mxq.E4M3, r.scale, gathered, mxq.E4M3)
+    torch.cuda.synchronize()
+    o_sg = oracle.min_scale(gathered.cpu().numpy())
+    assert _bits(sg) == _f32bits(o_sg)
+    assert np.array_equal(u8(rq), oracle.requantize_shared(q, mxq.E4M3, float(s), float(o_sg), mxq.E4M3))

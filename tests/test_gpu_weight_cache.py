@@ -61,3 +61,36 @@ def test_weight_cache_single_orientation_and_no_weight_copy():
     assert torch.equal(outs[1][0], outs[0][0]) and torch.equal(outs[2][0], outs[0][0])
     assert torch.equal(outs[1][1].q_row, full.q_row) and torch.equal(outs[1][1].s_row, full.s_row)
     assert torch.equal(outs[2][1].q_col, full.q_col) and torch.equal(outs[2][1].s_col, full.s_col)
+
+
+def test_weight_cache_full_shape_of_w():
+    """Two steps on the 36864 x 12288 weight of the GPT-175B layer (the shape the benchmark times): every output, both
+    cache orientations included, equals the oracle's byte for byte."""
+    need_gpu()
+    rows, cols = 36864, 12288
+    n = rows * cols
+    say("weight cache full shape", rows, cols)
+    theta = workloads.workload5_params(n, DEV)
+    m_q = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    m_scale = torch.ones(1, dtype=torch.float32, device=DEV)
+    v = torch.zeros(n, dtype=torch.float16, device=DEV)
+    o_theta = theta.cpu().numpy().copy()
+    o_mq = np.zeros(n, np.uint8); o_ms = np.ones(1, np.float32); o_v = np.zeros(n, np.uint16)
+    ws = torch.empty(mxq.workspace_bytes("adam", n), dtype=torch.uint8, device=DEV)
+    for t in (1, 2):
+        g = workloads.workload5_grad(n, t, DEV)
+        hp = mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.0, t)
+        cache = mxq.fp8_adam_step_mx_cache(theta, g, m_q, m_scale, v, None, hp, rows, cols, workspace=ws)
+        torch.cuda.synchronize()
+        say("  step", t, "oracle")
+        oracle.adam_step(o_theta, u16(g), o_mq, o_ms, o_v,
+                         oracle.AdamHP(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, step=t),
+                         want_w=False)
+        del g
+        assert np.array_equal(theta.cpu().numpy().view(np.uint32), o_theta.view(np.uint32)), f"theta t={t}"
+        assert np.array_equal(u8(m_q), o_mq) and np.float32(m_scale.item()) == o_ms[0], f"m t={t}"
+        assert np.array_equal(u16(v), o_v), f"v t={t}"
+        qr, sr, qc, sc = oracle.mx_quantize_f32(o_theta.reshape(rows, cols), oracle.RCEIL)
+        assert np.array_equal(u8(cache.s_row), sr) and np.array_equal(u8(cache.q_row), qr), f"row cache t={t}"
+        assert np.array_equal(u8(cache.s_col), sc) and np.array_equal(u8(cache.q_col), qc), f"col cache t={t}"
+        del cache, qr, sr, qc, sc
