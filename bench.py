@@ -193,11 +193,12 @@ def main():
     torch.cuda.synchronize()
 
     Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    parts = ["mx_quant_XWdY", "mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "pt_quant", "pt_gemms", "mx_quant_act",
+    parts = ["mx_quant_XWdY", "mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "pt_quant", "pt_gemm_fwd", "mx_quant_act",
              "grouped_q_up", "grouped_gemm_up", "grouped_q_down", "grouped_gemm_down", "adam", "small",
              "pt_quant_delayed", "adam_delayed", "wcache_fused", "wcache_unfused", "moe_swiglu_mlp", "swiglu_quant",
              "grad_cast", "grad_requant", "moe_fwd_train", "bwd_rw_quant", "bwd_dgrad_down", "bwd_swiglu_quant",
-             "bwd_dgrad_up", "bwd_wgrad_down", "bwd_wgrad_up", "mx_quant_act_row", "small_graph"]
+             "bwd_dgrad_up", "bwd_wgrad_down", "bwd_wgrad_up", "mx_quant_act_row", "small_graph", "pt_gemm_dgrad",
+             "pt_gemm_wgrad"]
     NEV = len(parts) + 1
 
     def step(ev):
@@ -217,8 +218,6 @@ def main():
         pd = mxq.pertensor_quantize(dY, mxq.E5M2, workspace=ws_pt)
         ev[5].record(stream)
         mxq.scaled_gemm(px.q, px.scale, pw.q, pw.scale, mxq.PER_TENSOR, mxq.E4M3, mxq.E4M3, out=Y)
-        mxq.scaled_gemm(pd.q, pd.scale, pw.q_t, pw.scale, mxq.PER_TENSOR, mxq.E5M2, mxq.E4M3, out=dX)
-        mxq.scaled_gemm(pd.q_t, pd.scale, px.q_t, px.scale, mxq.PER_TENSOR, mxq.E5M2, mxq.E4M3, out=dW)
         ev[6].record(stream)
         mxq.mx_quantize(act3, out=mx3)
         ev[7].record(stream)
@@ -289,6 +288,10 @@ def main():
         ev[29].record(stream)
         small_graph.replay()
         ev[30].record(stream)
+        mxq.scaled_gemm(pd.q, pd.scale, pw.q_t, pw.scale, mxq.PER_TENSOR, mxq.E5M2, mxq.E4M3, out=dX)
+        ev[31].record(stream)
+        mxq.scaled_gemm(pd.q_t, pd.scale, px.q_t, px.scale, mxq.PER_TENSOR, mxq.E5M2, mxq.E4M3, out=dW)
+        ev[32].record(stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -306,6 +309,7 @@ def main():
     ms = {p: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
           for i, p in enumerate(parts)}
     step_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][NEV - 1]) for s in range(args.steps)]))
+    ms["pt_gemms"] = ms["pt_gemm_fwd"] + ms["pt_gemm_dgrad"] + ms["pt_gemm_wgrad"]
     ms["grouped"] = sum(ms[p] for p in ("grouped_q_up", "grouped_gemm_up", "grouped_q_down", "grouped_gemm_down"))
     grouped_gemm_ms = ms["grouped_gemm_up"] + ms["grouped_gemm_down"]
     bwd_parts = ("bwd_rw_quant", "bwd_dgrad_down", "bwd_swiglu_quant", "bwd_dgrad_up", "bwd_wgrad_down",
@@ -335,6 +339,9 @@ def main():
         "mx_quant_XWdY_gbs": mxq_XWdY_bytes / (ms["mx_quant_XWdY"] * 1e-3) / 1e9,
         "pt_linear_tflops_incl_quant": 3 * flop_gemm / ((ms["pt_quant"] + ms["pt_gemms"]) * 1e-3) / 1e12,
         "pt_gemms_tflops": 3 * flop_gemm / (ms["pt_gemms"] * 1e-3) / 1e12,
+        "pt_gemm_fwd_tflops": flop_gemm / (ms["pt_gemm_fwd"] * 1e-3) / 1e12,
+        "pt_gemm_dgrad_tflops": flop_gemm / (ms["pt_gemm_dgrad"] * 1e-3) / 1e12,
+        "pt_gemm_wgrad_tflops": flop_gemm / (ms["pt_gemm_wgrad"] * 1e-3) / 1e12,
         "pt_quant_gbs": pt_bytes / (ms["pt_quant"] * 1e-3) / 1e9,
         "mx_quant_act_gbs": act_bytes / (ms["mx_quant_act"] * 1e-3) / 1e9,
         "mx_quant_act_row_gbs": (2 + 33 / 32) * act3.numel() / (ms["mx_quant_act_row"] * 1e-3) / 1e9,
