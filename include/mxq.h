@@ -20,8 +20,8 @@
  * 2^(byte-127); byte 0xFF (NaN) marks a 32-value block holding a NaN.
  *
  * Sources (page titles and sections):
- *   [OLMO11] "OLMo-core MoE, Section 11: MXFP8 Training" — Eq. 57, Eq. 58, Figures 47/49/50, Eq. 60,
- *            Section 11.3.5 / Table 24.
+ *   [OLMO11] "OLMo-core MoE, Section 11: MXFP8 Training" — Eq. 57, Eq. 58, Figures 47/49/50/55, Eq. 60,
+ *            Sections 11.2.1, 11.3.2, 11.3.4, 11.3.5 / Table 24, 11.4.1, 11.4.4 / Table 25.
  *   [LLMSB]  "3.8 Mixed Precision, bf16 & FP8 Training" — per-tensor scaling, delayed scaling, Exercise 6.
  *   [FP8-LM] "FP8-LM: Training FP8 Large Language Models" — tensor scaling, AdamW update, Eq. 7-8.
  */
