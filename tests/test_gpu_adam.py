@@ -95,3 +95,35 @@ def test_adam_workload5_full_size_sampled():
         assert np.array_equal(v[idx_t].cpu().numpy().view(np.uint16), ov)
         assert np.array_equal(w[idx_t].view(torch.int16).cpu().numpy().view(np.uint16), ow)
         del g
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_adam_zero_gradient_steps(fused):
+    """Degenerate steps: an all-zero gradient from the zero state (amax of m is 0, so the m scale is 448 / 1e-12 and
+    theta does not move), then a normal step, then a zero gradient again (m and v only decay). Bit for bit against
+    the oracle, for the plain step and for the step fused with the weight-cache refresh."""
+    need_gpu()
+    rows, cols = 64, 160
+    n = rows * cols
+    theta = workloads.workload5_params(n, DEV)
+    m_q = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    m_scale = torch.ones(1, dtype=torch.float32, device=DEV)
+    v = torch.zeros(n, dtype=torch.float16, device=DEV)
+    o_theta = theta.cpu().numpy().copy()
+    o_mq = np.zeros(n, np.uint8); o_ms = np.ones(1, np.float32); o_v = np.zeros(n, np.uint16)
+    zero = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    for t, g in ((1, zero), (2, workloads.workload5_grad(n, 2, DEV)), (3, zero)):
+        say("adam zero gradient", fused, t)
+        hp, ohp = _hp(t, 0.0)
+        if fused:
+            cache = mxq.fp8_adam_step_mx_cache(theta, g, m_q, m_scale, v, None, hp, rows, cols)
+        else:
+            mxq.fp8_adam_step(theta, g, m_q, m_scale, v, None, hp)
+        torch.cuda.synchronize()
+        oracle.adam_step(o_theta, u16(g), o_mq, o_ms, o_v, ohp, want_w=False)
+        assert np.array_equal(theta.cpu().numpy().view(np.uint32), o_theta.view(np.uint32)), f"theta t={t}"
+        assert np.array_equal(u8(m_q), o_mq) and np.float32(m_scale.item()) == o_ms[0], f"m t={t}"
+        assert np.array_equal(u16(v), o_v), f"v t={t}"
+        if fused:
+            ref = oracle.mx_quantize_f32(o_theta.reshape(rows, cols), oracle.RCEIL)
+            assert all(np.array_equal(u8(a), b) for a, b in zip(cache, ref)), f"caches t={t}"
