@@ -703,6 +703,21 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) { sa[j] = 0x7F7F7F7Fu; sb[j] = 0x7F7F7F7Fu; }
         }
+        if constexpr (MF == 2) {
+            // exact path: the stage's bf16-conversion scale operands, block-major: [4 blk + j]
+            uint32_t wa[4], wb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { wa[j] = sa[j]; wb[j] = sb[j]; }
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const int sh = 8 * (2 * (st & 1) + blk);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sa[4 * blk + j] = __float_as_uint(scale_operand((wa[j] >> sh) & 0xFFu));
+                    sb[4 * blk + j] = __float_as_uint(scale_operand((wb[j] >> sh) & 0xFFu));
+                }
+            }
+        }
     };
     auto read_stage = [&](auto sp_c, int st, v8i* fa, v8i* fb, uint32_t* sa, uint32_t* sb) {
 #pragma unroll
@@ -721,8 +736,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     // The matrix instructions of one stage, from fragments in registers.
     auto mma_stage = [&](auto par_c, int kt, const v8i* fa, const v8i* fb, const uint32_t* sa, const uint32_t* sb) {
         constexpr int PAR = decltype(par_c)::value;                // kt & 1 when known at compile time, else -1
-        const int odd = PAR < 0 ? (kt & 1) : PAR;
         if constexpr (MF == 1) {
+            const int odd = PAR < 0 ? (kt & 1) : PAR;
             const int sh = 8 * (2 * odd + fg);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -733,16 +748,15 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         } else {
             // Exact path: dequantize to bf16 and use the bf16 instruction. k-step s takes bytes 8s .. 8s+7 of each
             // lane's 32 (A and B lanes hold the same k values, so the product sums every k of the stage once);
-            // steps 0, 1 lie in the stage's first 32-block, steps 2, 3 in its second, so each block's scale operands
-            // are formed once.
+            // steps 0, 1 lie in the stage's first 32-block, steps 2, 3 in its second. The two blocks' scale operands
+            // were formed when the stage's scale words were read, a trip ahead (read_scales).
             float xa[2][4], xb[2][4];
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
-                const int sh = 8 * (2 * odd + blk);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) xa[blk][j] = scale_operand((sa[j] >> sh) & 0xFFu);
+                for (int j = 0; j < 4; ++j) xa[blk][j] = __uint_as_float(sa[4 * blk + j]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) xb[blk][i] = scale_operand((sb[i] >> sh) & 0xFFu);
+                for (int i = 0; i < 4; ++i) xb[blk][i] = __uint_as_float(sb[4 * blk + i]);
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -807,7 +821,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         wait_copies_barrier<0>();
     }
     v8i fa[4], fb[4];
-    uint32_t sa[4], sb[4];
+    constexpr int SAN = MF == 2 ? 8 : 4;                  // scale registers per operand (exact path: operands)
+    uint32_t sa[SAN], sb[SAN];
     read_stage(std::integral_constant<int, 0>{}, 0, fa, fb, sa, sb);
     // Stage 0's regions are refilled by the first trips: every wave's reads of them must have returned.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -819,7 +834,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     // Trip kt (kt + 1 < nk): copy the trip's pair, read stage kt + 1's fragments, multiply stage kt, then wait until
     // stage kt + 2 has landed. Two fragment register sets ping-pong between trips (no copies between iterations).
     v8i fa2[4], fb2[4];
-    uint32_t sa2[4], sb2[4];
+    uint32_t sa2[SAN], sb2[SAN];
     // PH_C: kt % 4 as a std::integral_constant when known (then the trip's pair exists in full), else -1.
     auto steady = [&](auto ph_c, int kt, v8i* ca, v8i* cb, uint32_t* csa, uint32_t* csb, v8i* na, v8i* nb,
                       uint32_t* nsa, uint32_t* nsb) {
@@ -914,7 +929,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         steady(dyn{}, kt, fa, fb, sa, sb, fa2, fb2, sa2, sb2);
         ++kt;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) { fa[j] = fa2[j]; fb[j] = fb2[j]; sa[j] = sa2[j]; sb[j] = sb2[j]; }
+        for (int j = 0; j < 4; ++j) { fa[j] = fa2[j]; fb[j] = fb2[j]; }
+#pragma unroll
+        for (int j = 0; j < SAN; ++j) { sa[j] = sa2[j]; sb[j] = sb2[j]; }
     }
     // Last stage (kt == nk - 1): its fragments are in registers and no copy is outstanding.
     __builtin_amdgcn_sched_barrier(0);
@@ -923,9 +940,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         // so those k-steps add exact zeros whatever lies past the expert's range (selects, not branches, so the
         // accumulators keep one path).
         const uint32_t keep = half_last ? 0u : 0xFFFFFFFFu;
-        const int sh1 = 8 * (2 * (kt & 1) + 1);
-        const uint32_t smask = half_last ? (0xFFu << sh1) : 0u;
-        const uint32_t sset = half_last ? (127u << sh1) : 0u;
+        const uint32_t one = __float_as_uint(scale_operand(127u));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -933,8 +948,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
                 fa[j][e] = (int)((uint32_t)fa[j][e] & keep);
                 fb[j][e] = (int)((uint32_t)fb[j][e] & keep);
             }
-            sa[j] = (sa[j] & ~smask) | sset;
-            sb[j] = (sb[j] & ~smask) | sset;
+            sa[4 + j] = half_last ? one : sa[4 + j];
+            sb[4 + j] = half_last ? one : sb[4 + j];
         }
     }
     mma_stage(dyn{}, kt, fa, fb, sa, sb);
