@@ -7,16 +7,19 @@
 // (Section 11.4.1, routed experts: forward, and dgrad with a strided expert operand) and over ragged expert ranges of
 // K with one output per expert (the routed Wgrad, whose contraction runs over each expert's tokens).
 //
-// Matrix instruction: v_mfma_scale_f32_32x32x64_f8f6f4. Operand layout (per lane l, g = l / 32): row l % 32;
+// FP8 matrix instruction of the large-tile kernel: v_mfma_scale_f32_32x32x64_f8f6f4. Operand layout (per lane l,
+// g = l / 32): row l % 32;
 // bytes 0-15 hold k = 16g .. 16g+15 and bytes 16-31 hold k = 32+16g .. 32+16g+15 of the 64-wide K window. The
 // E8M0 scale for (row r, 32-block b of the window) comes from lane r + 32b, byte chosen by op_sel. Output: lane l,
 // register j -> row 8(j/4) + 4g + j%4, column l % 32. The kernel feeds B as the instruction's first operand and A
 // as its second, so a lane's four consecutive accumulator registers are four consecutive n of one output row m
 // (8-byte bf16 stores).
 //
-// Tiling: 256 threads (4 waves, 2 x 2), a 128 x 128 output tile, waves own 64 x 64 (2 x 2 instructions).
-// K advances 128 bytes per stage; stages are double-buffered in LDS. LDS rows are 128 bytes with the 16-byte chunk
-// index XOR-swizzled by (row & 7), so the 16-byte fragment reads of 8 consecutive rows hit distinct banks.
+// Small-tile kernel (gemm_kernel): 256 threads (4 waves, 2 x 2), a 128 x 128 output tile, waves own 64 x 64, as
+// 4 x 4 v_mfma_scale_f32_16x16x128_f8f6f4 on the FP8 path or 2 x 2 v_mfma_f32_32x32x16_bf16 on operands dequantized
+// to bf16 (the exact path). K advances 128 bytes per stage; stages are double-buffered in LDS. LDS rows are 128 bytes
+// with the 16-byte chunk index XOR-swizzled by (row & 7), so the 16-byte fragment reads of 8 consecutive rows hit
+// distinct banks. The large-tile kernel (gemm_big_kernel) is described where it is defined.
 #include <type_traits>
 
 #include "mxq_device.h"
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
         }
     };
 
-    // accumulators: MF 0 -> 2 x 2 tiles of 32x32 (16 regs); MF 1 -> 4 x 4 tiles of 16x16 (4 regs)
+    // accumulators: MF 2 (exact path) -> 2 x 2 tiles of 32x32 (16 regs); MF 1 (FP8) -> 4 x 4 tiles of 16x16 (4 regs)
     v16f acc[2][2];
     v4f acc4[4][4];
 #pragma unroll
@@ -211,46 +214,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
         const int buf = kt & 1;
         if (kt + 1 < nk) load_stage((int64_t)(kt + 1) * BK);
 
-        if constexpr (MF == 0) {
-            uint32_t sa_reg[2], sb_reg[2];
-            if constexpr (MX) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) sa_reg[j] = sSA[buf][wm * 64 + j * 32 + fr] >> (8 * fg);
-#pragma unroll
-                for (int i = 0; i < 2; ++i) sb_reg[i] = sSB[buf][wn * 64 + i * 32 + fr] >> (8 * fg);
-            } else {
-                sa_reg[0] = sa_reg[1] = sb_reg[0] = sb_reg[1] = 0x7F7F7F7Fu;
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                v8i fa[2], fb[2];
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int row = wm * 64 + j * 32 + fr;
-                    uint4 x0 = *reinterpret_cast<const uint4*>(&sA[buf][swz(row, 4 * h + fg)]);
-                    uint4 x1 = *reinterpret_cast<const uint4*>(&sA[buf][swz(row, 4 * h + 2 + fg)]);
-                    fa[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int row = wn * 64 + i * 32 + fr;
-                    uint4 x0 = *reinterpret_cast<const uint4*>(&sB[buf][swz(row, 4 * h + fg)]);
-                    uint4 x1 = *reinterpret_cast<const uint4*>(&sB[buf][swz(row, 4 * h + 2 + fg)]);
-                    fb[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        if (h == 0)
-                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 0,
-                                                                                       (int)sb_reg[i], 0, (int)sa_reg[j]);
-                        else
-                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 2,
-                                                                                       (int)sb_reg[i], 2, (int)sa_reg[j]);
-                    }
-            }
-        } else if constexpr (MF == 2) {
+        if constexpr (MF == 2) {
             // Exact-accumulation variant: dequantize the FP8 codes (times their E8M0 block scale) to bf16 in
             // registers and use v_mfma_f32_32x32x16_bf16 (lane l: row l % 32, k = 8(l/32) .. +7 of a 16-wide window).
             // Window t of the 128-byte stage is LDS chunk t; lane half g reads its bytes 8g .. 8g+7.
@@ -353,7 +317,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
                 if (n + e < n_end) dst[e] = h4[e];
         }
     };
-    if constexpr (MF == 0 || MF == 2) {
+    if constexpr (MF == 2) {
         // 32x32 output: lane -> m = l % 32; register 4q+e -> n = 8q + 4(l/32) + e
 #pragma unroll
         for (int i = 0; i < 2; ++i)
