@@ -127,3 +127,29 @@ def test_adam_zero_gradient_steps(fused):
         if fused:
             ref = oracle.mx_quantize_f32(o_theta.reshape(rows, cols), oracle.RCEIL)
             assert all(np.array_equal(u8(a), b) for a, b in zip(cache, ref)), f"caches t={t}"
+
+
+def test_adam_first_moment_every_e4m3_code():
+    """The stored first moment holds every finite E4M3 code (subnormals, both signs, the maximum), so the step's decode
+    of m is checked on each of them: one step against the oracle, bit for bit."""
+    need_gpu()
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]                          # the two NaN codes are outside the contract
+    reps = 40
+    n = codes.size * reps
+    m0 = np.tile(codes, reps)
+    theta = workloads.workload5_params(n, DEV)
+    g = workloads.workload5_grad(n, 3, DEV)
+    m_q = torch.from_numpy(m0.copy()).to(DEV)
+    m_scale = torch.tensor([3.0], dtype=torch.float32, device=DEV)
+    v16 = oracle.f16_from_f32(np.abs(np.resize(np.linspace(1e-8, 1e-4, 997, dtype=np.float32), n)))
+    v = torch.from_numpy(v16.view(np.int16).copy()).view(torch.float16).to(DEV)
+    o_theta = theta.cpu().numpy().copy()
+    o_mq, o_ms, o_v = m0.copy(), np.array([3.0], np.float32), v16.copy()
+    hp, ohp = _hp(3, 0.0)
+    mxq.fp8_adam_step(theta, g, m_q, m_scale, v, None, hp)
+    torch.cuda.synchronize()
+    oracle.adam_step(o_theta, u16(g), o_mq, o_ms, o_v, ohp, want_w=False)
+    assert np.array_equal(theta.cpu().numpy().view(np.uint32), o_theta.view(np.uint32))
+    assert np.array_equal(u8(m_q), o_mq) and np.float32(m_scale.item()) == o_ms[0]
+    assert np.array_equal(u16(v), o_v)
