@@ -41,7 +41,8 @@ typedef enum {
     MXQ_ERR_NULL = 1,         /* a required pointer is NULL */
     MXQ_ERR_SHAPE = 2,        /* a size is negative, or not divisible as the operation requires */
     MXQ_ERR_ALIGN = 3,        /* a pointer is not 16-byte aligned */
-    MXQ_ERR_UNSUPPORTED = 4,  /* an enum value or combination the library does not implement */
+    MXQ_ERR_UNSUPPORTED = 4,  /* an enum value or combination the library does not implement, or an Adam beta
+                                 outside [0, 1) */
     MXQ_ERR_WORKSPACE = 5,    /* workspace missing or smaller than mxq_workspace_bytes() */
     MXQ_ERR_HIP = 6           /* a HIP launch or query failed */
 } mxq_status;
@@ -260,7 +261,9 @@ mxq_status grouped_wgrad_mx(const uint8_t* a_q, const uint8_t* a_s, const uint8_
                             const int64_t* group_offsets, int64_t G, int64_t M, int64_t N, int64_t Kt,
                             uint16_t* c_bf16, float* c_f32, hipStream_t stream);
 
-/* Adam hyper-parameters, passed by HOST pointer. step is the 1-based step count t. */
+/* Adam hyper-parameters, passed by HOST pointer. step is the 1-based step count t (MXQ_ERR_SHAPE if below 1);
+ * beta1 and beta2 lie in [0, 1) (MXQ_ERR_UNSUPPORTED otherwise, NaN included). Every Adam entry point checks both
+ * before its early return for an empty tensor, so a call with n == 0 still reports a bad setting. */
 typedef struct {
     float lr, beta1, beta2, eps, weight_decay;
     int64_t step;
@@ -275,7 +278,8 @@ typedef struct {
  *   theta -= lr ((m_t c1) / (sqrt(v_t c2) + eps) + wd theta);
  *   the new first-moment scale is 448 / max(amax(m_t), 1e-12) (current scaling), and m_q = E4M3(m_t * scale).
  * Every fp32 operation is rounded separately (no fused multiply-add); sqrt and division are correctly rounded; the
- * bias-correction scalars are computed on the host in double and rounded once to float.
+ * bias-correction scalars are computed on the host in double and rounded once to float, b^t as the product of t
+ * factors (the host loop ends once a further factor changes neither product, so any step count costs bounded time).
  * workspace: device scratch of at least mxq_workspace_bytes("adam", n) bytes, clobbered.
  */
 mxq_status fp8_adam_step(float* master, const uint16_t* grad_bf16, uint8_t* m_q, float* m_scale,

@@ -21,13 +21,23 @@ constexpr int64_t kMaxHistory = 1 << 20;
 
 constexpr int64_t kMaxGridY = 65535;
 
-// Adam's host scalars in double, each rounded once to float. beta^t is the product of t factors (it reaches 0 long
-// before t is large, after which further factors change nothing).
+// Adam's moment decay rates lie in [0, 1): the bias corrections divide by 1 - beta^t. NaN fails both comparisons.
+bool betas_ok(const mxq_adam_hparams& hp) {
+    return hp.beta1 >= 0.0f && hp.beta1 < 1.0f && hp.beta2 >= 0.0f && hp.beta2 < 1.0f;
+}
+
+// Adam's host scalars in double, each rounded once to float. beta^t is the product of t factors. The loop stops
+// once one more factor would change neither product: from there on every further factor returns the same values
+// (0, 1, or the smallest subnormal, where beta >= 0.5 leaves it in place), so the result equals the full product
+// and the time taken is bounded for any step count. A NaN product also stays NaN.
 mxq::AdamConsts adam_consts(const mxq_adam_hparams& hp) {
     double p1 = 1.0, p2 = 1.0;
-    for (int64_t t = 0; t < hp.step && (p1 != 0.0 || p2 != 0.0); ++t) {
-        p1 *= (double)hp.beta1;
-        p2 *= (double)hp.beta2;
+    for (int64_t t = 0; t < hp.step; ++t) {
+        const double n1 = p1 * (double)hp.beta1, n2 = p2 * (double)hp.beta2;
+        const bool fixed = (n1 == p1 || (n1 != n1 && p1 != p1)) && (n2 == p2 || (n2 != n2 && p2 != p2));
+        p1 = n1;
+        p2 = n2;
+        if (fixed) break;
     }
     mxq::AdamConsts k;
     k.b1 = hp.beta1;
@@ -52,7 +62,7 @@ const char* mxq_status_string(mxq_status s) {
         case MXQ_ERR_NULL: return "a required pointer is NULL";
         case MXQ_ERR_SHAPE: return "a size is negative or not divisible as the operation requires";
         case MXQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-        case MXQ_ERR_UNSUPPORTED: return "unsupported format, rule or scaling mode";
+        case MXQ_ERR_UNSUPPORTED: return "unsupported format, rule, scaling mode or optimizer setting";
         case MXQ_ERR_WORKSPACE: return "workspace missing or too small";
         case MXQ_ERR_HIP: return "HIP launch failed";
     }
@@ -292,6 +302,7 @@ mxq_status fp8_adam_step(float* master, const uint16_t* grad_bf16, uint8_t* m_q,
                          size_t workspace_bytes, hipStream_t stream) {
     if (!hp) return MXQ_ERR_NULL;
     if (n < 0 || hp->step < 1) return MXQ_ERR_SHAPE;
+    if (!betas_ok(*hp)) return MXQ_ERR_UNSUPPORTED;
     if (n == 0) return MXQ_OK;                                 // empty: no element and no scale changes
     if (!master || !grad_bf16 || !m_q || !m_scale || !v_fp16) return MXQ_ERR_NULL;
     if (!al16(master) || !al16(grad_bf16) || !al16(m_q) || !al16(v_fp16) || (w_bf16 && !al16(w_bf16)) || !al4(m_scale))
@@ -317,6 +328,7 @@ mxq_status fp8_adam_step_mx_cache(float* master, const uint16_t* grad_bf16, uint
     if (rule != MXQ_SCALE_RCEIL && rule != MXQ_SCALE_FLOOR) return MXQ_ERR_UNSUPPORTED;
     if (rows < 0 || cols < 0 || cols % 8 != 0 || hp->step < 1) return MXQ_ERR_SHAPE;
     if ((row && cols % 32 != 0) || (col && rows % 32 != 0)) return MXQ_ERR_SHAPE;
+    if (!betas_ok(*hp)) return MXQ_ERR_UNSUPPORTED;
     if ((rows + 63) / 64 > kMaxGridY) return MXQ_ERR_SHAPE;
     if (rows == 0 || cols == 0) return MXQ_OK;
     if (!master || !grad_bf16 || !m_q || !m_scale || !v_fp16) return MXQ_ERR_NULL;
@@ -340,6 +352,7 @@ mxq_status fp8_adam_step_delayed(float* master, const uint16_t* grad_bf16, uint8
                                  size_t workspace_bytes, hipStream_t stream) {
     if (!hp) return MXQ_ERR_NULL;
     if (n < 0 || hp->step < 1 || history_len < 1 || history_len > kMaxHistory) return MXQ_ERR_SHAPE;
+    if (!betas_ok(*hp)) return MXQ_ERR_UNSUPPORTED;
     if (n == 0) return MXQ_OK;
     if (!master || !grad_bf16 || !m_q || !m_scale || !v_fp16 || !m_history || !hist_pos) return MXQ_ERR_NULL;
     if (!al16(master) || !al16(grad_bf16) || !al16(m_q) || !al16(v_fp16) || (w_bf16 && !al16(w_bf16)) ||

@@ -228,3 +228,20 @@ def test_grouped_strided_and_wgrad_validation():
     assert w(None, P, P, P, P, 4, 64, 64, 128, P, None, None) == 1
     assert w(MIS, P, P, P, P, 4, 64, 64, 128, P, None, None) == 3
     assert w(P, P, P, P, P + 4, 4, 64, 64, 128, P, None, None) == 3
+
+
+@pytest.mark.parametrize("b1,b2", [(1.0, 0.95), (0.9, 1.0), (-0.1, 0.95), (0.9, -1e-30), (float("nan"), 0.95),
+                                   (0.9, float("inf"))])
+def test_adam_betas_outside_unit_interval_rejected(b1, b2):
+    """Adam's bias corrections divide by 1 - beta^t, so each beta must lie in [0, 1). The check precedes the early
+    return for an empty tensor, so it is exercised here with n == 0 and no device call."""
+    lib = _lib.load()
+    hp = _lib.AdamHParams(3e-4, b1, b2, 1e-8, 0.0, 5)
+    assert lib.fp8_adam_step(None, None, None, None, None, None, 0, C.byref(hp), None, 0, None) == 4
+    assert lib.fp8_adam_step_delayed(None, None, None, None, None, None, 0, C.byref(hp), None, None, 4, None, 0,
+                                     None) == 4
+    assert lib.fp8_adam_step_mx_cache(None, None, None, None, None, None, 0, 64, P, P, None, None, 0, C.byref(hp),
+                                      None, 0, None) == 4
+    ok = _lib.AdamHParams(3e-4, 0.0, 0.999, 1e-8, 0.0, 5)                  # 0 is allowed
+    assert lib.fp8_adam_step(None, None, None, None, None, None, 0, C.byref(ok), None, 0, None) == 0
+    assert lib.mxq_status_string(4).decode().endswith("optimizer setting")

@@ -42,6 +42,42 @@ def test_adam_steps_bit_exact(n, wd):
         assert np.array_equal(u16(w), o_w), f"w t={t}"
 
 
+def _products_fixed_at(b1, b2):
+    """Smallest t at which one more factor leaves both double products b1^t, b2^t (formed factor by factor, as the
+    oracle forms them) unchanged; every larger t gives the same products."""
+    b1, b2 = float(np.float32(b1)), float(np.float32(b2))
+    p1 = p2 = 1.0
+    t = 0
+    while not (p1 * b1 == p1 and p2 * b2 == p2):
+        p1, p2, t = p1 * b1, p2 * b2, t + 1
+    return t
+
+
+@pytest.mark.parametrize("step", [2 ** 40, 2 ** 62])
+def test_adam_huge_step_count_matches_oracle_at_the_fixed_point(step):
+    """A step count far beyond what any loop can run: the host's bias-correction products settle (the products stop
+    changing after about 14,500 factors for these betas), so the library returns at once, and its step equals the
+    oracle's at the step count where the products settle."""
+    need_gpu()
+    t_fix = _products_fixed_at(0.9, 0.95)
+    assert 1000 < t_fix < 100_000
+    n = 4099
+    theta = workloads.workload5_params(n, DEV)
+    m_q = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    m_scale = torch.ones(1, dtype=torch.float32, device=DEV)
+    v = torch.zeros(n, dtype=torch.float16, device=DEV)
+    w = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    o_theta = theta.cpu().numpy().copy()
+    o_mq = np.zeros(n, np.uint8); o_ms = np.ones(1, np.float32); o_v = np.zeros(n, np.uint16)
+    g = workloads.workload5_grad(n, 1, DEV)
+    mxq.fp8_adam_step(theta, g, m_q, m_scale, v, w, mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.0, step))
+    torch.cuda.synchronize()
+    _, o_w = oracle.adam_step(o_theta, u16(g), o_mq, o_ms, o_v, _hp(t_fix, 0.0)[1])
+    assert np.array_equal(theta.cpu().numpy().view(np.uint32), o_theta.view(np.uint32))
+    assert np.array_equal(u8(m_q), o_mq) and np.float32(m_scale.item()) == o_ms[0]
+    assert np.array_equal(u16(v), o_v) and np.array_equal(u16(w), o_w)
+
+
 def test_adam_without_weight_copy_and_zero_length():
     need_gpu()
     n = 4099
