@@ -22,7 +22,8 @@
  * Sources (page titles and sections):
  *   [OLMO11] "OLMo-core MoE, Section 11: MXFP8 Training" — Eq. 57, Eq. 58, Figures 47/49/50/55, Eq. 60,
  *            Sections 11.2.1, 11.3.2, 11.3.4, 11.3.5 / Table 24, 11.4.1, 11.4.4 / Table 25.
- *   [LLMSB]  "3.8 Mixed Precision, bf16 & FP8 Training" — per-tensor scaling, delayed scaling, Exercise 6.
+ *   [LLMSB]  "3.8 Mixed Precision, bf16 & FP8 Training" — per-tensor scaling, delayed scaling, Exercise 6,
+ *            "Tensor cores accumulate in fp32" (and its caveat on FP8 accumulators).
  *   [FP8-LM] "FP8-LM: Training FP8 Large Language Models" — tensor scaling, AdamW update, Eq. 7-8.
  */
 #ifndef MXQ_H
@@ -198,16 +199,33 @@ mxq_status fp8_requantize_shared(const uint8_t* q_in, int64_t n, mxq_fp8 fmt_in,
  *   MX_BLOCK32: a_scale = E8M0 bytes [M][K/32], b_scale = [N][K/32]; a_fmt = b_fmt = E4M3;
  *               C = sum_k (val(a_q) 2^(sa-127)) (val(b_q) 2^(sb-127)).
  * Requires K % 32 == 0 and K > 0; M, N >= 1 are arbitrary; c_bf16 needs only 2-byte alignment.
- * Accuracy: every output is within 2^-7 |y| + 2^-20 sum_k |a_k b_k| of the exact product y of the dequantized
- * operands on the workloads measured. gfx950's FP8 matrix instructions sum the products of each 32-value block in
- * a narrow window (small products lose low bits), so for K < 12288 the library dequantizes the operands exactly to
- * bf16 and uses the bf16 matrix instruction (fp32-quality accumulation, half the FP8 rate); from K >= 12288 it uses
- * the block-scaled FP8 instruction, whose error relative to the bound shrinks with K.
+ * Accuracy: gfx950's FP8 matrix instructions sum the products of each 32-value block in a narrow window (products
+ * far below the block's largest lose low bits). For K < 12288 the library therefore dequantizes the operands exactly
+ * to bf16 and uses the bf16 matrix instruction (fp32-quality accumulation, half the FP8 rate); from K >= 12288 it
+ * uses the block-scaled FP8 instruction. Every output is within 2^-7 |y| + 2^-20 sum_k |a_k b_k| of the exact
+ * product y of the dequantized operands for operands whose 32-value blocks hold values of similar magnitude, such
+ * as normally distributed data, where the FP8 instruction's error relative to that bound shrinks with K. For
+ * wide-range operands (rare large outliers, magnitudes spread over many binades, columns scaled differently) the FP8
+ * instruction's error exceeds that bound several times over at any K; use scaled_gemm_exact for those.
  */
 mxq_status scaled_gemm(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fmt,
                        const uint8_t* b_q, const void* b_scale, mxq_fp8 b_fmt,
                        int64_t M, int64_t N, int64_t K, mxq_scaling scaling,
                        uint16_t* c_bf16, int64_t ldc, hipStream_t stream);
+
+/*
+ * scaled_gemm on the exact path at every K: both operands are dequantized to bf16 in registers (every FP8 value times
+ * its power-of-two block scale, or the per-tensor code, is exact in bf16), multiplied with the bf16 matrix
+ * instruction and accumulated in fp32 ([LLMSB] "Tensor cores accumulate in fp32": narrow inputs, a wide accumulator;
+ * the same page's caveat that an FP8 accumulator need not keep full fp32 precision is what this path avoids).
+ * Arguments, layouts, requirements and outputs are those of scaled_gemm. The bound 2^-7 |y| + 2^-20 sum_k |a_k b_k|
+ * then holds for wide-range operands too; the matrix rate is half the FP8 instruction's for K >= 12288 (for
+ * K < 12288 scaled_gemm already takes this path, and the two give identical bytes).
+ */
+mxq_status scaled_gemm_exact(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fmt,
+                             const uint8_t* b_q, const void* b_scale, mxq_fp8 b_fmt,
+                             int64_t M, int64_t N, int64_t K, mxq_scaling scaling,
+                             uint16_t* c_bf16, int64_t ldc, hipStream_t stream);
 
 /*
  * Grouped MX GEMM over ragged expert groups ([OLMO11] Section 11.4.1, routed experts: the up/gate and down

@@ -50,6 +50,7 @@ struct GemmArgs {
     int64_t c_gstride;                 // token groups: distance from one expert's output to the next
     const int64_t* offsets;            // grouped only: [G+1]
     int64_t G;
+    int exact;                         // host only: take the exact path whatever K is
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
@@ -1066,7 +1067,7 @@ static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks_small, unsign
         else
             hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GM, 2>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
     } else {
-        const bool fp8 = a.K >= kFp8MinK;
+        const bool fp8 = !a.exact && a.K >= kFp8MinK;
         if (use_big(a, MX, GM == GM_ROWS)) {
             if (fp8) hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GM, 1>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
             else hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GM, 2>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
@@ -1080,9 +1081,9 @@ static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks_small, unsign
 
 hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt, const uint8_t* b_q,
                               const void* b_scale, int b_fmt, int64_t M, int64_t N, int64_t K, int mx,
-                              uint16_t* c, int64_t ldc, hipStream_t stream) {
+                              uint16_t* c, int64_t ldc, bool exact, hipStream_t stream) {
     GemmArgs a{};
-    a.a = a_q; a.b = b_q; a.c = c; a.M = M; a.N = N; a.K = K; a.ldc = ldc;
+    a.a = a_q; a.b = b_q; a.c = c; a.M = M; a.N = N; a.K = K; a.ldc = ldc; a.exact = exact ? 1 : 0;
     a.lda = K; a.ldb = K; a.ldsa = K / 32; a.ldsb = K / 32;
     if (mx) { a.sa = (const uint8_t*)a_scale; a.sb = (const uint8_t*)b_scale; }
     else { a.pa = (const float*)a_scale; a.pb = (const float*)b_scale; }

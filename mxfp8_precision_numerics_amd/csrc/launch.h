@@ -27,7 +27,7 @@ hipError_t launch_swiglu_mx_quantize(const uint16_t* c, int64_t rows, int64_t F,
 
 hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt, const uint8_t* b_q,
                               const void* b_scale, int b_fmt, int64_t M, int64_t N, int64_t K, int mx,
-                              uint16_t* c, int64_t ldc, hipStream_t stream);
+                              uint16_t* c, int64_t ldc, bool exact, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* offsets, int64_t G,
                                int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s, int64_t ldb,

@@ -20,6 +20,11 @@ Workloads (sizes are those of the five configurations; the tests also use smalle
   6  FP8 gradient all-reduce pieces: per rank r of 8, the weight gradient of workload 2's W (36864 x 12288 values),
      N(0, 1e-3 * 2^(r/4)) with round(2e-5 n) positions multiplied by 1000 before the bf16 cast (step t: index
      16 t + 2 r, positions 16 t + 2 r + 1).
+Wide-range operands (GEMM accuracy tests beyond the normal data of the configurations): N(0,1) values with
+  "outliers"    workload 3's recipe (0.1 % of positions x 100),
+  "loguniform"  random signs and magnitudes 2^u, u uniform in [-12, 12),
+  "colscale"    every column scaled by 2^u, u uniform in [-8, 8),
+  "sparse"      90 % of the values zeroed (uniform mask).
 """
 from __future__ import annotations
 
@@ -52,6 +57,27 @@ def uniform_f32(shape, lo: float, hi: float, workload: int, k: int, device="cpu"
 
 def normal_bf16(shape, std: float, workload: int, k: int, device="cpu") -> torch.Tensor:
     return normal_f32(shape, std, workload, k, device).to(torch.bfloat16)
+
+
+WIDE_RANGE_KINDS = ("outliers", "loguniform", "colscale", "sparse")
+
+
+def wide_range_bf16(shape, kind: str, workload: int, k: int, device="cpu") -> torch.Tensor:
+    """A [rows][cols] operand whose 32-value blocks span a wide range of magnitudes (kinds in the module notes)."""
+    rows, cols = shape
+    if kind == "outliers":
+        return normal_bf16_with_outliers(shape, 1.0, 0.001, 100.0, workload, k, k + 1, device)
+    x = normal_f32(shape, 1.0, workload, k, device)
+    u = _gen(workload, k + 1, device)
+    if kind == "loguniform":
+        x = torch.sign(x) * torch.exp2(torch.rand(tuple(shape), generator=u, device=device) * 24.0 - 12.0)
+    elif kind == "colscale":
+        x = x * torch.exp2(torch.rand((1, cols), generator=u, device=device) * 16.0 - 8.0)
+    elif kind == "sparse":
+        x = x * (torch.rand(tuple(shape), generator=u, device=device) < 0.1)
+    else:
+        raise ValueError(kind)
+    return x.to(torch.bfloat16)
 
 
 def normal_bf16_with_outliers(shape, std: float, frac: float, factor: float, workload: int, k: int,

@@ -274,3 +274,41 @@ def test_grouped_gemm_workload4_up_and_down_sampled():
             pad |= (rows >= offsets[g] + counts[g]) & (rows < offsets[g + 1])
         _bound_check(Ch, y, S, "workload4 " + name)
         assert np.all(Ch[pad] == 0)
+
+
+@pytest.mark.parametrize("kind", workloads.WIDE_RANGE_KINDS)
+@pytest.mark.parametrize("M,N,K", [(264, 272, 12288), (520, 528, 12288), (516, 520, 36864)])
+def test_exact_entry_point_meets_the_bound_on_wide_range_operands(kind, M, N, K):
+    """scaled_gemm_exact at K >= 12288 (where scaled_gemm takes the FP8 instruction), small and large tiles, MX and
+    per-tensor (E4M3 x E5M2), on operands whose blocks span a wide range of magnitudes: every element within the
+    bound."""
+    need_gpu()
+    say("gemm exact wide-range", kind, M, N, K)
+    A = workloads.wide_range_bf16((M, K), kind, 34, 2 * K + M, DEV)
+    B = workloads.wide_range_bf16((N, K), kind, 34, 2 * K + N + 5, DEV)
+    aq, as_, bq, bs = _mx_operands(A, B)
+    C = mxq.scaled_gemm(aq, as_, bq, bs, mxq.MX_BLOCK32, exact=True)
+    torch.cuda.synchronize()
+    y, S = oracle.gemm_ref(u8(aq), u8(as_), oracle.E4M3, u8(bq), u8(bs), oracle.E4M3, oracle.MX_BLOCK32)
+    _bound_check(C.float().cpu().numpy(), y, S, f"MX exact {kind}")
+    pa = mxq.pertensor_quantize(A, mxq.E4M3, want_qt=False)
+    pb = mxq.pertensor_quantize(B, mxq.E5M2, want_qt=False)
+    C = mxq.scaled_gemm(pa.q, pa.scale, pb.q, pb.scale, mxq.PER_TENSOR, mxq.E4M3, mxq.E5M2, exact=True)
+    torch.cuda.synchronize()
+    y, S = oracle.gemm_ref(u8(pa.q), np.float32(pa.scale.item()), oracle.E4M3, u8(pb.q),
+                           np.float32(pb.scale.item()), oracle.E5M2, oracle.PER_TENSOR)
+    _bound_check(C.float().cpu().numpy(), y, S, f"per-tensor exact {kind}")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 200, 4096), (520, 528, 8192), (512, 512, 12256)])
+def test_exact_entry_point_equals_scaled_gemm_below_the_fp8_threshold(M, N, K):
+    """Below K = 12288 scaled_gemm already takes the exact path: both entry points give identical bytes."""
+    need_gpu()
+    say("gemm exact == default", M, N, K)
+    A = workloads.normal_bf16((M, K), 1.0, 34, 1, DEV)
+    B = workloads.normal_bf16((N, K), 1.0, 34, 2, DEV)
+    aq, as_, bq, bs = _mx_operands(A, B)
+    c0 = mxq.scaled_gemm(aq, as_, bq, bs, mxq.MX_BLOCK32)
+    c1 = mxq.scaled_gemm(aq, as_, bq, bs, mxq.MX_BLOCK32, exact=True)
+    torch.cuda.synchronize()
+    assert torch.equal(c0.view(torch.int16), c1.view(torch.int16))
