@@ -235,7 +235,8 @@ mxq_status scaled_gemm_exact(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_
  *   a_q[total_rows][K], a_s[total_rows][K/32]; b_q[G][N][K], b_s[G][N][K/32]; c_bf16[total_rows][N].
  * Requires K % 32 == 0, N >= 1, 1 <= G <= 4096. The offsets are read on the device only (no host round trip); the
  * host cannot check them, so offsets that break the rules above give unspecified output rows (never stray writes:
- * rows are clamped to [0, total_rows)).
+ * rows are clamped to [0, total_rows)). The instruction choice and its accuracy are scaled_gemm's: the exact bf16
+ * path for K < 12288 (every routed projection of the workloads), the FP8 instruction from K >= 12288.
  */
 mxq_status grouped_scaled_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* group_offsets, int64_t G,
                                int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s,
