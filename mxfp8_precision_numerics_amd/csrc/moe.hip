@@ -21,6 +21,34 @@ namespace mxq {
 
 constexpr int MT_ROWS = 64, MT_COLS = 128, MT_THREADS = 256;
 
+// Column orientation of one 32-row block: the fp32 values d[0..31] of tile column c (rows grow .. grow+31) become
+// one E8M0 byte and 32 codes, stored at output column oc0 + c (skipped for columns at or past climit and for a
+// block past the last row).
+template <int RULE>
+__device__ __forceinline__ void mx_col_block_out(const float (&d)[32], int64_t c0, int c, int64_t grow, int64_t climit,
+                                                 int64_t oc0, int64_t rows, uint8_t* __restrict__ q_col,
+                                                 uint8_t* __restrict__ s_col) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) m = max(m, __float_as_uint(d[r]) & 0x7FFFFFFFu);
+    const uint32_t byte = mx_scale_byte_f32(m, RULE);
+    const float f = mx_inv_scale_f32(byte);
+    uint32_t out[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float y0 = clamp_keep_nan(d[4 * q] * f, 448.0f), y1 = clamp_keep_nan(d[4 * q + 1] * f, 448.0f);
+        const float y2 = clamp_keep_nan(d[4 * q + 2] * f, 448.0f), y3 = clamp_keep_nan(d[4 * q + 3] * f, 448.0f);
+        out[q] = cvt_f32_pair<FMT_E4M3, true>(cvt_f32_pair<FMT_E4M3, false>(0u, y0, y1), y2, y3);
+    }
+    if (c0 + c < climit && grow + 32 <= rows) {
+        const int64_t ocol = oc0 + c;
+        uint4* q = reinterpret_cast<uint4*>(q_col + ocol * rows + grow);
+        q[0] = make_uint4(out[0], out[1], out[2], out[3]);
+        q[1] = make_uint4(out[4], out[5], out[6], out[7]);
+        s_col[ocol * (rows / 32) + grow / 32] = (uint8_t)byte;
+    }
+}
+
 // Quantize the tile's fp32 values x[j][e] (row r0 + t/16 + 16 j, column c0 + 8 (t % 16) + e of the input) into the
 // output matrix [rows][ocols] at output column oc0 + (column - c0). Columns at or past climit are outside the input
 // (their x are 0 and nothing is stored for them). climit and ocols are multiples of 32, rows a multiple of 32.
@@ -63,31 +91,11 @@ __device__ __forceinline__ void mx_tile_out(const float (&x)[4][8], float* tile,
         }
         __syncthreads();
         const int c = tid & (MT_COLS - 1), b = tid >> 7;
-        const int64_t grow = r0 + 32 * b;
         float d[32];
-        uint32_t m = 0;
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            d[r] = tile[(32 * b + r) * MT_COLS + c];
-            m = max(m, __float_as_uint(d[r]) & 0x7FFFFFFFu);
-        }
+        for (int r = 0; r < 32; ++r) d[r] = tile[(32 * b + r) * MT_COLS + c];
         __syncthreads();                                      // the tile may be refilled after this
-        const uint32_t byte = mx_scale_byte_f32(m, RULE);
-        const float f = mx_inv_scale_f32(byte);
-        uint32_t out[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float y0 = clamp_keep_nan(d[4 * q] * f, 448.0f), y1 = clamp_keep_nan(d[4 * q + 1] * f, 448.0f);
-            const float y2 = clamp_keep_nan(d[4 * q + 2] * f, 448.0f), y3 = clamp_keep_nan(d[4 * q + 3] * f, 448.0f);
-            out[q] = cvt_f32_pair<FMT_E4M3, true>(cvt_f32_pair<FMT_E4M3, false>(0u, y0, y1), y2, y3);
-        }
-        if (c0 + c < climit && grow + 32 <= rows) {
-            const int64_t ocol = oc0 + c;
-            uint4* q = reinterpret_cast<uint4*>(q_col + ocol * rows + grow);
-            q[0] = make_uint4(out[0], out[1], out[2], out[3]);
-            q[1] = make_uint4(out[4], out[5], out[6], out[7]);
-            s_col[ocol * (rows / 32) + grow / 32] = (uint8_t)byte;
-        }
+        mx_col_block_out<RULE>(d, c0, c, r0 + 32 * b, climit, oc0, rows, q_col, s_col);
     }
 }
 
@@ -97,7 +105,11 @@ __global__ __launch_bounds__(MT_THREADS) void route_weighted_mx_kernel(const uin
                                                                       const float* __restrict__ p, int64_t rows,
                                                                       int64_t cols, uint8_t* q_row, uint8_t* s_row,
                                                                       uint8_t* q_col, uint8_t* s_col) {
-    __shared__ __attribute__((aligned(16))) float tile[COL ? MT_ROWS * MT_COLS : 1];
+    // The column orientation keeps the tile's bf16 gradient and its rows' route weights in LDS (16.25 KiB, so twice
+    // as many workgroups fit on a CU as with an fp32 tile) and forms each product again: p * dy is one fp32
+    // multiply, so both orientations quantize the same values.
+    __shared__ __attribute__((aligned(16))) uint16_t tile[COL ? MT_ROWS * MT_COLS : 1];
+    __shared__ float pw[COL ? MT_ROWS : 1];
     const int tid = threadIdx.x;
     const int ch = tid & 15, rr = tid >> 4;
     const int64_t r0 = (int64_t)blockIdx.y * MT_ROWS, c0 = (int64_t)blockIdx.x * MT_COLS;
@@ -106,17 +118,30 @@ __global__ __launch_bounds__(MT_THREADS) void route_weighted_mx_kernel(const uin
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t gr = r0 + rr + 16 * j;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        float w = 0.0f;
+        if (gr < rows) w = p[gr];
+        if (gc < cols && gr < rows) v = ldnt16(dy + gr * cols + gc);
+        const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[j][e] = 0.0f;
-        if (gc < cols && gr < rows) {
-            const float w = p[gr];
-            const uint4 v = ldnt16(dy + gr * cols + gc);
-            const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[j][e] = w * ((e & 1) ? bf16_hi(vw[e >> 1]) : bf16_lo(vw[e >> 1]));
+        for (int e = 0; e < 8; ++e) x[j][e] = w * ((e & 1) ? bf16_hi(vw[e >> 1]) : bf16_lo(vw[e >> 1]));
+        if constexpr (COL) {
+            *reinterpret_cast<uint4*>(&tile[(rr + 16 * j) * MT_COLS + 8 * ch]) = v;
+            if (ch == 0) pw[rr + 16 * j] = w;
         }
     }
-    mx_tile_out<RULE, ROW, COL>(x, tile, r0, c0, cols, c0, rows, cols, q_row, s_row, q_col, s_col);
+    if constexpr (ROW) mx_tile_out<RULE, true, false>(x, nullptr, r0, c0, cols, c0, rows, cols, q_row, s_row, q_col, s_col);
+    if constexpr (COL) {
+        __syncthreads();
+        const int c = tid & (MT_COLS - 1), b = tid >> 7;
+        float d[32];
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            const uint32_t h = tile[(32 * b + r) * MT_COLS + c];
+            d[r] = pw[32 * b + r] * __uint_as_float(h << 16);
+        }
+        mx_col_block_out<RULE>(d, c0, c, r0 + 32 * b, cols, c0, rows, q_col, s_col);
+    }
 }
 
 // ---------------------------------------------------------------------------------------- SwiGLU forward, saved
