@@ -83,9 +83,10 @@ __global__ void autoscale_finalize_kernel(const unsigned long long* __restrict__
 
 hipError_t launch_autoscale_cast(const uint16_t* g, int64_t n, int fmt, float* mu, uint8_t* q, float* scale_out,
                                  unsigned long long* overflow, unsigned long long* count, hipStream_t stream) {
-    int64_t blocks = (n / 8 + GC_THREADS * 4 - 1) / (GC_THREADS * 4);
+    // one 8-value chunk per thread over a full grid: more requests in flight than a looping grid of a few thousand
+    int64_t blocks = (n / 8 + GC_THREADS - 1) / GC_THREADS;
     if (blocks < 1) blocks = 1;
-    if (blocks > 4096) blocks = 4096;
+    if (blocks > (int64_t(1) << 30)) blocks = int64_t(1) << 30;
     hipLaunchKernelGGL(autoscale_prep_kernel, dim3(1), dim3(64), 0, stream, count);
     if (fmt == FMT_E4M3)
         hipLaunchKernelGGL(autoscale_cast_kernel<FMT_E4M3>, dim3((unsigned)blocks), dim3(GC_THREADS), 0, stream, g, n,
@@ -188,9 +189,10 @@ hipError_t launch_requantize_shared(const uint8_t* q_in, int64_t n, int fmt_in, 
                                     float* sum_out, hipStream_t stream) {
     hipLaunchKernelGGL(min_scale_kernel, dim3(1), dim3(GC_THREADS), 0, stream, scales, nranks, shared_out, sum_out);
     if (n > 0) {
-        int64_t blocks = (n / 16 + GC_THREADS * 4 - 1) / (GC_THREADS * 4);
+        // one 16-code chunk per thread; each workgroup's 256-entry table costs one evaluation per thread
+        int64_t blocks = (n / 16 + GC_THREADS - 1) / GC_THREADS;
         if (blocks < 1) blocks = 1;
-        if (blocks > 4096) blocks = 4096;
+        if (blocks > (int64_t(1) << 30)) blocks = int64_t(1) << 30;
         const dim3 grid((unsigned)blocks), blk(GC_THREADS);
         const float* sg = shared_out;
         if (fmt_in == FMT_E4M3 && fmt_out == FMT_E4M3)

@@ -446,7 +446,7 @@ hipError_t launch_swiglu_mx_quantize(const uint16_t* c, int64_t rows, int64_t F,
                                      hipStream_t stream) {
     const int64_t total = rows * (F / 8);
     int64_t blocks = (total + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
+    if (blocks > (int64_t(1) << 30)) blocks = int64_t(1) << 30;     // one chunk per thread (the loop is a guard)
     if (rule == RULE_FLOOR)
         hipLaunchKernelGGL(swiglu_mx_kernel<RULE_FLOOR>, dim3((unsigned)blocks), dim3(256), 0, stream, c, rows, F, q, s);
     else
