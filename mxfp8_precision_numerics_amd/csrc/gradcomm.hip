@@ -83,7 +83,7 @@ __global__ void autoscale_finalize_kernel(const unsigned long long* __restrict__
 
 hipError_t launch_autoscale_cast(const uint16_t* g, int64_t n, int fmt, float* mu, uint8_t* q, float* scale_out,
                                  unsigned long long* overflow, unsigned long long* count, hipStream_t stream) {
-    // one 8-value chunk per thread over a full grid: more requests in flight than a looping grid of a few thousand
+    // one 8-value chunk per thread over a full grid (measured faster than a looping grid of 4096 workgroups)
     int64_t blocks = (n / 8 + GC_THREADS - 1) / GC_THREADS;
     if (blocks < 1) blocks = 1;
     if (blocks > (int64_t(1) << 30)) blocks = int64_t(1) << 30;
