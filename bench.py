@@ -57,11 +57,11 @@ def log(*a):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
-    ap.add_argument("--profile-kernel", choices=["mx_gemm_fwd", "mx_gemm_wgrad", "copy"], default=None,
+    ap.add_argument("--profile-kernel", choices=PROFILE_KERNELS, default=None,
                     help="run only this kernel (10 launches) for hardware-counter passes, print its timing, exit")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -193,129 +193,149 @@ def main():
     torch.cuda.synchronize()
 
     Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    parts = ["mx_quant_XWdY", "mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "pt_quant", "pt_gemm_fwd", "mx_quant_act",
-             "grouped_q_up", "grouped_gemm_up", "grouped_q_down", "grouped_gemm_down", "adam", "small",
-             "pt_quant_delayed", "adam_delayed", "wcache_fused", "wcache_unfused", "moe_swiglu_mlp", "swiglu_quant",
-             "grad_cast", "grad_requant", "moe_fwd_train", "bwd_rw_quant", "bwd_dgrad_down", "bwd_swiglu_quant",
-             "bwd_dgrad_up", "bwd_wgrad_down", "bwd_wgrad_up", "mx_quant_act_row", "small_graph", "pt_gemm_dgrad",
-             "pt_gemm_wgrad"]
-    NEV = len(parts) + 1
+    # Parts bound by HBM bandwidth start with the last-level cache scrubbed (outside their timed window): a 512 MiB
+    # write evicts the 256 MB Infinity Cache, so no part reads its input from a cache a previous part filled.
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    HBM_PARTS = {"mx_quant_XWdY", "pt_quant", "mx_quant_act", "grouped_q_up", "grouped_q_down", "adam",
+                 "pt_quant_delayed", "adam_delayed", "wcache_fused", "wcache_unfused", "swiglu_quant", "grad_cast",
+                 "grad_requant", "bwd_rw_quant", "bwd_swiglu_quant", "mx_quant_act_row"}
+    parts = []
+    cur = {}
 
-    def step(ev):
-        ev[0].record(stream)
-        mxq.mx_quantize(X, out=mxX)
-        mxq.mx_quantize(W, out=mxW)
-        mxq.mx_quantize(dY, out=mxD)
-        ev[1].record(stream)
-        mxq.scaled_gemm(mxX.q_row, mxX.s_row, mxW.q_row, mxW.s_row, mxq.MX_BLOCK32, out=Y)            # Y = X W^T
-        ev[2].record(stream)
-        mxq.scaled_gemm(mxD.q_row, mxD.s_row, mxW.q_col, mxW.s_col, mxq.MX_BLOCK32, out=dX)          # dX = dY W
-        ev[3].record(stream)
-        mxq.scaled_gemm(mxD.q_col, mxD.s_col, mxX.q_col, mxX.s_col, mxq.MX_BLOCK32, out=dW)          # dW = dY^T X
-        ev[4].record(stream)
-        px = mxq.pertensor_quantize(X, mxq.E4M3, workspace=ws_pt)
-        pw = mxq.pertensor_quantize(W, mxq.E4M3, workspace=ws_pt)
-        pd = mxq.pertensor_quantize(dY, mxq.E5M2, workspace=ws_pt)
-        ev[5].record(stream)
-        mxq.scaled_gemm(px.q, px.scale, pw.q, pw.scale, mxq.PER_TENSOR, mxq.E4M3, mxq.E4M3, out=Y)
-        ev[6].record(stream)
-        mxq.mx_quantize(act3, out=mx3)
-        ev[7].record(stream)
-        mxq.mx_quantize(wl4["a_up"], colwise=False, out=mx_up)
-        ev[8].record(stream)
-        mxq.grouped_scaled_gemm(mx_up.q_row, mx_up.s_row, off4, qwu.q_row.view(G, d_ff, d_model),
-                                qwu.s_row.view(G, d_ff, d_model // 32), out=C_up)
-        ev[9].record(stream)
-        mxq.mx_quantize(wl4["a_down"], colwise=False, out=mx_dn)
-        ev[10].record(stream)
-        mxq.grouped_scaled_gemm(mx_dn.q_row, mx_dn.s_row, off4, qwd.q_row.view(G, d_model, d_ff),
-                                qwd.s_row.view(G, d_model, d_ff // 32), out=C_dn)
-        ev[11].record(stream)
-        mxq.fp8_adam_step(theta, grad, m_q, m_scale, v16, w16, hp, workspace=adam_ws)
-        ev[12].record(stream)
-        small_path()
-        ev[13].record(stream)
-        mxq.pertensor_quantize_delayed(X, hists["X"], hpos["X"], mxq.E4M3, workspace=ws_del)
-        mxq.pertensor_quantize_delayed(W, hists["W"], hpos["W"], mxq.E4M3, workspace=ws_del)
-        mxq.pertensor_quantize_delayed(dY, hists["dY"], hpos["dY"], mxq.E5M2, workspace=ws_del)
-        ev[14].record(stream)
-        mxq.fp8_adam_step_delayed(theta, grad, m_q, m_scale, v16, w16, hp, m_hist, m_pos, workspace=ws_adel)
-        ev[15].record(stream)
-        mxq.fp8_adam_step_mx_cache(th_w, g_w, mq_w, ms_w, v_w, None, hp, N, K, out=cache_w, workspace=ws_w)
-        ev[16].record(stream)
-        mxq.fp8_adam_step(th_w, g_w, mq_w, ms_w, v_w, wb_w, hp, workspace=ws_w)
-        mxq.mx_quantize(wb_w.view(N, K), out=cache_w)
-        ev[17].record(stream)
-        mxq.mx_quantize(wl4["a_up"], colwise=False, out=mx_up)
-        mxq.grouped_scaled_gemm(mx_up.q_row, mx_up.s_row, off4, qwgu.q_row.view(G, 2 * d_ff, d_model),
-                                qwgu.s_row.view(G, 2 * d_ff, d_model // 32), out=C_gu)
-        mxq.swiglu_mx_quantize(C_gu, out=mx_h)
-        mxq.grouped_scaled_gemm(mx_h.q_row, mx_h.s_row, off4, qwd.q_row.view(G, d_model, d_ff),
-                                qwd.s_row.view(G, d_model, d_ff // 32), out=C_dn)
-        ev[18].record(stream)
-        mxq.swiglu_mx_quantize(C_gu, out=mx_h)
-        ev[19].record(stream)
-        gc = mxq.fp8_autoscale_cast(dW, mu_g, mxq.E4M3, workspace=ws_g)
-        ev[20].record(stream)
+    def part(name, rec):
+        """Context for one timed part: scrub first if it is HBM-bound, then events around its launches."""
+        class _P:
+            def __enter__(self_):
+                if name in HBM_PARTS:
+                    scrub.zero_()
+                if name not in parts:
+                    parts.append(name)
+                e0, e1 = Ev(), Ev()
+                rec[name] = (e0, e1)
+                e0.record(stream)
+
+            def __exit__(self_, *exc):
+                rec[name][1].record(stream)
+                return False
+        return _P()
+
+    def step(rec):
+        with part("mx_quant_XWdY", rec):
+            mxq.mx_quantize(X, out=mxX)
+            mxq.mx_quantize(W, out=mxW)
+            mxq.mx_quantize(dY, out=mxD)
+        with part("mx_gemm_fwd", rec):
+            mxq.scaled_gemm(mxX.q_row, mxX.s_row, mxW.q_row, mxW.s_row, mxq.MX_BLOCK32, out=Y)          # Y = X W^T
+        with part("mx_gemm_dgrad", rec):
+            mxq.scaled_gemm(mxD.q_row, mxD.s_row, mxW.q_col, mxW.s_col, mxq.MX_BLOCK32, out=dX)        # dX = dY W
+        with part("mx_gemm_wgrad", rec):
+            mxq.scaled_gemm(mxD.q_col, mxD.s_col, mxX.q_col, mxX.s_col, mxq.MX_BLOCK32, out=dW)        # dW = dY^T X
+        with part("pt_quant", rec):
+            px = mxq.pertensor_quantize(X, mxq.E4M3, workspace=ws_pt)
+            pw = mxq.pertensor_quantize(W, mxq.E4M3, workspace=ws_pt)
+            pd = mxq.pertensor_quantize(dY, mxq.E5M2, workspace=ws_pt)
+        with part("pt_gemm_fwd", rec):
+            mxq.scaled_gemm(px.q, px.scale, pw.q, pw.scale, mxq.PER_TENSOR, mxq.E4M3, mxq.E4M3, out=Y)
+        with part("pt_gemm_dgrad", rec):
+            mxq.scaled_gemm(pd.q, pd.scale, pw.q_t, pw.scale, mxq.PER_TENSOR, mxq.E5M2, mxq.E4M3, out=dX)
+        with part("pt_gemm_wgrad", rec):
+            mxq.scaled_gemm(pd.q_t, pd.scale, px.q_t, px.scale, mxq.PER_TENSOR, mxq.E5M2, mxq.E4M3, out=dW)
+        with part("mx_quant_act", rec):
+            mxq.mx_quantize(act3, out=mx3)
+        with part("mx_quant_act_row", rec):
+            mxq.mx_quantize(act3, colwise=False, out=mx3_row)
+        with part("grouped_q_up", rec):
+            mxq.mx_quantize(wl4["a_up"], colwise=False, out=mx_up)
+        with part("grouped_gemm_up", rec):
+            mxq.grouped_scaled_gemm(mx_up.q_row, mx_up.s_row, off4, qwu.q_row.view(G, d_ff, d_model),
+                                    qwu.s_row.view(G, d_ff, d_model // 32), out=C_up)
+        with part("grouped_q_down", rec):
+            mxq.mx_quantize(wl4["a_down"], colwise=False, out=mx_dn)
+        with part("grouped_gemm_down", rec):
+            mxq.grouped_scaled_gemm(mx_dn.q_row, mx_dn.s_row, off4, qwd.q_row.view(G, d_model, d_ff),
+                                    qwd.s_row.view(G, d_model, d_ff // 32), out=C_dn)
+        with part("adam", rec):
+            mxq.fp8_adam_step(theta, grad, m_q, m_scale, v16, w16, hp, workspace=adam_ws)
+        with part("small", rec):
+            small_path()
+        with part("small_graph", rec):
+            small_graph.replay()
+        with part("pt_quant_delayed", rec):
+            mxq.pertensor_quantize_delayed(X, hists["X"], hpos["X"], mxq.E4M3, workspace=ws_del)
+            mxq.pertensor_quantize_delayed(W, hists["W"], hpos["W"], mxq.E4M3, workspace=ws_del)
+            mxq.pertensor_quantize_delayed(dY, hists["dY"], hpos["dY"], mxq.E5M2, workspace=ws_del)
+        with part("adam_delayed", rec):
+            mxq.fp8_adam_step_delayed(theta, grad, m_q, m_scale, v16, w16, hp, m_hist, m_pos, workspace=ws_adel)
+        with part("wcache_fused", rec):
+            mxq.fp8_adam_step_mx_cache(th_w, g_w, mq_w, ms_w, v_w, None, hp, N, K, out=cache_w, workspace=ws_w)
+        with part("wcache_unfused", rec):
+            mxq.fp8_adam_step(th_w, g_w, mq_w, ms_w, v_w, wb_w, hp, workspace=ws_w)
+            mxq.mx_quantize(wb_w.view(N, K), out=cache_w)
+        with part("moe_swiglu_mlp", rec):
+            mxq.mx_quantize(wl4["a_up"], colwise=False, out=mx_up)
+            mxq.grouped_scaled_gemm(mx_up.q_row, mx_up.s_row, off4, qwgu.q_row.view(G, 2 * d_ff, d_model),
+                                    qwgu.s_row.view(G, 2 * d_ff, d_model // 32), out=C_gu)
+            mxq.swiglu_mx_quantize(C_gu, out=mx_h)
+            mxq.grouped_scaled_gemm(mx_h.q_row, mx_h.s_row, off4, qwd.q_row.view(G, d_model, d_ff),
+                                    qwd.s_row.view(G, d_model, d_ff // 32), out=C_dn)
+        with part("swiglu_quant", rec):
+            mxq.swiglu_mx_quantize(C_gu, out=mx_h)
+        with part("grad_cast", rec):
+            gc = mxq.fp8_autoscale_cast(dW, mu_g, mxq.E4M3, workspace=ws_g)
         gathered[:1] = gc.scale
         gathered[1:] = others
-        mxq.fp8_requantize_shared(gc.q, mxq.E4M3, gc.scale, gathered, mxq.E4M3, out=q_req)
-        ev[21].record(stream)
-        mxq.mx_quantize(wl4["a_up"], out=mx_x2)
-        mxq.grouped_scaled_gemm(mx_x2.q_row, mx_x2.s_row, off4, qwgu.q_row.view(G, 2 * d_ff, d_model),
-                                qwgu.s_row.view(G, 2 * d_ff, d_model // 32), out=C_gu)
-        mxq.swiglu_mx_quantize_oriented(C_gu, out=mx_h2)
-        mxq.grouped_scaled_gemm(mx_h2.q_row, mx_h2.s_row, off4, qwd.q_row.view(G, d_model, d_ff),
-                                qwd.s_row.view(G, d_model, d_ff // 32), out=C_dn)
-        ev[22].record(stream)
-        mxq.route_weighted_mx_quantize(dy4, p4, out=mx_dyw)
-        ev[23].record(stream)
-        mxq.grouped_scaled_gemm_strided(mx_dyw.q_row, mx_dyw.s_row, off4, qwd_c.q_col, qwd_c.s_col, G, d_ff, d_model,
-                                        ldb=G * d_model, b_group_stride=d_model, ldbs=G * d_model // 32,
-                                        bs_group_stride=d_model // 32, out=dh4)
-        ev[24].record(stream)
-        mxq.swiglu_backward_mx_quantize(C_gu, dh4, out=mx_dc)
-        ev[25].record(stream)
-        mxq.grouped_scaled_gemm_strided(mx_dc.q_row, mx_dc.s_row, off4, qwgu.q_col, qwgu.s_col, G, d_model,
-                                        2 * d_ff, ldb=G * 2 * d_ff, b_group_stride=2 * d_ff,
-                                        ldbs=G * 2 * d_ff // 32, bs_group_stride=2 * d_ff // 32, out=dx4)
-        ev[26].record(stream)
-        mxq.grouped_wgrad_mx(mx_dyw.q_col, mx_dyw.s_col, mx_h2.q_col, mx_h2.s_col, off4, accumulate=sink_wd)
-        ev[27].record(stream)
-        mxq.grouped_wgrad_mx(mx_dc.q_col, mx_dc.s_col, mx_x2.q_col, mx_x2.s_col, off4, accumulate=sink_wgu)
-        ev[28].record(stream)
-        mxq.mx_quantize(act3, colwise=False, out=mx3_row)
-        ev[29].record(stream)
-        small_graph.replay()
-        ev[30].record(stream)
-        mxq.scaled_gemm(pd.q, pd.scale, pw.q_t, pw.scale, mxq.PER_TENSOR, mxq.E5M2, mxq.E4M3, out=dX)
-        ev[31].record(stream)
-        mxq.scaled_gemm(pd.q_t, pd.scale, px.q_t, px.scale, mxq.PER_TENSOR, mxq.E5M2, mxq.E4M3, out=dW)
-        ev[32].record(stream)
+        with part("grad_requant", rec):
+            mxq.fp8_requantize_shared(gc.q, mxq.E4M3, gc.scale, gathered, mxq.E4M3, out=q_req)
+        with part("moe_fwd_train", rec):
+            mxq.mx_quantize(wl4["a_up"], out=mx_x2)
+            mxq.grouped_scaled_gemm(mx_x2.q_row, mx_x2.s_row, off4, qwgu.q_row.view(G, 2 * d_ff, d_model),
+                                    qwgu.s_row.view(G, 2 * d_ff, d_model // 32), out=C_gu)
+            mxq.swiglu_mx_quantize_oriented(C_gu, out=mx_h2)
+            mxq.grouped_scaled_gemm(mx_h2.q_row, mx_h2.s_row, off4, qwd.q_row.view(G, d_model, d_ff),
+                                    qwd.s_row.view(G, d_model, d_ff // 32), out=C_dn)
+        with part("bwd_rw_quant", rec):
+            mxq.route_weighted_mx_quantize(dy4, p4, out=mx_dyw)
+        with part("bwd_dgrad_down", rec):
+            mxq.grouped_scaled_gemm_strided(mx_dyw.q_row, mx_dyw.s_row, off4, qwd_c.q_col, qwd_c.s_col, G, d_ff,
+                                            d_model, ldb=G * d_model, b_group_stride=d_model,
+                                            ldbs=G * d_model // 32, bs_group_stride=d_model // 32, out=dh4)
+        with part("bwd_swiglu_quant", rec):
+            mxq.swiglu_backward_mx_quantize(C_gu, dh4, out=mx_dc)
+        with part("bwd_dgrad_up", rec):
+            mxq.grouped_scaled_gemm_strided(mx_dc.q_row, mx_dc.s_row, off4, qwgu.q_col, qwgu.s_col, G, d_model,
+                                            2 * d_ff, ldb=G * 2 * d_ff, b_group_stride=2 * d_ff,
+                                            ldbs=G * 2 * d_ff // 32, bs_group_stride=2 * d_ff // 32, out=dx4)
+        with part("bwd_wgrad_down", rec):
+            mxq.grouped_wgrad_mx(mx_dyw.q_col, mx_dyw.s_col, mx_h2.q_col, mx_h2.s_col, off4, accumulate=sink_wd)
+        with part("bwd_wgrad_up", rec):
+            mxq.grouped_wgrad_mx(mx_dc.q_col, mx_dc.s_col, mx_x2.q_col, mx_x2.s_col, off4, accumulate=sink_wgu)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
-        step([Ev() for _ in range(NEV)])
+        step({})
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
-    evs = [[Ev() for _ in range(NEV)] for _ in range(args.steps)]
+    recs = [{} for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(evs[s])
+        step(recs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {p: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
-          for i, p in enumerate(parts)}
-    step_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][NEV - 1]) for s in range(args.steps)]))
+    # each part: the median over the timed steps of its event-timed device duration
+    ms = {p: float(np.median([recs[s][p][0].elapsed_time(recs[s][p][1]) for s in range(args.steps)])) for p in parts}
+    spread = {p: [round(float(np.min([recs[s][p][0].elapsed_time(recs[s][p][1]) for s in range(args.steps)])), 4),
+                  round(float(np.max([recs[s][p][0].elapsed_time(recs[s][p][1]) for s in range(args.steps)])), 4)]
+              for p in parts}
+    step_ms = float(np.median([recs[s][parts[0]][0].elapsed_time(recs[s][parts[-1]][1]) for s in range(args.steps)]))
     ms["pt_gemms"] = ms["pt_gemm_fwd"] + ms["pt_gemm_dgrad"] + ms["pt_gemm_wgrad"]
     ms["grouped"] = sum(ms[p] for p in ("grouped_q_up", "grouped_gemm_up", "grouped_q_down", "grouped_gemm_down"))
     grouped_gemm_ms = ms["grouped_gemm_up"] + ms["grouped_gemm_down"]
     bwd_parts = ("bwd_rw_quant", "bwd_dgrad_down", "bwd_swiglu_quant", "bwd_dgrad_up", "bwd_wgrad_down",
                  "bwd_wgrad_up")
     ms["moe_bwd"] = sum(ms[p] for p in bwd_parts)
-    log("per-part ms:", json.dumps({k: round(v, 4) for k, v in ms.items()}))
+    log("per-part ms (median):", json.dumps({k: round(v, 4) for k, v in ms.items()}))
 
     # ------------------------------------------------------------------ rates
     flop_gemm = 2.0 * M * N * K                              # each of fwd, dgrad, wgrad
@@ -373,27 +393,42 @@ def main():
         rate[k] = round(v, 3)
     log("rates:", json.dumps(rate))
 
-    attainable = measure_attainable(mxq, mxX.q_row, dev, stream)
+    attainable = measure_attainable(mxX.q_row, dev, stream)
     log("attainable:", json.dumps(attainable))
-    fwd_tflops = rate["mx_gemm_fwd_tflops"]
-    roofline = {"kernel": "scaled_gemm MX_BLOCK32 fwd 4096x36864x12288 (gemm_big_kernel, block-scaled FP8 MFMA)",
-                "bound": "mfma", "achieved": fwd_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(fwd_tflops / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic(),
-                "frac_of_attainable": round(fwd_tflops / attainable["mfma_fp8_tflops"], 4),
-                "algorithmic_flop_per_launch": flop_gemm, "avg_launch_ms": round(ms["mx_gemm_fwd"], 4)}
 
-    # The other large kernels of the step against their own bounds: wgrad (K = 4096) runs the exact path, whose
-    # matrix instruction is the bf16 one; the quantize and Adam streams are HBM-bound.
+    # Every MX GEMM is priced against the dense FP8 peak (its operands are FP8, whichever matrix instruction the
+    # library picks); the bf16-peak fraction of the exact-path GEMMs is kept as a secondary field. The headline
+    # roofline is the layer's dominant kernel, the GEMM that takes longest.
+    gemm_kernels = {
+        "mx_gemm_fwd": ("scaled_gemm MX_BLOCK32 fwd Y = X W^T, 4096x36864x12288", "mx_gemm_fwd_tflops"),
+        "mx_gemm_dgrad": ("scaled_gemm MX_BLOCK32 dgrad dX = dY W, 4096x12288x36864", "mx_gemm_dgrad_tflops"),
+        "mx_gemm_wgrad": ("scaled_gemm MX_BLOCK32 wgrad dW = dY^T X, 36864x12288x4096", "mx_gemm_wgrad_tflops"),
+    }
+
+    def gemm_roof(part_name):
+        label, key = gemm_kernels[part_name]
+        t = rate[key]
+        return {"kernel": label + " (" + path_of[part_name] + ")", "bound": "mfma", "achieved": t,
+                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(t / PEAK_FP8_TFLOPS, 4),
+                "traffic": measured_traffic(part_name),
+                "frac_of_attainable": round(t / attainable["mfma_fp8_tflops"], 4),
+                "frac_of_bf16_peak": round(t / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_flop_per_launch": flop_gemm, "avg_launch_ms": round(ms[part_name], 4),
+                "share_of_layer": round(ms[part_name] / mx_linear_ms, 4)}
+
+    path_of = {"mx_gemm_fwd": "K = 12288", "mx_gemm_dgrad": "K = 36864", "mx_gemm_wgrad": "K = 4096"}
+    dominant = max(gemm_kernels, key=lambda p: ms[p])
+    roofline = gemm_roof(dominant)
+
+    # The other large kernels of the step against their own bounds: the remaining MX GEMMs (FP8 peak) and the
+    # quantize and Adam streams (HBM).
     def hbm(name, gbs):
         return {"kernel": name, "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4),
                 "frac_of_attainable": round(gbs / attainable["hbm_copy_gbs"], 4)}
-    wg = rate["mx_gemm_wgrad_tflops"]
-    rooflines_other = [
-        {"kernel": "scaled_gemm MX_BLOCK32 wgrad 36864x12288x4096 (gemm_big_kernel, exact path: bf16 MFMA)",
-         "bound": "mfma", "achieved": wg, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-         "frac": round(wg / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(ms["mx_gemm_wgrad"], 4)},
+    rooflines_other = [gemm_roof(p) for p in gemm_kernels if p != dominant] + [
         hbm("mxq_quantize of X, W, dY, both orientations", rate["mx_quant_XWdY_gbs"]),
+        hbm("mxq_quantize 16384x8192 with outliers, both orientations", rate["mx_quant_act_gbs"]),
         hbm("fp8_adam_step, 1.3e9 params, 21 B/param (amax pass + update pass)", rate["adam_gbs"]),
         hbm("fp8_adam_step_delayed, 1.3e9 params, 18 B/param (one pass)", rate["adam_delayed_gbs"]),
     ]
@@ -413,6 +448,9 @@ def main():
         "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
         "device_ms_per_step": round(step_ms, 3),
         "parts_ms": {k: round(v, 4) for k, v in ms.items()},
+        "parts_ms_min_max": spread,
+        "timing": f"median of {args.steps} steps per part (events on the launch stream); HBM-bound parts start with "
+                  "the last-level cache scrubbed by a 512 MiB write outside their timed window",
         "rates": rate,
         "roofline": roofline,
         "rooflines_other": rooflines_other,
@@ -422,56 +460,92 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-GEMM_PMC_SUMMARY = os.path.join(ROOT, "profiles", "mx_gemm_fwd_4096x36864x12288_pmc.md")
-GEMM_SOURCE = os.path.join(ROOT, "mxfp8_precision_numerics_amd", "csrc", "gemm.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "mxfp8_precision_numerics_amd", "csrc")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the forward MX GEMM from the committed hardware-counter summary: FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch), each divided by what the same counter read per byte of a plain copy of known
-    size. None when no summary exists or when the GEMM source has changed since the counters were taken."""
+def measured_traffic(part):
+    """HBM bytes per launch of one kernel from its committed hardware-counter summary (profiles/*_pmc.md): the line
+    'bench-traffic: kernel=<part> fetch_kib=F write_kib=W copy_fetch_per_byte=a copy_write_per_byte=b source=<file>
+    source_sha256=<hash>' gives FETCH_SIZE and WRITE_SIZE (KiB per dispatch) and what the same counters read per byte
+    of a plain copy of known size; each counter is divided by its copy factor. None when no summary names the kernel,
+    or when the kernel's source has changed since the counters were taken."""
+    import glob
     import hashlib
     import re
 
-    try:
-        text = open(GEMM_PMC_SUMMARY).read()
-    except OSError:
-        return None
-    m = re.search(r"bench-traffic: fetch_kib=([\d.e+]+) write_kib=([\d.e+]+) copy_fetch_per_byte=([\d.e+-]+) "
-                  r"copy_write_per_byte=([\d.e+-]+) gemm_hip_sha256=([0-9a-f]{64})", text)
-    if not m:
-        return None
-    if hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest() != m.group(5):
-        return None
-    fetch = float(m.group(1)) * 1024 / float(m.group(3))
-    write = float(m.group(2)) * 1024 / float(m.group(4))
-    return round(fetch + write)
+    pat = re.compile(r"bench-traffic: kernel=(\S+) fetch_kib=([\d.e+]+) write_kib=([\d.e+]+) "
+                     r"copy_fetch_per_byte=([\d.e+-]+) copy_write_per_byte=([\d.e+-]+) source=(\S+) "
+                     r"source_sha256=([0-9a-f]{64})")
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*_pmc.md"))):
+        for m in pat.finditer(open(path).read()):
+            if m.group(1) != part:
+                continue
+            src = os.path.join(CSRC, m.group(6))
+            try:
+                if hashlib.sha256(open(src, "rb").read()).hexdigest() != m.group(7):
+                    return None
+            except OSError:
+                return None
+            fetch = float(m.group(2)) * 1024 / float(m.group(4))
+            write = float(m.group(3)) * 1024 / float(m.group(5))
+            return round(fetch + write)
+    return None
+
+
+PROFILE_KERNELS = ["mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "grouped_gemm_up", "grouped_gemm_down",
+                   "mx_quant_act", "adam", "copy"]
 
 
 def profile_kernel(name, dev):
-    """Ten launches of one kernel on seeded inputs, for rocprofv3 counter passes (one pass per counter set)."""
+    """Ten launches of one kernel (or one call) on the benchmark's seeded inputs, for rocprofv3 counter passes (one
+    pass per counter set). Prints the average event-timed duration of the call."""
     import torch
 
     import mxfp8_precision_numerics_amd as mxq
-    from mxfp8_precision_numerics_amd import workloads
+    from mxfp8_precision_numerics_amd import _probe, workloads
 
     if name == "copy":
         n = 1 << 30                                            # 1 GiB read + 1 GiB written per launch
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        run = lambda: dst.copy_(src)  # noqa: E731
-    elif name == "mx_gemm_wgrad":                             # dW = dY^T X, K = 4096 (exact bf16 path)
-        X, _, dY = workloads.workload2(dev)
-        qx = mxq.mx_quantize(X, rowwise=False)
-        qd = mxq.mx_quantize(dY, rowwise=False)
-        dW = torch.empty((dY.shape[1], X.shape[1]), dtype=torch.bfloat16, device=dev)
-        run = lambda: mxq.scaled_gemm(qd.q_col, qd.s_col, qx.q_col, qx.s_col, mxq.MX_BLOCK32, out=dW)  # noqa: E731
-    else:
-        X, W, _ = workloads.workload2(dev)
-        qx = mxq.mx_quantize(X, colwise=False)
-        qw = mxq.mx_quantize(W, colwise=False)
-        Y = torch.empty((X.shape[0], W.shape[0]), dtype=torch.bfloat16, device=dev)
-        run = lambda: mxq.scaled_gemm(qx.q_row, qx.s_row, qw.q_row, qw.s_row, mxq.MX_BLOCK32, out=Y)  # noqa: E731
+        run = lambda: _probe.copy(src, dst, 0, 8)  # noqa: E731
+    elif name in ("mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad"):
+        X, W, dY = workloads.workload2(dev)
+        qx = mxq.mx_quantize(X)
+        qw = mxq.mx_quantize(W)
+        qd = mxq.mx_quantize(dY)
+        del X, W, dY
+        a, b = {"mx_gemm_fwd": ((qx.q_row, qx.s_row), (qw.q_row, qw.s_row)),
+                "mx_gemm_dgrad": ((qd.q_row, qd.s_row), (qw.q_col, qw.s_col)),
+                "mx_gemm_wgrad": ((qd.q_col, qd.s_col), (qx.q_col, qx.s_col))}[name]
+        out = torch.empty((a[0].shape[0], b[0].shape[0]), dtype=torch.bfloat16, device=dev)
+        run = lambda: mxq.scaled_gemm(a[0], a[1], b[0], b[1], mxq.MX_BLOCK32, out=out)  # noqa: E731
+    elif name in ("grouped_gemm_up", "grouped_gemm_down"):
+        wl4 = workloads.workload4(dev)
+        off4 = torch.from_numpy(wl4["offsets"]).to(dev)
+        A, Wt = (wl4["a_up"], wl4["w_up"]) if name == "grouped_gemm_up" else (wl4["a_down"], wl4["w_down"])
+        G, Nn, Kk = Wt.shape
+        qa = mxq.mx_quantize(A, colwise=False)
+        qw = mxq.mx_quantize(Wt.reshape(G * Nn, Kk), colwise=False)
+        out = torch.empty((A.shape[0], Nn), dtype=torch.bfloat16, device=dev)
+        run = lambda: mxq.grouped_scaled_gemm(qa.q_row, qa.s_row, off4, qw.q_row.view(G, Nn, Kk),  # noqa: E731
+                                              qw.s_row.view(G, Nn, Kk // 32), out=out)
+    elif name == "mx_quant_act":
+        act3 = workloads.workload3(dev)
+        out = mxq.mx_quantize(act3)
+        run = lambda: mxq.mx_quantize(act3, out=out)  # noqa: E731
+    else:                                                      # adam: the two-pass step over 1.3e9 parameters
+        n = 1_300_000_000
+        theta = workloads.workload5_params(n, dev)
+        grad = workloads.workload5_grad(n, 2, dev)
+        m_q = torch.zeros(n, dtype=torch.uint8, device=dev)
+        m_scale = torch.ones(1, dtype=torch.float32, device=dev)
+        v16 = torch.zeros(n, dtype=torch.float16, device=dev)
+        w16 = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(mxq.workspace_bytes("adam", n), dtype=torch.uint8, device=dev)
+        hp = mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.0, 2)
+        run = lambda: mxq.fp8_adam_step(theta, grad, m_q, m_scale, v16, w16, hp, workspace=ws)  # noqa: E731
     run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -483,35 +557,53 @@ def profile_kernel(name, dev):
     print(json.dumps({"profile_kernel": name, "avg_ms": round(e0.elapsed_time(e1) / 10, 4)}), flush=True)
 
 
-def measure_attainable(mxq, operand_bytes, dev, stream):
-    """What this part sustains, measured in the same run beside the spec peaks: the library's streaming copy of 1 GiB
-    (HBM read + write; best of four grid sizes) and the MFMA-only loop of the block-scaled FP8 instruction on real
+def measure_attainable(operand_bytes, dev, stream):
+    """What this part sustains, measured in the same run beside the spec peaks (libmxq_probe.so): the best of a 1 GiB
+    streaming copy (HBM read + write) over looping and full grids with 4, 8 or 16 loads in flight per thread, the
+    best streaming read of the same 1 GiB, and the MFMA-only loop of the block-scaled FP8 instruction on real
     quantized operand bytes."""
     import torch
+
+    from mxfp8_precision_numerics_amd import _probe
 
     n = 1 << 30
     src = torch.ones(n, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
+    rsink = torch.empty(65536 * 16, dtype=torch.int32, device=dev)
     sink = torch.empty(256 * 256, dtype=torch.float32, device=dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    mxq.probe_mfma_fp8(operand_bytes, 200, 256, sink)
+    _probe.mfma_fp8(operand_bytes, 200, 256, sink)
     torch.cuda.synchronize()
-    copy_gbs = 0.0
-    for blocks in (1024, 2048, 4096, 8192):
-        mxq.probe_copy(src, dst, blocks)
+
+    def best(fn):
+        fn()
         ev[0].record(stream)
         for _ in range(10):
-            moved = mxq.probe_copy(src, dst, blocks)
+            moved = fn()
         ev[1].record(stream)
         torch.cuda.synchronize()
-        copy_gbs = max(copy_gbs, 10 * moved / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9)
+        return 10 * moved / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+
+    copy_gbs, copy_cfg, read_gbs, read_cfg = 0.0, None, 0.0, None
+    for blocks in (0, 1024, 2048, 4096, 8192):
+        for unroll in (4, 8, 16):
+            g = best(lambda: _probe.copy(src, dst, blocks, unroll))
+            if g > copy_gbs:
+                copy_gbs, copy_cfg = g, (blocks, unroll)
+            g = best(lambda: _probe.read(src, rsink, blocks, unroll))
+            if g > read_gbs:
+                read_gbs, read_cfg = g, (blocks, unroll)
     ev[2].record(stream)
-    flop = mxq.probe_mfma_fp8(operand_bytes, 8000, 256, sink)
+    flop = _probe.mfma_fp8(operand_bytes, 8000, 256, sink)
     ev[3].record(stream)
     torch.cuda.synchronize()
     mfma_tflops = flop / (ev[2].elapsed_time(ev[3]) * 1e-3) / 1e12
     del src, dst
+    grid = lambda c: ("full grid" if c[0] == 0 else f"{c[0]} looping workgroups") + f", {c[1]} loads in flight"  # noqa: E731
     return {"hbm_copy_gbs": round(copy_gbs, 1), "hbm_copy_frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
+            "hbm_copy_config": grid(copy_cfg),
+            "hbm_read_gbs": round(read_gbs, 1), "hbm_read_frac_of_peak": round(read_gbs / PEAK_HBM_GBS, 4),
+            "hbm_read_config": grid(read_cfg),
             "mfma_fp8_tflops": round(mfma_tflops, 1), "mfma_fp8_frac_of_peak": round(mfma_tflops / PEAK_FP8_TFLOPS, 4)}
 
 

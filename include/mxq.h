@@ -335,25 +335,6 @@ mxq_status fp8_adam_step_delayed(float* master, const uint16_t* grad_bf16, uint8
                                  float* m_history, int32_t* hist_pos, int64_t history_len, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
 
-/*
- * Measurement support (not a step of the method): an MFMA-only loop of the block-scaled FP8 instruction
- * (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales) that reports the matrix rate the part sustains, so that GEMM rates
- * can be read against it as well as against the dense peak. `blocks` workgroups of 256 threads each run
- * iters * 16 instructions per wave, i.e. blocks * 4 * iters * 16 * 131072 FLOP in all; there is no memory traffic in
- * the loop. operand_bytes: device, >= 131072 bytes (the operands; real quantized data gives a realistic bit toggle
- * rate), 16-byte aligned. sink: device float[blocks * 256], written. 1 <= blocks <= 65536, iters >= 1.
- */
-mxq_status mxq_probe_mfma_fp8(const uint8_t* operand_bytes, int64_t iters, int64_t blocks, float* sink,
-                              hipStream_t stream);
-
-/*
- * Measurement support (not a step of the method): a streaming device copy dst[0 .. bytes) = src[0 .. bytes) with
- * 16-byte non-temporal loads and stores over `blocks` workgroups of 256 threads (grid-stride), giving the HBM
- * read + write rate the part sustains. Device pointers, 16-byte aligned, not overlapping; bytes % 16 == 0;
- * 1 <= blocks <= 65536.
- */
-mxq_status mxq_probe_copy(const void* src, void* dst, int64_t bytes, int64_t blocks, hipStream_t stream);
-
 /* Workspace bytes needed by op ("pertensor", "adam", "pertensor_delayed", "adam_delayed" or "autoscale") for n
  * elements; 0 for an unknown op. op is a host string. */
 size_t mxq_workspace_bytes(const char* op, int64_t n);

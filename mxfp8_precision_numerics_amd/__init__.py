@@ -376,28 +376,3 @@ def fp8_requantize_shared(q: torch.Tensor, fmt_in: int, scale_in: torch.Tensor, 
                                            _stream(dev))
     _lib.check("fp8_requantize_shared", st)
     return out, sg, ssum
-
-
-def probe_mfma_fp8(operand_bytes: torch.Tensor, iters: int, blocks: int, sink: Optional[torch.Tensor] = None) -> int:
-    """Enqueue the MFMA-only measurement loop; returns the FLOP it performs (time it with events on the stream)."""
-    _dev(operand_bytes, torch.uint8, "operand_bytes")
-    if operand_bytes.numel() < 131072:
-        raise ValueError("operand_bytes must hold at least 131072 bytes")
-    dev = operand_bytes.device
-    if sink is None:
-        sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
-    st = _lib.load().mxq_probe_mfma_fp8(_ptr(operand_bytes), iters, blocks, _ptr(sink), _stream(dev))
-    _lib.check("mxq_probe_mfma_fp8", st)
-    return blocks * 4 * iters * 16 * 131072
-
-
-def probe_copy(src: torch.Tensor, dst: torch.Tensor, blocks: int = 4096) -> int:
-    """Enqueue the streaming copy dst = src (same byte size); returns the bytes moved (read + written)."""
-    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
-        raise ValueError("src and dst must be contiguous device tensors")
-    nbytes = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() != nbytes:
-        raise ValueError("src and dst must have the same size in bytes")
-    st = _lib.load().mxq_probe_copy(_ptr(src), _ptr(dst), nbytes, blocks, _stream(src.device))
-    _lib.check("mxq_probe_copy", st)
-    return 2 * nbytes

@@ -1,4 +1,5 @@
-"""Builds libmxq.so (the gfx950 kernels and the C ABI of include/mxq.h) in-tree with hipcc."""
+"""Builds, in-tree with hipcc for gfx950: libmxq.so (the kernels and the C ABI of include/mxq.h) and
+libmxq_probe.so (the measurement kernels of include/mxq_probe.h, loaded only by the benchmark and its tests)."""
 from __future__ import annotations
 
 import os
@@ -10,9 +11,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmxq.so")
+PROBE_LIB = os.path.join(PKG, "libmxq_probe.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["quantize.hip", "gemm.hip", "adam.hip", "gradcomm.hip", "moe.hip", "probe.hip", "abi.hip"]
+SOURCES = ["quantize.hip", "gemm.hip", "adam.hip", "gradcomm.hip", "moe.hip", "abi.hip"]
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -33,19 +36,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libmxq.so. Always recompiles."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(out)} failed:\n{r.stderr}")
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link libmxq.so and libmxq_probe.so. Always recompiles."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -38,8 +38,6 @@ SIGNATURES = {
     "fp8_quantize_pertensor_delayed": (_I, [_P, _I64, _I64, _I, _F, _P, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     "fp8_autoscale_cast": (_I, [_P, _I64, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "fp8_requantize_shared": (_I, [_P, _I64, _I, _P, _P, _I64, _I, _P, _P, _P, _P]),
-    "mxq_probe_mfma_fp8": (_I, [_P, _I64, _I64, _P, _P]),
-    "mxq_probe_copy": (_I, [_P, _P, _I64, _I64, _P]),
     "swiglu_mx_quantize": (_I, [_P, _I64, _I64, _P, _P, _I, _P]),
     "fp8_adam_step_mx_cache": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _I, C.POINTER(AdamHParams),
                                     _P, _SZ, _P]),

@@ -71,22 +71,6 @@ const char* mxq_status_string(mxq_status s) {
 
 int mxq_abi_version(void) { return 1; }
 
-mxq_status mxq_probe_mfma_fp8(const uint8_t* operand_bytes, int64_t iters, int64_t blocks, float* sink,
-                              hipStream_t stream) {
-    if (!operand_bytes || !sink) return MXQ_ERR_NULL;
-    if (iters < 1 || blocks < 1 || blocks > 65536) return MXQ_ERR_SHAPE;
-    if (!al16(operand_bytes) || !al4(sink)) return MXQ_ERR_ALIGN;
-    return hip_status(mxq::launch_mfma_probe(operand_bytes, iters, (int)blocks, sink, stream));
-}
-
-mxq_status mxq_probe_copy(const void* src, void* dst, int64_t bytes, int64_t blocks, hipStream_t stream) {
-    if (bytes < 0 || (bytes & 15) || blocks < 1 || blocks > 65536) return MXQ_ERR_SHAPE;
-    if (bytes > 0 && (!src || !dst)) return MXQ_ERR_NULL;
-    if (!al16(src) || !al16(dst)) return MXQ_ERR_ALIGN;
-    if (bytes == 0) return MXQ_OK;
-    return hip_status(mxq::launch_copy_probe(src, dst, bytes, (int)blocks, stream));
-}
-
 size_t mxq_workspace_bytes(const char* op, int64_t n) {
     if (!op || n < 0) return 0;
     if (strcmp(op, "pertensor") == 0) return pertensor_ws(n);

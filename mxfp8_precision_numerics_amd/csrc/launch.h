@@ -53,9 +53,6 @@ hipError_t launch_requantize_shared(const uint8_t* q_in, int64_t n, int fmt_in, 
                                     const float* scales, int nranks, int fmt_out, uint8_t* q_out, float* shared_out,
                                     float* sum_out, hipStream_t stream);
 
-hipError_t launch_mfma_probe(const uint8_t* ops, int64_t iters, int blocks, float* sink, hipStream_t stream);
-hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, int blocks, hipStream_t stream);
-
 int adam_parts(int64_t n);
 hipError_t launch_adam(float* master, const uint16_t* grad, uint8_t* m_q, float* m_scale, uint16_t* v16, uint16_t* w,
                        int64_t n, const AdamConsts& k, uint32_t* partial, float* consts, hipStream_t stream);

@@ -321,7 +321,8 @@ hipError_t launch_pertensor_quantize(const uint16_t* x, int64_t rows, int64_t co
                        fmt == FMT_E4M3 ? 448.0f : 57344.0f, margin, scale_in, amax_out, scale_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (!q && !q_t) return hipSuccess;
+    // an empty tensor still gets amax 0 and its scale; there are no codes to write
+    if ((!q && !q_t) || rows == 0 || cols == 0) return hipSuccess;
     QuantArgs a{x, rows, cols, q, nullptr, q_t, nullptr, scale_out, 0, 0, nullptr};
     return fmt == FMT_E4M3 ? launch_quant_mode<QM_PT_E4M3>(a, q != nullptr, q_t != nullptr, stream)
                            : launch_quant_mode<QM_PT_E5M2>(a, q != nullptr, q_t != nullptr, stream);

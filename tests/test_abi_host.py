@@ -11,12 +11,13 @@ from conftest import ROOT
 from mxfp8_precision_numerics_amd import _lib
 
 HEADER = os.path.join(ROOT, "include", "mxq.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "mxq_probe.h")
 P = 0x10000          # a fake 16-byte-aligned address: validation rejects before any use
 MIS = 0x10001        # misaligned
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)) - {"defined"})
 
@@ -27,6 +28,18 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.SIGNATURES), names
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_measurement_library_is_apart_from_the_method_library():
+    """The measurement kernels live in libmxq_probe.so (include/mxq_probe.h), not in the method's library."""
+    from mxfp8_precision_numerics_amd import _probe
+    lib, probe = _lib.load(), _probe.load()
+    names = declared_functions(PROBE_HEADER)
+    assert set(names) == set(_probe.SIGNATURES), names
+    for n in names:
+        assert hasattr(probe, n), n
+        assert not hasattr(lib, n), n
+        assert n not in declared_functions()
 
 
 def test_status_strings_and_version():
@@ -166,19 +179,28 @@ def test_gradcomm_validation():
 
 
 def test_probe_validation():
-    f = _lib.load().mxq_probe_mfma_fp8
+    from mxfp8_precision_numerics_amd import _probe
+    f = _probe.load().mxq_probe_mfma_fp8
     assert f(None, 10, 4, P, None) == 1
     assert f(P, 10, 4, None, None) == 1
     assert f(P, 0, 4, P, None) == 2
     assert f(P, 10, 0, P, None) == 2
     assert f(P, 10, 70000, P, None) == 2
     assert f(MIS, 10, 4, P, None) == 3
-    c = _lib.load().mxq_probe_copy
-    assert c(P, P, 24, 4, None) == 2                 # bytes % 16
-    assert c(P, P, 32, 0, None) == 2
-    assert c(None, P, 32, 4, None) == 1
-    assert c(MIS, P, 32, 4, None) == 3
-    assert c(None, None, 0, 4, None) == 0            # empty
+    c = _probe.load().mxq_probe_copy
+    assert c(P, P, 24, 4, 4, None) == 2                 # bytes % 16
+    assert c(P, P, 32, -1, 4, None) == 2
+    assert c(P, P, 32, 4, 5, None) == 2                 # unroll 4, 8 or 16
+    assert c(None, P, 32, 4, 4, None) == 1
+    assert c(MIS, P, 32, 4, 8, None) == 3
+    assert c(None, None, 0, 4, 16, None) == 0           # empty
+    r = _probe.load().mxq_probe_read
+    assert r(P, 24, 0, 8, P, None) == 2
+    assert r(P, 32, 0, 3, P, None) == 2
+    assert r(P, 32, 0, 8, None, None) == 1
+    assert r(None, 32, 0, 8, P, None) == 1
+    assert r(MIS, 32, 0, 8, P, None) == 3
+    assert r(None, 0, 0, 8, P, None) == 0
 
 
 def test_routed_backward_validation():

@@ -178,49 +178,80 @@ def _sampled(C, y_rows, S_rows, y_cols, S_cols, rows, cols, what):
     return max(w1, w2)
 
 
+def _stratified(n, k, rng):
+    """k indices in [0, n): one drawn at random from each of k equal bands, so every band of n / k is hit (64 rows
+    of 4096 put 4 in every 256-row tile; 64 columns of 12288 put one in every 192 columns)."""
+    edges = np.linspace(0, n, k + 1).astype(np.int64)
+    return np.array([rng.integers(edges[i], edges[i + 1]) for i in range(k)], np.int64)
+
+
+def _check_full_rows_cols(C, aq, sa, fa, bq, sb, fb, scaling, rng, what, k=64):
+    """k full rows and k full columns of C (stratified) against the oracle's fp64 GEMM at the bound."""
+    M, N = aq.shape[0], bq.shape[0]
+    rows, cols = _stratified(M, k, rng), _stratified(N, k, rng)
+    yr, Sr = oracle.gemm_ref(aq, sa, fa, bq, sb, fb, scaling, rows=rows)
+    yc, Sc = oracle.gemm_ref(aq, sa, fa, bq, sb, fb, scaling, cols=cols)
+    return _sampled(C, yr, Sr, yc, Sc, rows, cols, what)
+
+
 def test_workload2_linear_fwd_dgrad_wgrad_full_size_sampled():
     """GPT-175B QKV shape, per-tensor current scaling: Y = X W^T (E4M3 x E4M3), dX = dY W (E5M2 x E4M3, B = W^T),
-    dW = dY^T X (E5M2 x E4M3, A = dY^T, B = X^T). 8 full rows and 8 full columns of each output are checked."""
+    dW = dY^T X (E5M2 x E4M3, A = dY^T, B = X^T), launched as the benchmark launches them. 64 full rows and 64 full
+    columns of each output (stratified, so every 256 x 256 output tile holds checked elements) are checked."""
     need_gpu()
     X, W, dY = workloads.workload2(DEV)
     px = mxq.pertensor_quantize(X, mxq.E4M3)
     pw = mxq.pertensor_quantize(W, mxq.E4M3)
     pd = mxq.pertensor_quantize(dY, mxq.E5M2)
+    del X, W, dY
     sx, sw, sd = (np.float32(p.scale.item()) for p in (px, pw, pd))
     rng = np.random.default_rng(2)
     E4, E5 = oracle.E4M3, oracle.E5M2
-    cases = [("fwd", px.q, sx, E4, mxq.E4M3, pw.q, sw, E4, mxq.E4M3),
-             ("dgrad", pd.q, sd, E5, mxq.E5M2, pw.q_t, sw, E4, mxq.E4M3),
-             ("wgrad", pd.q_t, sd, E5, mxq.E5M2, px.q_t, sx, E4, mxq.E4M3)]
-    for name, aq, sa, oa, fa, bq, sb, ob, fb in cases:
-        M, N = aq.shape[0], bq.shape[0]
-        say("workload2", name, M, N, aq.shape[1])
-        C = mxq.scaled_gemm(aq, torch.tensor([sa], device=DEV), bq, torch.tensor([sb], device=DEV),
-                            mxq.PER_TENSOR, fa, fb)
+    cases = [("fwd", px.q, px.scale, sx, E4, mxq.E4M3, pw.q, pw.scale, sw, E4, mxq.E4M3),
+             ("dgrad", pd.q, pd.scale, sd, E5, mxq.E5M2, pw.q_t, pw.scale, sw, E4, mxq.E4M3),
+             ("wgrad", pd.q_t, pd.scale, sd, E5, mxq.E5M2, px.q_t, px.scale, sx, E4, mxq.E4M3)]
+    for name, aq, sa_t, sa, oa, fa, bq, sb_t, sb, ob, fb in cases:
+        say("workload2 per-tensor", name, aq.shape[0], bq.shape[0], aq.shape[1])
+        C = mxq.scaled_gemm(aq, sa_t, bq, sb_t, mxq.PER_TENSOR, fa, fb)
         torch.cuda.synchronize()
-        rows = np.sort(rng.choice(M, 8, replace=False)); cols = np.sort(rng.choice(N, 8, replace=False))
-        aqh, bqh = u8(aq), u8(bq)
-        yr, Sr = oracle.gemm_ref(aqh, sa, oa, bqh, sb, ob, oracle.PER_TENSOR, rows=rows)
-        yc, Sc = oracle.gemm_ref(aqh, sa, oa, bqh, sb, ob, oracle.PER_TENSOR, cols=cols)
-        worst = _sampled(C, yr, Sr, yc, Sc, rows, cols, name)
+        worst = _check_full_rows_cols(C, u8(aq), sa, oa, u8(bq), sb, ob, oracle.PER_TENSOR, rng, name)
         say("  worst |err|/S", worst)
         del C
 
 
-def test_mx_gemm_workload2_fwd_shape_sampled():
-    """The dense MX GEMM at the GPT-175B QKV forward shape (4096 x 36864 x 12288)."""
+@pytest.mark.parametrize("which", ["fwd", "dgrad", "wgrad"])
+def test_mx_linear_full_size_sampled(which):
+    """The MX linear layer's three GEMMs exactly as the benchmark launches them ('OLMo-core MoE, Section 11: MXFP8
+    Training', Section 11.3.2, Eq. 60): fwd = row(X) x row(W) (4096 x 36864 x 12288), dgrad = row(dY) x col(W)
+    (4096 x 12288 x 36864), wgrad = col(dY) x col(X) (36864 x 12288 x 4096), each operand from mxq_quantize of the
+    seeded bf16 tensors in both orientations. 64 full rows and 64 full columns of each output, stratified."""
     need_gpu()
-    X, W, _ = workloads.workload2(DEV)
-    qx = mxq.mx_quantize(X, colwise=False)
-    qw = mxq.mx_quantize(W, colwise=False)
-    C = mxq.scaled_gemm(qx.q_row, qx.s_row, qw.q_row, qw.s_row, mxq.MX_BLOCK32)
+    X, W, dY = workloads.workload2(DEV)
+    qx, qw, qd = mxq.mx_quantize(X), mxq.mx_quantize(W), mxq.mx_quantize(dY)
+    del X, W, dY
+    a, b = {"fwd": ((qx.q_row, qx.s_row), (qw.q_row, qw.s_row)),
+            "dgrad": ((qd.q_row, qd.s_row), (qw.q_col, qw.s_col)),
+            "wgrad": ((qd.q_col, qd.s_col), (qx.q_col, qx.s_col))}[which]
+    say("workload2 MX", which, a[0].shape[0], b[0].shape[0], a[0].shape[1])
+    C = mxq.scaled_gemm(a[0], a[1], b[0], b[1], mxq.MX_BLOCK32)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(3)
-    rows = np.sort(rng.choice(4096, 8, replace=False)); cols = np.sort(rng.choice(36864, 8, replace=False))
-    a, s_a, b, s_b = u8(qx.q_row), u8(qx.s_row), u8(qw.q_row), u8(qw.s_row)
-    yr, Sr = oracle.gemm_ref(a, s_a, oracle.E4M3, b, s_b, oracle.E4M3, oracle.MX_BLOCK32, rows=rows)
-    yc, Sc = oracle.gemm_ref(a, s_a, oracle.E4M3, b, s_b, oracle.E4M3, oracle.MX_BLOCK32, cols=cols)
-    say("  worst |err|/S", _sampled(C, yr, Sr, yc, Sc, rows, cols, "mx fwd"))
+    rng = np.random.default_rng({"fwd": 3, "dgrad": 5, "wgrad": 7}[which])
+    worst = _check_full_rows_cols(C, u8(a[0]), u8(a[1]), oracle.E4M3, u8(b[0]), u8(b[1]), oracle.E4M3,
+                                  oracle.MX_BLOCK32, rng, "mx " + which)
+    say("  worst |err|/S", worst)
+
+
+def test_mx_gemm_default_at_k36864_all_elements():
+    """The default MX GEMM at the dgrad's contraction length (K = 36864) on a mid-size output, every element."""
+    need_gpu()
+    M, N, K = 520, 528, 36864
+    A = workloads.normal_bf16((M, K), 1.0, 28, 1, DEV)
+    B = workloads.normal_bf16((N, K), 1.0, 28, 2, DEV)
+    qa, sa, qb, sb = _mx_operands(A, B)
+    C = mxq.scaled_gemm(qa, sa, qb, sb, mxq.MX_BLOCK32)
+    torch.cuda.synchronize()
+    y, S = oracle.gemm_ref(u8(qa), u8(sa), oracle.E4M3, u8(qb), u8(sb), oracle.E4M3, oracle.MX_BLOCK32)
+    say("  worst |err|/S", _bound_check(C.float().cpu().numpy(), y, S, f"mx {M}x{N}x{K}"))
 
 
 # ----------------------------------------------------------------------------------------------- grouped

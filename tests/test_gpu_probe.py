@@ -1,28 +1,45 @@
-"""GPU checks of the measurement kernels bench.py uses for the attainable ceilings: the streaming copy reproduces its
-source byte for byte (several grid sizes, a size that ends inside a grid-stride trip), and the MFMA-only loop over
-operands of E4M3 1.0 (0x38) with unit scales leaves every lane the closed-form sum 16 accumulators x 16 values x
-(64 products of 1) x iters."""
+"""GPU checks of the measurement kernels (libmxq_probe.so) the benchmark uses for the sustained ceilings: the streaming
+copy reproduces its source byte for byte (looping and full grids, 4, 8 and 16 loads in flight, sizes that end inside a
+trip), the streaming read leaves the xor of the words read, and the MFMA-only loop over operands of E4M3 1.0 (0x38)
+with unit scales leaves every lane the closed-form sum 16 accumulators x 16 values x (64 products of 1) x iters."""
 import numpy as np
 import pytest
 import torch
 
-import mxfp8_precision_numerics_amd as mxq
 from gpu_util import DEV, need_gpu
+from mxfp8_precision_numerics_amd import _probe
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("nbytes,blocks", [(16, 1), (1 << 20, 4), (3 * (1 << 20) + 48, 7), (64 << 20, 4096)])
-def test_copy_probe_is_a_copy(nbytes, blocks):
+@pytest.mark.parametrize("nbytes,blocks,unroll", [(16, 1, 4), (1 << 20, 4, 8), (3 * (1 << 20) + 48, 7, 16),
+                                                  (64 << 20, 4096, 4), (3 * (1 << 20) + 48, 0, 4),
+                                                  (64 << 20, 0, 8), (5 * 4096 * 16 + 16, 0, 16)])
+def test_copy_probe_is_a_copy(nbytes, blocks, unroll):
+    need_gpu()
+    g = torch.Generator(device=DEV)
+    g.manual_seed(nbytes + blocks)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=DEV, generator=g)
+    dst = torch.zeros_like(src)
+    moved = _probe.copy(src, dst, blocks, unroll)
+    torch.cuda.synchronize()
+    assert moved == 2 * nbytes
+    assert torch.equal(src, dst)
+
+
+@pytest.mark.parametrize("nbytes,blocks,unroll", [(16, 0, 8), (3 * (1 << 20) + 48, 0, 8), (1 << 20, 5, 16),
+                                                  (7 << 20, 0, 4)])
+def test_read_probe_xor(nbytes, blocks, unroll):
     need_gpu()
     g = torch.Generator(device=DEV)
     g.manual_seed(nbytes)
     src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=DEV, generator=g)
-    dst = torch.zeros_like(src)
-    moved = mxq.probe_copy(src, dst, blocks)
+    groups = blocks if blocks > 0 else nbytes // (4096 * unroll) + 1
+    sink = torch.zeros(groups, dtype=torch.int32, device=DEV)
+    assert _probe.read(src, sink, blocks, unroll) == nbytes
     torch.cuda.synchronize()
-    assert moved == 2 * nbytes
-    assert torch.equal(src, dst)
+    words = src.cpu().numpy().view(np.uint32)
+    assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == np.bitwise_xor.reduce(words)
 
 
 @pytest.mark.parametrize("iters", [1, 2, 7])
@@ -30,7 +47,7 @@ def test_mfma_probe_closed_form(iters):
     need_gpu()
     ops = torch.full((131072,), 0x38, dtype=torch.uint8, device=DEV)
     sink = torch.empty(3 * 256, dtype=torch.float32, device=DEV)
-    flop = mxq.probe_mfma_fp8(ops, iters, 3, sink)
+    flop = _probe.mfma_fp8(ops, iters, 3, sink)
     torch.cuda.synchronize()
     assert flop == 3 * 4 * iters * 16 * 131072
     assert np.all(sink.cpu().numpy() == np.float32(16 * 16 * 64 * iters))

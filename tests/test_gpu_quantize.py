@@ -157,3 +157,29 @@ def test_pertensor_workload2_tensors_full_size():
                                ("dY", dY, mxq.E5M2, oracle.E5M2)):
         say("workload2 per-tensor", name, tuple(t.shape))
         _check_pt(t, fmt, ofmt)
+
+
+@pytest.mark.parametrize("rows,cols", [(0, 64), (64, 0), (0, 0)])
+@pytest.mark.parametrize("fmt,fmax", [(mxq.E4M3, 448.0), (mxq.E5M2, 57344.0)])
+def test_pertensor_empty_tensor_with_outputs(rows, cols, fmt, fmax):
+    """An empty x with both code outputs given: MXQ_OK, amax 0 and the scale of the 1e-12 clamp, and nothing written
+    to q or q_t (guard bytes stay as they were)."""
+    import ctypes as C
+
+    from mxfp8_precision_numerics_amd import _lib
+    need_gpu()
+    x = torch.empty(16, dtype=torch.bfloat16, device=DEV)
+    q = torch.full((64,), 0x5A, dtype=torch.uint8, device=DEV)
+    qt = torch.full((64,), 0x5A, dtype=torch.uint8, device=DEV)
+    amax = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    scale = torch.zeros(1, dtype=torch.float32, device=DEV)
+    ws = torch.empty(mxq.workspace_bytes("pertensor", 0), dtype=torch.uint8, device=DEV)
+    ptr = lambda t: C.c_void_p(t.data_ptr())  # noqa: E731
+    st = _lib.load().fp8_quantize_pertensor(ptr(x), rows, cols, fmt, C.c_float(1.0), None, ptr(amax), ptr(scale),
+                                            ptr(q), ptr(qt), ptr(ws), ws.numel(),
+                                            C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0
+    assert amax.item() == 0.0
+    assert scale.item() == np.float32(fmax) / np.float32(1e-12)
+    assert torch.all(q == 0x5A) and torch.all(qt == 0x5A)
