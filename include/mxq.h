@@ -146,6 +146,19 @@ mxq_status fp8_quantize_pertensor(const uint16_t* x_bf16, int64_t rows, int64_t 
                                   hipStream_t stream);
 
 /*
+ * fp8_quantize_pertensor without a workspace, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). Arguments, outputs and errors are those of
+ * fp8_quantize_pertensor without workspace and workspace_bytes. The amax pass's partial maxima go to a scratch array
+ * of the library's own (2048 words, 8 KiB per GPU, kept until the process ends), which holds the partials of any
+ * size; a size whose partials would not fit returns MXQ_ERR_WORKSPACE. The call allocates nothing. Its first call on
+ * a GPU looks up that GPU's copy of the array (MXQ_ERR_HIP if the lookup fails). Calls that overlap on one GPU share
+ * the array and race: order them on one stream, or use fp8_quantize_pertensor with workspaces of their own.
+ */
+mxq_status fp8_quantize_pertensor_noalloc(const uint16_t* x_bf16, int64_t rows, int64_t cols, mxq_fp8 fmt,
+                                          float margin, const float* scale_in, float* amax_out, float* scale_out,
+                                          uint8_t* q, uint8_t* q_t, hipStream_t stream);
+
+/*
  * Delayed per-tensor scaling: one pass over x instead of two ([LLMSB] "Per-tensor scaling and the delayed-scaling
  * recipe", the DelayedScale sketch; [FP8-LM] Section 3.4, delayed scaling).
  *   amax_history: device float[history_len] (in/out), hist_pos: device int32[1] (in/out, 0 <= pos < history_len),

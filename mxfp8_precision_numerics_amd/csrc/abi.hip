@@ -168,6 +168,25 @@ mxq_status fp8_quantize_pertensor(const uint16_t* x_bf16, int64_t rows, int64_t 
                                                      scale_out, q, q_t, static_cast<uint32_t*>(workspace), stream));
 }
 
+mxq_status fp8_quantize_pertensor_noalloc(const uint16_t* x_bf16, int64_t rows, int64_t cols, mxq_fp8 fmt,
+                                          float margin, const float* scale_in, float* amax_out, float* scale_out,
+                                          uint8_t* q, uint8_t* q_t, hipStream_t stream) {
+    if (!amax_out || !scale_out) return MXQ_ERR_NULL;
+    if (fmt != MXQ_E4M3 && fmt != MXQ_E5M2) return MXQ_ERR_UNSUPPORTED;
+    if (rows < 0 || cols < 0 || cols % 8 != 0) return MXQ_ERR_SHAPE;
+    if (q_t && rows % 32 != 0) return MXQ_ERR_SHAPE;
+    if ((rows + 127) / 128 > kMaxGridY) return MXQ_ERR_SHAPE;
+    if (rows * cols > 0 && !x_bf16) return MXQ_ERR_NULL;
+    if (!al16(x_bf16) || (q && !al16(q)) || (q_t && !al16(q_t))) return MXQ_ERR_ALIGN;
+    if (!al4(amax_out) || !al4(scale_out) || (scale_in && !al4(scale_in))) return MXQ_ERR_ALIGN;
+    uint32_t* scratch = nullptr;
+    size_t scratch_bytes = 0;
+    if (mxq::pertensor_scratch(stream, &scratch, &scratch_bytes) != hipSuccess) return MXQ_ERR_HIP;
+    if (pertensor_ws(rows * cols) > scratch_bytes) return MXQ_ERR_WORKSPACE;   // partials would not fit
+    return hip_status(mxq::launch_pertensor_quantize(x_bf16, rows, cols, (int)fmt, margin, scale_in, amax_out,
+                                                     scale_out, q, q_t, scratch, stream));
+}
+
 mxq_status fp8_quantize_pertensor_delayed(const uint16_t* x_bf16, int64_t rows, int64_t cols, mxq_fp8 fmt,
                                           float margin, float* amax_history, int32_t* hist_pos, int64_t history_len,
                                           float* amax_out, float* scale_out, uint8_t* q, uint8_t* q_t,

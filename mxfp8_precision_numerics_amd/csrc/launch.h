@@ -14,6 +14,8 @@ hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uin
                               uint8_t* q_col, uint8_t* s_col, int rule, hipStream_t stream);
 
 int pertensor_amax_parts(int64_t n);
+// The device scratch of the allocation-free per-tensor quantize on the stream's device, and its size in bytes.
+hipError_t pertensor_scratch(hipStream_t stream, uint32_t** ptr, size_t* bytes);
 hipError_t launch_pertensor_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, float margin,
                                      const float* scale_in, float* amax_out, float* scale_out, uint8_t* q,
                                      uint8_t* q_t, uint32_t* partial, hipStream_t stream);

@@ -10,6 +10,8 @@
 // row orientation is encoded straight from registers (a 32-value block spans 4 lanes; its amax is a DPP quad max)
 // while the tile is also written to LDS, from which each thread re-reads a column pair of 32 rows for the column
 // orientation, stored transposed so each block's 32 codes are contiguous. One pass over x emits both.
+#include <mutex>
+
 #include "mxq_device.h"
 #include "launch.h"
 
@@ -326,6 +328,46 @@ hipError_t launch_pertensor_quantize(const uint16_t* x, int64_t rows, int64_t co
     QuantArgs a{x, rows, cols, q, nullptr, q_t, nullptr, scale_out, 0, 0, nullptr};
     return fmt == FMT_E4M3 ? launch_quant_mode<QM_PT_E4M3>(a, q != nullptr, q_t != nullptr, stream)
                            : launch_quant_mode<QM_PT_E5M2>(a, q != nullptr, q_t != nullptr, stream);
+}
+
+// ------------------------------------------------------------------------ allocation-free per-tensor quantize
+// fp8_quantize_pertensor_noalloc keeps the amax pass's partial maxima in this file-scope device array instead of a
+// caller workspace. pertensor_amax_parts never exceeds 2048, so the array holds the partials of any size; each GPU
+// keeps its own copy until the process ends. Calls that overlap on one GPU share it and race; every partial is written
+// by its workgroup before the finalize kernel reads it, so nothing has to be cleared between calls.
+constexpr int kScratchWords = 2048;
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static uint32_t* g_scratch[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the device of `stream` (the current device for the null stream), found once per
+// device with that device current. In host code the array's name is only a stand-in, so kernels get this address.
+hipError_t pertensor_scratch(hipStream_t stream, uint32_t** ptr, size_t* bytes) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch[dev] = static_cast<uint32_t*>(p);
+    }
+    *ptr = g_scratch[dev];
+    *bytes = sizeof(uint32_t) * kScratchWords;
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------------------- delayed scaling
