@@ -192,10 +192,11 @@ def pertensor_quantize_delayed(x: torch.Tensor, amax_history: torch.Tensor, hist
 
 def scaled_gemm(a_q: torch.Tensor, a_scale: torch.Tensor, b_q: torch.Tensor, b_scale: torch.Tensor,
                 scaling: int = MX_BLOCK32, a_fmt: int = E4M3, b_fmt: int = E4M3,
-                out: Optional[torch.Tensor] = None, exact: bool = False) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, exact: bool = False, path: str = "checked") -> torch.Tensor:
     """C[M][N] = A[M][K] B[N][K]^T in bf16. MX: scales are E8M0 grids [M][K/32], [N][K/32]; per-tensor: float32[1].
-    exact=True calls scaled_gemm_exact (bf16 products of the exactly dequantized operands at every K), for operands
-    whose blocks span a wide range of magnitudes."""
+    path "checked" calls scaled_gemm (the FP8 instruction where a device-side range check allows it, else the exact
+    path), "exact" (or exact=True) scaled_gemm_exact, "fp8" scaled_gemm_fp8 (FP8 instruction at every K, bound not
+    guaranteed)."""
     _dev(a_q, torch.uint8, "a_q"); _dev(b_q, torch.uint8, "b_q")
     M, K = a_q.shape
     N = b_q.shape[0]
@@ -204,7 +205,9 @@ def scaled_gemm(a_q: torch.Tensor, a_scale: torch.Tensor, b_q: torch.Tensor, b_s
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
     ldc = out.stride(0)
-    name = "scaled_gemm_exact" if exact else "scaled_gemm"
+    if exact:
+        path = "exact"
+    name = {"checked": "scaled_gemm", "exact": "scaled_gemm_exact", "fp8": "scaled_gemm_fp8"}[path]
     st = getattr(_lib.load(), name)(_ptr(a_q), _ptr(a_scale), a_fmt, _ptr(b_q), _ptr(b_scale), b_fmt, M, N, K,
                                     scaling, _ptr(out), ldc, _stream(a_q.device))
     _lib.check(name, st)

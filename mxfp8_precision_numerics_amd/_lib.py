@@ -34,6 +34,7 @@ SIGNATURES = {
     "fp8_quantize_pertensor_noalloc": (_I, [_P, _I64, _I64, _I, _F, _P, _P, _P, _P, _P, _P]),
     "scaled_gemm": (_I, [_P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _I, _P, _I64, _P]),
     "scaled_gemm_exact": (_I, [_P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _I, _P, _I64, _P]),
+    "scaled_gemm_fp8": (_I, [_P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _I, _P, _I64, _P]),
     "grouped_scaled_gemm": (_I, [_P, _P, _P, _I64, _I64, _P, _P, _I64, _I64, _P, _P]),
     "fp8_adam_step": (_I, [_P, _P, _P, _P, _P, _P, _I64, C.POINTER(AdamHParams), _P, _SZ, _P]),
     "fp8_quantize_pertensor_delayed": (_I, [_P, _I64, _I64, _I, _F, _P, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]),

@@ -245,7 +245,7 @@ namespace {
 
 mxq_status scaled_gemm_impl(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fmt, const uint8_t* b_q,
                             const void* b_scale, mxq_fp8 b_fmt, int64_t M, int64_t N, int64_t K, mxq_scaling scaling,
-                            uint16_t* c_bf16, int64_t ldc, bool exact, hipStream_t stream) {
+                            uint16_t* c_bf16, int64_t ldc, int path, hipStream_t stream) {
     if (scaling != MXQ_PER_TENSOR && scaling != MXQ_MX_BLOCK32) return MXQ_ERR_UNSUPPORTED;
     if ((a_fmt != MXQ_E4M3 && a_fmt != MXQ_E5M2) || (b_fmt != MXQ_E4M3 && b_fmt != MXQ_E5M2)) return MXQ_ERR_UNSUPPORTED;
     if (scaling == MXQ_MX_BLOCK32 && (a_fmt != MXQ_E4M3 || b_fmt != MXQ_E4M3)) return MXQ_ERR_UNSUPPORTED;
@@ -256,7 +256,7 @@ mxq_status scaled_gemm_impl(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_f
     if (scaling == MXQ_MX_BLOCK32 ? (!al16(a_scale) || !al16(b_scale)) : (!al4(a_scale) || !al4(b_scale)))
         return MXQ_ERR_ALIGN;
     return hip_status(mxq::launch_scaled_gemm(a_q, a_scale, (int)a_fmt, b_q, b_scale, (int)b_fmt, M, N, K,
-                                              scaling == MXQ_MX_BLOCK32 ? 1 : 0, c_bf16, ldc, exact, stream));
+                                              scaling == MXQ_MX_BLOCK32 ? 1 : 0, c_bf16, ldc, path, stream));
 }
 
 }  // namespace
@@ -266,13 +266,22 @@ extern "C" {
 mxq_status scaled_gemm(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fmt, const uint8_t* b_q,
                        const void* b_scale, mxq_fp8 b_fmt, int64_t M, int64_t N, int64_t K, mxq_scaling scaling,
                        uint16_t* c_bf16, int64_t ldc, hipStream_t stream) {
-    return scaled_gemm_impl(a_q, a_scale, a_fmt, b_q, b_scale, b_fmt, M, N, K, scaling, c_bf16, ldc, false, stream);
+    return scaled_gemm_impl(a_q, a_scale, a_fmt, b_q, b_scale, b_fmt, M, N, K, scaling, c_bf16, ldc,
+                            mxq::GEMM_PATH_CHECKED, stream);
 }
 
 mxq_status scaled_gemm_exact(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fmt, const uint8_t* b_q,
                              const void* b_scale, mxq_fp8 b_fmt, int64_t M, int64_t N, int64_t K, mxq_scaling scaling,
                              uint16_t* c_bf16, int64_t ldc, hipStream_t stream) {
-    return scaled_gemm_impl(a_q, a_scale, a_fmt, b_q, b_scale, b_fmt, M, N, K, scaling, c_bf16, ldc, true, stream);
+    return scaled_gemm_impl(a_q, a_scale, a_fmt, b_q, b_scale, b_fmt, M, N, K, scaling, c_bf16, ldc,
+                            mxq::GEMM_PATH_EXACT, stream);
+}
+
+mxq_status scaled_gemm_fp8(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fmt, const uint8_t* b_q,
+                           const void* b_scale, mxq_fp8 b_fmt, int64_t M, int64_t N, int64_t K, mxq_scaling scaling,
+                           uint16_t* c_bf16, int64_t ldc, hipStream_t stream) {
+    return scaled_gemm_impl(a_q, a_scale, a_fmt, b_q, b_scale, b_fmt, M, N, K, scaling, c_bf16, ldc,
+                            mxq::GEMM_PATH_FP8, stream);
 }
 
 mxq_status grouped_scaled_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* group_offsets, int64_t G,

@@ -15,6 +15,11 @@
 // as its second, so a lane's four consecutive accumulator registers are four consecutive n of one output row m
 // (8-byte bf16 stores).
 //
+// Paths (see the path-selection notes below): scaled_gemm takes the FP8 instruction only on large tiles at
+// K >= 12288 when a device-side range check of both operands allows it, and otherwise the exact path (operands
+// dequantized to bf16 exactly, bf16 instruction, fp32 accumulation); scaled_gemm_exact always takes the exact path,
+// scaled_gemm_fp8 always the FP8 instruction. The grouped variants take the exact path.
+//
 // Small-tile kernel (gemm_kernel): 256 threads (4 waves, 2 x 2), a 128 x 128 output tile, waves own 64 x 64, as
 // 4 x 4 v_mfma_scale_f32_16x16x128_f8f6f4 on the FP8 path or 2 x 2 v_mfma_f32_32x32x16_bf16 on operands dequantized
 // to bf16 (the exact path). K advances 128 bytes per stage; stages are double-buffered in LDS. LDS rows are 128 bytes
@@ -50,8 +55,12 @@ struct GemmArgs {
     int64_t c_gstride;                 // token groups: distance from one expert's output to the next
     const int64_t* offsets;            // grouped only: [G+1]
     int64_t G;
-    int exact;                         // host only: take the exact path whatever K is
+    int gate;                          // large tiles, no groups: 0 = always run; 1 (FP8) / 2 (exact) = run the tile
+                                       // only if its first output element holds kGateFp8 / kGateExact
 };
+
+// Tile gates of the checked path (bf16 NaN patterns the epilogue never writes for finite results).
+constexpr uint16_t kGateFp8 = 0x7FA1u, kGateExact = 0x7FA2u;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
 
@@ -410,8 +419,9 @@ __device__ __forceinline__ void wait_copies_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
+// One output tile (workgroup-uniform index bid) of the large-tile kernel; returning ends the tile.
 template <bool MX, int FA, int FB, int GM, int MF>
-__global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_in) {
     // Token groups: every expert has its own K range (a multiple of 32, not of the 64-byte stage) and scale rows of
     // any byte alignment; they run the exact path only.
     constexpr bool TOK = GM == GM_TOKENS;
@@ -443,7 +453,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         // XCD shares the large experts at the front), grouped by GROUP_M2 row tiles of one expert.
         const int tiles_m = (int)((g.M + TB - 1) / TB);
         const int tiles_mm = (int)g.G * tiles_m;
-        const int v = blockIdx.x;
+        const int v = bid_in;
         const int per_group = GROUP_M2 * tiles_n;
         const int first_m = (v / per_group) * GROUP_M2;
         const int gm = min(GROUP_M2, tiles_mm - first_m);
@@ -463,7 +473,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         if (Cb) Cb += grp * g.c_gstride;
         if (Cf) Cf += grp * g.c_gstride;
     } else if constexpr (GM == GM_ROWS) {
-        const int64_t bid = blockIdx.x;
+        const int64_t bid = bid_in;
         const int64_t t = bid / tiles_n;
         n0 = (bid % tiles_n) * TB;
         int64_t acc_t = 0, grp = -1, lo = 0, hi = 0;
@@ -483,7 +493,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
     } else {
         const int tiles_m = (int)((g.M + TB - 1) / TB);
         const int T = tiles_m * tiles_n;
-        const int bid = blockIdx.x;
+        const int bid = bid_in;
         const int T8 = T & ~7;
         const int v = bid < T8 ? (bid & 7) * (T8 >> 3) + (bid >> 3) : bid;
         const int per_group = GROUP_M2 * tiles_n;
@@ -493,6 +503,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         m0 = (int64_t)(first_m + r % gm) * TB;
         n0 = (int64_t)(r / gm) * TB;
         m_end = (m0 + TB < g.M) ? m0 + TB : g.M;
+        if (g.gate) {
+            // Checked path: the tile's first output element names the kernel that computes it (written by
+            // gate_broadcast_kernel; only this workgroup writes the tile, and only after this read).
+            const uint32_t v = __builtin_amdgcn_readfirstlane((uint32_t)Cb[m0 * g.ldc + n0]);
+            if (v != (g.gate == 1 ? kGateFp8 : kGateExact)) return;
+        }
     }
     const int64_t n_end = (n0 + TB < g.N) ? n0 + TB : g.N;
 
@@ -1029,14 +1045,124 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
         }
 }
 
+template <bool MX, int FA, int FB, int GM, int MF>
+__global__ __launch_bounds__(GTHREADS, 1) void gemm_big_kernel(GemmArgs g) {
+    gemm_big_tile<MX, FA, FB, GM, MF>(g, blockIdx.x);
+}
+
+// The exact half of the checked path's kernel pair on a persistent grid: each workgroup walks tiles blockIdx.x,
+// blockIdx.x + gridDim.x, ... and computes those its gate names. When the check picks the FP8 instruction (the usual
+// case) this launch is one gate read per tile on a grid of one workgroup per CU, instead of a full grid of
+// workgroups that each hold 144 KiB of LDS only to read their gate.
+template <bool MX, int FA, int FB>
+__global__ __launch_bounds__(GTHREADS, 1) void gemm_big_gated_loop_kernel(GemmArgs g, int tiles) {
+    for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
+        __syncthreads();                           // the previous tile's LDS reads are done before new copies land
+        gemm_big_tile<MX, FA, FB, GM_NONE, 2>(g, t);
+    }
+}
+
 // Path selection. The FP8 matrix instructions (v_mfma_*_f8f6f4 and the older *_fp8_fp8 forms) sum the products of
-// one 32-value block with a narrow internal window: products far below the block's largest lose low-order bits,
-// an error of up to ~2^-12 of sum |a b| per instruction on wide-range data, while block sums and the fp32
-// accumulator input are combined exactly. The bf16 instruction accumulates at fp32 quality. Measured on MX-quantized
-// N(0,1) operands against the bound |err| <= 2^-7 |y| + 2^-20 sum|a b|, the FP8 path's worst ratio is 2.2 at K = 1024,
-// 0.98 at 4096, 0.89 at 8192, 0.70 at 12288 and 0.49 at 36864 (0.5 is bf16 output rounding alone). The FP8 path is
-// therefore used from K >= kFp8MinK (worst ratio <= 0.75); below it the operands are dequantized to bf16 (exact) for the bf16 instruction.
+// one instruction's K window with a narrow internal window: products far below the largest lose low-order bits, an
+// error of up to ~2^-12 of sum |a b| per instruction on wide-range data, while window sums and the fp32 accumulator
+// input are combined exactly. The bf16 instruction accumulates at fp32 quality. Measured on MX-quantized N(0,1)
+// operands against the bound |err| <= 2^-7 |y| + 2^-20 sum|a b|, the FP8 path's worst ratio is 2.2 at K = 1024, 0.98
+// at 4096, 0.89 at 8192, 0.70 at 12288 and 0.49 at 36864 (0.5 is bf16 output rounding alone); on operands whose
+// windows mix magnitudes far apart (rare large outliers, values spread over many binades, many zeros) it exceeds
+// the bound at every K. The checked path (scaled_gemm) therefore takes the FP8 instruction only from K >= kFp8MinK
+// and only when no 64-value window of either operand holds kWideCount or more codes (zeros included) more than
+// kWideBinades binades below the window's largest (range_check_kernel); otherwise the exact path: operands
+// dequantized to bf16 (exact) for the bf16 instruction.
 constexpr int64_t kFp8MinK = 12288;
+constexpr int kWideBinades = 6, kWideCount = 24;
+
+// ------------------------------------------------------------------ operand range check (checked path)
+// Every 64-value window of K (the large-tile kernel's stage, one FP8 instruction's K span) of either operand is
+// checked. A code's binade is its exponent field (E4M3: bits 6..3, E5M2: bits 6..2; zeros and subnormals read 0)
+// plus, for MX, its 32-block's scale byte; the window is wide if it holds a nonzero code and at least kWideCount
+// codes lie more than kWideBinades binades below the window's largest. A window of zeros is never wide (its products
+// are exact). Any wide window sets *word (one atomic per workgroup that found one). Reads every code once:
+// (M + N) K bytes, plus (M + N) K / 32 scale bytes for MX.
+struct RangeOperand {
+    const uint8_t* q;      // [rows][K] codes: window w is bytes 64 w .. 64 w + 63
+    const uint8_t* s;      // MX: [rows][K/32] E8M0 bytes: window w's two blocks are bytes 2 w, 2 w + 1
+    int64_t windows;       // rows * K / 64
+    int sh;                // exponent field shift: 3 (E4M3) or 2 (E5M2)
+};
+
+__device__ __forceinline__ uint32_t max_u16x2_pk(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+// Workgroups [0, blocks_a) take A's windows, the rest B's; a workgroup takes 256 consecutive windows (windows are
+// contiguous in memory, so a window's bytes and its scale bytes follow from its index alone). Four lanes share a
+// window: lane quarter k holds bytes 16k .. 16k + 15 (quarters 0-1 the first 32-block, 2-3 the second), so each load
+// instruction of a wave reads 1 KiB contiguous. With mag the code's magnitude (bits 6..0) and e = mag >> sh,
+// "e + scale < top - kWideBinades" is "mag < (top - kWideBinades - scale) << sh", compared four bytes at a time.
+template <bool MX>
+__global__ __launch_bounds__(256) void range_check_kernel(RangeOperand a, RangeOperand b, int64_t blocks_a,
+                                                          uint32_t* __restrict__ word) {
+    constexpr int U = 4;                                   // 64 windows per workgroup per trip, 4 trips
+    const bool isa = (int64_t)blockIdx.x < blocks_a;
+    const RangeOperand o = isa ? a : b;
+    const int64_t w0 = ((int64_t)blockIdx.x - (isa ? 0 : blocks_a)) * 256;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, quarter = lane & 3;
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t w = w0 + 64 * u + 16 * wave + (lane >> 2);
+        v[u] = w < o.windows ? ldnt16(o.q + 64 * w + 16 * quarter) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    int wide = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t w = w0 + 64 * u + 16 * wave + (lane >> 2);
+        const uint32_t m0 = v[u].x & 0x7F7F7F7Fu, m1 = v[u].y & 0x7F7F7F7Fu;
+        const uint32_t m2 = v[u].z & 0x7F7F7F7Fu, m3 = v[u].w & 0x7F7F7F7Fu;
+        uint32_t nz = m0 | m1 | m2 | m3;
+        uint32_t lo = max_u16x2_pk(max_u16x2_pk(m0 & 0x00FF00FFu, m1 & 0x00FF00FFu),
+                                   max_u16x2_pk(m2 & 0x00FF00FFu, m3 & 0x00FF00FFu));
+        uint32_t hi = max_u16x2_pk(max_u16x2_pk(m0 & 0xFF00FF00u, m1 & 0xFF00FF00u),
+                                   max_u16x2_pk(m2 & 0xFF00FF00u, m3 & 0xFF00FF00u));
+        uint32_t bm = max(max(lo & 0xFFFFu, lo >> 16), max(hi & 0xFFFFu, hi >> 16) >> 8);
+        bm = max(bm, (uint32_t)__builtin_amdgcn_mov_dpp((int)bm, 0xB1, 0xF, 0xF, false));   // the block's two lanes
+        int sx = 0;
+        if constexpr (MX) sx = w < o.windows ? (int)o.s[2 * w + (quarter >> 1)] : 0;
+        int top = (int)(bm >> o.sh) + sx;
+        top = max(top, __builtin_amdgcn_mov_dpp(top, 0x4E, 0xF, 0xF, false));             // the other block
+        const int th = min(min(max(top - kWideBinades - sx, 0), 32) << o.sh, 128);
+        const uint32_t th4 = (uint32_t)th * 0x01010101u;
+        int cnt = 16 - __builtin_popcount(((m0 | 0x80808080u) - th4) & 0x80808080u)
+                     - __builtin_popcount(((m1 | 0x80808080u) - th4) & 0x80808080u)
+                     - __builtin_popcount(((m2 | 0x80808080u) - th4) & 0x80808080u)
+                     - __builtin_popcount(((m3 | 0x80808080u) - th4) & 0x80808080u);
+        cnt += __builtin_amdgcn_mov_dpp(cnt, 0xB1, 0xF, 0xF, false);
+        cnt += __builtin_amdgcn_mov_dpp(cnt, 0x4E, 0xF, 0xF, false);
+        nz |= (uint32_t)__builtin_amdgcn_mov_dpp((int)nz, 0xB1, 0xF, 0xF, false);
+        nz |= (uint32_t)__builtin_amdgcn_mov_dpp((int)nz, 0x4E, 0xF, 0xF, false);
+        wide |= (nz != 0 && cnt >= kWideCount) ? 1 : 0;
+    }
+    // One atomic per workgroup that found a wide window, skipped once the flag is seen set (an agent-scope load,
+    // so a set flag is seen from any XCD): on wide-range operands most workgroups find one, and same-address atomics
+    // from all of them would serialize.
+    if (__syncthreads_or(wide) && threadIdx.x == 0 &&
+        __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u)
+        atomicOr(word, 1u);
+}
+
+__global__ void gate_clear_kernel(uint32_t* __restrict__ word) { *word = 0u; }
+
+// Writes each large tile's gate into its first output element: kGateExact if a wide window was found, else
+// kGateFp8. The flag word lies in output row 1, which holds no tile's first element.
+__global__ __launch_bounds__(256) void gate_broadcast_kernel(const uint32_t* __restrict__ word, uint16_t* c,
+                                                             int64_t ldc, int64_t tiles_m, int64_t tiles_n) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= tiles_m * tiles_n) return;
+    const uint16_t v = *word ? kGateExact : kGateFp8;
+    const int64_t tm = t / tiles_n;
+    c[tm * TB * ldc + (t - tm * tiles_n) * TB] = v;
+}
 
 // Large tiles when K is a whole number of 64-byte stages, the output spans at least a few tiles, and a tile's
 // 256 rows stay below 2^31 bytes (the kernel's 32-bit buffer offsets). Its copies move 16-byte pieces, so operand row
@@ -1059,7 +1185,8 @@ static bool use_big_tokens(const GemmArgs& a) {
 }
 
 template <bool MX, int FA, int FB, int GM>
-static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks_small, unsigned blocks_big, hipStream_t stream) {
+static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks_small, unsigned blocks_big, int path,
+                                hipStream_t stream) {
     if constexpr (GM == GM_TOKENS) {
         // Expert K ranges differ, so every expert runs the exact path (which meets the bound at any K).
         if (blocks_big > 0 && use_big_tokens(a))
@@ -1067,12 +1194,32 @@ static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks_small, unsign
         else
             hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GM, 2>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
     } else {
-        const bool fp8 = !a.exact && a.K >= kFp8MinK;
-        if (use_big(a, MX, GM == GM_ROWS)) {
-            if (fp8) hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GM, 1>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
-            else hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GM, 2>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
+        const bool big = use_big(a, MX, GM == GM_ROWS);
+        if (GM == GM_NONE && path == GEMM_PATH_CHECKED && big && a.K >= kFp8MinK) {
+            // Checked path: clear the flag word (in output row 1), check both operands, write every tile's gate,
+            // then the FP8 and exact kernels as a pair; each tile runs in the one its gate names.
+            uint32_t* word = reinterpret_cast<uint32_t*>((reinterpret_cast<uintptr_t>(a.c + a.ldc + 2) + 3) & ~uintptr_t(3));
+            const int64_t tiles_m = (a.M + TB - 1) / TB, tiles_n = (a.N + TB - 1) / TB;
+            RangeOperand ra{a.a, a.sa, a.M * (a.K / 64), FA == FMT_E4M3 ? 3 : 2};
+            RangeOperand rb{a.b, a.sb, a.N * (a.K / 64), FB == FMT_E4M3 ? 3 : 2};
+            const int64_t blocks_a = (ra.windows + 255) / 256, blocks_b = (rb.windows + 255) / 256;
+            hipLaunchKernelGGL(gate_clear_kernel, dim3(1), dim3(1), 0, stream, word);
+            hipLaunchKernelGGL((range_check_kernel<MX>), dim3((unsigned)(blocks_a + blocks_b)), dim3(256), 0, stream,
+                               ra, rb, blocks_a, word);
+            hipLaunchKernelGGL(gate_broadcast_kernel, dim3((unsigned)((tiles_m * tiles_n + 255) / 256)), dim3(256), 0,
+                               stream, word, a.c, a.ldc, tiles_m, tiles_n);
+            GemmArgs g1 = a, g2 = a;
+            g1.gate = 1;
+            g2.gate = 2;
+            const int tiles = (int)(tiles_m * tiles_n);
+            hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GM, 1>), dim3(blocks_big), dim3(GTHREADS), 0, stream, g1);
+            hipLaunchKernelGGL((gemm_big_gated_loop_kernel<MX, FA, FB>), dim3((unsigned)(tiles < 256 ? tiles : 256)),
+                               dim3(GTHREADS), 0, stream, g2, tiles);
+        } else if (GM == GM_NONE && path == GEMM_PATH_FP8) {
+            if (big) hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GM, 1>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
+            else hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GM, 1>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
         } else {
-            if (fp8) hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GM, 1>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
+            if (big) hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GM, 2>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
             else hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GM, 2>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
         }
     }
@@ -1081,9 +1228,9 @@ static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks_small, unsign
 
 hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt, const uint8_t* b_q,
                               const void* b_scale, int b_fmt, int64_t M, int64_t N, int64_t K, int mx,
-                              uint16_t* c, int64_t ldc, bool exact, hipStream_t stream) {
+                              uint16_t* c, int64_t ldc, int path, hipStream_t stream) {
     GemmArgs a{};
-    a.a = a_q; a.b = b_q; a.c = c; a.M = M; a.N = N; a.K = K; a.ldc = ldc; a.exact = exact ? 1 : 0;
+    a.a = a_q; a.b = b_q; a.c = c; a.M = M; a.N = N; a.K = K; a.ldc = ldc;
     a.lda = K; a.ldb = K; a.ldsa = K / 32; a.ldsb = K / 32;
     if (mx) { a.sa = (const uint8_t*)a_scale; a.sb = (const uint8_t*)b_scale; }
     else { a.pa = (const float*)a_scale; a.pb = (const float*)b_scale; }
@@ -1091,11 +1238,11 @@ hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt
     const int64_t big = ((M + TB - 1) / TB) * ((N + TB - 1) / TB);
     if (small > 0x7FFFFFFF) return hipErrorInvalidValue;
     const unsigned bs = (unsigned)small, bb = (unsigned)big;
-    if (mx) return launch_gemm_t<true, 0, 0, GM_NONE>(a, bs, bb, stream);
-    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 0, 0, GM_NONE>(a, bs, bb, stream);
-    if (a_fmt == FMT_E5M2 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 1, 0, GM_NONE>(a, bs, bb, stream);
-    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E5M2) return launch_gemm_t<false, 0, 1, GM_NONE>(a, bs, bb, stream);
-    return launch_gemm_t<false, 1, 1, GM_NONE>(a, bs, bb, stream);
+    if (mx) return launch_gemm_t<true, 0, 0, GM_NONE>(a, bs, bb, path, stream);
+    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 0, 0, GM_NONE>(a, bs, bb, path, stream);
+    if (a_fmt == FMT_E5M2 && b_fmt == FMT_E4M3) return launch_gemm_t<false, 1, 0, GM_NONE>(a, bs, bb, path, stream);
+    if (a_fmt == FMT_E4M3 && b_fmt == FMT_E5M2) return launch_gemm_t<false, 0, 1, GM_NONE>(a, bs, bb, path, stream);
+    return launch_gemm_t<false, 1, 1, GM_NONE>(a, bs, bb, path, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* offsets, int64_t G,
@@ -1110,7 +1257,7 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int
     const int64_t small = ((total_rows + BM - 1) / BM + G) * ((N + BN - 1) / BN);
     const int64_t big = ((total_rows + TB - 1) / TB + G) * ((N + TB - 1) / TB);
     if (small > 0x7FFFFFFF) return hipErrorInvalidValue;
-    return launch_gemm_t<true, 0, 0, GM_ROWS>(a, (unsigned)small, (unsigned)big, stream);
+    return launch_gemm_t<true, 0, 0, GM_ROWS>(a, (unsigned)small, (unsigned)big, GEMM_PATH_EXACT, stream);
 }
 
 hipError_t launch_grouped_wgrad(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
@@ -1123,7 +1270,7 @@ hipError_t launch_grouped_wgrad(const uint8_t* a_q, const uint8_t* a_s, const ui
     const int64_t blocks = G * ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int64_t big = G * ((M + TB - 1) / TB) * ((N + TB - 1) / TB);
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    return launch_gemm_t<true, 0, 0, GM_TOKENS>(a, (unsigned)blocks, (unsigned)big, stream);
+    return launch_gemm_t<true, 0, 0, GM_TOKENS>(a, (unsigned)blocks, (unsigned)big, GEMM_PATH_EXACT, stream);
 }
 
 }  // namespace mxq

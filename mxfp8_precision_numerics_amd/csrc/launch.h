@@ -27,9 +27,13 @@ hipError_t launch_pertensor_quantize_delayed(const uint16_t* x, int64_t rows, in
 hipError_t launch_swiglu_mx_quantize(const uint16_t* c, int64_t rows, int64_t F, uint8_t* q, uint8_t* s, int rule,
                                      hipStream_t stream);
 
+// GEMM paths: CHECKED takes the FP8 instruction only for large tiles at K >= 12288 whose operands pass the device-side
+// range check (else the exact path); EXACT dequantizes to bf16 for the bf16 instruction at every K; FP8 takes the
+// FP8 instruction at every K.
+enum : int { GEMM_PATH_CHECKED = 0, GEMM_PATH_EXACT = 1, GEMM_PATH_FP8 = 2 };
 hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt, const uint8_t* b_q,
                               const void* b_scale, int b_fmt, int64_t M, int64_t N, int64_t K, int mx,
-                              uint16_t* c, int64_t ldc, bool exact, hipStream_t stream);
+                              uint16_t* c, int64_t ldc, int path, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* offsets, int64_t G,
                                int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s, int64_t ldb,

@@ -85,7 +85,7 @@ def test_pertensor_validation():
     assert f(MIS, 64, 64, 0, C.c_float(1.0), None, P, P, P, P, P, ws, None) == 3
 
 
-@pytest.mark.parametrize("name", ["scaled_gemm", "scaled_gemm_exact"])
+@pytest.mark.parametrize("name", ["scaled_gemm", "scaled_gemm_exact", "scaled_gemm_fp8"])
 def test_gemm_validation(name):
     f = getattr(_lib.load(), name)
     assert f(None, P, 0, P, P, 0, 64, 64, 64, 1, P, 64, None) == 1

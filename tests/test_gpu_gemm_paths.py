@@ -1,0 +1,196 @@
+"""GPU checks of scaled_gemm's path choice and of the three GEMM entry points.
+
+- scaled_gemm picks the FP8 instruction (large tiles, K >= 12288) only when no 64-value K window of either operand
+  is "wide": a window holding a nonzero code in which 24 or more codes lie more than 6 binades below the window's
+  largest (binade = exponent field, plus the 32-block's scale byte for MX). The choice happens on the device; here it
+  is read from the output bytes, which equal scaled_gemm_fp8's when the FP8 instruction ran and scaled_gemm_exact's
+  when the exact path ran, and compared with that definition evaluated on the host, on operands with one planted
+  window at either side of each boundary (23 / 24 small codes, MX scales 6 / 7 binades apart, a window of zeros).
+- scaled_gemm keeps |C - y| <= 2^-7 |y| + 2^-20 sum|a b| on every element for wide-range operands (outliers, spread
+  magnitudes, scaled columns, mostly zeros) at K = 12288 and 36864, MX and per-tensor, while normal operands still
+  take the FP8 instruction.
+- The K threshold itself: scaled_gemm_fp8 (FP8 instruction at every K) on MX-quantized N(0,1) operands exceeds the
+  bound at K = 1024 and stays within it at K = 12288 and 36864, while the exact path stays within it at every K.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_precision_numerics_amd as mxq
+import oracle
+from gpu_util import DEV, need_gpu, say, u8
+from mxfp8_precision_numerics_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+REL, ABS_S = 2.0 ** -7, 2.0 ** -20
+
+
+def _ratio(C, y, S):
+    err = np.abs(C.float().cpu().numpy().astype(np.float64) - y)
+    return float(np.max(err / (REL * np.abs(y) + ABS_S * S)))
+
+
+def any_wide_window(q, s, fmt):
+    """The range check's definition, evaluated plainly on the host: q [rows][K] codes, s [rows][K/32] E8M0 bytes (MX)
+    or None (per-tensor)."""
+    q = q.astype(np.int64)
+    rows, K = q.shape
+    e = (q >> 3) & 15 if fmt == mxq.E4M3 else (q >> 2) & 31
+    if s is not None:
+        e = e + np.repeat(s.astype(np.int64), 32, axis=1)
+    w = e.reshape(rows, K // 64, 64)
+    nonzero = ((q & 0x7F) != 0).reshape(rows, K // 64, 64).any(axis=2)
+    top = w.max(axis=2, keepdims=True)
+    small = (w < top - 6).sum(axis=2)
+    return bool(((small >= 24) & nonzero).any())
+
+
+def _to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _run_three(aq, asc, bq, bsc, scaling, fa, fb):
+    outs = {}
+    for path in ("checked", "fp8", "exact"):
+        outs[path] = mxq.scaled_gemm(aq, asc, bq, bsc, scaling, fa, fb, path=path)
+    torch.cuda.synchronize()
+    return outs
+
+
+# Planted cases on MX operands (M = N = 512, K = 12288): (name, operand, row, window, codes of the window as
+# (count of 0x08 codes, rest 0x70), scale-byte offset of the window's second block, or None to keep the scales)
+MX_CASES = [
+    ("normal", None, 0, 0, None, None),
+    ("a: 23 small codes", "a", 5, 7, 23, None),
+    ("a: 24 small codes", "a", 5, 7, 24, None),
+    ("b: 23 small codes", "b", 300, 100, 23, None),
+    ("b: 24 small codes", "b", 300, 100, 24, None),
+    ("a: window of zeros", "a", 11, 40, "zeros", None),
+    ("a: second block's scale 6 binades lower", "a", 9, 3, 0, -6),
+    ("a: second block's scale 7 binades lower", "a", 9, 3, 0, -7),
+]
+
+
+@pytest.mark.parametrize("case", MX_CASES, ids=[c[0] for c in MX_CASES])
+def test_checked_path_choice_mx(case):
+    need_gpu()
+    name, which, row, win, small, sdiff = case
+    say("checked path mx", name)
+    M = N = 512
+    K = 12288
+    A = workloads.normal_bf16((M, K), 1.0, 41, 1, DEV)
+    B = workloads.normal_bf16((N, K), 1.0, 41, 2, DEV)
+    qa, qb = mxq.mx_quantize(A, colwise=False), mxq.mx_quantize(B, colwise=False)
+    ops = {"a": [u8(qa.q_row), u8(qa.s_row)], "b": [u8(qb.q_row), u8(qb.s_row)]}
+    if which is not None:
+        q, s = ops[which]
+        k0 = 64 * win
+        if small == "zeros":
+            q[row, k0:k0 + 64] = 0
+            s[row, 2 * win:2 * win + 2] = 0
+        else:
+            q[row, k0:k0 + 64] = 0x70
+            q[row, k0:k0 + small] = 0x08
+            if sdiff is not None:
+                s[row, 2 * win] = 127
+                s[row, 2 * win + 1] = 127 + sdiff
+    want_exact = any_wide_window(*ops["a"], mxq.E4M3) or any_wide_window(*ops["b"], mxq.E4M3)
+    expected = {"normal": False, "a: 23 small codes": False, "a: 24 small codes": True, "b: 23 small codes": False,
+                "b: 24 small codes": True, "a: window of zeros": False,
+                "a: second block's scale 6 binades lower": False,
+                "a: second block's scale 7 binades lower": True}[name]
+    assert want_exact == expected                      # the definition itself reads the planted windows as meant
+    dq = [_to_dev(x) for x in ops["a"] + ops["b"]]
+    outs = _run_three(dq[0], dq[1], dq[2], dq[3], mxq.MX_BLOCK32, mxq.E4M3, mxq.E4M3)
+    ref = outs["exact"] if want_exact else outs["fp8"]
+    assert torch.equal(outs["checked"].view(torch.int16), ref.view(torch.int16)), "path chosen"
+    assert not torch.equal(outs["fp8"].view(torch.int16), outs["exact"].view(torch.int16))   # the paths differ
+    y, S = oracle.gemm_ref(ops["a"][0], ops["a"][1], oracle.E4M3, ops["b"][0], ops["b"][1], oracle.E4M3,
+                           oracle.MX_BLOCK32)
+    assert _ratio(outs["checked"], y, S) <= 1.0
+
+
+@pytest.mark.parametrize("fa,fb", [(mxq.E4M3, mxq.E4M3), (mxq.E5M2, mxq.E4M3)])
+@pytest.mark.parametrize("small", [None, 23, 24])
+def test_checked_path_choice_pertensor(fa, fb, small):
+    """Per-tensor operands (E5M2 A as in dgrad / wgrad): a planted window in A with 23 or 24 small codes."""
+    need_gpu()
+    say("checked path per-tensor", fa, fb, small)
+    M = N = 512
+    K = 12288
+    A = workloads.normal_bf16((M, K), 1e-3 if fa == mxq.E5M2 else 1.0, 42, 1, DEV)
+    B = workloads.normal_bf16((N, K), 0.02, 42, 2, DEV)
+    pa, pb = mxq.pertensor_quantize(A, fa, want_qt=False), mxq.pertensor_quantize(B, fb, want_qt=False)
+    qa = u8(pa.q)
+    if small is not None:
+        big_code, small_code = (0x74, 0x04) if fa == mxq.E5M2 else (0x70, 0x08)
+        qa[17, 640:704] = big_code
+        qa[17, 640:640 + small] = small_code
+    want_exact = any_wide_window(qa, None, fa) or any_wide_window(u8(pb.q), None, fb)
+    assert want_exact == (small == 24)
+    outs = _run_three(_to_dev(qa), pa.scale, pb.q, pb.scale, mxq.PER_TENSOR, fa, fb)
+    ref = outs["exact"] if want_exact else outs["fp8"]
+    assert torch.equal(outs["checked"].view(torch.int16), ref.view(torch.int16)), "path chosen"
+    of = {mxq.E4M3: oracle.E4M3, mxq.E5M2: oracle.E5M2}
+    y, S = oracle.gemm_ref(qa, np.float32(pa.scale.item()), of[fa], u8(pb.q), np.float32(pb.scale.item()), of[fb],
+                           oracle.PER_TENSOR)
+    assert _ratio(outs["checked"], y, S) <= 1.0
+
+
+@pytest.mark.parametrize("kind", workloads.WIDE_RANGE_KINDS)
+@pytest.mark.parametrize("M,N,K", [(520, 528, 12288), (516, 520, 36864)])
+def test_default_meets_the_bound_on_wide_range_operands(kind, M, N, K):
+    """scaled_gemm (the default) on wide-range operands where the FP8 instruction alone breaks the bound: every element
+    within it, MX and per-tensor (E4M3 x E5M2); the check routes them to the exact path."""
+    need_gpu()
+    say("default gemm wide-range", kind, M, N, K)
+    A = workloads.wide_range_bf16((M, K), kind, 34, 2 * K + M, DEV)
+    B = workloads.wide_range_bf16((N, K), kind, 34, 2 * K + N + 5, DEV)
+    qa, qb = mxq.mx_quantize(A, colwise=False), mxq.mx_quantize(B, colwise=False)
+    outs = _run_three(qa.q_row, qa.s_row, qb.q_row, qb.s_row, mxq.MX_BLOCK32, mxq.E4M3, mxq.E4M3)
+    y, S = oracle.gemm_ref(u8(qa.q_row), u8(qa.s_row), oracle.E4M3, u8(qb.q_row), u8(qb.s_row), oracle.E4M3,
+                           oracle.MX_BLOCK32)
+    r_def, r_fp8 = _ratio(outs["checked"], y, S), _ratio(outs["fp8"], y, S)
+    say(f"  MX worst ratio: default {r_def:.3f}, FP8 instruction alone {r_fp8:.3f}")
+    assert r_def <= 1.0
+    assert torch.equal(outs["checked"].view(torch.int16), outs["exact"].view(torch.int16))
+    pa = mxq.pertensor_quantize(A, mxq.E4M3, want_qt=False)
+    pb = mxq.pertensor_quantize(B, mxq.E5M2, want_qt=False)
+    outs = _run_three(pa.q, pa.scale, pb.q, pb.scale, mxq.PER_TENSOR, mxq.E4M3, mxq.E5M2)
+    y, S = oracle.gemm_ref(u8(pa.q), np.float32(pa.scale.item()), oracle.E4M3, u8(pb.q),
+                           np.float32(pb.scale.item()), oracle.E5M2, oracle.PER_TENSOR)
+    r_def = _ratio(outs["checked"], y, S)
+    say(f"  per-tensor worst ratio: default {r_def:.3f}, FP8 instruction alone {_ratio(outs['fp8'], y, S):.3f}")
+    assert r_def <= 1.0
+
+
+@pytest.mark.parametrize("K", [12288, 36864])
+def test_default_takes_fp8_on_normal_operands(K):
+    """Normally distributed operands (the workloads' data) keep the FP8 instruction under the check."""
+    need_gpu()
+    A = workloads.normal_bf16((520, K), 1.0, 43, 1, DEV)
+    B = workloads.normal_bf16((528, K), 1.0, 43, 2, DEV)
+    qa, qb = mxq.mx_quantize(A, colwise=False), mxq.mx_quantize(B, colwise=False)
+    outs = _run_three(qa.q_row, qa.s_row, qb.q_row, qb.s_row, mxq.MX_BLOCK32, mxq.E4M3, mxq.E4M3)
+    assert torch.equal(outs["checked"].view(torch.int16), outs["fp8"].view(torch.int16))
+
+
+def test_fp8_instruction_k_threshold():
+    """Why scaled_gemm needs K >= 12288 for the FP8 instruction: on MX-quantized N(0,1) operands (520 x 528 outputs)
+    the FP8 instruction alone exceeds the bound at K = 1024 and meets it at K = 12288 and 36864; the exact path meets
+    it at every K. The worst ratios are printed for the record."""
+    need_gpu()
+    ratios = {}
+    for K in (1024, 4096, 12288, 36864):
+        A = workloads.normal_bf16((520, K), 1.0, 44, K, DEV)
+        B = workloads.normal_bf16((528, K), 1.0, 44, K + 1, DEV)
+        qa, qb = mxq.mx_quantize(A, colwise=False), mxq.mx_quantize(B, colwise=False)
+        outs = _run_three(qa.q_row, qa.s_row, qb.q_row, qb.s_row, mxq.MX_BLOCK32, mxq.E4M3, mxq.E4M3)
+        y, S = oracle.gemm_ref(u8(qa.q_row), u8(qa.s_row), oracle.E4M3, u8(qb.q_row), u8(qb.s_row), oracle.E4M3,
+                               oracle.MX_BLOCK32)
+        ratios[K] = (_ratio(outs["fp8"], y, S), _ratio(outs["exact"], y, S), _ratio(outs["checked"], y, S))
+        say(f"  K={K}: worst |err|/bound FP8 {ratios[K][0]:.3f}, exact {ratios[K][1]:.3f}, default {ratios[K][2]:.3f}")
+    assert ratios[1024][0] > 1.0
+    assert ratios[12288][0] <= 1.0 and ratios[36864][0] <= 1.0
+    assert all(r[1] <= 1.0 and r[2] <= 1.0 for r in ratios.values())
