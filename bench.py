@@ -119,6 +119,7 @@ def main():
 
     # preallocated outputs (the library never allocates)
     u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+    words = torch.zeros((3, 2), dtype=torch.int32, device=dev)     # range words of X, W, dY: [row, col]
     mxX = mxq.MXTensor(u8(M, K), u8(M, K // 32), u8(K, M), u8(K, M // 32))
     mxW = mxq.MXTensor(u8(N, K), u8(N, K // 32), u8(K, N), u8(K, N // 32))
     mxD = mxq.MXTensor(u8(M, N), u8(M, N // 32), u8(N, M), u8(N, M // 32))
@@ -220,16 +221,23 @@ def main():
         return _P()
 
     def step(rec):
+        # the MX linear layer: each quantize also emits its orientations' range words, and each GEMM picks the FP8
+        # instruction or the exact path from its operands' words on the device
         with part("mx_quant_XWdY", rec):
-            mxq.mx_quantize(X, out=mxX)
-            mxq.mx_quantize(W, out=mxW)
-            mxq.mx_quantize(dY, out=mxD)
-        with part("mx_gemm_fwd", rec):
-            mxq.scaled_gemm(mxX.q_row, mxX.s_row, mxW.q_row, mxW.s_row, mxq.MX_BLOCK32, out=Y)          # Y = X W^T
-        with part("mx_gemm_dgrad", rec):
-            mxq.scaled_gemm(mxD.q_row, mxD.s_row, mxW.q_col, mxW.s_col, mxq.MX_BLOCK32, out=dX)        # dX = dY W
-        with part("mx_gemm_wgrad", rec):
-            mxq.scaled_gemm(mxD.q_col, mxD.s_col, mxX.q_col, mxX.s_col, mxq.MX_BLOCK32, out=dW)        # dW = dY^T X
+            mxq.mx_quantize_ranged(X, out=mxX, words=words[0])
+            mxq.mx_quantize_ranged(W, out=mxW, words=words[1])
+            mxq.mx_quantize_ranged(dY, out=mxD, words=words[2])
+        with part("mx_gemm_fwd", rec):                                                             # Y = X W^T
+            mxq.scaled_gemm_ranged(mxX.q_row, mxX.s_row, words[0, 0:1], mxW.q_row, mxW.s_row, words[1, 0:1], out=Y)
+        with part("mx_gemm_dgrad", rec):                                                           # dX = dY W
+            mxq.scaled_gemm_ranged(mxD.q_row, mxD.s_row, words[2, 0:1], mxW.q_col, mxW.s_col, words[1, 1:2], out=dX)
+        with part("mx_gemm_wgrad", rec):                                                           # dW = dY^T X
+            mxq.scaled_gemm_ranged(mxD.q_col, mxD.s_col, words[2, 1:2], mxX.q_col, mxX.s_col, words[0, 1:2], out=dW)
+        # the same fwd and dgrad through the default entry point, which checks the codes itself
+        with part("mx_gemm_fwd_checked", rec):
+            mxq.scaled_gemm(mxX.q_row, mxX.s_row, mxW.q_row, mxW.s_row, mxq.MX_BLOCK32, out=Y)
+        with part("mx_gemm_dgrad_checked", rec):
+            mxq.scaled_gemm(mxD.q_row, mxD.s_row, mxW.q_col, mxW.s_col, mxq.MX_BLOCK32, out=dX)
         with part("pt_quant", rec):
             px = mxq.pertensor_quantize(X, mxq.E4M3, workspace=ws_pt)
             pw = mxq.pertensor_quantize(W, mxq.E4M3, workspace=ws_pt)
@@ -259,6 +267,15 @@ def main():
         with part("small", rec):
             small_path()
         with part("small_graph", rec):
+            small_graph.replay()
+        # the same two with the stream kept busy (a ~0.1 ms spin) while the host submits, so the window holds device
+        # time only: an idle stream exposes the host's submission latency, which is larger for a graph launch than
+        # for three kernel launches on this stack
+        torch.cuda._sleep(200_000)
+        with part("small_queued", rec):
+            small_path()
+        torch.cuda._sleep(200_000)
+        with part("small_graph_queued", rec):
             small_graph.replay()
         with part("pt_quant_delayed", rec):
             mxq.pertensor_quantize_delayed(X, hists["X"], hpos["X"], mxq.E4M3, workspace=ws_del)
@@ -356,6 +373,11 @@ def main():
         "mx_gemm_fwd_tflops": flop_gemm / (ms["mx_gemm_fwd"] * 1e-3) / 1e12,
         "mx_gemm_dgrad_tflops": flop_gemm / (ms["mx_gemm_dgrad"] * 1e-3) / 1e12,
         "mx_gemm_wgrad_tflops": flop_gemm / (ms["mx_gemm_wgrad"] * 1e-3) / 1e12,
+        "mx_gemm_fwd_checked_tflops": flop_gemm / (ms["mx_gemm_fwd_checked"] * 1e-3) / 1e12,
+        "mx_gemm_dgrad_checked_tflops": flop_gemm / (ms["mx_gemm_dgrad_checked"] * 1e-3) / 1e12,
+        "mx_linear_tflops_incl_quant_checked_gemms": 3 * flop_gemm / ((mx_linear_ms - ms["mx_gemm_fwd"]
+                                                                        - ms["mx_gemm_dgrad"] + ms["mx_gemm_fwd_checked"]
+                                                                        + ms["mx_gemm_dgrad_checked"]) * 1e-3) / 1e12,
         "mx_quant_XWdY_gbs": mxq_XWdY_bytes / (ms["mx_quant_XWdY"] * 1e-3) / 1e9,
         "pt_linear_tflops_incl_quant": 3 * flop_gemm / ((ms["pt_quant"] + ms["pt_gemms"]) * 1e-3) / 1e12,
         "pt_gemms_tflops": 3 * flop_gemm / (ms["pt_gemms"] * 1e-3) / 1e12,
@@ -371,6 +393,8 @@ def main():
         "adam_gbs_vs_18B_ideal": 18 * n_adam / (ms["adam"] * 1e-3) / 1e9,
         "small_us": ms["small"] * 1e3,
         "small_graph_us": ms["small_graph"] * 1e3,
+        "small_queued_us": ms["small_queued"] * 1e3,
+        "small_graph_queued_us": ms["small_graph_queued"] * 1e3,
         "pt_quant_delayed_gbs": sum(4 * r * c for r, c in ((M, K), (N, K), (M, N))) / (ms["pt_quant_delayed"] * 1e-3) / 1e9,
         "adam_delayed_gbs": 18 * n_adam / (ms["adam_delayed"] * 1e-3) / 1e9,
         "wcache_fused_gbs": (21 + 2 / 32) * N * K / (ms["wcache_fused"] * 1e-3) / 1e9,
@@ -400,9 +424,9 @@ def main():
     # library picks); the bf16-peak fraction of the exact-path GEMMs is kept as a secondary field. The headline
     # roofline is the layer's dominant kernel, the GEMM that takes longest.
     gemm_kernels = {
-        "mx_gemm_fwd": ("scaled_gemm MX_BLOCK32 fwd Y = X W^T, 4096x36864x12288", "mx_gemm_fwd_tflops"),
-        "mx_gemm_dgrad": ("scaled_gemm MX_BLOCK32 dgrad dX = dY W, 4096x12288x36864", "mx_gemm_dgrad_tflops"),
-        "mx_gemm_wgrad": ("scaled_gemm MX_BLOCK32 wgrad dW = dY^T X, 36864x12288x4096", "mx_gemm_wgrad_tflops"),
+        "mx_gemm_fwd": ("scaled_gemm_ranged fwd Y = X W^T, 4096x36864x12288", "mx_gemm_fwd_tflops"),
+        "mx_gemm_dgrad": ("scaled_gemm_ranged dgrad dX = dY W, 4096x12288x36864", "mx_gemm_dgrad_tflops"),
+        "mx_gemm_wgrad": ("scaled_gemm_ranged wgrad dW = dY^T X, 36864x12288x4096", "mx_gemm_wgrad_tflops"),
     }
 
     def gemm_roof(part_name):
@@ -416,7 +440,9 @@ def main():
                 "algorithmic_flop_per_launch": flop_gemm, "avg_launch_ms": round(ms[part_name], 4),
                 "share_of_layer": round(ms[part_name] / mx_linear_ms, 4)}
 
-    path_of = {"mx_gemm_fwd": "K = 12288", "mx_gemm_dgrad": "K = 36864", "mx_gemm_wgrad": "K = 4096"}
+    path_of = {"mx_gemm_fwd": "K = 12288, range words 0: block-scaled FP8 MFMA",
+               "mx_gemm_dgrad": "K = 36864, range words 0: block-scaled FP8 MFMA",
+               "mx_gemm_wgrad": "K = 4096: exact path, bf16 MFMA on exactly dequantized operands"}
     dominant = max(gemm_kernels, key=lambda p: ms[p])
     roofline = gemm_roof(dominant)
 
@@ -442,8 +468,10 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)", "data": "synthetic",
         "config": {"workload": "GPT-175B QKV linear fwd+dgrad+wgrad in MXFP8 (X 4096x12288, W 36864x12288, "
-                               "dY 4096x36864), quantize of X, W, dY included; plus per-tensor layer, MX quantize "
-                               "16384x8192, grouped 64-expert GEMM and FP8 Adam over 1.3e9 params in the same step",
+                               "dY 4096x36864): mxq_quantize_ranged of X, W, dY (both orientations, range words) "
+                               "and three scaled_gemm_ranged GEMMs, quantize included; plus per-tensor layer, MX "
+                               "quantize 16384x8192, grouped 64-expert GEMM and FP8 Adam over 1.3e9 params in the "
+                               "same step",
                    "gemm_flop_per_step": 3 * flop_gemm},
         "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
         "device_ms_per_step": round(step_ms, 3),
@@ -512,15 +540,13 @@ def profile_kernel(name, dev):
         run = lambda: _probe.copy(src, dst, 0, 8)  # noqa: E731
     elif name in ("mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad"):
         X, W, dY = workloads.workload2(dev)
-        qx = mxq.mx_quantize(X)
-        qw = mxq.mx_quantize(W)
-        qd = mxq.mx_quantize(dY)
+        (qx, wx), (qw, ww), (qd, wd) = (mxq.mx_quantize_ranged(t) for t in (X, W, dY))
         del X, W, dY
-        a, b = {"mx_gemm_fwd": ((qx.q_row, qx.s_row), (qw.q_row, qw.s_row)),
-                "mx_gemm_dgrad": ((qd.q_row, qd.s_row), (qw.q_col, qw.s_col)),
-                "mx_gemm_wgrad": ((qd.q_col, qd.s_col), (qx.q_col, qx.s_col))}[name]
+        a, b = {"mx_gemm_fwd": ((qx.q_row, qx.s_row, wx[0:1]), (qw.q_row, qw.s_row, ww[0:1])),
+                "mx_gemm_dgrad": ((qd.q_row, qd.s_row, wd[0:1]), (qw.q_col, qw.s_col, ww[1:2])),
+                "mx_gemm_wgrad": ((qd.q_col, qd.s_col, wd[1:2]), (qx.q_col, qx.s_col, wx[1:2]))}[name]
         out = torch.empty((a[0].shape[0], b[0].shape[0]), dtype=torch.bfloat16, device=dev)
-        run = lambda: mxq.scaled_gemm(a[0], a[1], b[0], b[1], mxq.MX_BLOCK32, out=out)  # noqa: E731
+        run = lambda: mxq.scaled_gemm_ranged(a[0], a[1], a[2], b[0], b[1], b[2], out=out)  # noqa: E731
     elif name in ("grouped_gemm_up", "grouped_gemm_down"):
         wl4 = workloads.workload4(dev)
         off4 = torch.from_numpy(wl4["offsets"]).to(dev)

@@ -75,6 +75,21 @@ mxq_status mxq_quantize(const uint16_t* x_bf16, int64_t rows, int64_t cols,
                         mxq_scale_rule rule, hipStream_t stream);
 
 /*
+ * mxq_quantize that also classifies the operand for the FP8 matrix instruction, so that scaled_gemm_ranged can pick its
+ * instruction without re-reading the codes. Arguments and outputs are those of mxq_quantize, plus:
+ *   wide_row (device uint32, required with q_row): 1 if any 64-value window along a row of q_row is wide, else 0;
+ *   wide_col (device uint32, required with q_col): the same for the windows along a row of q_col (64 rows of x).
+ * A window is wide when it holds a nonzero code and 24 or more of its codes lie more than 6 binades below its largest
+ * (a code's binade: its E4M3 exponent field plus its block's scale byte): the definition scaled_gemm's range check
+ * applies to its operands, so the two classify the same codes identically. Requires cols % 64 == 0 for the row
+ * orientation and rows % 64 == 0 for the column orientation (whole windows). The words are cleared and set by the
+ * call's own kernels; an empty x gives 0.
+ */
+mxq_status mxq_quantize_ranged(const uint16_t* x_bf16, int64_t rows, int64_t cols,
+                               uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                               mxq_scale_rule rule, uint32_t* wide_row, uint32_t* wide_col, hipStream_t stream);
+
+/*
  * Fused SwiGLU + MXFP8 row quantize of the routed experts' hidden representation ([OLMO11] Section 11.4.1: a fused
  * SwiGLU-plus-quantization step produces the down projection's operand with no separate BF16-to-MXFP8 pass).
  *   c_bf16[rows][2F]: the up/gate GEMM output, gate in columns [0, F), up in [F, 2F);
@@ -258,6 +273,19 @@ mxq_status scaled_gemm_fp8(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fm
                            const uint8_t* b_q, const void* b_scale, mxq_fp8 b_fmt,
                            int64_t M, int64_t N, int64_t K, mxq_scaling scaling,
                            uint16_t* c_bf16, int64_t ldc, hipStream_t stream);
+
+/*
+ * The MX scaled_gemm with its instruction picked from range words instead of a range check: a_wide and b_wide are
+ * device uint32 words that mxq_quantize_ranged wrote for these operands (the orientation each operand was taken from).
+ * When M, N >= 512, K >= 12288 and K % 512 == 0, the FP8 and exact kernels run as a pair and the words, read on the
+ * device, pick the FP8 instruction if both are 0 and the exact path otherwise; other shapes take the exact path. The
+ * result is byte for byte scaled_gemm's for the same operands, without reading the codes twice. Words that do not
+ * belong to these operands void the accuracy statement. a_scale, b_scale are E8M0 grids [M][K/32], [N][K/32];
+ * everything else is as in scaled_gemm with MX_BLOCK32 and E4M3 operands.
+ */
+mxq_status scaled_gemm_ranged(const uint8_t* a_q, const uint8_t* a_scale, const uint32_t* a_wide,
+                              const uint8_t* b_q, const uint8_t* b_scale, const uint32_t* b_wide,
+                              int64_t M, int64_t N, int64_t K, uint16_t* c_bf16, int64_t ldc, hipStream_t stream);
 
 /*
  * Grouped MX GEMM over ragged expert groups ([OLMO11] Section 11.4.1, routed experts: the up/gate and down

@@ -22,7 +22,7 @@ import torch
 from . import _lib
 from ._lib import E4M3, E5M2, FLOOR, MX_BLOCK32, PER_TENSOR, RCEIL, AdamHParams, MXQError  # noqa: F401
 
-__all__ = ["mx_quantize", "pertensor_quantize", "scaled_gemm", "grouped_scaled_gemm", "fp8_adam_step",
+__all__ = ["mx_quantize", "mx_quantize_ranged", "pertensor_quantize", "scaled_gemm", "scaled_gemm_ranged", "grouped_scaled_gemm", "fp8_adam_step",
            "swiglu_mx_quantize", "swiglu_mx_quantize_oriented", "swiglu_backward_mx_quantize", "route_weighted_mx_quantize",
            "grouped_scaled_gemm_strided", "grouped_wgrad_mx",
            "workspace_bytes", "MXTensor", "AdamHParams", "MXQError", "E4M3", "E5M2", "RCEIL", "FLOOR",
@@ -70,6 +70,48 @@ def mx_quantize(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, rul
     st = _lib.load().mxq_quantize(_ptr(x), rows, cols, _ptr(out.q_row), _ptr(out.s_row), _ptr(out.q_col),
                                   _ptr(out.s_col), rule, _stream(x.device))
     _lib.check("mxq_quantize", st)
+    return out
+
+
+def mx_quantize_ranged(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, rule: int = RCEIL,
+                       out: Optional[MXTensor] = None, words: Optional[torch.Tensor] = None):
+    """mx_quantize plus each orientation's range word (int32 device scalars: 1 if a 64-value window is wide).
+    Returns (MXTensor, words) with words = int32[2]: [row orientation, column orientation]."""
+    _dev(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    dev = x.device
+    if out is None:
+        e = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+        out = MXTensor(e(rows, cols) if rowwise else None, e(rows, cols // 32) if rowwise else None,
+                       e(cols, rows) if colwise else None, e(cols, rows // 32) if colwise else None)
+    if words is None:
+        words = torch.zeros(2, dtype=torch.int32, device=dev)
+    st = _lib.load().mxq_quantize_ranged(_ptr(x), rows, cols, _ptr(out.q_row), _ptr(out.s_row), _ptr(out.q_col),
+                                         _ptr(out.s_col), rule,
+                                         C.c_void_p(words.data_ptr()) if out.q_row is not None else None,
+                                         C.c_void_p(words.data_ptr() + 4) if out.q_col is not None else None,
+                                         _stream(dev))
+    _lib.check("mxq_quantize_ranged", st)
+    return out, words
+
+
+def scaled_gemm_ranged(a_q: torch.Tensor, a_s: torch.Tensor, a_wide: torch.Tensor, b_q: torch.Tensor,
+                       b_s: torch.Tensor, b_wide: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MX C = A B^T (bf16) with the instruction picked on the device from the operands' range words (int32 device
+    scalars, e.g. words[0:1] / words[1:2] of mx_quantize_ranged)."""
+    _dev(a_q, torch.uint8, "a_q"); _dev(b_q, torch.uint8, "b_q")
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    if b_q.shape[1] != K:
+        raise ValueError("a_q and b_q must share K")
+    if not (a_wide.is_cuda and b_wide.is_cuda and a_wide.dtype == torch.int32 and b_wide.dtype == torch.int32):
+        raise ValueError("range words must be int32 device tensors")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+    st = _lib.load().scaled_gemm_ranged(_ptr(a_q), _ptr(a_s), C.c_void_p(a_wide.data_ptr()), _ptr(b_q), _ptr(b_s),
+                                        C.c_void_p(b_wide.data_ptr()), M, N, K, _ptr(out), out.stride(0),
+                                        _stream(a_q.device))
+    _lib.check("scaled_gemm_ranged", st)
     return out
 
 

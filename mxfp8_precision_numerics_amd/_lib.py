@@ -30,6 +30,8 @@ SIGNATURES = {
     "mxq_abi_version": (_I, []),
     "mxq_workspace_bytes": (_SZ, [C.c_char_p, _I64]),
     "mxq_quantize": (_I, [_P, _I64, _I64, _P, _P, _P, _P, _I, _P]),
+    "mxq_quantize_ranged": (_I, [_P, _I64, _I64, _P, _P, _P, _P, _I, _P, _P, _P]),
+    "scaled_gemm_ranged": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "fp8_quantize_pertensor": (_I, [_P, _I64, _I64, _I, _F, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fp8_quantize_pertensor_noalloc": (_I, [_P, _I64, _I64, _I, _F, _P, _P, _P, _P, _P, _P]),
     "scaled_gemm": (_I, [_P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _I, _P, _I64, _P]),

@@ -95,6 +95,29 @@ mxq_status mxq_quantize(const uint16_t* x_bf16, int64_t rows, int64_t cols, uint
     return hip_status(mxq::launch_mx_quantize(x_bf16, rows, cols, q_row, s_row, q_col, s_col, (int)rule, stream));
 }
 
+mxq_status mxq_quantize_ranged(const uint16_t* x_bf16, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
+                               uint8_t* q_col, uint8_t* s_col, mxq_scale_rule rule, uint32_t* wide_row,
+                               uint32_t* wide_col, hipStream_t stream) {
+    if ((q_row == nullptr) != (s_row == nullptr) || (q_col == nullptr) != (s_col == nullptr)) return MXQ_ERR_NULL;
+    const bool row = q_row != nullptr, col = q_col != nullptr;
+    if (!row && !col) return MXQ_ERR_NULL;
+    if ((row && !wide_row) || (col && !wide_col)) return MXQ_ERR_NULL;
+    if (rule != MXQ_SCALE_RCEIL && rule != MXQ_SCALE_FLOOR) return MXQ_ERR_UNSUPPORTED;
+    if (rows < 0 || cols < 0 || cols % 8 != 0) return MXQ_ERR_SHAPE;
+    if ((row && cols % 64 != 0) || (col && rows % 64 != 0)) return MXQ_ERR_SHAPE;   // whole 64-value windows
+    if ((rows + 127) / 128 > kMaxGridY) return MXQ_ERR_SHAPE;
+    if ((row && !al4(wide_row)) || (col && !al4(wide_col))) return MXQ_ERR_ALIGN;
+    if (rows == 0 || cols == 0) {
+        // nothing to quantize; the words still say "no wide window"
+        return hip_status(mxq::launch_mx_quantize_ranged(x_bf16, 0, 0, q_row, s_row, q_col, s_col, (int)rule,
+                                                         wide_row, wide_col, stream));
+    }
+    if (!x_bf16) return MXQ_ERR_NULL;
+    if (!al16(x_bf16) || (row && !al16(q_row)) || (col && !al16(q_col))) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_mx_quantize_ranged(x_bf16, rows, cols, q_row, s_row, q_col, s_col, (int)rule,
+                                                     wide_row, wide_col, stream));
+}
+
 mxq_status swiglu_mx_quantize(const uint16_t* c_bf16, int64_t rows, int64_t F, uint8_t* q, uint8_t* s,
                               mxq_scale_rule rule, hipStream_t stream) {
     if (rule != MXQ_SCALE_RCEIL && rule != MXQ_SCALE_FLOOR) return MXQ_ERR_UNSUPPORTED;
@@ -245,7 +268,8 @@ namespace {
 
 mxq_status scaled_gemm_impl(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fmt, const uint8_t* b_q,
                             const void* b_scale, mxq_fp8 b_fmt, int64_t M, int64_t N, int64_t K, mxq_scaling scaling,
-                            uint16_t* c_bf16, int64_t ldc, int path, hipStream_t stream) {
+                            uint16_t* c_bf16, int64_t ldc, int path, hipStream_t stream,
+                            const uint32_t* a_wide = nullptr, const uint32_t* b_wide = nullptr) {
     if (scaling != MXQ_PER_TENSOR && scaling != MXQ_MX_BLOCK32) return MXQ_ERR_UNSUPPORTED;
     if ((a_fmt != MXQ_E4M3 && a_fmt != MXQ_E5M2) || (b_fmt != MXQ_E4M3 && b_fmt != MXQ_E5M2)) return MXQ_ERR_UNSUPPORTED;
     if (scaling == MXQ_MX_BLOCK32 && (a_fmt != MXQ_E4M3 || b_fmt != MXQ_E4M3)) return MXQ_ERR_UNSUPPORTED;
@@ -256,7 +280,8 @@ mxq_status scaled_gemm_impl(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_f
     if (scaling == MXQ_MX_BLOCK32 ? (!al16(a_scale) || !al16(b_scale)) : (!al4(a_scale) || !al4(b_scale)))
         return MXQ_ERR_ALIGN;
     return hip_status(mxq::launch_scaled_gemm(a_q, a_scale, (int)a_fmt, b_q, b_scale, (int)b_fmt, M, N, K,
-                                              scaling == MXQ_MX_BLOCK32 ? 1 : 0, c_bf16, ldc, path, stream));
+                                              scaling == MXQ_MX_BLOCK32 ? 1 : 0, c_bf16, ldc, path, a_wide, b_wide,
+                                              stream));
 }
 
 }  // namespace
@@ -282,6 +307,15 @@ mxq_status scaled_gemm_fp8(const uint8_t* a_q, const void* a_scale, mxq_fp8 a_fm
                            uint16_t* c_bf16, int64_t ldc, hipStream_t stream) {
     return scaled_gemm_impl(a_q, a_scale, a_fmt, b_q, b_scale, b_fmt, M, N, K, scaling, c_bf16, ldc,
                             mxq::GEMM_PATH_FP8, stream);
+}
+
+mxq_status scaled_gemm_ranged(const uint8_t* a_q, const uint8_t* a_scale, const uint32_t* a_wide,
+                              const uint8_t* b_q, const uint8_t* b_scale, const uint32_t* b_wide, int64_t M,
+                              int64_t N, int64_t K, uint16_t* c_bf16, int64_t ldc, hipStream_t stream) {
+    if (!a_wide || !b_wide) return MXQ_ERR_NULL;
+    if (!al4(a_wide) || !al4(b_wide)) return MXQ_ERR_ALIGN;
+    return scaled_gemm_impl(a_q, a_scale, MXQ_E4M3, b_q, b_scale, MXQ_E4M3, M, N, K, MXQ_MX_BLOCK32, c_bf16, ldc,
+                            mxq::GEMM_PATH_RANGED, stream, a_wide, b_wide);
 }
 
 mxq_status grouped_scaled_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* group_offsets, int64_t G,

@@ -56,7 +56,10 @@ struct GemmArgs {
     const int64_t* offsets;            // grouped only: [G+1]
     int64_t G;
     int gate;                          // large tiles, no groups: 0 = always run; 1 (FP8) / 2 (exact) = run the tile
-                                       // only if its first output element holds kGateFp8 / kGateExact
+                                       // only if its first output element holds kGateFp8 / kGateExact; 3 (FP8) /
+                                       // 4 (exact) = run only if the range words *wa | *wb are 0 / nonzero
+    const uint32_t* wa;                // gates 3, 4: the operands' range words
+    const uint32_t* wb;
 };
 
 // Tile gates of the checked path (bf16 NaN patterns the epilogue never writes for finite results).
@@ -503,11 +506,15 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
         m0 = (int64_t)(first_m + r % gm) * TB;
         n0 = (int64_t)(r / gm) * TB;
         m_end = (m0 + TB < g.M) ? m0 + TB : g.M;
-        if (g.gate) {
+        if (g.gate == 1 || g.gate == 2) {
             // Checked path: the tile's first output element names the kernel that computes it (written by
             // gate_broadcast_kernel; only this workgroup writes the tile, and only after this read).
             const uint32_t v = __builtin_amdgcn_readfirstlane((uint32_t)Cb[m0 * g.ldc + n0]);
             if (v != (g.gate == 1 ? kGateFp8 : kGateExact)) return;
+        } else if (g.gate) {
+            // Ranged path: the operands' range words, written by the quantizers, pick the kernel.
+            const uint32_t wide = __builtin_amdgcn_readfirstlane(*g.wa | *g.wb);
+            if ((wide != 0u) != (g.gate == 4)) return;
         }
     }
     const int64_t n_end = (n0 + TB < g.N) ? n0 + TB : g.N;
@@ -1074,7 +1081,6 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_big_gated_loop_kernel(GemmAr
 // kWideBinades binades below the window's largest (range_check_kernel); otherwise the exact path: operands
 // dequantized to bf16 (exact) for the bf16 instruction.
 constexpr int64_t kFp8MinK = 12288;
-constexpr int kWideBinades = 6, kWideCount = 24;
 
 // ------------------------------------------------------------------ operand range check (checked path)
 // Every 64-value window of K (the large-tile kernel's stage, one FP8 instruction's K span) of either operand is
@@ -1089,11 +1095,6 @@ struct RangeOperand {
     int64_t windows;       // rows * K / 64
     int sh;                // exponent field shift: 3 (E4M3) or 2 (E5M2)
 };
-
-__device__ __forceinline__ uint32_t max_u16x2_pk(uint32_t a, uint32_t b) {
-    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
-                                                                  __builtin_bit_cast(u16x2, b)));
-}
 
 // Workgroups [0, blocks_a) take A's windows, the rest B's; a workgroup takes 256 consecutive windows (windows are
 // contiguous in memory, so a window's bytes and its scale bytes follow from its index alone). Four lanes share a
@@ -1215,6 +1216,15 @@ static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks_small, unsign
             hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GM, 1>), dim3(blocks_big), dim3(GTHREADS), 0, stream, g1);
             hipLaunchKernelGGL((gemm_big_gated_loop_kernel<MX, FA, FB>), dim3((unsigned)(tiles < 256 ? tiles : 256)),
                                dim3(GTHREADS), 0, stream, g2, tiles);
+        } else if (GM == GM_NONE && path == GEMM_PATH_RANGED && big && a.K >= kFp8MinK) {
+            // Ranged path: the FP8 and exact kernels as a pair, picked by the operands' range words on the device.
+            const int64_t tiles = ((a.M + TB - 1) / TB) * ((a.N + TB - 1) / TB);
+            GemmArgs g1 = a, g2 = a;
+            g1.gate = 3;
+            g2.gate = 4;
+            hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GM, 1>), dim3(blocks_big), dim3(GTHREADS), 0, stream, g1);
+            hipLaunchKernelGGL((gemm_big_gated_loop_kernel<MX, FA, FB>), dim3((unsigned)(tiles < 256 ? tiles : 256)),
+                               dim3(GTHREADS), 0, stream, g2, (int)tiles);
         } else if (GM == GM_NONE && path == GEMM_PATH_FP8) {
             if (big) hipLaunchKernelGGL((gemm_big_kernel<MX, FA, FB, GM, 1>), dim3(blocks_big), dim3(GTHREADS), 0, stream, a);
             else hipLaunchKernelGGL((gemm_kernel<MX, FA, FB, GM, 1>), dim3(blocks_small), dim3(GTHREADS), 0, stream, a);
@@ -1228,9 +1238,10 @@ static hipError_t launch_gemm_t(const GemmArgs& a, unsigned blocks_small, unsign
 
 hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt, const uint8_t* b_q,
                               const void* b_scale, int b_fmt, int64_t M, int64_t N, int64_t K, int mx,
-                              uint16_t* c, int64_t ldc, int path, hipStream_t stream) {
+                              uint16_t* c, int64_t ldc, int path, const uint32_t* a_wide, const uint32_t* b_wide,
+                              hipStream_t stream) {
     GemmArgs a{};
-    a.a = a_q; a.b = b_q; a.c = c; a.M = M; a.N = N; a.K = K; a.ldc = ldc;
+    a.a = a_q; a.b = b_q; a.c = c; a.M = M; a.N = N; a.K = K; a.ldc = ldc; a.wa = a_wide; a.wb = b_wide;
     a.lda = K; a.ldb = K; a.ldsa = K / 32; a.ldsb = K / 32;
     if (mx) { a.sa = (const uint8_t*)a_scale; a.sb = (const uint8_t*)b_scale; }
     else { a.pa = (const float*)a_scale; a.pb = (const float*)b_scale; }

@@ -13,6 +13,11 @@ struct AdamConsts {
 hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
                               uint8_t* q_col, uint8_t* s_col, int rule, hipStream_t stream);
 
+// mxq_quantize plus the range words of each emitted orientation (1 if a 64-value window is wide, else 0).
+hipError_t launch_mx_quantize_ranged(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
+                                     uint8_t* q_col, uint8_t* s_col, int rule, uint32_t* wide_row,
+                                     uint32_t* wide_col, hipStream_t stream);
+
 int pertensor_amax_parts(int64_t n);
 // The device scratch of the allocation-free per-tensor quantize on the stream's device, and its size in bytes.
 hipError_t pertensor_scratch(hipStream_t stream, uint32_t** ptr, size_t* bytes);
@@ -28,12 +33,14 @@ hipError_t launch_swiglu_mx_quantize(const uint16_t* c, int64_t rows, int64_t F,
                                      hipStream_t stream);
 
 // GEMM paths: CHECKED takes the FP8 instruction only for large tiles at K >= 12288 whose operands pass the device-side
-// range check (else the exact path); EXACT dequantizes to bf16 for the bf16 instruction at every K; FP8 takes the
-// FP8 instruction at every K.
-enum : int { GEMM_PATH_CHECKED = 0, GEMM_PATH_EXACT = 1, GEMM_PATH_FP8 = 2 };
+// range check (else the exact path); RANGED decides the same way from the operands' range words (a_wide, b_wide)
+// instead of checking; EXACT dequantizes to bf16 for the bf16 instruction at every K; FP8 takes the FP8 instruction
+// at every K.
+enum : int { GEMM_PATH_CHECKED = 0, GEMM_PATH_EXACT = 1, GEMM_PATH_FP8 = 2, GEMM_PATH_RANGED = 3 };
 hipError_t launch_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_fmt, const uint8_t* b_q,
                               const void* b_scale, int b_fmt, int64_t M, int64_t N, int64_t K, int mx,
-                              uint16_t* c, int64_t ldc, int path, hipStream_t stream);
+                              uint16_t* c, int64_t ldc, int path, const uint32_t* a_wide, const uint32_t* b_wide,
+                              hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_s, const int64_t* offsets, int64_t G,
                                int64_t total_rows, const uint8_t* b_q, const uint8_t* b_s, int64_t ldb,

@@ -24,6 +24,30 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 enum : int { RULE_RCEIL = 0, RULE_FLOOR = 1 };
 
+// Operand range classes for the FP8 matrix instruction (the GEMM's range check and the quantizers' range words use
+// the same definition): a 64-value window of K (one instruction's K span) is wide if it holds a nonzero code and at
+// least kWideCount of its codes lie more than kWideBinades binades below the window's largest, a code's binade being
+// its exponent field plus, for MX, its 32-block's scale byte.
+constexpr int kWideBinades = 6, kWideCount = 24;
+
+// Per-16-bit-lane unsigned max of two packed pairs.
+__device__ __forceinline__ uint32_t max_u16x2_pk(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+// Largest magnitude (bits 6..0) among the 8 FP8 codes of two words.
+__device__ __forceinline__ uint32_t max_code_mag8(uint32_t m0, uint32_t m1) {
+    const uint32_t lo = max_u16x2_pk(m0 & 0x00FF00FFu, m1 & 0x00FF00FFu);
+    const uint32_t hi = max_u16x2_pk(m0 & 0xFF00FF00u, m1 & 0xFF00FF00u);
+    return max(max(lo & 0xFFFFu, lo >> 16), max(hi & 0xFFFFu, hi >> 16) >> 8);
+}
+
+// How many of the 4 code magnitudes (bits 6..0 of each byte of m) lie below th (0 <= th <= 128).
+__device__ __forceinline__ int count_below4(uint32_t m, uint32_t th4) {
+    return 4 - __builtin_popcount(((m | 0x80808080u) - th4) & 0x80808080u);
+}
+
 // ------------------------------------------------------------------ streaming (non-temporal) memory access
 __device__ __forceinline__ uint4 ldnt16(const void* p) {
     u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));

@@ -33,7 +33,14 @@ struct QuantArgs {
     int srow_words;     // s_row rows hold whole 4-byte words per 128-column tile (cols % 128 == 0, 4-aligned)
     int scol_words;     // s_col likewise (rows % 128 == 0, 4-aligned)
     uint32_t* amax_word;  // AMAX: running max of |x| as a bf16 magnitude pattern (atomic max, one per workgroup)
+    uint32_t* wide_row;   // RANGE: set to 1 if a 64-value window of the row orientation is wide (cleared before)
+    uint32_t* wide_col;   // RANGE: likewise for the column orientation
 };
+
+// RANGE: one atomic per workgroup that found a wide window, skipped once the flag is seen set.
+__device__ __forceinline__ void raise_wide(uint32_t* word) {
+    if (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) atomicOr(word, 1u);
+}
 
 template <int MODE>
 __device__ __forceinline__ uint32_t pt_cvt_quad(float s, uint32_t p0, uint32_t p1) {
@@ -44,11 +51,17 @@ __device__ __forceinline__ uint32_t pt_cvt_quad(float s, uint32_t p0, uint32_t p
     return cvt_f32_pair<FMT, true>(cvt_f32_pair<FMT, false>(0u, a, b), c, d);
 }
 
-template <int MODE, bool ROW, bool COL, bool AMAX = false>
+// RANGE (MX only): also classify every 64-value window of each emitted orientation as the GEMM's range check does
+// (kWideBinades, kWideCount) from the codes and scale bytes just formed, and raise wide_row / wide_col if any is wide.
+// Row windows are 8 lanes of a tile row (two quads); column windows are the 32-row blocks b and b ^ 1 of a column,
+// held by threads tid and tid ^ 64, which trade their block's top binade and small-code count through LDS.
+template <int MODE, bool ROW, bool COL, bool AMAX = false, bool RANGE = false>
 __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
     constexpr bool MX = MODE == QM_MX_RCEIL || MODE == QM_MX_FLOOR;
     constexpr int RULE = MODE == QM_MX_FLOOR ? RULE_FLOOR : RULE_RCEIL;
+    static_assert(!RANGE || MX, "range words are computed for MX operands");
     __shared__ uint32_t lds[COL ? QT * QT / 2 : 1];
+    int wide_r = 0, wide_c = 0;
 
     const int tid = threadIdx.x;
     const int64_t r0 = (int64_t)blockIdx.y * QT, c0 = (int64_t)blockIdx.x * QT;
@@ -100,6 +113,23 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
                     uint32_t thr = mx_sat_threshold(byte);
                     lo = mx_patch4(lo, v[j].x, v[j].y, thr);
                     hi = mx_patch4(hi, v[j].z, v[j].w, thr);
+                }
+                if constexpr (RANGE) {
+                    // window = chunks 8w .. 8w + 7 of the tile row: this quad's block and the one at chunk ^ 4
+                    const uint32_t ml = lo & 0x7F7F7F7Fu, mh = hi & 0x7F7F7F7Fu;
+                    const int tb = (int)(quad_max(max_code_mag8(ml, mh)) >> 3) + (int)byte;
+                    const int top = max(tb, __shfl_xor(tb, 4, 16));
+                    const uint32_t th4 = (uint32_t)min(min(max(top - kWideBinades - (int)byte, 0), 32) << 3, 128) *
+                                         0x01010101u;
+                    int cnt = count_below4(ml, th4) + count_below4(mh, th4);
+                    uint32_t nz = ml | mh;
+                    cnt += __builtin_amdgcn_mov_dpp(cnt, 0xB1, 0xF, 0xF, false);
+                    cnt += __builtin_amdgcn_mov_dpp(cnt, 0x4E, 0xF, 0xF, false);
+                    cnt += __shfl_xor(cnt, 4, 16);
+                    nz |= (uint32_t)__builtin_amdgcn_mov_dpp((int)nz, 0xB1, 0xF, 0xF, false);
+                    nz |= (uint32_t)__builtin_amdgcn_mov_dpp((int)nz, 0x4E, 0xF, 0xF, false);
+                    nz |= (uint32_t)__shfl_xor((int)nz, 4, 16);
+                    wide_r |= (nz != 0 && cnt >= kWideCount) ? 1 : 0;
                 }
                 // The 16 lanes of a tile row hold its 4 block bytes at chunks 0, 4, 8, 12; chunk 0 gathers them.
                 const uint32_t b4 = (uint32_t)__shfl_down((int)byte, 4, 16);
@@ -163,10 +193,47 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
                 out1[i] = pt_cvt_quad<MODE>(pt_scale, h0, h1);
             }
         }
+        // RANGE: this thread's two column blocks (rows 32b .. 32b+31 of columns 2p, 2p+1): top binade and, after the
+        // trade with the other block of the window (thread tid ^ 64), the small-code count against the window's top.
+        // The trades use LDS words past the transposed codes and scale bytes (which end at byte QT*QT + 4*QT).
+        int ctop[2] = {0, 0};
+        uint32_t cnz[2] = {0u, 0u};
+        if constexpr (RANGE) {
+            uint32_t mm[2] = {0u, 0u};
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                const uint32_t e0 = out0[i] & 0x7F7F7F7Fu, e1 = out0[i + 1] & 0x7F7F7F7Fu;
+                const uint32_t f0 = out1[i] & 0x7F7F7F7Fu, f1 = out1[i + 1] & 0x7F7F7F7Fu;
+                mm[0] = max(mm[0], max_code_mag8(e0, e1));
+                mm[1] = max(mm[1], max_code_mag8(f0, f1));
+                cnz[0] |= e0 | e1;
+                cnz[1] |= f0 | f1;
+            }
+            ctop[0] = (int)(mm[0] >> 3) + (int)sb0;
+            ctop[1] = (int)(mm[1] >> 3) + (int)sb1;
+        }
         // Transpose the codes once more through LDS so that the global stores write whole 128-byte lines: output
         // row c (column c of x) is 128 bytes; its 16-byte chunk k sits at chunk k ^ ((c >> 1) & 7) to spread the
         // writes of neighbouring columns over the banks.
         __syncthreads();                                           // every thread has read its input column pair
+        int* xtop = reinterpret_cast<int*>(lds) + (QT * QT + 4 * QT) / 4;   // [256][2] block tops
+        int* xcnt = xtop + 2 * QTHREADS;                                    // [256][2] small counts | nonzero flag
+        if constexpr (RANGE) {
+            xtop[2 * tid] = ctop[0];
+            xtop[2 * tid + 1] = ctop[1];
+            __syncthreads();
+            const int partner = tid ^ 64;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int top = max(ctop[h], xtop[2 * partner + h]);
+                const int sbh = (int)(h ? sb1 : sb0);
+                const uint32_t th4 = (uint32_t)min(min(max(top - kWideBinades - sbh, 0), 32) << 3, 128) * 0x01010101u;
+                int cnt = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) cnt += count_below4((h ? out1[i] : out0[i]) & 0x7F7F7F7Fu, th4);
+                xcnt[2 * tid + h] = cnt | (cnz[h] != 0 ? 0x100 : 0);
+            }
+        }
         uint8_t* obuf = reinterpret_cast<uint8_t*>(lds);           // 128 x 128 codes, then 128 x 4 scale bytes
         {
             const int c_even = 2 * p, c_odd = 2 * p + 1;
@@ -183,6 +250,16 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
             }
         }
         __syncthreads();
+        if constexpr (RANGE) {
+            if ((b & 1) == 0) {                                    // the window's first block decides
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int mine = xcnt[2 * tid + h], other = xcnt[2 * (tid ^ 64) + h];
+                    const int cnt = (mine & 0xFF) + (other & 0xFF);
+                    wide_c |= (((mine | other) & 0x100) != 0 && cnt >= kWideCount) ? 1 : 0;
+                }
+            }
+        }
 #pragma unroll
         for (int pass = 0; pass < QT / 32; ++pass) {               // 32 output rows (x columns) per pass
             const int c = 32 * pass + (tid >> 3), k = tid & 7;
@@ -208,6 +285,24 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
             }
         }
     }
+    if constexpr (RANGE) {
+        if constexpr (COL) {
+            // per-wave flags in LDS words past the column trades (no extra LDS, so occupancy stays at 5 per CU)
+            int* flags = reinterpret_cast<int*>(lds) + (QT * QT + 4 * QT) / 4 + 4 * QTHREADS;
+            const bool fr = __ballot(wide_r) != 0, fc = __ballot(wide_c) != 0;
+            if ((tid & 63) == 0) {
+                flags[2 * (tid >> 6)] = fr ? 1 : 0;
+                flags[2 * (tid >> 6) + 1] = fc ? 1 : 0;
+            }
+            __syncthreads();
+            if (tid == 0) {
+                if (ROW && (flags[0] | flags[2] | flags[4] | flags[6])) raise_wide(a.wide_row);
+                if (flags[1] | flags[3] | flags[5] | flags[7]) raise_wide(a.wide_col);
+            }
+        } else {
+            if (__syncthreads_or(wide_r) && tid == 0) raise_wide(a.wide_row);
+        }
+    }
     if constexpr (AMAX) {
         __shared__ uint32_t red[QTHREADS / 64];
         uint32_t m = amax_local;
@@ -230,6 +325,34 @@ static hipError_t launch_quant_mode(const QuantArgs& a, bool row, bool col, hipS
     else if (row) hipLaunchKernelGGL((quant_tile_kernel<MODE, true, false>), grid, dim3(QTHREADS), 0, stream, a);
     else hipLaunchKernelGGL((quant_tile_kernel<MODE, false, true>), grid, dim3(QTHREADS), 0, stream, a);
     return hipGetLastError();
+}
+
+__global__ void clear_words_kernel(uint32_t* w0, uint32_t* w1) {
+    if (w0) *w0 = 0u;
+    if (w1) *w1 = 0u;
+}
+
+template <int MODE>
+static hipError_t launch_quant_ranged(const QuantArgs& a, bool row, bool col, hipStream_t stream) {
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(1), 0, stream, row ? a.wide_row : nullptr,
+                       col ? a.wide_col : nullptr);
+    if (a.rows == 0 || a.cols == 0) return hipGetLastError();
+    dim3 grid((unsigned)((a.cols + QT - 1) / QT), (unsigned)((a.rows + QT - 1) / QT));
+    if (row && col) hipLaunchKernelGGL((quant_tile_kernel<MODE, true, true, false, true>), grid, dim3(QTHREADS), 0, stream, a);
+    else if (row) hipLaunchKernelGGL((quant_tile_kernel<MODE, true, false, false, true>), grid, dim3(QTHREADS), 0, stream, a);
+    else hipLaunchKernelGGL((quant_tile_kernel<MODE, false, true, false, true>), grid, dim3(QTHREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize_ranged(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
+                                     uint8_t* q_col, uint8_t* s_col, int rule, uint32_t* wide_row,
+                                     uint32_t* wide_col, hipStream_t stream) {
+    QuantArgs a{x, rows, cols, q_row, s_row, q_col, s_col, nullptr, 0, 0, nullptr, wide_row, wide_col};
+    a.srow_words = cols % QT == 0 && (reinterpret_cast<uintptr_t>(s_row) & 3) == 0;
+    a.scol_words = rows % QT == 0 && (reinterpret_cast<uintptr_t>(s_col) & 3) == 0;
+    bool row = q_row != nullptr, col = q_col != nullptr;
+    return rule == RULE_FLOOR ? launch_quant_ranged<QM_MX_FLOOR>(a, row, col, stream)
+                              : launch_quant_ranged<QM_MX_RCEIL>(a, row, col, stream);
 }
 
 hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,

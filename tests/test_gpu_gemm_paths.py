@@ -18,6 +18,7 @@ import torch
 
 import mxfp8_precision_numerics_amd as mxq
 import oracle
+import gpu_util
 from gpu_util import DEV, need_gpu, say, u8
 from mxfp8_precision_numerics_amd import workloads
 
@@ -32,18 +33,7 @@ def _ratio(C, y, S):
 
 
 def any_wide_window(q, s, fmt):
-    """The range check's definition, evaluated plainly on the host: q [rows][K] codes, s [rows][K/32] E8M0 bytes (MX)
-    or None (per-tensor)."""
-    q = q.astype(np.int64)
-    rows, K = q.shape
-    e = (q >> 3) & 15 if fmt == mxq.E4M3 else (q >> 2) & 31
-    if s is not None:
-        e = e + np.repeat(s.astype(np.int64), 32, axis=1)
-    w = e.reshape(rows, K // 64, 64)
-    nonzero = ((q & 0x7F) != 0).reshape(rows, K // 64, 64).any(axis=2)
-    top = w.max(axis=2, keepdims=True)
-    small = (w < top - 6).sum(axis=2)
-    return bool(((small >= 24) & nonzero).any())
+    return gpu_util.any_wide_window(q, s, fmt == mxq.E4M3)
 
 
 def _to_dev(a):
