@@ -808,6 +808,161 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
     } else {
         wait_copies_barrier<0>();
     }
+    if constexpr (MF == 2) {
+    // Exact path, pipelined over the stage's four 16-value k-steps. k-step s takes bytes 8s .. 8s+7 of each lane's
+    // 32 (steps 0, 1 lie in the stage's first 32-block, 2, 3 in its second). While k-step s's 16 matrix instructions
+    // run, k-step s + 1 is converted to bf16 (two conversions per matrix instruction), and the next stage's fragments
+    // stream into the registers of k-steps already converted: bytes 0-15 during k-step 1, bytes 16-31 during k-step 3,
+    // where the next stage's k-step 0 is converted too. One fragment register set thus serves both stages, which
+    // leaves room for two sets of converted operands.
+    v8i F[8];                                  // F[j]: A rows wm*128 + 32j + (lane % 32); F[4 + i]: B rows wn*128 + 32i
+    uint32_t SA[2][8], SB[2][8];               // conversion scale operands [4 blk + j] of the current and next stage
+    v8bf CV[2][8];                             // converted k-steps: CV[s & 1][j] A, [4 + i] B
+    // chunk half h (bytes 16h .. 16h+15) of all eight fragments of stage st
+    auto read_chunk = [&](auto sp_c, int st, auto h_c) {
+        constexpr int H = decltype(h_c)::value;
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            const uint4 x = f < 4 ? *reinterpret_cast<const uint4*>(&sA[0][0] + frag_off(std::true_type{}, sp_c, st,
+                                                                                          4 * wm + f, H))
+                                  : *reinterpret_cast<const uint4*>(&sB[0][0] + frag_off(std::false_type{}, sp_c, st,
+                                                                                          4 * wn + f - 4, H));
+            F[f][4 * H] = (int)x.x; F[f][4 * H + 1] = (int)x.y; F[f][4 * H + 2] = (int)x.z; F[f][4 * H + 3] = (int)x.w;
+        }
+    };
+    // fragment f's k-step s, with the scale operands of its block
+    auto convert = [&](int s, int f, const uint32_t* sa, const uint32_t* sb, v8bf* cv) {
+        const uint2 x = make_uint2((uint32_t)F[f][2 * s], (uint32_t)F[f][2 * s + 1]);
+        if (f < 4) cv[f] = dequant8_bf16<FA>(x, __uint_as_float(sa[4 * (s >> 1) + f]));
+        else cv[f] = dequant8_bf16<FB>(x, __uint_as_float(sb[4 * (s >> 1) + f - 4]));
+    };
+    // k-step S: its 16 matrix instructions from CV[S & 1]. Between them: the conversion of k-step CS (0 .. 3 of the
+    // stage whose scales are csa/csb; -1 none) into CV[(S + 1) & 1], one fragment per two instructions, and, if
+    // RH >= 0, chunk half RH of the next stage's fragments (stage st_next, position SPN), one fragment per two.
+    auto kstep = [&](auto s_c, auto cs_c, const uint32_t* csa, const uint32_t* csb, auto rh_c, auto spn_c,
+                     int st_next) {
+        constexpr int S = decltype(s_c)::value, CS = decltype(cs_c)::value, RH = decltype(rh_c)::value;
+        auto read_f = [&](int f) {
+            const uint4 x = f < 4 ? *reinterpret_cast<const uint4*>(&sA[0][0] +
+                                        frag_off(std::true_type{}, spn_c, st_next, 4 * wm + f, RH))
+                                  : *reinterpret_cast<const uint4*>(&sB[0][0] +
+                                        frag_off(std::false_type{}, spn_c, st_next, 4 * wn + f - 4, RH));
+            F[f][4 * RH] = (int)x.x; F[f][4 * RH + 1] = (int)x.y;
+            F[f][4 * RH + 2] = (int)x.z; F[f][4 * RH + 3] = (int)x.w;
+        };
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = q >> 2, j = q & 3;
+            acc16[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(CV[S & 1][4 + i], CV[S & 1][j], acc16[i][j], 0, 0, 0);
+            if constexpr (CS >= 0) {
+                if (q & 1) convert(CS, q >> 1, csa, csb, CV[(S + 1) & 1]);
+            }
+            if constexpr (RH >= 0) {
+                if ((q & 1) == 0 && q > 0) read_f((q >> 1) - 1);   // the fragment whose last conversion just issued
+            }
+        }
+        if constexpr (RH >= 0) read_f(7);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // one matrix instruction
+            if constexpr (RH >= 0) {
+                if ((q & 1) == 0 && q > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one fragment read
+            }
+            if constexpr (CS >= 0) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0); // two conversions
+        }
+        __builtin_amdgcn_sched_barrier(0);                                            // k-steps do not mix
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using NONE = std::integral_constant<int, -1>;
+    // Trip kt (kt + 1 < nk): the trip's copies, then stage kt's four k-steps with stage kt + 1's fragments, scales
+    // and k-step 0 conversion folded in, then the wait until stage kt + 2 has landed.
+    auto trip = [&](auto ph_c, int kt, uint32_t* csa, uint32_t* csb, uint32_t* nsa, uint32_t* nsb) {
+        constexpr int PH = decltype(ph_c)::value;
+        using SP = std::integral_constant<int, PH < 0 ? -1 : (PH + 1) % 4>;     // stage kt + 1 mod 4
+#pragma unroll
+        for (int c = 0; c < 8; ++c) trip_copy(ph_c, kt, c);
+        const bool scales = trip_scales(kt);
+        __builtin_amdgcn_sched_barrier(0);
+        kstep(I0{}, I1{}, csa, csb, I0{}, SP{}, kt + 1);        // bytes 0-15 of stage kt + 1 follow their conversions
+        read_scales(kt + 1, nsa, nsb);
+        kstep(I1{}, I2{}, csa, csb, NONE{}, SP{}, kt + 1);
+        kstep(I2{}, I3{}, csa, csb, I1{}, SP{}, kt + 1);        // bytes 16-31 likewise
+        // k-step 3: convert the next stage's k-step 0 (bytes 0-15 arrived during k-step 0) with its own scales
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = q >> 2, j = q & 3;
+            acc16[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(CV[1][4 + i], CV[1][j], acc16[i][j], 0, 0, 0);
+            if (q & 1) convert(0, q >> 1, nsa, nsb, CV[0]);
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        pin_accumulators();
+        if constexpr (PH >= 0) {
+            if (scales) wait_copies_barrier<8 + kScaleCopies>();
+            else wait_copies_barrier<8>();
+        } else {
+            trip_wait(kt, scales);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+    };
+    // The last stage (its fragments, scales and k-step 0 conversion are in registers; no copy is outstanding).
+    auto last_stage = [&](uint32_t* csa, uint32_t* csb) {
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (TOK) {
+            // A half last stage sums only its first block: the second block's codes become 0 and its scale bytes
+            // 2^0, so k-steps 2 and 3 add exact zeros whatever lies past the expert's range (selects, not branches).
+            const uint32_t keep = half_last ? 0u : 0xFFFFFFFFu;
+            const uint32_t one = __float_as_uint(scale_operand(127u));
+#pragma unroll
+            for (int f = 0; f < 8; ++f)
+#pragma unroll
+                for (int e = 4; e < 8; ++e) F[f][e] = (int)((uint32_t)F[f][e] & keep);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                csa[4 + j] = half_last ? one : csa[4 + j];
+                csb[4 + j] = half_last ? one : csb[4 + j];
+            }
+        }
+        kstep(I0{}, I1{}, csa, csb, NONE{}, NONE{}, 0);
+        kstep(I1{}, I2{}, csa, csb, NONE{}, NONE{}, 0);
+        kstep(I2{}, I3{}, csa, csb, NONE{}, NONE{}, 0);
+        kstep(I3{}, NONE{}, csa, csb, NONE{}, NONE{}, 0);
+    };
+    // prologue: stage 0's fragments, scales and k-step 0
+    read_chunk(I0{}, 0, I0{});
+    read_chunk(I0{}, 0, I1{});
+    read_scales(0, SA[0], SB[0]);
+    // Stage 0's regions are refilled by the first trips: every wave's reads of them must have returned.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) convert(0, f, SA[0], SB[0], CV[0]);
+    using dyn = std::integral_constant<int, -1>;
+    int kt = 0;
+    for (; kt + 7 < nk; kt += 4) {                               // kt % 4 == 0; every pair of these trips is whole
+        trip(I0{}, kt, SA[0], SB[0], SA[1], SB[1]);
+        trip(I1{}, kt + 1, SA[1], SB[1], SA[0], SB[0]);
+        trip(I2{}, kt + 2, SA[0], SB[0], SA[1], SB[1]);
+        trip(I3{}, kt + 3, SA[1], SB[1], SA[0], SB[0]);
+    }
+    for (; kt + 2 < nk; kt += 2) {
+        trip(dyn{}, kt, SA[0], SB[0], SA[1], SB[1]);
+        trip(dyn{}, kt + 1, SA[1], SB[1], SA[0], SB[0]);
+    }
+    if (kt + 1 < nk) {
+        trip(dyn{}, kt, SA[0], SB[0], SA[1], SB[1]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { SA[0][e] = SA[1][e]; SB[0][e] = SB[1][e]; }
+    }
+    last_stage(SA[0], SB[0]);
+    } else {
     v8i fa[4], fb[4];
     constexpr int SAN = MF == 2 ? 8 : 4;                  // scale registers per operand (exact path: operands)
     uint32_t sa[SAN], sb[SAN];
@@ -941,6 +1096,7 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
         }
     }
     mma_stage(dyn{}, kt, fa, fb, sa, sb);
+    }
     }
 
     // ------------------------------------------------------------------ epilogue
