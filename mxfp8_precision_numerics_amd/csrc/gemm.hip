@@ -90,6 +90,50 @@ __device__ __forceinline__ v8bf dequant8_bf16(uint2 x, float scale) {
     return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// Row-grouped GEMMs: the expert group that holds row tile t (tiles of TH rows, numbered group by group, each group's
+// rows [off[q], off[q+1]) clamped to [0, M) and cut into ceil(rows / TH) tiles). Each wave scans 64 groups at a time:
+// lane l loads group base + l's offsets, a wave prefix sum of the tile counts finds the group, so a workgroup pays one
+// round of loads per 64 groups instead of a dependent load per group. grp = -1 when t lies past the last tile.
+struct RowTile {
+    int64_t grp, lo, hi;      // group, first row of the tile, end of the group's rows
+};
+
+template <int TH>
+__device__ __forceinline__ RowTile find_row_tile(const GemmArgs& g, int64_t t) {
+    const int lane = threadIdx.x & 63;
+    RowTile r{-1, 0, 0};
+    int64_t before = 0;                          // tiles of the groups already scanned
+    for (int64_t base = 0; base < g.G; base += 64) {
+        const int64_t q = base + lane;
+        int64_t a0 = 0, a1 = 0;
+        int nt = 0;
+        if (q < g.G) {
+            a0 = g.offsets[q];
+            a1 = g.offsets[q + 1];
+            a0 = a0 < 0 ? 0 : (a0 > g.M ? g.M : a0);
+            a1 = a1 < a0 ? a0 : (a1 > g.M ? g.M : a1);
+            nt = (int)((a1 - a0 + TH - 1) / TH);
+        }
+        int incl = nt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += v;
+        }
+        const uint64_t hit = __ballot(before + incl > t);
+        if (hit) {
+            const int L = __ffsll((unsigned long long)hit) - 1;
+            const int64_t excl = before + __shfl(incl - nt, L, 64);
+            r.grp = base + L;
+            r.lo = __shfl(a0, L, 64) + (t - excl) * TH;
+            r.hi = __shfl(a1, L, 64);
+            return r;
+        }
+        before += __shfl(incl, 63, 64);
+    }
+    return r;
+}
+
 template <bool MX, int FA, int FB, int GM, int MF>
 __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * BK];
@@ -115,15 +159,8 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
         const int64_t bid = blockIdx.x;
         const int64_t t = bid / tiles_n;
         n0 = (bid % tiles_n) * BN;
-        int64_t acc = 0, grp = -1, lo = 0, hi = 0;
-        for (int64_t q = 0; q < g.G; ++q) {
-            int64_t a0 = g.offsets[q], a1 = g.offsets[q + 1];
-            a0 = a0 < 0 ? 0 : (a0 > g.M ? g.M : a0);
-            a1 = a1 < a0 ? a0 : (a1 > g.M ? g.M : a1);
-            int64_t nt = (a1 - a0 + BM - 1) / BM;
-            if (t < acc + nt) { grp = q; lo = a0 + (t - acc) * BM; hi = a1; break; }
-            acc += nt;
-        }
+        const RowTile rt = find_row_tile<BM>(g, t);
+        const int64_t grp = rt.grp, lo = rt.lo, hi = rt.hi;
         if (grp < 0) return;                          // more workgroups than tiles: nothing to do
         m0 = lo;
         m_end = (lo + BM < hi) ? lo + BM : hi;
@@ -479,15 +516,8 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
         const int64_t bid = bid_in;
         const int64_t t = bid / tiles_n;
         n0 = (bid % tiles_n) * TB;
-        int64_t acc_t = 0, grp = -1, lo = 0, hi = 0;
-        for (int64_t q = 0; q < g.G; ++q) {
-            int64_t a0 = g.offsets[q], a1 = g.offsets[q + 1];
-            a0 = a0 < 0 ? 0 : (a0 > g.M ? g.M : a0);
-            a1 = a1 < a0 ? a0 : (a1 > g.M ? g.M : a1);
-            const int64_t nt = (a1 - a0 + TB - 1) / TB;
-            if (t < acc_t + nt) { grp = q; lo = a0 + (t - acc_t) * TB; hi = a1; break; }
-            acc_t += nt;
-        }
+        const RowTile rt = find_row_tile<TB>(g, t);
+        const int64_t grp = rt.grp, lo = rt.lo, hi = rt.hi;
         if (grp < 0) return;
         m0 = lo;
         m_end = (lo + TB < hi) ? lo + TB : hi;
