@@ -866,12 +866,64 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
         if (f < 4) cv[f] = dequant8_bf16<FA>(x, __uint_as_float(sa[4 * (s >> 1) + f]));
         else cv[f] = dequant8_bf16<FB>(x, __uint_as_float(sb[4 * (s >> 1) + f - 4]));
     };
+    // Raw scale words of stage st for the fragment rows (LDS reads only; the operands are formed later, by
+    // scale_op, so no wait for these reads sits between matrix instructions): MX rows word w of the group in
+    // ra[j] / rb[i]; token groups words w and w + 1 in [j] and [4 + j]; per-tensor unit scales.
+    auto scale_words = [&](int st, uint32_t* ra, uint32_t* rb) {
+        const int w = (st % SG) >> 1;
+        if constexpr (TOK) {
+            const uint32_t* cSA = sSA[(st / SG) & 1];
+            const uint32_t* cSB = sSB[(st / SG) & 1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = wm * 128 + 32 * j + fr;
+                ra[j] = cSA[TB * w + row];
+                ra[4 + j] = cSA[TB * (w + 1) + row];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = wn * 128 + 32 * i + fr;
+                rb[i] = cSB[TB * w + row];
+                rb[4 + i] = cSB[TB * (w + 1) + row];
+            }
+        } else if constexpr (MX) {
+            const uint32_t* cSA = sSA[(st / SG) & 1];
+            const uint32_t* cSB = sSB[(st / SG) & 1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ra[j] = cSA[(wm * 128 + 32 * j + fr) * 4 + w];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rb[i] = cSB[(wn * 128 + 32 * i + fr) * 4 + w];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { ra[j] = 0x7F7F7F7Fu; rb[j] = 0x7F7F7F7Fu; }
+        }
+    };
+    // Conversion scale operand e (0 .. 15; A [4 blk + j] for e < 8, B [4 blk + i] after) of stage st from its raw
+    // words, as read_scales forms it.
+    auto scale_op = [&](int st, const uint32_t* ra, const uint32_t* rb, int e, uint32_t* sa, uint32_t* sb) {
+        const bool is_a = e < 8;
+        const int blk = (e >> 2) & 1, r = e & 3;
+        const uint32_t* raw = is_a ? ra : rb;
+        uint32_t word;
+        if constexpr (TOK) word = __builtin_amdgcn_alignbyte(raw[4 + r], raw[r], shifts >> ((is_a ? 0 : 8) + 2 * r));
+        else word = raw[r];
+        const uint32_t v = __float_as_uint(scale_operand((word >> (8 * (2 * (st & 1) + blk))) & 0xFFu));
+        if (is_a) sa[4 * blk + r] = v;
+        else sb[4 * blk + r] = v;
+    };
     // k-step S: its 16 matrix instructions from CV[S & 1]. Between them: the conversion of k-step CS (0 .. 3 of the
-    // stage whose scales are csa/csb; -1 none) into CV[(S + 1) & 1], one fragment per two instructions, and, if
-    // RH >= 0, chunk half RH of the next stage's fragments (stage st_next, position SPN), one fragment per two.
+    // stage whose scales are csa/csb; -1 none) into CV[(S + 1) & 1], one fragment per two instructions; if
+    // RH >= 0, chunk half RH of the next stage's fragments (stage st_next, position SPN), one fragment per two;
+    // with XS, the next stage's scale operand q after instruction q (from the raw words xra / xrb into xsa / xsb);
+    // with CP >= 0, the trip's copy instructions CP .. CP + NC - 1 (copy(c)), spread evenly (copy c after
+    // instruction (16 / NC) (c + 1/2) - 1), fenced so each stays between its matrix instructions: a copy that finds
+    // the memory queue full then stalls the wave while a matrix instruction is still running.
     auto kstep = [&](auto s_c, auto cs_c, const uint32_t* csa, const uint32_t* csb, auto rh_c, auto spn_c,
-                     int st_next) {
+                     int st_next, auto xs_c, const uint32_t* xra, const uint32_t* xrb, uint32_t* xsa,
+                     uint32_t* xsb, auto cp_c, auto nc_c, auto&& copy) {
         constexpr int S = decltype(s_c)::value, CS = decltype(cs_c)::value, RH = decltype(rh_c)::value;
+        constexpr bool XS = decltype(xs_c)::value;
+        constexpr int CP = decltype(cp_c)::value, NC = decltype(nc_c)::value;
         auto read_f = [&](int f) {
             const uint4 x = f < 4 ? *reinterpret_cast<const uint4*>(&sA[0][0] +
                                         frag_off(std::true_type{}, spn_c, st_next, 4 * wm + f, RH))
@@ -880,8 +932,7 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
             F[f][4 * RH] = (int)x.x; F[f][4 * RH + 1] = (int)x.y;
             F[f][4 * RH + 2] = (int)x.z; F[f][4 * RH + 3] = (int)x.w;
         };
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        auto slot = [&](int q) {
             const int i = q >> 2, j = q & 3;
             acc16[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(CV[S & 1][4 + i], CV[S & 1][j], acc16[i][j], 0, 0, 0);
             if constexpr (CS >= 0) {
@@ -890,17 +941,61 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
             if constexpr (RH >= 0) {
                 if ((q & 1) == 0 && q > 0) read_f((q >> 1) - 1);   // the fragment whose last conversion just issued
             }
-        }
-        if constexpr (RH >= 0) read_f(7);
+            if constexpr (XS) scale_op(st_next, xra, xrb, q, xsa, xsb);
+        };
+        constexpr int NV = (CS >= 0 ? 2 : 0) + (XS ? 2 : 0);
+        auto groups = [&](int q0, int q1) {                     // the scheduling pattern of instructions q0 .. q1
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // one matrix instruction
-            if constexpr (RH >= 0) {
-                if ((q & 1) == 0 && q > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one fragment read
+            for (int q = q0; q <= q1; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // one matrix instruction
+                if constexpr (RH >= 0) {
+                    if ((q & 1) == 0 && q > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a fragment read
+                }
+                if constexpr (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // conversions, scales
             }
-            if constexpr (CS >= 0) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0); // two conversions
+        };
+        if constexpr (CP < 0) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) slot(q);
+            if constexpr (RH >= 0) read_f(7);
+            groups(0, 15);
+        } else {
+            constexpr int D = 16 / NC;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int q0 = c == 0 ? 0 : D * c - D / 2, q1 = D * c + D / 2 - 1;
+#pragma unroll
+                for (int q = q0; q <= q1; ++q) slot(q);
+                groups(q0, q1);
+                __builtin_amdgcn_sched_barrier(0);
+                copy(CP + c);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int q = 16 - D / 2; q < 16; ++q) slot(q);
+            if constexpr (RH >= 0) read_f(7);
+            groups(16 - D / 2, 15);
         }
         __builtin_amdgcn_sched_barrier(0);                                            // k-steps do not mix
+    };
+    // The next stage's k-step 0 operands and its scale operands, used after the trip's wait: this empty statement
+    // keeps the compiler from moving their conversions past the branch of the next trip's scale copy, which would
+    // put them all between two matrix instructions instead of spread over k-step 3.
+    auto pin_converted = [&](const uint32_t* nsa, const uint32_t* nsb) {
+        asm volatile("" :: "v"(CV[0][0]), "v"(CV[0][1]), "v"(CV[0][2]), "v"(CV[0][3]),
+                           "v"(CV[0][4]), "v"(CV[0][5]), "v"(CV[0][6]), "v"(CV[0][7]));
+        asm volatile("" :: "v"(nsa[0]), "v"(nsa[1]), "v"(nsa[2]), "v"(nsa[3]), "v"(nsa[4]), "v"(nsa[5]),
+                           "v"(nsa[6]), "v"(nsa[7]));
+        asm volatile("" :: "v"(nsb[0]), "v"(nsb[1]), "v"(nsb[2]), "v"(nsb[3]), "v"(nsb[4]), "v"(nsb[5]),
+                           "v"(nsb[6]), "v"(nsb[7]));
+    };
+    // k-step without scale operands
+    auto no_copy = [](int) {};
+    using NOCP = std::integral_constant<int, -1>;
+    auto kstep_ = [&](auto s_c, auto cs_c, const uint32_t* csa, const uint32_t* csb, auto rh_c, auto spn_c,
+                      int st_next) {
+        kstep(s_c, cs_c, csa, csb, rh_c, spn_c, st_next, std::false_type{}, nullptr, nullptr, nullptr, nullptr,
+              NOCP{}, NOCP{}, no_copy);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -912,28 +1007,26 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
     auto trip = [&](auto ph_c, int kt, uint32_t* csa, uint32_t* csb, uint32_t* nsa, uint32_t* nsb) {
         constexpr int PH = decltype(ph_c)::value;
         using SP = std::integral_constant<int, PH < 0 ? -1 : (PH + 1) % 4>;     // stage kt + 1 mod 4
-#pragma unroll
-        for (int c = 0; c < 8; ++c) trip_copy(ph_c, kt, c);
-        const bool scales = trip_scales(kt);
+        // stage kt + 1's scale words, read ahead of the trip's fragment reads: LDS reads return in order, so the
+        // wait before their use in k-step 1 does not hold for the fragment reads issued after them
+        uint32_t ra[8], rb[8];
+        scale_words(kt + 1, ra, rb);
         __builtin_amdgcn_sched_barrier(0);
-        kstep(I0{}, I1{}, csa, csb, I0{}, SP{}, kt + 1);        // bytes 0-15 of stage kt + 1 follow their conversions
-        read_scales(kt + 1, nsa, nsb);
-        kstep(I1{}, I2{}, csa, csb, NONE{}, SP{}, kt + 1);
-        kstep(I2{}, I3{}, csa, csb, I1{}, SP{}, kt + 1);        // bytes 16-31 likewise
-        // k-step 3: convert the next stage's k-step 0 (bytes 0-15 arrived during k-step 0) with its own scales
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int i = q >> 2, j = q & 3;
-            acc16[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(CV[1][4 + i], CV[1][j], acc16[i][j], 0, 0, 0);
-            if (q & 1) convert(0, q >> 1, nsa, nsb, CV[0]);
-        }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        auto copy = [&](int c) { trip_copy(ph_c, kt, c); };
+        using C2 = std::integral_constant<int, 2>;
+        // bytes 0-15 of stage kt + 1 follow their conversions, bytes 16-31 likewise; the trip's copies go two per
+        // k-step; k-step 3 converts the next stage's k-step 0 (its bytes arrived during k-step 0) with its scales
+        kstep(I0{}, I1{}, csa, csb, I0{}, SP{}, kt + 1, std::false_type{}, nullptr, nullptr, nullptr, nullptr, I0{},
+              C2{}, copy);
+        kstep(I1{}, I2{}, csa, csb, NONE{}, SP{}, kt + 1, std::true_type{}, ra, rb, nsa, nsb, I2{}, C2{}, copy);
+        kstep(I2{}, I3{}, csa, csb, I1{}, SP{}, kt + 1, std::false_type{}, nullptr, nullptr, nullptr, nullptr,
+              std::integral_constant<int, 4>{}, C2{}, copy);
+        kstep(I3{}, I0{}, nsa, nsb, NONE{}, SP{}, kt + 1, std::false_type{}, nullptr, nullptr, nullptr, nullptr,
+              std::integral_constant<int, 6>{}, C2{}, copy);
         pin_accumulators();
+        pin_converted(nsa, nsb);
+        // the scale copies (a branch) go last, so the trip's matrix instructions share one basic block
+        const bool scales = trip_scales(kt);
         if constexpr (PH >= 0) {
             if (scales) wait_copies_barrier<8 + kScaleCopies>();
             else wait_copies_barrier<8>();
@@ -960,10 +1053,10 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
                 csb[4 + j] = half_last ? one : csb[4 + j];
             }
         }
-        kstep(I0{}, I1{}, csa, csb, NONE{}, NONE{}, 0);
-        kstep(I1{}, I2{}, csa, csb, NONE{}, NONE{}, 0);
-        kstep(I2{}, I3{}, csa, csb, NONE{}, NONE{}, 0);
-        kstep(I3{}, NONE{}, csa, csb, NONE{}, NONE{}, 0);
+        kstep_(I0{}, I1{}, csa, csb, NONE{}, NONE{}, 0);
+        kstep_(I1{}, I2{}, csa, csb, NONE{}, NONE{}, 0);
+        kstep_(I2{}, I3{}, csa, csb, NONE{}, NONE{}, 0);
+        kstep_(I3{}, NONE{}, csa, csb, NONE{}, NONE{}, 0);
     };
     // prologue: stage 0's fragments, scales and k-step 0
     read_chunk(I0{}, 0, I0{});
