@@ -448,14 +448,15 @@ def main():
 
     # The other large kernels of the step against their own bounds: the remaining MX GEMMs (FP8 peak) and the
     # quantize and Adam streams (HBM).
-    def hbm(name, gbs):
+    def hbm(name, gbs, part=None):
         return {"kernel": name, "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4),
-                "frac_of_attainable": round(gbs / attainable["hbm_copy_gbs"], 4)}
+                "frac_of_attainable": round(gbs / attainable["hbm_copy_gbs"], 4),
+                "traffic": measured_traffic(part) if part else None}
     rooflines_other = [gemm_roof(p) for p in gemm_kernels if p != dominant] + [
         hbm("mxq_quantize of X, W, dY, both orientations", rate["mx_quant_XWdY_gbs"]),
-        hbm("mxq_quantize 16384x8192 with outliers, both orientations", rate["mx_quant_act_gbs"]),
-        hbm("fp8_adam_step, 1.3e9 params, 21 B/param (amax pass + update pass)", rate["adam_gbs"]),
+        hbm("mxq_quantize 16384x8192 with outliers, both orientations", rate["mx_quant_act_gbs"], "mx_quant_act"),
+        hbm("fp8_adam_step, 1.3e9 params, 21 B/param (amax pass + update pass)", rate["adam_gbs"], "adam"),
         hbm("fp8_adam_step_delayed, 1.3e9 params, 18 B/param (one pass)", rate["adam_delayed_gbs"]),
     ]
 

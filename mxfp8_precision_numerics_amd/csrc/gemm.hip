@@ -414,6 +414,7 @@ constexpr int TB = 256;
 constexpr int KS = 64;
 constexpr int SG = 8;
 constexpr int GROUP_M2 = 4;
+constexpr int64_t kXcdChunk = 32;   // CUs per XCD: the workgroups of the large-tile kernel one XCD holds at once
 // Issue slot (of the 16 matrix instructions of a stage) after which each of a trip's 8 copy instructions goes.
 constexpr int kCopySlot[8] = {1, 3, 5, 7, 9, 11, 13, 15};
 
@@ -513,7 +514,13 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
         if (Cb) Cb += grp * g.c_gstride;
         if (Cf) Cf += grp * g.c_gstride;
     } else if constexpr (GM == GM_ROWS) {
-        const int64_t bid = bid_in;
+        // XCD-aware order: workgroup b runs on XCD b % 8, and each XCD in turn takes a chunk of kXcdChunk consecutive
+        // tiles (one per CU of the XCD), so the workgroups resident on an XCD share an expert's weight tiles and row
+        // tiles in its L2. Workgroups past the last whole round keep their own index (the map stays a bijection).
+        const int64_t nb = gridDim.x, b = bid_in, round = 8 * kXcdChunk;
+        const int64_t bid = b < (nb / round) * round
+                                ? (b >> 3) / kXcdChunk * round + (b & 7) * kXcdChunk + (b >> 3) % kXcdChunk
+                                : b;
         const int64_t t = bid / tiles_n;
         n0 = (bid % tiles_n) * TB;
         const RowTile rt = find_row_tile<TB>(g, t);
