@@ -269,8 +269,7 @@ def main():
         with part("small_graph", rec):
             small_graph.replay()
         # the same two with the stream kept busy (a ~0.1 ms spin) while the host submits, so the window holds device
-        # time only: an idle stream exposes the host's submission latency, which is larger for a graph launch than
-        # for three kernel launches on this stack
+        # time only and not the host's submission latency
         torch.cuda._sleep(200_000)
         with part("small_queued", rec):
             small_path()
