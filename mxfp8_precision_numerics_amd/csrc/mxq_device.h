@@ -90,10 +90,11 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
 //   floor: e = floor(log2 amax) - 8 = E - 127 - 8, clamped likewise.
 //   Infinity clamps to e = 127 (byte 254); a NaN gives byte 255.
 __device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits, int rule) {
-    if (amax_bits >= 0x7F80u) return amax_bits == 0x7F80u ? 254u : 255u;
-    int E = (int)(amax_bits >> 7), mant = (int)(amax_bits & 0x7F);
-    int b = E - 8 + ((rule == RULE_RCEIL && mant > 0x60) ? 1 : 0);
-    return b < 0 ? 0u : (uint32_t)b;
+    // selects rather than branches: the non-finite case is rare but a branch costs every block its exec-mask juggling
+    const int E = (int)(amax_bits >> 7), mant = (int)(amax_bits & 0x7F);
+    const int b = max(E - 8 + ((rule == RULE_RCEIL && mant > 0x60) ? 1 : 0), 0);
+    const uint32_t nonfinite = amax_bits == 0x7F80u ? 254u : 255u;
+    return amax_bits >= 0x7F80u ? nonfinite : (uint32_t)b;
 }
 
 // The same rule for an fp32 block maximum (magnitude bits): NaN -> 0xFF, +inf -> 254 (e = 127), otherwise

@@ -42,6 +42,14 @@ __device__ __forceinline__ void raise_wide(uint32_t* word) {
     if (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) atomicOr(word, 1u);
 }
 
+// RANGE: the byte-replicated threshold below which a code magnitude byte lies more than kWideBinades binades under
+// its window's top, for a block with scale byte `byte`; `top` is the window's largest binade + 1 (0 when the window
+// holds no nonzero code). Clamped to [0, 128]: 0 counts no code, 128 every code (bit 7 of a magnitude byte is 0).
+__device__ __forceinline__ uint32_t wide_th4(int top, int byte) {
+    const int t = min(max(top - 1 - kWideBinades - byte, 0), 16) << 3;
+    return __builtin_amdgcn_perm(0u, (uint32_t)t, 0u);       // byte 0 of t in all four bytes
+}
+
 template <int MODE>
 __device__ __forceinline__ uint32_t pt_cvt_quad(float s, uint32_t p0, uint32_t p1) {
     constexpr int FMT = MODE == QM_PT_E4M3 ? FMT_E4M3 : FMT_E5M2;
@@ -99,9 +107,21 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
     }
 
     if constexpr (ROW) {
+        // This thread's row of chunk j is lrow + 16 j; its code and scale pointers advance 16 rows per chunk (no 64-bit
+        // index arithmetic per chunk).
+        const int lrow = tid >> 4;
+        const int64_t rows_left = a.rows - r0;
+        uint8_t* qr = a.q_row + (r0 + lrow) * a.cols + gc;
+        const int64_t qr_step = 16 * a.cols;
+        uint8_t* sr = nullptr;
+        int64_t sr_step = 0;
+        if constexpr (MX) {
+            sr = a.s_row + (r0 + lrow) * (a.cols / 32) + (a.srow_words ? c0 / 32 : gc / 32);
+            sr_step = 16 * (a.cols / 32);
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int64_t gr = r0 + (tid >> 4) + 16 * j;
+            const bool ok = col_ok && lrow + 16 * j < rows_left;
             uint32_t lo, hi;
             if constexpr (MX) {
                 uint32_t m = quad_max(amax_bits8(v[j]));
@@ -115,41 +135,40 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
                     hi = mx_patch4(hi, v[j].z, v[j].w, thr);
                 }
                 if constexpr (RANGE) {
-                    // window = chunks 8w .. 8w + 7 of the tile row: this quad's block and the one at chunk ^ 4
+                    // window = chunks 8w .. 8w + 7 of the tile row: this quad's block and the one at chunk ^ 4. A
+                    // block's top is 0 when all its codes are 0, else its largest binade + 1, so the window's top is
+                    // 0 exactly when the window holds no nonzero code.
                     const uint32_t ml = lo & 0x7F7F7F7Fu, mh = hi & 0x7F7F7F7Fu;
-                    const int tb = (int)(quad_max(max_code_mag8(ml, mh)) >> 3) + (int)byte;
+                    const uint32_t qm = quad_max(max_code_mag8(ml, mh));
+                    const int tb = qm ? (int)(qm >> 3) + (int)byte + 1 : 0;
                     const int top = max(tb, __shfl_xor(tb, 4, 16));
-                    const uint32_t th4 = (uint32_t)min(min(max(top - kWideBinades - (int)byte, 0), 32) << 3, 128) *
-                                         0x01010101u;
+                    const uint32_t th4 = wide_th4(top, (int)byte);
                     int cnt = count_below4(ml, th4) + count_below4(mh, th4);
-                    uint32_t nz = ml | mh;
                     cnt += __builtin_amdgcn_mov_dpp(cnt, 0xB1, 0xF, 0xF, false);
                     cnt += __builtin_amdgcn_mov_dpp(cnt, 0x4E, 0xF, 0xF, false);
                     cnt += __shfl_xor(cnt, 4, 16);
-                    nz |= (uint32_t)__builtin_amdgcn_mov_dpp((int)nz, 0xB1, 0xF, 0xF, false);
-                    nz |= (uint32_t)__builtin_amdgcn_mov_dpp((int)nz, 0x4E, 0xF, 0xF, false);
-                    nz |= (uint32_t)__shfl_xor((int)nz, 4, 16);
-                    wide_r |= (nz != 0 && cnt >= kWideCount) ? 1 : 0;
+                    wide_r |= (top > 0 && cnt >= kWideCount) ? 1 : 0;
                 }
-                // The 16 lanes of a tile row hold its 4 block bytes at chunks 0, 4, 8, 12; chunk 0 gathers them.
-                const uint32_t b4 = (uint32_t)__shfl_down((int)byte, 4, 16);
-                const uint32_t b8 = (uint32_t)__shfl_down((int)byte, 8, 16);
-                const uint32_t b12 = (uint32_t)__shfl_down((int)byte, 12, 16);
-                if (col_ok && gr < a.rows) {
-                    stnt8(a.q_row + gr * a.cols + gc, make_uint2(lo, hi));
+                // The 16 lanes of a tile row hold its 4 block bytes at chunks 0, 4, 8, 12; chunk 0 gathers them with
+                // row shifts (lane i reads lane i + 4, i + 8, i + 12 of its 16-lane row).
+                const uint32_t b4 = (uint32_t)__builtin_amdgcn_mov_dpp((int)byte, 0x104, 0xF, 0xF, false);
+                const uint32_t b8 = (uint32_t)__builtin_amdgcn_mov_dpp((int)byte, 0x108, 0xF, 0xF, false);
+                const uint32_t b12 = (uint32_t)__builtin_amdgcn_mov_dpp((int)byte, 0x10C, 0xF, 0xF, false);
+                if (ok) {
+                    stnt8(qr, make_uint2(lo, hi));
                     if (a.srow_words) {
-                        if (ch == 0)
-                            *reinterpret_cast<uint32_t*>(a.s_row + gr * (a.cols / 32) + c0 / 32) =
-                                byte | (b4 << 8) | (b8 << 16) | (b12 << 24);
+                        if (ch == 0) *reinterpret_cast<uint32_t*>(sr) = byte | (b4 << 8) | (b8 << 16) | (b12 << 24);
                     } else if ((tid & 3) == 0) {
-                        a.s_row[gr * (a.cols / 32) + gc / 32] = (uint8_t)byte;
+                        *sr = (uint8_t)byte;
                     }
                 }
+                sr += sr_step;
             } else {
                 lo = pt_cvt_quad<MODE>(pt_scale, v[j].x, v[j].y);
                 hi = pt_cvt_quad<MODE>(pt_scale, v[j].z, v[j].w);
-                if (col_ok && gr < a.rows) stnt8(a.q_row + gr * a.cols + gc, make_uint2(lo, hi));
+                if (ok) stnt8(qr, make_uint2(lo, hi));
             }
+            qr += qr_step;
         }
     }
 
@@ -196,8 +215,8 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
         // RANGE: this thread's two column blocks (rows 32b .. 32b+31 of columns 2p, 2p+1): top binade and, after the
         // trade with the other block of the window (thread tid ^ 64), the small-code count against the window's top.
         // The trades use LDS words past the transposed codes and scale bytes (which end at byte QT*QT + 4*QT).
+        // (a block's top is 0 when all its codes are 0, else its largest binade + 1, as in the row path)
         int ctop[2] = {0, 0};
-        uint32_t cnz[2] = {0u, 0u};
         if constexpr (RANGE) {
             uint32_t mm[2] = {0u, 0u};
 #pragma unroll
@@ -206,18 +225,17 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
                 const uint32_t f0 = out1[i] & 0x7F7F7F7Fu, f1 = out1[i + 1] & 0x7F7F7F7Fu;
                 mm[0] = max(mm[0], max_code_mag8(e0, e1));
                 mm[1] = max(mm[1], max_code_mag8(f0, f1));
-                cnz[0] |= e0 | e1;
-                cnz[1] |= f0 | f1;
             }
-            ctop[0] = (int)(mm[0] >> 3) + (int)sb0;
-            ctop[1] = (int)(mm[1] >> 3) + (int)sb1;
+            ctop[0] = mm[0] ? (int)(mm[0] >> 3) + (int)sb0 + 1 : 0;
+            ctop[1] = mm[1] ? (int)(mm[1] >> 3) + (int)sb1 + 1 : 0;
         }
         // Transpose the codes once more through LDS so that the global stores write whole 128-byte lines: output
         // row c (column c of x) is 128 bytes; its 16-byte chunk k sits at chunk k ^ ((c >> 1) & 7) to spread the
         // writes of neighbouring columns over the banks.
         __syncthreads();                                           // every thread has read its input column pair
         int* xtop = reinterpret_cast<int*>(lds) + (QT * QT + 4 * QT) / 4;   // [256][2] block tops
-        int* xcnt = xtop + 2 * QTHREADS;                                    // [256][2] small counts | nonzero flag
+        int* xcnt = xtop + 2 * QTHREADS;                                    // [256][2] small counts
+        int wtop[2] = {0, 0};                                               // the windows' tops
         if constexpr (RANGE) {
             xtop[2 * tid] = ctop[0];
             xtop[2 * tid + 1] = ctop[1];
@@ -225,13 +243,12 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
             const int partner = tid ^ 64;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int top = max(ctop[h], xtop[2 * partner + h]);
-                const int sbh = (int)(h ? sb1 : sb0);
-                const uint32_t th4 = (uint32_t)min(min(max(top - kWideBinades - sbh, 0), 32) << 3, 128) * 0x01010101u;
+                wtop[h] = max(ctop[h], xtop[2 * partner + h]);
+                const uint32_t th4 = wide_th4(wtop[h], (int)(h ? sb1 : sb0));
                 int cnt = 0;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) cnt += count_below4((h ? out1[i] : out0[i]) & 0x7F7F7F7Fu, th4);
-                xcnt[2 * tid + h] = cnt | (cnz[h] != 0 ? 0x100 : 0);
+                xcnt[2 * tid + h] = cnt;
             }
         }
         uint8_t* obuf = reinterpret_cast<uint8_t*>(lds);           // 128 x 128 codes, then 128 x 4 scale bytes
@@ -254,9 +271,8 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
             if ((b & 1) == 0) {                                    // the window's first block decides
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int mine = xcnt[2 * tid + h], other = xcnt[2 * (tid ^ 64) + h];
-                    const int cnt = (mine & 0xFF) + (other & 0xFF);
-                    wide_c |= (((mine | other) & 0x100) != 0 && cnt >= kWideCount) ? 1 : 0;
+                    const int cnt = xcnt[2 * tid + h] + xcnt[2 * (tid ^ 64) + h];
+                    wide_c |= (wtop[h] > 0 && cnt >= kWideCount) ? 1 : 0;
                 }
             }
         }
