@@ -128,7 +128,9 @@ __device__ __forceinline__ uint32_t cvt_mx_pair(uint32_t old, uint32_t bf16_pair
 
 // 4 bf16 (two pairs) -> 4 E4M3 codes in one dword, divided by the block scale.
 __device__ __forceinline__ uint32_t cvt_mx_quad(uint32_t p0, uint32_t p1, float scale) {
-    return cvt_mx_pair<true>(cvt_mx_pair<false>(0u, p0, scale), p1, scale);
+    // the two conversions write bytes 0-1 and 2-3, so the first one's untouched half can start as any value (an
+    // unspecified one spares a register copy)
+    return cvt_mx_pair<true>(cvt_mx_pair<false>(__builtin_nondeterministic_value(p0), p0, scale), p1, scale);
 }
 
 template <int FMT, bool HI>

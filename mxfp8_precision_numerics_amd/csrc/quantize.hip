@@ -79,15 +79,20 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
     float pt_scale = 0.0f;
     if constexpr (!MX) pt_scale = *a.scale;
 
+    // chunk j of this thread: tile row (tid >> 4) + 16 j, 8 values from column gc; pointers advance 16 rows per chunk
+    const int64_t rows_in_tile = a.rows - r0;                // may exceed QT
     uint4 v[8];
+    {
+        const uint16_t* xp = a.x + (r0 + (tid >> 4)) * a.cols + gc;
+        const int64_t xstep = 16 * a.cols;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int row = (tid >> 4) + 16 * j;
-        const int64_t gr = r0 + row;
-        if (col_ok && gr < a.rows)
-            v[j] = ldnt16(a.x + gr * a.cols + gc);
-        else
-            v[j] = make_uint4(0u, 0u, 0u, 0u);
+        for (int j = 0; j < 8; ++j) {
+            if (col_ok && (tid >> 4) + 16 * j < rows_in_tile)
+                v[j] = ldnt16(xp);
+            else
+                v[j] = make_uint4(0u, 0u, 0u, 0u);
+            xp += xstep;
+        }
     }
 
     // AMAX: this thread's max |x| (bf16 magnitude patterns; NaN patterns sort above infinity; padding loaded as 0);
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
         // This thread's row of chunk j is lrow + 16 j; its code and scale pointers advance 16 rows per chunk (no 64-bit
         // index arithmetic per chunk).
         const int lrow = tid >> 4;
-        const int64_t rows_left = a.rows - r0;
+        const int64_t rows_left = rows_in_tile;
         uint8_t* qr = a.q_row + (r0 + lrow) * a.cols + gc;
         const int64_t qr_step = 16 * a.cols;
         uint8_t* sr = nullptr;
@@ -276,13 +281,21 @@ __global__ __launch_bounds__(QTHREADS) void quant_tile_kernel(QuantArgs a) {
                 }
             }
         }
+        {
+            // output row c = 32 pass + tid / 8 (column c0 + c of x), bytes 16 k .. 16 k + 15 of its 128
+            const int k = tid & 7;
+            const int64_t cols_in_tile = a.cols - c0;
+            const bool row_ok = 16 * k < rows_in_tile;             // rows % 32 == 0: a 16-row chunk is whole
+            uint8_t* qc = a.q_col + (c0 + (tid >> 3)) * a.rows + r0 + 16 * k;
+            const int64_t qc_step = 32 * a.rows;
 #pragma unroll
-        for (int pass = 0; pass < QT / 32; ++pass) {               // 32 output rows (x columns) per pass
-            const int c = 32 * pass + (tid >> 3), k = tid & 7;
-            const int64_t gc2 = c0 + c, gr2 = r0 + 16 * k;
-            if (gc2 < a.cols && gr2 < a.rows) {                    // rows % 32 == 0: a 16-row chunk is whole
-                const uint4 val = *reinterpret_cast<const uint4*>(obuf + c * QT + 16 * (k ^ ((c >> 1) & 7)));
-                *reinterpret_cast<uint4*>(a.q_col + gc2 * a.rows + gr2) = val;
+            for (int pass = 0; pass < QT / 32; ++pass) {           // 32 output rows (x columns) per pass
+                const int c = 32 * pass + (tid >> 3);
+                if (c < cols_in_tile && row_ok) {
+                    const uint4 val = *reinterpret_cast<const uint4*>(obuf + c * QT + 16 * (k ^ ((c >> 1) & 7)));
+                    *reinterpret_cast<uint4*>(qc) = val;
+                }
+                qc += qc_step;
             }
         }
         if constexpr (MX) {
