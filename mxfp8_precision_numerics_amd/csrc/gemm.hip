@@ -849,9 +849,9 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
     // Exact path, pipelined over the stage's four 16-value k-steps. k-step s takes bytes 8s .. 8s+7 of each lane's
     // 32 (steps 0, 1 lie in the stage's first 32-block, 2, 3 in its second). While k-step s's 16 matrix instructions
     // run, k-step s + 1 is converted to bf16 (two conversions per matrix instruction), and the next stage's fragments
-    // stream into the registers of k-steps already converted: bytes 0-15 during k-step 1, bytes 16-31 during k-step 3,
-    // where the next stage's k-step 0 is converted too. One fragment register set thus serves both stages, which
-    // leaves room for two sets of converted operands.
+    // stream into the registers of k-steps already converted: bytes 0-15 during k-step 0, bytes 16-31 during k-step 2;
+    // k-step 3 converts the next stage's k-step 0. One fragment register set thus serves both stages, which leaves
+    // room for two sets of converted operands.
     v8i F[8];                                  // F[j]: A rows wm*128 + 32j + (lane % 32); F[4 + i]: B rows wn*128 + 32i
     uint32_t SA[2][8], SB[2][8];               // conversion scale operands [4 blk + j] of the current and next stage
     v8bf CV[2][8];                             // converted k-steps: CV[s & 1][j] A, [4 + i] B
@@ -1009,8 +1009,9 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
     using NONE = std::integral_constant<int, -1>;
-    // Trip kt (kt + 1 < nk): the trip's copies, then stage kt's four k-steps with stage kt + 1's fragments, scales
-    // and k-step 0 conversion folded in, then the wait until stage kt + 2 has landed.
+    // Trip kt (kt + 1 < nk): stage kt's four k-steps with the trip's copies (two per k-step) and stage kt + 1's
+    // fragments, scale operands and k-step 0 conversion folded in, then the scale copies and the wait until stage
+    // kt + 2 has landed.
     auto trip = [&](auto ph_c, int kt, uint32_t* csa, uint32_t* csb, uint32_t* nsa, uint32_t* nsb) {
         constexpr int PH = decltype(ph_c)::value;
         using SP = std::integral_constant<int, PH < 0 ? -1 : (PH + 1) % 4>;     // stage kt + 1 mod 4
