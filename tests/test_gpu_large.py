@@ -1,0 +1,163 @@
+"""GPU checks past 32-bit offsets: every entry point here is driven with tensors of more than 2^31 elements (or
+operands of more than 2^31 bytes), and slabs at the far end (and around the 2^31 boundary) are compared with the
+oracle, so that an index or byte offset computed in 32 bits anywhere on the path would show.
+
+- mx_quantize, both orientations, x of 66048 x 32768 bf16 (2.16e9 elements): the row-orientation codes and scales of
+  three 32-row slabs (the first rows, across element 2^31, the last rows) and the column-orientation codes and scales
+  of the same rows (those land past byte 2^31 of q_col for the high columns), bit for bit.
+- fp8_quantize_pertensor on the same x with its largest magnitude planted at the last element: amax and scale equal
+  the oracle's (the slab holding the planted value has the tensor's amax), q and q^T of the last rows bit for bit.
+- scaled_gemm (checked, FP8 instruction and exact path; large and small tiles) and grouped_scaled_gemm with an MX
+  operand of 196608 x 12288 codes (2.4 GB): rows past byte 2^31 and around it within the bound of the oracle's fp64
+  GEMM.
+- fp8_adam_step over 2^31 + 4099 parameters (a ragged tail): the m scale equals the oracle's over every element and
+  sampled elements past 2^31 (and the tail) match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_precision_numerics_amd as mxq
+import oracle
+from gpu_util import DEV, need_gpu, say, u8, u16
+from mxfp8_precision_numerics_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+REL, ABS_S = 2.0 ** -7, 2.0 ** -20
+QR, QC = 66048, 32768                      # 2,164,260,864 elements
+GM, GK = 196608, 12288                     # 2,415,919,104 code bytes
+PLANT = 100.0                              # far above any N(0, 1) sample, exact in bf16
+
+
+@pytest.fixture(scope="module")
+def big_x():
+    need_gpu()
+    say("large x", QR, QC)
+    x = workloads.normal_bf16((QR, QC), 1.0, 61, 1, DEV)
+    x[-1, -1] = PLANT
+    yield x
+    del x
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def big_a():
+    need_gpu()
+    say("large A", GM, GK)
+    qa = mxq.mx_quantize(workloads.normal_bf16((GM, GK), 1.0, 62, 1, DEV), colwise=False)
+    torch.cuda.empty_cache()
+    yield qa
+    del qa
+    torch.cuda.empty_cache()
+
+
+def _slabs(rows, cols, block):
+    """Row slabs (start, stop): the first rows, the rows holding element (or byte) 2^31, the last rows."""
+    cross = (2 ** 31 // cols) // block * block
+    return [(0, block), (cross, cross + 2 * block), (rows - 3 * block, rows)]
+
+
+def test_mx_quantize_past_2_31_elements(big_x):
+    say("mx_quantize past 2^31 elements")
+    out = mxq.mx_quantize(big_x)
+    torch.cuda.synchronize()
+    for r0, r1 in _slabs(QR, QC, 32):
+        xs = u16(big_x[r0:r1])
+        q_row, s_row, q_col, s_col = oracle.mx_quantize(xs)
+        assert np.array_equal(u8(out.q_row[r0:r1]), q_row), (r0, r1)
+        assert np.array_equal(u8(out.s_row[r0:r1]), s_row), (r0, r1)
+        assert np.array_equal(u8(out.q_col[:, r0:r1]), q_col), (r0, r1)
+        assert np.array_equal(u8(out.s_col[:, r0 // 32:r1 // 32]), s_col), (r0, r1)
+    del out
+    torch.cuda.empty_cache()
+
+
+def test_pertensor_quantize_past_2_31_elements(big_x):
+    say("fp8_quantize_pertensor past 2^31 elements")
+    pt = mxq.pertensor_quantize(big_x, mxq.E4M3)
+    torch.cuda.synchronize()
+    r0 = QR - 64
+    amax, scale, q, qt = oracle.pertensor_quantize(u16(big_x[r0:]), oracle.E4M3)
+    assert amax == PLANT
+    assert np.float32(pt.amax.item()) == np.float32(amax) and np.float32(pt.scale.item()) == scale
+    assert np.array_equal(u8(pt.q[r0:]), q)
+    assert np.array_equal(u8(pt.q_t[:, r0:]), qt)
+    del pt
+    torch.cuda.empty_cache()
+
+
+def _ratio(C, y, S):
+    err = np.abs(C.float().cpu().numpy().astype(np.float64) - y)
+    return float(np.max(err / (REL * np.abs(y) + ABS_S * S)))
+
+
+@pytest.mark.parametrize("N,path", [(512, "checked"), (512, "exact"), (256, "fp8"), (256, "exact")],
+                         ids=["large tiles checked", "large tiles exact", "small tiles fp8", "small tiles exact"])
+def test_scaled_gemm_past_2_31_bytes(big_a, N, path):
+    say("scaled_gemm past 2^31 bytes", N, path)
+    qb = mxq.mx_quantize(workloads.normal_bf16((N, GK), 1.0, 62, 2, DEV), colwise=False)
+    C = mxq.scaled_gemm(big_a.q_row, big_a.s_row, qb.q_row, qb.s_row, mxq.MX_BLOCK32, path=path)
+    torch.cuda.synchronize()
+    bq, bs = u8(qb.q_row), u8(qb.s_row)
+    for r0, r1 in _slabs(GM, GK, 64)[1:]:
+        y, S = oracle.gemm_ref(u8(big_a.q_row[r0:r1]), u8(big_a.s_row[r0:r1]), oracle.E4M3, bq, bs, oracle.E4M3,
+                               oracle.MX_BLOCK32)
+        r = _ratio(C[r0:r1], y, S)
+        say(f"  rows {r0}..{r1}: worst |err| / bound {r:.3f}")
+        assert r <= 1.0
+
+
+def test_grouped_gemm_past_2_31_bytes(big_a):
+    say("grouped_scaled_gemm past 2^31 bytes")
+    G, N = 4, 512
+    offsets = np.array([0, 32768, 65536 + 96, 131072 + 32, GM], np.int64)
+    W = workloads.normal_bf16((G * N, GK), 1.0, 62, 3, DEV)
+    qw = mxq.mx_quantize(W, colwise=False)
+    del W
+    bq, bs = qw.q_row.view(G, N, GK), qw.s_row.view(G, N, GK // 32)
+    C = mxq.grouped_scaled_gemm(big_a.q_row, big_a.s_row, torch.from_numpy(offsets).to(DEV), bq, bs)
+    torch.cuda.synchronize()
+    hq, hs = u8(bq), u8(bs)
+    for r0, r1 in _slabs(GM, GK, 64)[1:]:
+        # the slab lies in the last group, whose rows start at offsets[3]
+        sub_off = np.array([0, 0, 0, 0, r1 - r0], np.int64)
+        y, S = oracle.grouped_gemm_ref(u8(big_a.q_row[r0:r1]), u8(big_a.s_row[r0:r1]), sub_off, hq, hs)
+        r = _ratio(C[r0:r1], y, S)
+        say(f"  rows {r0}..{r1}: worst |err| / bound {r:.3f}")
+        assert r <= 1.0
+
+
+def test_adam_past_2_31_elements():
+    need_gpu()
+    n = 2 ** 31 + 4099
+    say("adam past 2^31 elements", n)
+    theta = workloads.workload5_params(n, DEV)
+    m_q = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    m_scale = torch.ones(1, dtype=torch.float32, device=DEV)
+    v = torch.zeros(n, dtype=torch.float16, device=DEV)
+    w = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    g = workloads.workload5_grad(n, 1, DEV)
+    hp = mxq.AdamHParams(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+    ohp = oracle.AdamHP(1e-4, 0.9, 0.95, 1e-8, 0.1, 1)
+    rng = np.random.default_rng(63)
+    idx = np.unique(np.concatenate([rng.choice(n, 200_000, replace=False), np.arange(2 ** 31 - 64, 2 ** 31 + 64),
+                                    np.arange(n - 4099 - 8, n)])).astype(np.int64)
+    gh, mh, vh = u16(g), u8(m_q), u16(v)
+    idx_t = torch.from_numpy(idx).to(DEV)
+    th_s = theta[idx_t].cpu().numpy()
+    amax = oracle.adam_amax(gh, mh, vh, np.float32(1.0), ohp)
+    s_new = np.float32(448.0) / np.float32(max(amax, 1e-12))
+    full_th = np.zeros(n, np.float32)
+    full_th[idx] = th_s
+    om, oq, ov, ow = oracle.adam_elements(full_th, gh, mh, vh, np.float32(1.0), s_new, idx, ohp)
+    del gh, mh, vh, full_th
+    mxq.fp8_adam_step(theta, g, m_q, m_scale, v, w, hp)
+    torch.cuda.synchronize()
+    assert np.float32(m_scale.item()) == s_new
+    assert np.array_equal(theta[idx_t].cpu().numpy().view(np.uint32), om.view(np.uint32))
+    assert np.array_equal(m_q[idx_t].cpu().numpy(), oq)
+    assert np.array_equal(v[idx_t].cpu().numpy().view(np.uint16), ov)
+    assert np.array_equal(w[idx_t].view(torch.int16).cpu().numpy().view(np.uint16), ow)
+    del theta, m_q, v, w, g
+    torch.cuda.empty_cache()
