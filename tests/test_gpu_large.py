@@ -12,6 +12,10 @@ oracle, so that an index or byte offset computed in 32 bits anywhere on the path
   GEMM.
 - fp8_adam_step over 2^31 + 4099 parameters (a ragged tail): the m scale equals the oracle's over every element and
   sampled elements past 2^31 (and the tail) match bit for bit.
+- On the same 2.16e9-element x: the delayed-scaling cast (amax, history, q and q^T of the last rows), the auto-scaled
+  gradient cast and the requantize to a shared scale (only the planted value saturates, so the overflow count and
+  the next mu follow from the last rows), and the fused SwiGLU quantize with x as [gate | up]; and the Adam step fused
+  with the weight-cache refresh on a 66048 x 32768 weight, both cache orientations of three row slabs.
 """
 import numpy as np
 import pytest
@@ -160,4 +164,99 @@ def test_adam_past_2_31_elements():
     assert np.array_equal(v[idx_t].cpu().numpy().view(np.uint16), ov)
     assert np.array_equal(w[idx_t].view(torch.int16).cpu().numpy().view(np.uint16), ow)
     del theta, m_q, v, w, g
+    torch.cuda.empty_cache()
+
+
+def _bits(t):
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
+def test_pertensor_delayed_past_2_31_elements(big_x):
+    say("fp8_quantize_pertensor_delayed past 2^31 elements")
+    hist = torch.tensor([3.0, 5.0], dtype=torch.float32, device=DEV)
+    pos = torch.zeros(1, dtype=torch.int32, device=DEV)
+    r = mxq.pertensor_quantize_delayed(big_x, hist, pos, mxq.E4M3)
+    torch.cuda.synchronize()
+    r0 = QR - 64
+    o_hist, o_pos = np.array([3.0, 5.0], np.float32), np.zeros(1, np.int32)
+    a, s, q, qt = oracle.pertensor_quantize_delayed(u16(big_x[r0:]), o_hist, o_pos, oracle.E4M3)
+    assert a == PLANT and np.float32(r.amax.item()) == np.float32(a)
+    assert _bits(r.scale)[0] == np.float32(s).view(np.uint32)
+    assert np.array_equal(u8(r.q[r0:]), q) and np.array_equal(u8(r.q_t[:, r0:]), qt)
+    assert np.array_equal(_bits(hist), o_hist.view(np.uint32)) and int(pos.item()) == int(o_pos[0])
+    del r
+    torch.cuda.empty_cache()
+
+
+def test_autoscale_and_requantize_past_2_31_elements(big_x):
+    say("fp8_autoscale_cast + fp8_requantize_shared past 2^31 elements")
+    g = big_x.view(-1)
+    mu = torch.tensor([5.0], dtype=torch.float32, device=DEV)
+    r = mxq.fp8_autoscale_cast(g, mu, mxq.E4M3)
+    torch.cuda.synchronize()
+    tail = 64 * QC                      # the last 64 rows; 5 x PLANT is the only value past 448
+    q, cnt, s, o_mu = oracle.autoscale_cast(u16(g[-tail:]), 5.0, oracle.E4M3)
+    assert cnt == 1 and int(r.overflow.item()) == 1
+    assert _bits(r.scale)[0] == s.view(np.uint32) and _bits(mu)[0] == o_mu.view(np.uint32)
+    assert np.array_equal(u8(r.q[-tail:]), q)
+    gathered = torch.cat([r.scale, 2.0 ** torch.arange(-3, 4, dtype=torch.float32, device=DEV)])
+    rq, sg, _ = mxq.fp8_requantize_shared(r.q, mxq.E4M3, r.scale, gathered, mxq.E4M3)
+    torch.cuda.synchronize()
+    o_sg = oracle.min_scale(gathered.cpu().numpy())
+    assert _bits(sg)[0] == o_sg.view(np.uint32)
+    assert np.array_equal(u8(rq[-tail:]), oracle.requantize_shared(q, oracle.E4M3, float(s), float(o_sg), oracle.E4M3))
+    del r, rq
+    torch.cuda.empty_cache()
+
+
+def test_swiglu_quantize_past_2_31_elements(big_x):
+    say("swiglu_mx_quantize past 2^31 input elements")
+    out = mxq.swiglu_mx_quantize(big_x)
+    torch.cuda.synchronize()
+    for r0, r1 in _slabs(QR, QC, 32):
+        q, s, _ = oracle.swiglu_mx_quantize(u16(big_x[r0:r1]))
+        assert np.array_equal(u8(out.q_row[r0:r1]), q), (r0, r1)
+        assert np.array_equal(u8(out.s_row[r0:r1]), s), (r0, r1)
+    del out
+    torch.cuda.empty_cache()
+
+
+def test_adam_weight_cache_past_2_31_elements():
+    need_gpu()
+    rows, cols = QR, QC
+    n = rows * cols
+    say("fp8_adam_step_mx_cache past 2^31 elements", rows, cols)
+    theta = workloads.workload5_params(n, DEV)
+    m_q = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    m_scale = torch.ones(1, dtype=torch.float32, device=DEV)
+    v = torch.zeros(n, dtype=torch.float16, device=DEV)
+    g = workloads.workload5_grad(n, 1, DEV)
+    hp = mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.1, 1)
+    ohp = oracle.AdamHP(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+    slabs = _slabs(rows, cols, 32)
+    idx = np.concatenate([np.arange(r0 * cols, r1 * cols, dtype=np.int64) for r0, r1 in slabs])
+    gh, mh, vh = u16(g), u8(m_q), u16(v)
+    idx_t = torch.from_numpy(idx).to(DEV)
+    th_s = theta[idx_t].cpu().numpy()
+    amax = oracle.adam_amax(gh, mh, vh, np.float32(1.0), ohp)
+    s_new = np.float32(448.0) / np.float32(max(amax, 1e-12))
+    full_th = np.zeros(n, np.float32)
+    full_th[idx] = th_s
+    om, oq, ov, _ = oracle.adam_elements(full_th, gh, mh, vh, np.float32(1.0), s_new, idx, ohp)
+    del gh, mh, vh, full_th
+    cache = mxq.fp8_adam_step_mx_cache(theta, g, m_q, m_scale, v, None, hp, rows, cols)
+    torch.cuda.synchronize()
+    assert np.float32(m_scale.item()) == s_new
+    assert np.array_equal(theta[idx_t].cpu().numpy().view(np.uint32), om.view(np.uint32))
+    assert np.array_equal(m_q[idx_t].cpu().numpy(), oq)
+    assert np.array_equal(v[idx_t].cpu().numpy().view(np.uint16), ov)
+    at = 0
+    for r0, r1 in slabs:
+        k = (r1 - r0) * cols
+        qr, sr, qc, sc = oracle.mx_quantize_f32(om[at:at + k].reshape(r1 - r0, cols))
+        at += k
+        assert np.array_equal(u8(cache.q_row[r0:r1]), qr) and np.array_equal(u8(cache.s_row[r0:r1]), sr), (r0, r1)
+        assert np.array_equal(u8(cache.q_col[:, r0:r1]), qc), (r0, r1)
+        assert np.array_equal(u8(cache.s_col[:, r0 // 32:r1 // 32]), sc), (r0, r1)
+    del theta, m_q, v, g, cache
     torch.cuda.empty_cache()
