@@ -16,6 +16,11 @@ oracle, so that an index or byte offset computed in 32 bits anywhere on the path
   gradient cast and the requantize to a shared scale (only the planted value saturates, so the overflow count and
   the next mu follow from the last rows), and the fused SwiGLU quantize with x as [gate | up]; and the Adam step fused
   with the weight-cache refresh on a 66048 x 32768 weight, both cache orientations of three row slabs.
+- The rest of the boundary: mxq_quantize_ranged (codes of both orientations), scaled_gemm_ranged on the large operand
+  with its range words, swiglu_mx_quantize_oriented, route_weighted_mx_quantize and swiglu_backward_mx_quantize on x
+  (both orientations), grouped_scaled_gemm_strided with B at padded row and expert strides, grouped_wgrad_mx over
+  4.2e6 tokens (a 2.1 GB operand, so the token-range kernel runs past byte 2^31), and fp8_adam_step_delayed over
+  2^31 + 4099 parameters.
 """
 import numpy as np
 import pytest
@@ -47,12 +52,13 @@ def big_x():
 
 @pytest.fixture(scope="module")
 def big_a():
+    """The MX row orientation of a 196608 x 12288 operand and its range words (from mx_quantize_ranged)."""
     need_gpu()
     say("large A", GM, GK)
-    qa = mxq.mx_quantize(workloads.normal_bf16((GM, GK), 1.0, 62, 1, DEV), colwise=False)
+    qa, wa = mxq.mx_quantize_ranged(workloads.normal_bf16((GM, GK), 1.0, 62, 1, DEV), colwise=False)
     torch.cuda.empty_cache()
-    yield qa
-    del qa
+    yield qa, wa
+    del qa, wa
     torch.cuda.empty_cache()
 
 
@@ -100,6 +106,7 @@ def _ratio(C, y, S):
                          ids=["large tiles checked", "large tiles exact", "small tiles fp8", "small tiles exact"])
 def test_scaled_gemm_past_2_31_bytes(big_a, N, path):
     say("scaled_gemm past 2^31 bytes", N, path)
+    big_a = big_a[0]
     qb = mxq.mx_quantize(workloads.normal_bf16((N, GK), 1.0, 62, 2, DEV), colwise=False)
     C = mxq.scaled_gemm(big_a.q_row, big_a.s_row, qb.q_row, qb.s_row, mxq.MX_BLOCK32, path=path)
     torch.cuda.synchronize()
@@ -114,6 +121,7 @@ def test_scaled_gemm_past_2_31_bytes(big_a, N, path):
 
 def test_grouped_gemm_past_2_31_bytes(big_a):
     say("grouped_scaled_gemm past 2^31 bytes")
+    big_a = big_a[0]
     G, N = 4, 512
     offsets = np.array([0, 32768, 65536 + 96, 131072 + 32, GM], np.int64)
     W = workloads.normal_bf16((G * N, GK), 1.0, 62, 3, DEV)
@@ -259,4 +267,162 @@ def test_adam_weight_cache_past_2_31_elements():
         assert np.array_equal(u8(cache.q_col[:, r0:r1]), qc), (r0, r1)
         assert np.array_equal(u8(cache.s_col[:, r0 // 32:r1 // 32]), sc), (r0, r1)
     del theta, m_q, v, g, cache
+    torch.cuda.empty_cache()
+
+
+def _check_mx_slabs(out, ref_fn, rows, block=32):
+    """Both orientations of `out` on the three row slabs, against ref_fn(r0, r1) -> (q_row, s_row, q_col, s_col)."""
+    for r0, r1 in _slabs(rows, QC, block):
+        q_row, s_row, q_col, s_col = ref_fn(r0, r1)[:4]
+        assert np.array_equal(u8(out.q_row[r0:r1]), q_row), (r0, r1)
+        assert np.array_equal(u8(out.s_row[r0:r1]), s_row), (r0, r1)
+        assert np.array_equal(u8(out.q_col[:, r0:r1]), q_col), (r0, r1)
+        assert np.array_equal(u8(out.s_col[:, r0 // 32:r1 // 32]), s_col), (r0, r1)
+
+
+def test_ranged_quantize_past_2_31_elements(big_x):
+    say("mxq_quantize_ranged past 2^31 elements")
+    out, words = mxq.mx_quantize_ranged(big_x)
+    torch.cuda.synchronize()
+    _check_mx_slabs(out, lambda r0, r1: oracle.mx_quantize(u16(big_x[r0:r1])), QR)
+    assert set(words.cpu().tolist()) <= {0, 1}
+    del out
+    torch.cuda.empty_cache()
+
+
+def test_scaled_gemm_ranged_past_2_31_bytes(big_a):
+    say("scaled_gemm_ranged past 2^31 bytes")
+    qa, wa = big_a
+    qb, wb = mxq.mx_quantize_ranged(workloads.normal_bf16((512, GK), 1.0, 62, 2, DEV), colwise=False)
+    C = mxq.scaled_gemm_ranged(qa.q_row, qa.s_row, wa[0:1], qb.q_row, qb.s_row, wb[0:1])
+    torch.cuda.synchronize()
+    bq, bs = u8(qb.q_row), u8(qb.s_row)
+    for r0, r1 in _slabs(GM, GK, 64)[1:]:
+        y, S = oracle.gemm_ref(u8(qa.q_row[r0:r1]), u8(qa.s_row[r0:r1]), oracle.E4M3, bq, bs, oracle.E4M3,
+                               oracle.MX_BLOCK32)
+        r = _ratio(C[r0:r1], y, S)
+        say(f"  rows {r0}..{r1}: worst |err| / bound {r:.3f}")
+        assert r <= 1.0
+
+
+def test_swiglu_oriented_past_2_31_elements(big_x):
+    say("swiglu_mx_quantize_oriented past 2^31 input elements")
+    out = mxq.swiglu_mx_quantize_oriented(big_x)
+    torch.cuda.synchronize()
+
+    def ref(r0, r1):
+        q, s, h = oracle.swiglu_mx_quantize(u16(big_x[r0:r1]), want_h=True)
+        _, _, qc, sc = oracle.mx_quantize_f32(h, rowwise=False)
+        return q, s, qc, sc
+    _check_mx_slabs(out, ref, QR)
+    del out
+    torch.cuda.empty_cache()
+
+
+def test_route_weighted_quantize_past_2_31_elements(big_x):
+    say("route_weighted_mx_quantize past 2^31 elements")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(64)
+    p = torch.rand(QR, generator=gen, device=DEV) * 0.99 + 0.01
+    out = mxq.route_weighted_mx_quantize(big_x, p)
+    torch.cuda.synchronize()
+    ph = p.cpu().numpy()
+    _check_mx_slabs(out, lambda r0, r1: oracle.route_weighted_mx_quantize(u16(big_x[r0:r1]), ph[r0:r1]), QR)
+    del out
+    torch.cuda.empty_cache()
+
+
+def test_swiglu_backward_quantize_past_2_31_elements(big_x):
+    say("swiglu_backward_mx_quantize past 2^31 elements")
+    dh = workloads.normal_bf16((QR, QC // 2), 1.0, 61, 2, DEV)
+    out = mxq.swiglu_backward_mx_quantize(big_x, dh)
+    torch.cuda.synchronize()
+    _check_mx_slabs(out, lambda r0, r1: oracle.swiglu_bwd_mx_quantize(u16(big_x[r0:r1]), u16(dh[r0:r1])), QR)
+    del out, dh
+    torch.cuda.empty_cache()
+
+
+def test_grouped_gemm_strided_past_2_31_bytes(big_a):
+    say("grouped_scaled_gemm_strided past 2^31 bytes")
+    qa = big_a[0]
+    G, N = 4, 512
+    ldb, ldbs = GK + 256, GK // 32 + 16                      # padded rows (16-byte multiples)
+    bgs, bsgs = N * ldb + 4096, N * ldbs + 64                 # padded experts
+    offsets = np.array([0, 32768, 65536 + 96, 131072 + 32, GM], np.int64)
+    qw = mxq.mx_quantize(workloads.normal_bf16((G * N, GK), 1.0, 62, 4, DEV), colwise=False)
+    bq_store = torch.zeros(G * bgs, dtype=torch.uint8, device=DEV)
+    bs_store = torch.zeros(G * bsgs, dtype=torch.uint8, device=DEV)
+    bq_store.as_strided((G, N, GK), (bgs, ldb, 1)).copy_(qw.q_row.view(G, N, GK))
+    bs_store.as_strided((G, N, GK // 32), (bsgs, ldbs, 1)).copy_(qw.s_row.view(G, N, GK // 32))
+    C = mxq.grouped_scaled_gemm_strided(qa.q_row, qa.s_row, torch.from_numpy(offsets).to(DEV), bq_store, bs_store,
+                                        G, N, GK, ldb, bgs, ldbs, bsgs)
+    torch.cuda.synchronize()
+    hq, hs = u8(qw.q_row).reshape(G, N, GK), u8(qw.s_row).reshape(G, N, GK // 32)
+    for r0, r1 in _slabs(GM, GK, 64)[1:]:
+        sub_off = np.array([0, 0, 0, 0, r1 - r0], np.int64)      # the slab lies in the last group
+        y, S = oracle.grouped_gemm_ref(u8(qa.q_row[r0:r1]), u8(qa.s_row[r0:r1]), sub_off, hq, hs)
+        r = _ratio(C[r0:r1], y, S)
+        say(f"  rows {r0}..{r1}: worst |err| / bound {r:.3f}")
+        assert r <= 1.0
+
+
+def test_grouped_wgrad_past_2_31_bytes():
+    need_gpu()
+    M, N, Kt = 512, 256, 4_194_304 + 1024                      # a_q: 2,148,007,936 bytes
+    say("grouped_wgrad_mx past 2^31 bytes", M, N, Kt)
+    qa = mxq.mx_quantize(workloads.normal_bf16((M, Kt), 1.0, 65, 1, DEV), colwise=False)
+    qb = mxq.mx_quantize(workloads.normal_bf16((N, Kt), 1.0, 65, 2, DEV), colwise=False)
+    torch.cuda.empty_cache()
+    offsets = np.array([0, 1_048_576 + 32, 2_097_152 + 64, 3_145_728 + 96, Kt], np.int64)
+    C = mxq.grouped_wgrad_mx(qa.q_row, qa.s_row, qb.q_row, qb.s_row, torch.from_numpy(offsets).to(DEV))
+    torch.cuda.synchronize()
+    rows = np.arange(M - 8, M, dtype=np.int64)
+    cols = np.array([0, 1, 77, 128, 200, 253, 254, 255], np.int64)
+    y, S = oracle.grouped_wgrad_ref(u8(qa.q_row[M - 8:]), u8(qa.s_row[M - 8:]), u8(qb.q_row[cols]),
+                                    u8(qb.s_row[cols]), offsets)
+    got = C[:, M - 8:][:, :, torch.from_numpy(cols).to(DEV)]
+    r = _ratio(got, y, S)
+    say(f"  worst |err| / bound {r:.3f}")
+    assert r <= 1.0
+    del qa, qb, C
+    torch.cuda.empty_cache()
+
+
+def test_adam_delayed_past_2_31_elements():
+    need_gpu()
+    n = 2 ** 31 + 4099
+    say("fp8_adam_step_delayed past 2^31 elements", n)
+    theta = workloads.workload5_params(n, DEV)
+    m_q = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    m_scale = torch.ones(1, dtype=torch.float32, device=DEV)
+    v = torch.zeros(n, dtype=torch.float16, device=DEV)
+    w = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    g = workloads.workload5_grad(n, 1, DEV)
+    hist = torch.tensor([2e-4, 1e-4], dtype=torch.float32, device=DEV)
+    pos = torch.ones(1, dtype=torch.int32, device=DEV)
+    o_hist, o_pos = np.array([2e-4, 1e-4], np.float32), np.ones(1, np.int32)
+    hp = mxq.AdamHParams(3e-4, 0.9, 0.95, 1e-8, 0.1, 1)
+    ohp = oracle.AdamHP(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+    rng = np.random.default_rng(66)
+    idx = np.unique(np.concatenate([rng.choice(n, 200_000, replace=False), np.arange(2 ** 31 - 64, 2 ** 31 + 64),
+                                    np.arange(n - 4099 - 8, n)])).astype(np.int64)
+    gh, mh, vh = u16(g), u8(m_q), u16(v)
+    idx_t = torch.from_numpy(idx).to(DEV)
+    th_s = theta[idx_t].cpu().numpy()
+    s_new = oracle.delayed_scale(o_hist, oracle.E4M3)           # from the history as it was before the step
+    amax = oracle.adam_amax(gh, mh, vh, np.float32(1.0), ohp)
+    full_th = np.zeros(n, np.float32)
+    full_th[idx] = th_s
+    om, oq, ov, ow = oracle.adam_elements(full_th, gh, mh, vh, np.float32(1.0), s_new, idx, ohp)
+    del gh, mh, vh, full_th
+    oracle.history_push(o_hist, o_pos, amax)
+    mxq.fp8_adam_step_delayed(theta, g, m_q, m_scale, v, w, hp, hist, pos)
+    torch.cuda.synchronize()
+    assert _bits(m_scale)[0] == s_new.view(np.uint32)
+    assert np.array_equal(_bits(hist), o_hist.view(np.uint32)) and int(pos.item()) == int(o_pos[0])
+    assert np.array_equal(theta[idx_t].cpu().numpy().view(np.uint32), om.view(np.uint32))
+    assert np.array_equal(m_q[idx_t].cpu().numpy(), oq)
+    assert np.array_equal(v[idx_t].cpu().numpy().view(np.uint16), ov)
+    assert np.array_equal(w[idx_t].view(torch.int16).cpu().numpy().view(np.uint16), ow)
+    del theta, m_q, v, w, g
     torch.cuda.empty_cache()

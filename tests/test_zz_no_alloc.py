@@ -1,7 +1,8 @@
 """fp8_quantize_pertensor_noalloc (the allocation-free entry point, scratch in the library's own device array)
 against fp8_quantize_pertensor (caller workspace), through the C ABI: amax, scale, q and q_t bit for bit, on two
 calls in a row, the second with a smaller input (the array keeps the first call's partials), in both formats, plus a
-delayed-mode call (scale_in given) and a check of the second call against the oracle."""
+delayed-mode call (scale_in given), a check of the second call against the oracle, and a tensor of more than 2^31
+elements checked against the oracle on its last rows."""
 import ctypes as C
 
 import numpy as np
@@ -67,3 +68,21 @@ def test_noalloc_delayed_scale_and_repeat():
         assert torch.equal(r.view(torch.uint8), g.view(torch.uint8))
     assert got1[1].item() == 3.0
     assert torch.equal(got2[2], ref[2][:64])
+
+
+def test_noalloc_past_2_31_elements():
+    """A 66048 x 32768 tensor (2.16e9 elements, its largest magnitude planted at the last element): amax and scale
+    equal the oracle's on the last rows (which hold the tensor's amax), and q and q_t of those rows bit for bit."""
+    need_gpu()
+    rows, cols = 66048, 32768
+    say("noalloc per-tensor past 2^31 elements", rows, cols)
+    x = workloads.normal_bf16((rows, cols), 1.0, 40, 9, DEV)
+    x[-1, -1] = 100.0
+    amax, scale, q, qt = _run("fp8_quantize_pertensor_noalloc", x, 0)
+    torch.cuda.synchronize()
+    r0 = rows - 64
+    oa, osc, oq, oqt = oracle.pertensor_quantize(u16(x[r0:]), oracle.E4M3)
+    assert oa == 100.0 and amax.item() == oa and np.float32(scale.item()) == osc
+    assert np.array_equal(u8(q[r0:]), oq) and np.array_equal(u8(qt[:, r0:]), oqt)
+    del x, q, qt
+    torch.cuda.empty_cache()
