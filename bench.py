@@ -522,7 +522,7 @@ def measured_traffic(part):
 
 
 PROFILE_KERNELS = ["mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad", "grouped_gemm_up", "grouped_gemm_down",
-                   "mx_quant_act", "adam", "copy"]
+                   "mx_quant_act", "adam", "copy", "read_lds"]
 
 
 def profile_kernel(name, dev):
@@ -538,6 +538,11 @@ def profile_kernel(name, dev):
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         run = lambda: _probe.copy(src, dst, 0, 8)  # noqa: E731
+    elif name == "read_lds":
+        n = 1 << 30                                            # 1 GiB read into LDS by the GEMM's copy instruction
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        sink = torch.empty(256, dtype=torch.int32, device=dev)
+        run = lambda: _probe.read_lds(src, sink, 256)  # noqa: E731
     elif name in ("mx_gemm_fwd", "mx_gemm_dgrad", "mx_gemm_wgrad"):
         X, W, dY = workloads.workload2(dev)
         (qx, wx), (qw, ww), (qd, wd) = (mxq.mx_quantize_ranged(t) for t in (X, W, dY))

@@ -43,6 +43,15 @@ mxq_status mxq_probe_copy(const void* src, void* dst, int64_t bytes, int64_t blo
 mxq_status mxq_probe_read(const void* src, int64_t bytes, int64_t blocks, int64_t unroll, uint32_t* sink,
                           hipStream_t stream);
 
+/*
+ * A streaming read of src[0 .. bytes) into LDS with the large-tile GEMM's global-to-LDS copy instruction
+ * (buffer_load_dwordx4 ... lds, 1 KiB per wave instruction): `blocks` workgroups of 256 threads loop over the 64 KiB
+ * pieces of src, and workgroup w writes the xor of every 32-bit word it read to sink[w] (sink: device uint32[blocks]).
+ * It gives the hardware counters' bytes per byte for that load path. bytes % 65536 == 0; src 16-byte aligned;
+ * 1 <= blocks <= 65536. bytes == 0 writes sink[w] = 0.
+ */
+mxq_status mxq_probe_read_lds(const void* src, int64_t bytes, int64_t blocks, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

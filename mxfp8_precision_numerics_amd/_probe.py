@@ -17,6 +17,7 @@ SIGNATURES = {
     "mxq_probe_mfma_fp8": (_I, [_P, _I64, _I64, _P, _P]),
     "mxq_probe_copy": (_I, [_P, _P, _I64, _I64, _I64, _P]),
     "mxq_probe_read": (_I, [_P, _I64, _I64, _I64, _P, _P]),
+    "mxq_probe_read_lds": (_I, [_P, _I64, _I64, _P, _P]),
 }
 
 _lib_probe = None
@@ -86,4 +87,15 @@ def read(src: torch.Tensor, sink: torch.Tensor, blocks: int = 0, unroll: int = 8
         raise ValueError(f"sink needs {groups} entries")
     _lib.check("mxq_probe_read", load().mxq_probe_read(_ptr(src), nbytes, blocks, unroll, _ptr(sink),
                                                        _stream(src.device)))
+    return nbytes
+
+
+def read_lds(src: torch.Tensor, sink: torch.Tensor, blocks: int = 256) -> int:
+    """Enqueue a streaming read of src into LDS through the GEMM's global-to-LDS copy instruction (one xor word per
+    workgroup into sink, int32[blocks]). src holds a whole number of 64 KiB pieces. Returns the bytes read."""
+    nbytes = _bytes(src)
+    if not (sink.is_cuda and sink.dtype == torch.int32) or sink.numel() < blocks:
+        raise ValueError(f"sink must be an int32 device tensor of at least {blocks} entries")
+    _lib.check("mxq_probe_read_lds", load().mxq_probe_read_lds(_ptr(src), nbytes, blocks, _ptr(sink),
+                                                               _stream(src.device)))
     return nbytes

@@ -6,6 +6,8 @@
 //   bytes (real quantized data toggles bits as a GEMM's operands do).
 // - A streaming copy and a streaming read: 16-byte non-temporal accesses, 4, 8 or 16 loads in flight per thread, over
 //   a fixed grid that loops or over one workgroup per piece of the data.
+// - A streaming read into LDS with the large-tile GEMM's copy instruction (buffer_load_dwordx4 ... lds), so that the
+//   hardware counters' bytes per byte of that load path can be read off a transfer of known size.
 #include <stdint.h>
 
 #include "mxq_device.h"
@@ -96,6 +98,45 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
     if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
+// Read into LDS: workgroup w streams the 64 KiB pieces w, w + gridDim.x, ... Each wave moves its 16 KiB of a piece
+// with 16 instructions that each land 1 KiB (lane l's 16 bytes at slot l), waits for them, then reads its own slots
+// back and xors every word into the workgroup's sink word, so every byte is used and the result can be checked.
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256, 1) void read_lds_probe_kernel(const uint8_t* __restrict__ src, int64_t pieces,
+                                                                uint32_t* __restrict__ sink) {
+    __shared__ __attribute__((aligned(16))) uint4 buf[4096];          // 64 KiB: 16 KiB per wave
+    __shared__ uint32_t part[4];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(&buf[wave * 1024]));
+    uint32_t x = 0;
+    for (int64_t p = blockIdx.x; p < pieces; p += gridDim.x) {
+        const uint64_t base = reinterpret_cast<uint64_t>(src + p * 65536);
+        const v4i rsrc = v4i{(int)__builtin_amdgcn_readfirstlane((uint32_t)base),
+                             (int)(__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) & 0xFFFFu), 65536,
+                             0x00020000};
+        const int voff = wave * 16384 + lane * 16;
+        // the previous piece's reads of these slots have returned before the slots are refilled
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :: "v"(voff + 1024 * c), "s"(rsrc), "{m0}"(lds0 + 1024 * c) : "memory");
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const uint4 v = buf[wave * 1024 + c * 64 + lane];
+            x ^= v.x ^ v.y ^ v.z ^ v.w;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off, 64);
+    if (lane == 0) part[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 template <int U>
 static hipError_t launch_copy_u(const void* src, void* dst, int64_t n16, int blocks, hipStream_t stream) {
     const uint4* s = static_cast<const uint4*>(src);
@@ -116,6 +157,12 @@ static hipError_t launch_read_u(const void* src, int64_t n16, int blocks, uint32
     else
         hipLaunchKernelGGL((read_probe_kernel<U, false>), dim3((unsigned)((n16 + 256 * U - 1) / (256 * U))), dim3(256),
                            0, stream, s, n16, sink);
+    return hipGetLastError();
+}
+
+static hipError_t launch_read_lds(const void* src, int64_t pieces, int blocks, uint32_t* sink, hipStream_t stream) {
+    hipLaunchKernelGGL(read_lds_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint8_t*>(src), pieces, sink);
     return hipGetLastError();
 }
 
@@ -163,6 +210,13 @@ mxq_status mxq_probe_read(const void* src, int64_t bytes, int64_t blocks, int64_
                  : unroll == 8 ? mxq::launch_read_u<8>(src, n16, (int)blocks, sink, stream)
                                : mxq::launch_read_u<16>(src, n16, (int)blocks, sink, stream);
     return e == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+mxq_status mxq_probe_read_lds(const void* src, int64_t bytes, int64_t blocks, uint32_t* sink, hipStream_t stream) {
+    if (bytes < 0 || bytes % 65536 != 0 || blocks < 1 || blocks > 65536) return MXQ_ERR_SHAPE;
+    if (!sink || (bytes > 0 && !src)) return MXQ_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(src) & 15u) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return MXQ_ERR_ALIGN;
+    return mxq::launch_read_lds(src, bytes / 65536, (int)blocks, sink, stream) == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
 }  // extern "C"

@@ -201,6 +201,14 @@ def test_probe_validation():
     assert r(None, 32, 0, 8, P, None) == 1
     assert r(MIS, 32, 0, 8, P, None) == 3
     assert r(None, 0, 0, 8, P, None) == 0
+    d = _probe.load().mxq_probe_read_lds
+    assert d(P, 65536 + 16, 4, P, None) == 2             # whole 64 KiB pieces only
+    assert d(P, -65536, 4, P, None) == 2
+    assert d(P, 65536, 0, P, None) == 2                  # 1 <= blocks <= 65536
+    assert d(P, 65536, 70000, P, None) == 2
+    assert d(P, 65536, 4, None, None) == 1
+    assert d(None, 65536, 4, P, None) == 1
+    assert d(MIS, 65536, 4, P, None) == 3
 
 
 def test_routed_backward_validation():
