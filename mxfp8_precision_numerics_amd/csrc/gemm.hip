@@ -405,14 +405,18 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs g) {
 // Within a block, position p of a row holds chunk p ^ swz8(row), so the 16-byte fragment reads of 16 consecutive
 // rows hit distinct banks. Rows past the end of an operand are clamped to its last row (their outputs are never
 // stored), so every access stays inside the caller's buffers.
-// MX scales: one 16-byte lane per row covers SG = 8 stages (16 blocks); the groups are double-buffered and a group's
-// copies are issued four trips before its first stage is read.
+// MX scales: on the FP8 instruction's path a group covers SGM = 16 stages, 32 scale bytes per row, copied as two
+// 16-byte halves by a pair of lanes (32 rows per copy instruction, so each instruction touches half as many rows'
+// cache lines as one 16-byte lane per row would); the exact path and token groups keep groups of SG = 8 stages, one
+// 16-byte lane per row. The groups are double-buffered and a group's copies are issued four trips before its first
+// stage is read.
 // Tile order: each XCD (which receives every eighth workgroup) walks a contiguous run of a grouped-M order, so its
 // resident workgroups share A and B tiles in its L2. Row groups take their tiles group by group; token groups run
 // expert-major in launch order (see the token-group notes in the kernel).
 constexpr int TB = 256;
 constexpr int KS = 64;
 constexpr int SG = 8;
+constexpr int SGM = 16;
 constexpr int GROUP_M2 = 4;
 constexpr int64_t kXcdChunk = 32;   // CUs per XCD: the workgroups of the large-tile kernel one XCD holds at once
 // Issue slot (of the 16 matrix instructions of a stage) after which each of a trip's 8 copy instructions goes.
@@ -469,9 +473,10 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
     static_assert(!TOK || (MX && MF == 2), "token-grouped contractions are MX on the exact path");
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][2 * TB * KS];
     __shared__ __attribute__((aligned(16))) uint8_t sB[2][2 * TB * KS];
-    // MX scales, double-buffered by group of SG stages (16 blocks per row). Rows: [row][4 words]. Token groups:
+    // MX scales, double-buffered by group of SGX stages (2 blocks per stage). Rows: [row][SCW words]. Token groups:
     // [word][row], 5 words from the 4-byte-aligned address at or below the row's first scale byte of the group.
-    constexpr int SCW = TOK ? 5 : 4;
+    constexpr int SGX = (TOK || MF == 2) ? SG : SGM;
+    constexpr int SCW = TOK ? 5 : SGX / 2;
     __shared__ __attribute__((aligned(16))) uint32_t sSA[2][MX ? TB * SCW : 1];
     __shared__ __attribute__((aligned(16))) uint32_t sSB[2][MX ? TB * SCW : 1];
 
@@ -581,6 +586,7 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
     }
     v4i rSA = rA, rSB = rB;
     int sa_off = 0, sb_off = 0;
+    int sa_off2[2] = {0, 0}, sb_off2[2] = {0, 0};
     if constexpr (TOK) {
         // Scale bytes of row r for the expert start at byte r * lds + k0 / 32 of the grid (any alignment). Each lane
         // copies 4-byte words from the aligned address at or below it; a word holding a byte of the grid lies in
@@ -592,6 +598,18 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
         rSB = buffer_rsrc(g.sb, (uint32_t)((g.N * g.ldsb + 3) & ~int64_t(3)));
         sa_off = (int)(((m0 + ar) * g.ldsa + k0 / 32) & ~int64_t(3));
         sb_off = (int)(((n0 + br) * g.ldsb + k0 / 32) & ~int64_t(3));
+    } else if constexpr (MX && SGX == SGM) {
+        // copy k (0, 1) of a wave: rows 32 (2 wave + k) + lane / 2, bytes 16 (lane % 2) .. + 15 of the row's group
+        rSA = buffer_rsrc(g.sa + m0 * g.ldsa);
+        rSB = buffer_rsrc(Bs + n0 * g.ldsb);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int row = 32 * (2 * wave + k) + (lane >> 1);
+            const int ar = (m0 + row < m_end) ? row : (int)(m_end - 1 - m0);
+            const int br = (n0 + row < n_end) ? row : (int)(n_end - 1 - n0);
+            sa_off2[k] = ar * (int)g.ldsa + 16 * (lane & 1);
+            sb_off2[k] = br * (int)g.ldsb + 16 * (lane & 1);
+        }
     } else if constexpr (MX) {
         const int row = 64 * wave + lane;
         const int ar = (m0 + row < m_end) ? row : (int)(m_end - 1 - m0);
@@ -634,7 +652,7 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
             dma_to_lds<16>(IS_A ? rA : rB, lds, IS_A ? a_off[c] : b_off[c], s0 * KS);
     };
     auto copy_scales = [&](int s) {                       // the scale group whose first stage is s
-        const int gb = (s / SG) & 1;
+        const int gb = (s / SGX) & 1;
         if constexpr (TOK) {
 #pragma unroll
             for (int w = 0; w < 5; ++w) {
@@ -642,11 +660,23 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
                 dma_to_lds<4>(rSB, lds_offset(&sSB[gb][TB * w + 64 * wave]), sb_off, s * KS / 32 + 4 * w);
             }
         } else {
-            dma_to_lds<16>(rSA, lds_offset(&sSA[gb][256 * wave]), sa_off, s * KS / 32);
-            dma_to_lds<16>(rSB, lds_offset(&sSB[gb][256 * wave]), sb_off, s * KS / 32);
+            if constexpr (SGX == SGM) {
+                // a half whose 8 stages lie past K is not read (K is a whole number of 8-stage halves)
+                const bool half_in = s + 8 * (lane & 1) < nk;
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    if (half_in) {
+                        dma_to_lds<16>(rSA, lds_offset(&sSA[gb][32 * (2 * wave + k) * SCW]), sa_off2[k], s * KS / 32);
+                        dma_to_lds<16>(rSB, lds_offset(&sSB[gb][32 * (2 * wave + k) * SCW]), sb_off2[k], s * KS / 32);
+                    }
+                }
+            } else {
+                dma_to_lds<16>(rSA, lds_offset(&sSA[gb][256 * wave]), sa_off, s * KS / 32);
+                dma_to_lds<16>(rSB, lds_offset(&sSB[gb][256 * wave]), sb_off, s * KS / 32);
+            }
         }
     };
-    constexpr int kScaleCopies = TOK ? 10 : 2;
+    constexpr int kScaleCopies = TOK ? 10 : (SGX == SGM ? 4 : 2);
     // Copy instruction c of trip t: the pair starting at stage t + 3 (A on odd t, B on even t), if any. PH = t % 4 when
     // known at compile time (then the pair exists in full), else -1.
     auto trip_copy = [&](auto ph_c, int t, int c) {
@@ -664,7 +694,7 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
     auto trip_scales = [&](int t) -> bool {
         if constexpr (MX) {
             const int s = t + 4;
-            if (s % SG == 0 && s < nk) { copy_scales(s); return true; }
+            if (s % SGX == 0 && s < nk) { copy_scales(s); return true; }
         }
         return false;
     };
@@ -678,7 +708,7 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
     // ------------------------------------------------------------------ fragments
     // 32 x 32 x 64 operand of lane l: row l % 32, global chunks g and 2 + g of the 64-byte stage row (g = l / 32),
     // i.e. k = 16g .. 16g+15 and 32+16g .. 32+16g+15. Its scale operand is the scale of (row, block g), stage word
-    // (st % SG) / 2, byte 2 (st % 2) + g.
+    // (st % SGX) / 2, byte 2 (st % 2) + g.
     const int fr = lane & 31, fg = lane >> 5;
     const int fsw = swz8(fr);                  // rows wm*128 + 32j + fr share bits 2..3 with fr
     const int frow = (fr >> 3) * 1024 + (fr & 7) * KS;   // lane's row within its 32-row group (block, row in block)
@@ -703,9 +733,9 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
     auto read_scales = [&](int st, uint32_t* sa, uint32_t* sb) {
         if constexpr (TOK) {
             // word w of the group = bytes 4w .. 4w+3 after the row's shift
-            const uint32_t* cSA = sSA[(st / SG) & 1];
-            const uint32_t* cSB = sSB[(st / SG) & 1];
-            const int w = (st % SG) >> 1;
+            const uint32_t* cSA = sSA[(st / SGX) & 1];
+            const uint32_t* cSB = sSB[(st / SGX) & 1];
+            const int w = (st % SGX) >> 1;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = wm * 128 + 32 * j + fr;
@@ -717,13 +747,13 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
                 sb[i] = __builtin_amdgcn_alignbyte(cSB[TB * (w + 1) + row], cSB[TB * w + row], shifts >> (8 + 2 * i));
             }
         } else if constexpr (MX) {
-            const uint32_t* cSA = sSA[(st / SG) & 1];
-            const uint32_t* cSB = sSB[(st / SG) & 1];
-            const int w = (st % SG) >> 1;
+            const uint32_t* cSA = sSA[(st / SGX) & 1];
+            const uint32_t* cSB = sSB[(st / SGX) & 1];
+            const int w = (st % SGX) >> 1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sa[j] = cSA[(wm * 128 + 32 * j + fr) * 4 + w];
+            for (int j = 0; j < 4; ++j) sa[j] = cSA[(wm * 128 + 32 * j + fr) * SCW + w];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sb[i] = cSB[(wn * 128 + 32 * i + fr) * 4 + w];
+            for (int i = 0; i < 4; ++i) sb[i] = cSB[(wn * 128 + 32 * i + fr) * SCW + w];
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) { sa[j] = 0x7F7F7F7Fu; sb[j] = 0x7F7F7F7Fu; }
@@ -877,10 +907,10 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
     // scale_op, so no wait for these reads sits between matrix instructions): MX rows word w of the group in
     // ra[j] / rb[i]; token groups words w and w + 1 in [j] and [4 + j]; per-tensor unit scales.
     auto scale_words = [&](int st, uint32_t* ra, uint32_t* rb) {
-        const int w = (st % SG) >> 1;
+        const int w = (st % SGX) >> 1;
         if constexpr (TOK) {
-            const uint32_t* cSA = sSA[(st / SG) & 1];
-            const uint32_t* cSB = sSB[(st / SG) & 1];
+            const uint32_t* cSA = sSA[(st / SGX) & 1];
+            const uint32_t* cSB = sSB[(st / SGX) & 1];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = wm * 128 + 32 * j + fr;
@@ -894,12 +924,12 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
                 rb[4 + i] = cSB[TB * (w + 1) + row];
             }
         } else if constexpr (MX) {
-            const uint32_t* cSA = sSA[(st / SG) & 1];
-            const uint32_t* cSB = sSB[(st / SG) & 1];
+            const uint32_t* cSA = sSA[(st / SGX) & 1];
+            const uint32_t* cSB = sSB[(st / SGX) & 1];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ra[j] = cSA[(wm * 128 + 32 * j + fr) * 4 + w];
+            for (int j = 0; j < 4; ++j) ra[j] = cSA[(wm * 128 + 32 * j + fr) * SCW + w];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rb[i] = cSB[(wn * 128 + 32 * i + fr) * 4 + w];
+            for (int i = 0; i < 4; ++i) rb[i] = cSB[(wn * 128 + 32 * i + fr) * SCW + w];
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) { ra[j] = 0x7F7F7F7Fu; rb[j] = 0x7F7F7F7Fu; }
@@ -1118,14 +1148,16 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
         if constexpr (MF == 1) {
             // FP8 path: 16 issue slots, each one matrix instruction; the 16 fragment reads of stage kt + 1 go two per
             // slot in the first 8 slots and (MX) its 8 scale reads two per slot in the next 4, so they have returned
-            // well before the wait that ends the trip; the trip's 8 copy instructions go in the slots kCopySlot names.
-            // Spreading the copies keeps a wave that finds the memory queue full from stalling its matrix
-            // instructions behind a burst of copy issues. The scheduling barriers keep the slots in this order.
+            // well before the wait that ends the trip; the trip's 8 copy instructions go in the slots kCopySlot names,
+            // and a scale group's copies (every SGM trips) after slot 7, not at the end of the trip where a stall on
+            // them would hold the wave back from the barrier. Spreading the copies keeps a wave that finds the memory
+            // queue full from stalling its matrix instructions behind a burst of copy issues. The scheduling barriers
+            // keep the slots in this order.
             const int odd = PH < 0 ? (kt & 1) : (PH & 1);
             const int sh = 8 * (2 * odd + fg);
-            const uint32_t* cSA = sSA[((kt + 1) / SG) & 1];
-            const uint32_t* cSB = sSB[((kt + 1) / SG) & 1];
-            const int sw = ((kt + 1) % SG) >> 1;
+            const uint32_t* cSA = sSA[((kt + 1) / SGX) & 1];
+            const uint32_t* cSB = sSB[((kt + 1) / SGX) & 1];
+            const int sw = ((kt + 1) % SGX) >> 1;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int i = q >> 2, j = q & 3;
@@ -1156,8 +1188,8 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
                     } else if (q >= 8 && q < 12) {
 #pragma unroll
                         for (int e = 2 * (q - 8); e < 2 * (q - 8) + 2; ++e) {
-                            if (e < 4) nsa[e] = cSA[(wm * 128 + 32 * e + fr) * 4 + sw];
-                            else nsb[e - 4] = cSB[(wn * 128 + 32 * (e - 4) + fr) * 4 + sw];
+                            if (e < 4) nsa[e] = cSA[(wm * 128 + 32 * e + fr) * SCW + sw];
+                            else nsb[e - 4] = cSB[(wn * 128 + 32 * (e - 4) + fr) * SCW + sw];
                         }
                     }
                 } else if (q == 0) {
@@ -1167,7 +1199,7 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
 #pragma unroll
                 for (int c = 0; c < 8; ++c)
                     if (q == kCopySlot[c]) trip_copy(ph_c, kt, c);
-                if (q == 15) scales = trip_scales(kt);
+                if (q == 7) scales = trip_scales(kt);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
@@ -1458,7 +1490,8 @@ __global__ __launch_bounds__(256) void gate_broadcast_kernel(const uint32_t* __r
 // Large tiles when K is a whole number of 64-byte stages, the output spans at least a few tiles, and a tile's
 // 256 rows stay below 2^31 bytes (the kernel's 32-bit buffer offsets). Its copies move 16-byte pieces, so operand row
 // strides (and, for row groups, the distance between experts) are multiples of 16 bytes. MX operands also need K to
-// be a whole number of scale groups (SG stages, 16 scale bytes per row) and 16-byte scale rows.
+// be a whole number of 16-byte scale pieces (SG stages, 16 scale bytes per row; a group copies two) and 16-byte scale
+// rows.
 static bool use_big(const GemmArgs& a, bool mx, bool grouped) {
     constexpr int64_t kLim = int64_t(1) << 23;                  // 256 rows x stride < 2^31
     if (a.K % (mx ? KS * SG : KS) != 0 || a.M < 512 || a.N < 512 || a.K > (int64_t(1) << 22)) return false;
