@@ -130,6 +130,11 @@ def main():
     dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     dW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     ws_pt = torch.empty(mxq.workspace_bytes("pertensor", N * K), dtype=torch.uint8, device=dev)
+    f32 = lambda: torch.empty(1, dtype=torch.float32, device=dev)  # noqa: E731
+    # per-tensor casts' codes (q, q^T) and scalars; the delayed casts reuse them once the per-tensor GEMMs have run
+    pt_out = {"X": mxq.PerTensorFP8(u8(M, K), u8(K, M), f32(), f32()),
+              "W": mxq.PerTensorFP8(u8(N, K), u8(K, N), f32(), f32()),
+              "dY": mxq.PerTensorFP8(u8(M, N), u8(N, M), f32(), f32())}
     # grouped: weights quantized once (cache), activations each step
     G, d_ff, d_model = wl4["w_up"].shape
     qwu = mxq.mx_quantize(wl4["w_up"].reshape(G * d_ff, d_model), colwise=False)
@@ -191,6 +196,8 @@ def main():
     others = 2.0 ** torch.arange(-3, 4, dtype=torch.float32, device=dev)
     gathered = torch.empty(8, dtype=torch.float32, device=dev)
     q_req = torch.empty(nw, dtype=torch.uint8, device=dev)
+    gc_out = mxq.AutoScaled(torch.empty((N, K), dtype=torch.uint8, device=dev), f32(),
+                            torch.empty(1, dtype=torch.int64, device=dev))
     torch.cuda.synchronize()
 
     Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -239,9 +246,9 @@ def main():
         with part("mx_gemm_dgrad_checked", rec):
             mxq.scaled_gemm(mxD.q_row, mxD.s_row, mxW.q_col, mxW.s_col, mxq.MX_BLOCK32, out=dX)
         with part("pt_quant", rec):
-            px = mxq.pertensor_quantize(X, mxq.E4M3, workspace=ws_pt)
-            pw = mxq.pertensor_quantize(W, mxq.E4M3, workspace=ws_pt)
-            pd = mxq.pertensor_quantize(dY, mxq.E5M2, workspace=ws_pt)
+            px = mxq.pertensor_quantize(X, mxq.E4M3, workspace=ws_pt, out=pt_out["X"])
+            pw = mxq.pertensor_quantize(W, mxq.E4M3, workspace=ws_pt, out=pt_out["W"])
+            pd = mxq.pertensor_quantize(dY, mxq.E5M2, workspace=ws_pt, out=pt_out["dY"])
         with part("pt_gemm_fwd", rec):
             mxq.scaled_gemm(px.q, px.scale, pw.q, pw.scale, mxq.PER_TENSOR, mxq.E4M3, mxq.E4M3, out=Y)
         with part("pt_gemm_dgrad", rec):
@@ -277,9 +284,9 @@ def main():
         with part("small_graph_queued", rec):
             small_graph.replay()
         with part("pt_quant_delayed", rec):
-            mxq.pertensor_quantize_delayed(X, hists["X"], hpos["X"], mxq.E4M3, workspace=ws_del)
-            mxq.pertensor_quantize_delayed(W, hists["W"], hpos["W"], mxq.E4M3, workspace=ws_del)
-            mxq.pertensor_quantize_delayed(dY, hists["dY"], hpos["dY"], mxq.E5M2, workspace=ws_del)
+            mxq.pertensor_quantize_delayed(X, hists["X"], hpos["X"], mxq.E4M3, workspace=ws_del, out=pt_out["X"])
+            mxq.pertensor_quantize_delayed(W, hists["W"], hpos["W"], mxq.E4M3, workspace=ws_del, out=pt_out["W"])
+            mxq.pertensor_quantize_delayed(dY, hists["dY"], hpos["dY"], mxq.E5M2, workspace=ws_del, out=pt_out["dY"])
         with part("adam_delayed", rec):
             mxq.fp8_adam_step_delayed(theta, grad, m_q, m_scale, v16, w16, hp, m_hist, m_pos, workspace=ws_adel)
         with part("wcache_fused", rec):
@@ -297,7 +304,7 @@ def main():
         with part("swiglu_quant", rec):
             mxq.swiglu_mx_quantize(C_gu, out=mx_h)
         with part("grad_cast", rec):
-            gc = mxq.fp8_autoscale_cast(dW, mu_g, mxq.E4M3, workspace=ws_g)
+            gc = mxq.fp8_autoscale_cast(dW, mu_g, mxq.E4M3, workspace=ws_g, out=gc_out)
         gathered[:1] = gc.scale
         gathered[1:] = others
         with part("grad_requant", rec):

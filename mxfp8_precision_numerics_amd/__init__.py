@@ -190,15 +190,32 @@ class PerTensorFP8(NamedTuple):
     scale: torch.Tensor             # float32[1] on the device (q ~ x * scale)
 
 
+def _pt_out(x: torch.Tensor, want_q: bool, want_qt: bool, out: Optional[PerTensorFP8]):
+    """Output buffers of a per-tensor cast: `out` checked against x's shape (its q / q_t, either may be None, decide
+    which orientations are written), else new ones."""
+    rows, cols = x.shape
+    dev = x.device
+    if out is None:
+        return (torch.empty((rows, cols), dtype=torch.uint8, device=dev) if want_q else None,
+                torch.empty((cols, rows), dtype=torch.uint8, device=dev) if want_qt else None,
+                torch.empty(1, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.float32, device=dev))
+    for t, shape, dt, name in ((out.q, (rows, cols), torch.uint8, "out.q"), (out.q_t, (cols, rows), torch.uint8, "out.q_t"),
+                               (out.amax, (1,), torch.float32, "out.amax"), (out.scale, (1,), torch.float32, "out.scale")):
+        if t is None and name in ("out.q", "out.q_t"):
+            continue
+        if t is None or tuple(t.shape) != shape or t.dtype != dt or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {shape} on {dev}")
+    return out.q, out.q_t, out.amax, out.scale
+
+
 def pertensor_quantize(x: torch.Tensor, fmt: int = E4M3, margin: float = 1.0, scale_in: Optional[torch.Tensor] = None,
-                       want_q: bool = True, want_qt: bool = True, workspace: Optional[torch.Tensor] = None) -> PerTensorFP8:
+                       want_q: bool = True, want_qt: bool = True, workspace: Optional[torch.Tensor] = None,
+                       out: Optional[PerTensorFP8] = None) -> PerTensorFP8:
+    """Per-tensor FP8 cast of x (bf16 [rows][cols]) to q and its transpose q_t. `out` reuses caller buffers."""
     _dev(x, torch.bfloat16, "x")
     rows, cols = x.shape
     dev = x.device
-    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev) if want_q else None
-    qt = torch.empty((cols, rows), dtype=torch.uint8, device=dev) if want_qt else None
-    amax = torch.empty(1, dtype=torch.float32, device=dev)
-    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    q, qt, amax, scale = _pt_out(x, want_q, want_qt, out)
     nbytes = workspace_bytes("pertensor", rows * cols)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -213,16 +230,14 @@ def pertensor_quantize(x: torch.Tensor, fmt: int = E4M3, margin: float = 1.0, sc
 
 def pertensor_quantize_delayed(x: torch.Tensor, amax_history: torch.Tensor, hist_pos: torch.Tensor, fmt: int = E4M3,
                                margin: float = 1.0, want_q: bool = True, want_qt: bool = True,
-                               workspace: Optional[torch.Tensor] = None) -> PerTensorFP8:
+                               workspace: Optional[torch.Tensor] = None,
+                               out: Optional[PerTensorFP8] = None) -> PerTensorFP8:
     """Delayed-scaling cast: scale from the amax history (float32[H], updated in place with this call's amax at
-    hist_pos, an int32[1] that advances)."""
+    hist_pos, an int32[1] that advances). `out` reuses caller buffers."""
     _dev(x, torch.bfloat16, "x"); _dev(amax_history, torch.float32, "amax_history"); _dev(hist_pos, torch.int32, "hist_pos")
     rows, cols = x.shape
     dev = x.device
-    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev) if want_q else None
-    qt = torch.empty((cols, rows), dtype=torch.uint8, device=dev) if want_qt else None
-    amax = torch.empty(1, dtype=torch.float32, device=dev)
-    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    q, qt, amax, scale = _pt_out(x, want_q, want_qt, out)
     if workspace is None:
         workspace = torch.empty(workspace_bytes("pertensor_delayed", rows * cols), dtype=torch.uint8, device=dev)
     st = _lib.load().fp8_quantize_pertensor_delayed(_ptr(x), rows, cols, fmt, C.c_float(margin), _ptr(amax_history),
@@ -386,14 +401,22 @@ class AutoScaled(NamedTuple):
 
 
 def fp8_autoscale_cast(g: torch.Tensor, mu: torch.Tensor, fmt: int = E4M3,
-                       workspace: Optional[torch.Tensor] = None) -> AutoScaled:
-    """q = FP8(mu * g); mu (float32[1], device) is updated in place for the next step."""
+                       workspace: Optional[torch.Tensor] = None, out: Optional[AutoScaled] = None) -> AutoScaled:
+    """q = FP8(mu * g); mu (float32[1], device) is updated in place for the next step. `out` reuses caller buffers
+    (q uint8 of g's shape, scale float32[1], overflow int64[1])."""
     _dev(g, torch.bfloat16, "g"); _dev(mu, torch.float32, "mu")
     dev = g.device
     n = g.numel()
-    q = torch.empty(g.shape, dtype=torch.uint8, device=dev)
-    scale = torch.empty(1, dtype=torch.float32, device=dev)
-    overflow = torch.empty(1, dtype=torch.int64, device=dev)
+    if out is None:
+        q = torch.empty(g.shape, dtype=torch.uint8, device=dev)
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+        overflow = torch.empty(1, dtype=torch.int64, device=dev)
+    else:
+        q, scale, overflow = out.q, out.scale, out.overflow
+        for t, shape, dt, name in ((q, tuple(g.shape), torch.uint8, "out.q"), (scale, (1,), torch.float32, "out.scale"),
+                                   (overflow, (1,), torch.int64, "out.overflow")):
+            if tuple(t.shape) != shape or t.dtype != dt or t.device != dev or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {shape} on {dev}")
     if workspace is None:
         workspace = torch.empty(workspace_bytes("autoscale", n), dtype=torch.uint8, device=dev)
     st = _lib.load().fp8_autoscale_cast(_ptr(g), n, fmt, _ptr(mu), _ptr(q), _ptr(scale), _ptr(overflow),
