@@ -871,10 +871,16 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
     if (nk > 2) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) copy_pair(std::true_type{}, std::false_type{}, 1, 2, c);   // A (2, 3)
-        wait_copies_barrier<8>();                               // stages 0 and 1 have landed
-    } else {
-        wait_copies_barrier<0>();
     }
+    // The zeroed accumulators are written here, while the first stages are in flight, rather than after the wait
+    // (where the compiler would otherwise put their 256 register writes, just before the first matrix instruction).
+    // The statement reads and rewrites each one, so the sixteen zero blocks stay distinct registers.
+    asm volatile("" : "+a"(acc16[0][0]), "+a"(acc16[0][1]), "+a"(acc16[0][2]), "+a"(acc16[0][3]),
+                      "+a"(acc16[1][0]), "+a"(acc16[1][1]), "+a"(acc16[1][2]), "+a"(acc16[1][3]),
+                      "+a"(acc16[2][0]), "+a"(acc16[2][1]), "+a"(acc16[2][2]), "+a"(acc16[2][3]),
+                      "+a"(acc16[3][0]), "+a"(acc16[3][1]), "+a"(acc16[3][2]), "+a"(acc16[3][3]));
+    if (nk > 2) wait_copies_barrier<8>();                       // stages 0 and 1 have landed
+    else wait_copies_barrier<0>();
     if constexpr (MF == 2) {
     // Exact path, pipelined over the stage's four 16-value k-steps. k-step s takes bytes 8s .. 8s+7 of each lane's
     // 32 (steps 0, 1 lie in the stage's first 32-block, 2, 3 in its second). While k-step s's 16 matrix instructions
@@ -1266,7 +1272,11 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
     // Lane l holds, for output row m (l % 32), the columns 8q + 4g + 0..3 (g = l / 32) of each 32-column block in
     // accumulator registers 4q .. 4q+3. After rounding to bf16 pairs, swapping register sets q = 2p + 1 of the lower
     // half-wave with q = 2p of the upper (v_permlane32_swap) leaves lane l with the 8 consecutive columns
-    // 16p + 8g .. 16p + 8g + 7, stored as one 16-byte write.
+    // 16p + 8g .. 16p + 8g + 7 (p = 0, 1) of its row. A second swap between 16-lane rows (v_permlane16_swap: lanes
+    // l and l + 16 of each half-wave trade lane l's p = 1 set for lane l + 16's p = 0 set) leaves lane l with
+    // columns 16h + 8g .. + 7 (h = (l / 16) % 2) of rows r and 16 + r (r = l % 16). Each 16-byte store then writes 64
+    // contiguous bytes into each of 16 rows, rather than 32 bytes into each of 32, which halves the partial-line
+    // write requests per store.
     float post = 1.0f;
     if constexpr (!MX) post = 1.0f / (g.pa[0] * g.pb[0]);
     if constexpr (TOK) {
@@ -1353,13 +1363,21 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
                     w[2 * pq][h] = r[0];
                     w[2 * pq + 1][h] = r[1];
                 }
-            const int64_t m = m0 + wm * 128 + j * 32 + fr;
-            if (m >= m_end) continue;
+            // d[p]: columns 16p + 8g .. + 7 of row fr; after the swap d[rh]: columns 16h + 8g .. + 7 of row 16rh + r
+            uint32_t d[2][4] = {{w[0][0], w[0][1], w[1][0], w[1][1]}, {w[2][0], w[2][1], w[3][0], w[3][1]}};
 #pragma unroll
-            for (int pq = 0; pq < 2; ++pq) {
-                const int64_t n = n0 + wn * 128 + i * 32 + 16 * pq + 8 * fg;
+            for (int e = 0; e < 4; ++e) {
+                const auto r = __builtin_amdgcn_permlane16_swap(d[0][e], d[1][e], false, false);
+                d[0][e] = r[0];
+                d[1][e] = r[1];
+            }
+#pragma unroll
+            for (int rh = 0; rh < 2; ++rh) {
+                const int64_t m = m0 + wm * 128 + j * 32 + 16 * rh + (fr & 15);
+                if (m >= m_end) continue;
+                const int64_t n = n0 + wn * 128 + i * 32 + 16 * ((lane >> 4) & 1) + 8 * fg;
                 uint16_t* dst = Cb + m * g.ldc + n;
-                const uint32_t v4[4] = {w[2 * pq][0], w[2 * pq][1], w[2 * pq + 1][0], w[2 * pq + 1][1]};
+                const uint32_t* v4 = d[rh];
                 if (vec_ok && n + 8 <= n_end) {
                     *reinterpret_cast<uint4*>(dst) = make_uint4(v4[0], v4[1], v4[2], v4[3]);
                 } else {
