@@ -38,7 +38,10 @@ def _mx_operands(A_bf16, B_bf16_nk):
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (200, 136, 96), (130, 260, 160), (1, 1, 32), (64, 512, 2048),
                                    (384, 128, 1024), (33, 47, 224),
                                    # large-tile kernel (M, N >= 512, K % 128 == 0): exact path, then the FP8 path
-                                   (640, 776, 1024), (520, 1030, 12288)])
+                                   (640, 776, 1024), (520, 1030, 12288),
+                                   # last tile of 17 rows (a 16-row half of a store block with one row in range)
+                                   # and 24 columns, on both paths
+                                   (529, 536, 1024), (529, 536, 12288)])
 def test_mx_gemm_all_elements(M, N, K):
     need_gpu()
     say("mx gemm", M, N, K)
@@ -86,7 +89,7 @@ def test_gemm_exact_special_cases():
 
 
 @pytest.mark.parametrize("fa,fb", [(mxq.E4M3, mxq.E4M3), (mxq.E5M2, mxq.E4M3), (mxq.E4M3, mxq.E5M2), (mxq.E5M2, mxq.E5M2)])
-@pytest.mark.parametrize("M,N,K", [(256, 384, 512), (77, 129, 96), (544, 520, 12288)])
+@pytest.mark.parametrize("M,N,K", [(256, 384, 512), (77, 129, 96), (544, 520, 12288), (529, 536, 1024)])
 def test_pertensor_gemm_all_elements(fa, fb, M, N, K):
     need_gpu()
     say("per-tensor gemm", fa, fb, M, N, K)
