@@ -1285,33 +1285,59 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, const int bid_i
             const bool vec_f = (g.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(Cf) & 15) == 0;
             if (vec_f && m_end - m0 == TB && n_end - n0 == TB) {
                 // whole tile, one column block i at a time: block i + 1's 16 loads are in flight while block i is
-                // added and stored
-                auto sink_ptr = [&](int i, int j, int q) {
-                    return Cf + (m0 + wm * 128 + j * 32 + fr) * g.ldc + n0 + wn * 128 + i * 32 + 8 * q + 4 * fg;
+                // added and stored. Lanes l and l + 16 of each half-wave trade register sets (v_permlane16_swap) so
+                // that lane l holds columns 16 h2 + 4 (2 h + g) .. + 3 (h = (l / 16) % 2) of rows r and 16 + r
+                // (r = l % 16): each 16-byte access then covers 64 contiguous bytes in each of 16 rows rather than
+                // 32 bytes in each of 32.
+                const int hk = 2 * ((lane >> 4) & 1) + fg;
+                // accumulators permuted in place first: register set 4q .. 4q + 3 holds columns 8q + 4g .. + 3 of
+                // row fr; after the swap set 2 h2 + rh holds columns 16 h2 + 4 hk .. + 3 of row 16 rh + r
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const auto r = __builtin_amdgcn_permlane16_swap(
+                                    __float_as_uint(acc16[i][j][8 * h2 + e]), __float_as_uint(acc16[i][j][8 * h2 + 4 + e]),
+                                    false, false);
+                                acc16[i][j][8 * h2 + e] = __uint_as_float(r[0]);
+                                acc16[i][j][8 * h2 + 4 + e] = __uint_as_float(r[1]);
+                            }
+                auto sink_ptr = [&](int i, int j, int rh, int h2) {
+                    return Cf + (m0 + wm * 128 + j * 32 + 16 * rh + (fr & 15)) * g.ldc + n0 + wn * 128 + i * 32 +
+                           16 * h2 + 4 * hk;
                 };
-                float4 o[2][4][4];
+                float4 o[2][4][4];                             // [buffer][j][2 rh + h2]
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) o[0][j][q] = *reinterpret_cast<const float4*>(sink_ptr(0, j, q));
+                    for (int x = 0; x < 4; ++x)
+                        o[0][j][x] = *reinterpret_cast<const float4*>(sink_ptr(0, j, x >> 1, x & 1));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (i + 1 < 4) {
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
 #pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                o[(i + 1) & 1][j][q] = *reinterpret_cast<const float4*>(sink_ptr(i + 1, j, q));
+                            for (int x = 0; x < 4; ++x)
+                                o[(i + 1) & 1][j][x] =
+                                    *reinterpret_cast<const float4*>(sink_ptr(i + 1, j, x >> 1, x & 1));
                     }
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float4 v = o[i & 1][j][q];
-                            *reinterpret_cast<float4*>(sink_ptr(i, j, q)) =
-                                make_float4(v.x + acc16[i][j][4 * q], v.y + acc16[i][j][4 * q + 1],
-                                            v.z + acc16[i][j][4 * q + 2], v.w + acc16[i][j][4 * q + 3]);
-                        }
+                        for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+                            for (int h2 = 0; h2 < 2; ++h2) {
+                                const float4 s = o[i & 1][j][2 * rh + h2];
+                                const int x = 4 * (2 * h2 + rh);
+                                *reinterpret_cast<float4*>(sink_ptr(i, j, rh, h2)) =
+                                    make_float4(s.x + acc16[i][j][x], s.y + acc16[i][j][x + 1],
+                                                s.z + acc16[i][j][x + 2], s.w + acc16[i][j][x + 3]);
+                            }
                 }
                 return;
             }
